@@ -1,0 +1,31 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def pytest_runtest_setup(item):
+    # Name the case before it runs, so a GPU run that ends abruptly still says
+    # which test was on the device.
+    if item.get_closest_marker("gpu") is not None:
+        print(f"\n[gpu-case] {item.nodeid}", flush=True)
+
+
+@pytest.fixture
+def golden():
+    import json
+
+    def load(name):
+        with open(os.path.join(GOLDEN, name)) as f:
+            return json.load(f)
+    return load
