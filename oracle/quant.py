@@ -18,7 +18,7 @@ What the pages fix, and the reading taken where they leave it open:
   by the STORED scale, so dequantization uses exactly the value quantization
   used; round() is round-half-to-even; codes are clamped to [-127, 127].
 * Asymmetric INT4 (report section 3.2, "非对称"): reading: a float offset z
-  (fp16, the group minimum rounded toward -inf) and an fp16 scale
+  (fp16, the group minimum rounded toward -inf, a zero stored as +0) and an fp16 scale
   s = (max - z) / 15; codes = clamp(rne((x - z) / s), 0, 15); x_hat = q*s + z.
   Two codes per byte, the even channel in the low nibble.
 
@@ -67,6 +67,9 @@ def fp16_round_down(v):
     too_big = h.astype(np.float32) > v
     h = np.where(too_big, np.nextafter(h, np.float16(-np.inf)), h).astype(np.float16)
     h = np.where(np.isneginf(h), np.float16(-F16_MAX), h).astype(np.float16)
+    # a zero-point of zero is stored as +0 (the sign of a zero minimum is not
+    # well defined when a group holds both +0 and -0)
+    h = np.where(h == 0, np.float16(0.0), h).astype(np.float16)
     return h
 
 

@@ -266,3 +266,12 @@ def test_int4_zero_point_rounds_down(golden):
     assert int(z.view(np.uint16)[0]) == g["zero_bits"]
     # the scale here is an fp16 subnormal, where the s/2 error bound does not hold
     assert float(s[0]) < 2.0 ** -14
+
+
+def test_zero_point_of_negative_zero_is_positive_zero():
+    x = np.array([-0.0] + [0.0] * 15, np.float32)
+    q, s, z = Q.quantize_asym_int4(x, 16)
+    assert int(z.view(np.uint16)[0]) == 0
+    x = np.array([-0.0] + [1.0] * 15, np.float32)
+    q, s, z = Q.quantize_asym_int4(x, 16)
+    assert int(z.view(np.uint16)[0]) == 0
