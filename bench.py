@@ -1,0 +1,332 @@
+#!/usr/bin/env python3
+"""Absorbed MLA decode on one MI355X: KV-tokens/s and achieved HBM GB/s.
+
+A step is one decode step of the whole hot path over every layer of the
+workload: quantize-on-append of one new token per sequence, then absorbed
+decode attention (absorb through W_UK, split-KV partial attention over the
+quantized cache, merge and W_UV projection), all through libmla_kv.so.
+
+Default workload: DeepSeek-V2-Lite-shaped, 27 layers, 16 heads, batch 64,
+ragged lengths uniform in [1024, 16384], INT8 latent + INT8 k_pe cache. The
+INT4 workload (1 layer, batch 32, 16 heads, 32768 tokens, asymmetric INT4)
+is measured in the same run and reported under "int4".
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "absorbed MLA decode KV-tokens/s and achieved HBM GB/s (% peak), INT8 & INT4"
+KERNEL_SRC = os.path.join(ROOT, "mla_latent_kv_cache_amd", "csrc", "mla_kv.hip")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def row_bytes(fmt):
+    from oracle import accounting  # byte arithmetic only
+    return accounting.cache_row_bytes(fmt)
+
+
+# ----------------------------------------------------------------- GPU side
+
+class Runner:
+    """Holds one workload's cache, weights, queries and the ctypes calls of a step."""
+
+    def __init__(self, wid, extra_steps):
+        import torch
+        from mla_latent_kv_cache_amd import LatentCache, _lib
+        from mla_latent_kv_cache_amd import workloads as W
+        self.torch = torch
+        self.W = W
+        self.wid = wid
+        self.w = w = W.WORKLOADS[wid]
+        self.lens0 = W.lengths(wid)
+        ragged = isinstance(w.seq, tuple)
+        cap = int(self.lens0.max()) + w.append + extra_steps
+        cap = (cap + 15) // 16 * 16
+        dev = torch.device("cuda:0")
+        t0 = time.time()
+        self.cache = cache = LatentCache(w.fmt, w.layers, w.batch, cap, device=dev)
+        for layer in range(w.layers):
+            ckv, kpe = W.latent_batch(wid, layer, int(self.lens0.max()), device=dev,
+                                      counts=self.lens0 if ragged else None)
+            cache.append(layer, ckv, kpe, n_new=self.lens0 if ragged else None)
+            del ckv, kpe
+        torch.cuda.synchronize()
+        log(f"{w.name}: prefilled {int(self.lens0.sum()) * w.layers} tokens "
+            f"({cache.bytes() / 1e9:.2f} GB of cache planes) in {time.time() - t0:.1f}s")
+        self.H = w.heads
+        self.splits = w.num_splits
+        self.q = [W.queries(wid, layer, dev) for layer in range(w.layers)]
+        self.wts = [W.weights(wid, layer, dev) for layer in range(w.layers)]
+        steps_new = [W.latent_batch(wid, layer, extra_steps, device=dev, kind="step")
+                     for layer in range(w.layers)]
+        self.new = [[(steps_new[l][0][:, i:i + 1].contiguous(), steps_new[l][1][:, i:i + 1].contiguous())
+                     for l in range(w.layers)] for i in range(extra_steps)]
+        self.ws = cache.workspace(self.H, self.splits)
+        self.out = torch.empty((w.batch, self.H, 128), dtype=torch.float32, device=dev)
+        self.lib = _lib.lib()
+        self.check = _lib.check
+        self.stream = torch.cuda.current_stream()
+        self.sp = ctypes.c_void_p(self.stream.cuda_stream)
+        self.cref = ctypes.byref(cache.struct)
+        self.scale = ctypes.c_float(W.SOFTMAX_SCALE)
+        vp = lambda t: ctypes.c_void_p(t.data_ptr())
+        self.args_q = [(vp(qn), vp(qp)) for qn, qp in self.q]
+        self.args_w = [(vp(wuk), vp(wuv)) for wuk, wuv in self.wts]
+        self.args_new = [[(vp(c), vp(k)) for c, k in step] for step in self.new]
+        self.ws_p, self.ws_n = vp(self.ws), ctypes.c_size_t(self.ws.numel())
+        self.out_p = vp(self.out)
+        self.steps_done = 0
+        self.ns = cache.auto_splits(self.H) if self.splits == 0 else self.splits
+
+    def step(self, events=None):
+        """One decode step over every layer. events: list to append (start, end) pairs
+        recorded around each partial-attention launch."""
+        L = self.lib
+        i = self.steps_done
+        for layer in range(self.w.layers):
+            c, k = self.args_new[i][layer]
+            st = L.mla_cache_append(self.cref, layer, c, k, 1, None, self.sp)
+            if st:
+                self.check(st, "append")
+            qn, qp = self.args_q[layer]
+            wuk, wuv = self.args_w[layer]
+            st = L.mla_decode_absorb(self.cref, qn, qp, wuk, self.H, self.scale, self.splits, self.ws_p,
+                                     self.ws_n, self.sp)
+            if st:
+                self.check(st, "absorb")
+            if events is not None:
+                e0 = self.torch.cuda.Event(enable_timing=True)
+                e1 = self.torch.cuda.Event(enable_timing=True)
+                e0.record(self.stream)
+            st = L.mla_decode_partial(self.cref, layer, self.H, self.splits, self.ws_p, self.ws_n, self.sp)
+            if st:
+                self.check(st, "partial")
+            if events is not None:
+                e1.record(self.stream)
+                events.append((e0, e1, layer))
+            st = L.mla_decode_combine(self.cref, wuv, self.H, self.splits, self.ws_p, self.ws_n,
+                                      self.out_p, self.sp)
+            if st:
+                self.check(st, "combine")
+        self.cache._lens += 1  # host mirror: one token per sequence per layer
+        self.steps_done += 1
+
+    def kv_tokens(self, step_index):
+        """Tokens attended in the given step (1-based count of appended tokens)."""
+        return int(self.w.layers * (self.lens0 + step_index).sum())
+
+    def layer_tokens(self, step_index):
+        return int((self.lens0 + step_index).sum())
+
+    def algorithmic_bytes(self, step_index):
+        """Bytes the method must move in one step (per-token cache rows, the
+        weights, the queries, the output and the appended rows)."""
+        w = self.w
+        cache = self.kv_tokens(step_index) * row_bytes(w.fmt)
+        weights = w.layers * 2 * w.heads * 128 * 512 * 2
+        queries = w.layers * w.batch * w.heads * 192 * 2
+        output = w.layers * w.batch * w.heads * 128 * 4
+        append = w.layers * w.batch * (1152 + row_bytes(w.fmt))
+        return cache + weights + queries + output + append
+
+
+def measure(wid, steps, warmup):
+    import torch
+    r = Runner(wid, steps + warmup)
+    for _ in range(warmup):
+        r.step()
+    torch.cuda.synchronize()
+    log(f"{r.w.name}: warmup done ({warmup} steps); timing {steps} steps")
+    events = []
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(r.stream)
+    for _ in range(steps):
+        r.step(events)
+    t_end.record(r.stream)
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end)
+    first = warmup + 1
+    kv = sum(r.kv_tokens(first + i) for i in range(steps))
+    algo = sum(r.algorithmic_bytes(first + i) for i in range(steps))
+    part_ms = [e0.elapsed_time(e1) for e0, e1, _ in events]
+    # algorithmic bytes of each partial launch: the cache rows it attends
+    part_bytes = []
+    for i in range(steps):
+        per_launch = r.layer_tokens(first + i) * row_bytes(r.w.fmt)
+        part_bytes += [per_launch] * r.w.layers
+    avg_ms = float(np.mean(part_ms))
+    avg_bytes = float(np.mean(part_bytes))
+    res = {
+        "workload": r.w.name, "fmt": r.w.fmt, "layers": r.w.layers, "batch": r.w.batch,
+        "heads": r.w.heads, "num_splits": r.ns, "ms_per_step": ms / steps,
+        "kv_tokens_per_step": kv / steps, "value": kv / (ms / 1e3),
+        "gb_per_s": algo / (ms / 1e3) / 1e9,
+        "partial_avg_us": avg_ms * 1e3, "partial_bytes_per_launch": avg_bytes,
+        "partial_gb_per_s": avg_bytes / (avg_ms / 1e3) / 1e9,
+        "partial_launches": len(part_ms),
+    }
+    res["hbm_frac"] = res["gb_per_s"] / HBM_PEAK_GBS
+    log(f"{r.w.name}: {res['ms_per_step']:.3f} ms/step, {res['value'] / 1e9:.2f} G KV-tokens/s, "
+        f"{res['gb_per_s']:.0f} GB/s step ({100 * res['hbm_frac']:.1f}% of 8 TB/s); partial kernel "
+        f"{res['partial_avg_us']:.1f} us/launch, {res['partial_gb_per_s']:.0f} GB/s")
+    del r
+    torch.cuda.empty_cache()
+    return res
+
+
+def stored_traffic(name):
+    """Counter-measured HBM bytes per partial launch, from profiles/, if the
+    kernel source is unchanged since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"pmc_partial_{name}.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_source_sha256_16:\s*(\w+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != kernel_sha():
+        return None
+    return float(t.group(1))
+
+
+def roofline(res):
+    return {
+        "bound": "hbm", "achieved": round(res["partial_gb_per_s"], 1), "peak": HBM_PEAK_GBS,
+        "unit": "GB/s", "frac": round(res["partial_gb_per_s"] / HBM_PEAK_GBS, 4),
+        "traffic": stored_traffic(res["workload"]),
+        "kernel": "split_kernel (mla_decode_partial)",
+        "per_launch_bytes": res["partial_bytes_per_launch"],
+        "avg_launch_us": round(res["partial_avg_us"], 2),
+    }
+
+
+# ----------------------------------------------------------------- CPU side
+
+def cpu_baseline(wid, seconds):
+    """The oracle as it stands, on the host cores, over a bounded sample of the
+    workload: whole sequences of layer 0, one decode step each (quantize the new
+    token, dequantize the cache rows, absorbed decode in float64)."""
+    import torch
+    from mla_latent_kv_cache_amd import workloads as W
+    from oracle import attention as A
+    from oracle import quant as Q
+    w = W.WORKLOADS[wid]
+    lens = W.lengths(wid)
+    wuk, wuv = (t.float().numpy() for t in W.weights(wid, 0, "cpu"))
+    qn, qp = (t.float().numpy() for t in W.queries(wid, 0, "cpu"))
+    tokens, elapsed, seqs = 0, 0.0, 0
+    b = 0
+    while elapsed < seconds and b < w.batch:
+        c, k = W.latent_rows(wid, 0, b, int(lens[b]), "cpu")
+        planes = Q.quantize_rows(c.float().numpy(), k.float().numpy(), w.fmt)
+        nc, nk = W.latent_rows(wid, 0, b, 1, "cpu", kind="step")
+        nc, nk = nc.float().numpy(), nk.float().numpy()
+        t0 = time.perf_counter()
+        new = Q.quantize_rows(nc, nk, w.fmt)
+        full = {key: np.concatenate([planes[key], new[key]]) for key in planes}
+        ch, kh = Q.dequantize_rows(full, w.fmt)
+        A.decode_absorbed(qn[b], qp[b], wuk, wuv, ch, kh, W.SOFTMAX_SCALE)
+        elapsed += time.perf_counter() - t0
+        tokens += int(lens[b]) + 1
+        seqs += 1
+        b += 1
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = None
+    cores = len(os.sched_getaffinity(0))
+    return {
+        "value": tokens / elapsed, "unit": "KV-tokens/s",
+        "cores": threads if threads else cores, "kind": "oracle",
+        "sample": f"{seqs} sequences of layer 0 of {w.name} ({tokens} KV tokens), one decode step "
+                  f"each: oracle quantize of the new token, fp64 dequantize and absorbed decode; "
+                  f"{elapsed:.1f}s on {cores} host cores visible, BLAS threads {threads}",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3, help="index into workloads.WORKLOADS")
+    ap.add_argument("--int4-workload", type=int, default=2, help="-1 to skip")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="0 to skip the CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the decode path here is single-GPU "
+              "(see DESIGN.md for how it would shard). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    from mla_latent_kv_cache_amd import workloads as W
+
+    main_res = measure(args.workload, args.steps, args.warmup)
+    int4 = None
+    if args.int4_workload >= 0:
+        r4 = measure(args.int4_workload, args.steps, args.warmup)
+        int4 = {k: r4[k] for k in ("workload", "value", "ms_per_step", "gb_per_s", "hbm_frac",
+                                   "kv_tokens_per_step", "num_splits")}
+        int4["unit"] = "KV-tokens/s"
+        int4["roofline"] = roofline(r4)
+    cpu = None
+    if args.cpu_seconds > 0:
+        log("timing the oracle on the host cores")
+        cpu = cpu_baseline(args.workload, args.cpu_seconds)
+    w = W.WORKLOADS[args.workload]
+    line = {
+        "metric": METRIC,
+        "value": main_res["value"],
+        "unit": "KV-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "cache_format": w.fmt, "layers": w.layers, "batch": w.batch,
+            "heads": w.heads, "kv_lora_rank": 512, "rope_dim": 64, "seq_lens": "uniform [1024, 16384]"
+            if isinstance(w.seq, tuple) else w.seq, "num_splits": main_res["num_splits"],
+            "kv_tokens_per_step": main_res["kv_tokens_per_step"], "parallelism": "single GPU",
+        },
+        "gb_per_s": main_res["gb_per_s"],
+        "hbm_frac": main_res["hbm_frac"],
+        "roofline": roofline(main_res),
+        "cpu_baseline": cpu,
+        "int4": int4,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

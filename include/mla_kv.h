@@ -1,0 +1,201 @@
+/*
+ * mla_kv.h — C ABI of the absorbed-MLA decode library for MI355X (gfx950).
+ *
+ * What the library computes (one transformer layer, one decode step):
+ *
+ *   The cache keeps, per token, the 512-d latent c_kv and the 64-d RoPE key
+ *   k_pe instead of per-head keys and values ("Absorbed MLA Cache Optimization
+ *   on DeepSeek-V2-Lite", section 2.1: AbsorbedMLACache.store / get; section
+ *   3.1: 512 + 64 = 576 values per token). The latent is optionally quantized
+ *   per 16-channel group to symmetric INT8 or asymmetric INT4, k_pe per
+ *   8-channel group to INT8 (same report, section 3.2 / 4.2 tables: 32 blocks,
+ *   8 blocks), each group with an fp16 scale (and an fp16 zero-point for INT4).
+ *
+ *   Attention for head h follows the per-head softmax(q K^T * scale) V of the
+ *   tutorial "DeepSeek的MLA技术" (MLAttentionWithCache.forward_with_cache),
+ *   with K_t = [W_UK[h] c_t || k_pe_t] and V_t = c_t W_UV[h] (its MLA
+ *   mechanism, step 2), computed without expanding any token:
+ *     q_abs   = q_nope W_UK[h]                               (512)
+ *     s_t     = scale * (q_abs . c_t + q_pe . k_pe_t)
+ *     o_lat   = sum_t softmax(s)_t c_t                        (512)
+ *     out[h]  = o_lat W_UV[h]                                 (128)
+ *
+ * Conventions for every call:
+ *   - Every pointer argument except `cache` and the status string is a DEVICE
+ *     pointer, allocated and owned by the caller. The library allocates no
+ *     memory and keeps no state between calls; calls are reentrant.
+ *   - `hip_stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously on it; no call synchronizes the host.
+ *   - Arguments are checked on the host before anything is enqueued; a
+ *     negative mla_status is returned and nothing is launched on error. A
+ *     failed launch returns MLA_ERR_HIP.
+ *   - bf16 / fp16 values are passed as their 16-bit patterns (uint16_t or an
+ *     untyped pointer). All planes are dense, row-major, 16-byte aligned.
+ */
+#ifndef MLA_KV_H
+#define MLA_KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = -1, /* null pointer, bad size, layer out of range, misalignment */
+  MLA_ERR_UNSUPPORTED = -2, /* a dimension or head count this build does not handle */
+  MLA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  MLA_ERR_CAPACITY = -4,    /* (Python binding) an append would exceed capacity */
+  MLA_ERR_HIP = -5          /* a HIP launch or runtime call failed */
+} mla_status;
+
+/* Latent storage format. k_pe is bf16 for MLA_FMT_BF16 and INT8 otherwise. */
+typedef enum {
+  MLA_FMT_BF16 = 0, /* c_kv and k_pe copied as bf16 */
+  MLA_FMT_INT8 = 1, /* c_kv symmetric INT8 per 16 channels, k_pe INT8 per 8 channels */
+  MLA_FMT_INT4 = 2  /* c_kv asymmetric INT4 per 16 channels (2 codes/byte), k_pe INT8 */
+} mla_format;
+
+/*
+ * The cache of all layers of one model, for a batch of sequences.
+ *
+ * Planes, each [num_layers][batch][capacity][row] with the row sizes:
+ *   ckv     BF16: 512 x bf16 (1024 B)   INT8: 512 x int8 (512 B)
+ *           INT4: 256 x uint8 (256 B), byte k = code[2k] | code[2k+1] << 4
+ *   kpe     BF16: 64 x bf16 (128 B)     INT8 / INT4: 64 x int8 (64 B)
+ *   scale   INT8 / INT4: 40 x fp16 (80 B): the 32 latent-group scales, then
+ *           the 8 k_pe-group scales. NULL for BF16.
+ *   zero    INT4 only: 32 x fp16 (64 B) latent-group zero-points. NULL otherwise.
+ *   seq_lens  int32 [num_layers][batch]: tokens stored per (layer, sequence).
+ *
+ * Quantization of one group x (the definition parity is checked against):
+ *   INT8:  s = fp16_rne(max|x| / 127), q = clamp(rne(x / s), -127, 127),
+ *          x_hat = q * s; s == 0 gives q = 0.
+ *   INT4:  z = fp16 rounded toward -inf of min x, s = fp16_rne((max x - z) / 15)
+ *          (each stored as +0 when zero), q = clamp(rne((x - z) / s), 0, 15),
+ *          x_hat = q * s + z; s == 0 gives q = 0.
+ *   Every step is one IEEE fp32 operation; fp16 results that would overflow
+ *   saturate to +-65504. Inputs must be finite. The decode path dequantizes
+ *   to fp16, so dequantized magnitudes must stay below 65504.
+ */
+typedef struct mla_cache {
+  int32_t format;       /* mla_format */
+  int32_t num_layers;   /* >= 1 */
+  int32_t batch;        /* >= 1 */
+  int32_t capacity;     /* tokens per (layer, sequence), >= 1 */
+  int32_t kv_lora_rank; /* latent width: must be 512 */
+  int32_t rope_dim;     /* k_pe width: must be 64 */
+  int32_t group_latent; /* latent channels per group: must be 16 */
+  int32_t group_rope;   /* k_pe channels per group: must be 8 */
+  void *ckv;
+  void *kpe;
+  uint16_t *scale;
+  uint16_t *zero;
+  int32_t *seq_lens;
+} mla_cache;
+
+/*
+ * Quantize-on-append ("store" of section 2.1 of the report: quantize
+ * compressed_kv as it is stored, and keep k_pe beside it).
+ *
+ *   ckv_new  bf16 [batch][t_new][512]   latent of the new tokens
+ *   kpe_new  bf16 [batch][t_new][64]    RoPE key of the new tokens (already rotated)
+ *   t_new    rows per sequence in ckv_new / kpe_new, >= 0 (0 is a no-op)
+ *   n_new    optional int32 [batch] (device): sequence b appends only its first
+ *            n_new[b] rows, 0 <= n_new[b] <= t_new. NULL: every sequence
+ *            appends t_new rows.
+ *
+ * Sequence b's rows go to positions seq_lens[layer][b] .. +n-1 of `layer`,
+ * then seq_lens[layer][b] grows by n. Rows that would land at or past
+ * `capacity` are not written and seq_lens stops at capacity: the device
+ * cannot report it, so a caller must keep lengths within capacity (the Python
+ * binding tracks them and raises MLA_ERR_CAPACITY first).
+ */
+int mla_cache_append(const mla_cache *cache, int32_t layer, const void *ckv_new,
+                     const void *kpe_new, int32_t t_new, const int32_t *n_new,
+                     void *hip_stream);
+
+/*
+ * Workspace bytes that mla_decode_attn needs for this cache, head count and
+ * split count (0 = the split count the library would choose). Writes the size
+ * to *bytes and returns MLA_OK, or returns a negative status.
+ */
+int mla_decode_workspace_bytes(const mla_cache *cache, int32_t heads, int32_t num_splits,
+                               size_t *bytes);
+
+/*
+ * The split count mla_decode_attn uses for num_splits = 0 with this cache and
+ * head count (it depends on capacity, batch and the device's CU count only,
+ * never on seq_lens, which live on the device).
+ */
+int mla_decode_auto_splits(const mla_cache *cache, int32_t heads, int32_t *num_splits);
+
+/*
+ * Absorbed decode attention for one layer and one new query token per sequence.
+ *
+ *   q_nope   bf16 [batch][heads][128]  non-RoPE query part
+ *   q_pe     bf16 [batch][heads][64]   RoPE query part (already rotated)
+ *   w_uk     bf16 [heads][128][512]    key up-projection: K_nope[h] = W_UK[h] c
+ *   w_uv     bf16 [heads][512][128]    value up-projection: V[h] = c W_UV[h]
+ *   heads    16, 32, 64 or 128
+ *   softmax_scale   multiplies q.k before the softmax (e.g. 1/sqrt(192))
+ *   num_splits      KV splits per sequence, 0 = auto, else 1..4096. Split s
+ *                   covers tokens [s*chunk, (s+1)*chunk) with chunk =
+ *                   ceil(capacity / num_splits) rounded up to 16.
+ *   workspace       device scratch of at least mla_decode_workspace_bytes;
+ *                   its contents on entry do not matter
+ *   out      fp32 [batch][heads][128]
+ *
+ * Sequence b attends to its first seq_lens[layer][b] cached tokens; a sequence
+ * with no tokens gets an all-zero output row. Results do not depend on
+ * workspace contents and are bit-identical from run to run for a fixed split
+ * count; they differ between split counts only by rounding.
+ */
+int mla_decode_attn(const mla_cache *cache, int32_t layer, const void *q_nope,
+                    const void *q_pe, const void *w_uk, const void *w_uv, int32_t heads,
+                    float softmax_scale, int32_t num_splits, void *workspace,
+                    size_t workspace_bytes, float *out, void *hip_stream);
+
+/*
+ * The three phases of mla_decode_attn, for callers that schedule them
+ * separately (for example to time or overlap them). Calling, on one stream and
+ * with one workspace, mla_decode_absorb, then mla_decode_partial, then
+ * mla_decode_combine with the same cache, heads and num_splits is exactly
+ * mla_decode_attn: same kernels, same results. Arguments mean what they mean
+ * there; each phase validates them the same way.
+ *
+ *   absorb    q_abs = softmax_scale * log2(e) * q_nope W_UK[h], and q_pe scaled
+ *             the same way, into the workspace (fp16)
+ *   partial   split-KV attention of each (sequence, split) over the cache of
+ *             `layer`: per-split running max, sum and unnormalized latent sum
+ *             into the workspace (the hot loop)
+ *   combine   log-sum-exp merge of the splits, normalization, and projection
+ *             through W_UV into out
+ */
+int mla_decode_absorb(const mla_cache *cache, const void *q_nope, const void *q_pe,
+                      const void *w_uk, int32_t heads, float softmax_scale, int32_t num_splits,
+                      void *workspace, size_t workspace_bytes, void *hip_stream);
+int mla_decode_partial(const mla_cache *cache, int32_t layer, int32_t heads, int32_t num_splits,
+                       void *workspace, size_t workspace_bytes, void *hip_stream);
+int mla_decode_combine(const mla_cache *cache, const void *w_uv, int32_t heads, int32_t num_splits,
+                       void *workspace, size_t workspace_bytes, float *out, void *hip_stream);
+
+/*
+ * Dequantize one layer of the cache ("get" of section 2.1 of the report):
+ *   ckv_out  fp32 [batch][capacity][512], kpe_out fp32 [batch][capacity][64].
+ * Rows at or past seq_lens[layer][b] are written as zeros. Either output may
+ * be NULL to skip it. A test and inspection aid, not on the decode path.
+ */
+int mla_cache_get(const mla_cache *cache, int32_t layer, float *ckv_out, float *kpe_out,
+                  void *hip_stream);
+
+/* Static description of a status code. */
+const char *mla_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_KV_H */

@@ -1,0 +1,209 @@
+"""Python face of the library: a latent KV cache held in torch device tensors.
+
+torch provides device memory and the current stream; every computation is a
+call into libmla_kv.so (see include/mla_kv.h for the operations and the
+passages of the pages they follow).
+"""
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import FORMATS, MlaCacheStruct, MlaError, check
+
+LATENT = 512
+ROPE = 64
+NOPE = 128
+VDIM = 128
+N_SCALES = 40
+N_ZEROS = 32
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+class LatentCache:
+    """Per-layer latent cache planes for `batch` sequences of up to `capacity` tokens.
+
+    Layout (see include/mla_kv.h): ckv, kpe, scale, zero are
+    [num_layers, batch, capacity, row] tensors; seq_lens is int32 [num_layers, batch].
+    A host mirror of the lengths guards capacity before each append.
+    """
+
+    def __init__(self, fmt, num_layers, batch, capacity, device="cuda"):
+        if fmt not in FORMATS:
+            raise ValueError(f"format must be one of {list(FORMATS)}")
+        self.fmt = fmt
+        self.num_layers, self.batch, self.capacity = int(num_layers), int(batch), int(capacity)
+        self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
+        shape = (self.num_layers, self.batch, self.capacity)
+        kw = dict(device=self.device)
+        if fmt == "bf16":
+            self.ckv = torch.empty(shape + (LATENT,), dtype=torch.bfloat16, **kw)
+            self.kpe = torch.empty(shape + (ROPE,), dtype=torch.bfloat16, **kw)
+            self.scale = None
+            self.zero = None
+        else:
+            ck = LATENT if fmt == "int8" else LATENT // 2
+            self.ckv = torch.empty(shape + (ck,), dtype=torch.int8 if fmt == "int8" else torch.uint8, **kw)
+            self.kpe = torch.empty(shape + (ROPE,), dtype=torch.int8, **kw)
+            self.scale = torch.empty(shape + (N_SCALES,), dtype=torch.float16, **kw)
+            self.zero = torch.empty(shape + (N_ZEROS,), dtype=torch.float16, **kw) if fmt == "int4" else None
+        self.seq_lens = torch.zeros((self.num_layers, self.batch), dtype=torch.int32, **kw)
+        self._lens = np.zeros((self.num_layers, self.batch), dtype=np.int64)
+        self.struct = MlaCacheStruct(
+            FORMATS[fmt], self.num_layers, self.batch, self.capacity, LATENT, ROPE, 16, 8,
+            self.ckv.data_ptr(), self.kpe.data_ptr(),
+            self.scale.data_ptr() if self.scale is not None else 0,
+            self.zero.data_ptr() if self.zero is not None else 0,
+            self.seq_lens.data_ptr())
+
+    # ------------------------------------------------------------ queries
+    def lengths(self, layer=None):
+        """Host mirror of seq_lens (the device copy is the one the kernels use)."""
+        return self._lens.copy() if layer is None else self._lens[layer].copy()
+
+    def bytes(self):
+        """Device bytes of all cache planes."""
+        return sum(t.numel() * t.element_size() for t in (self.ckv, self.kpe, self.scale, self.zero)
+                   if t is not None)
+
+    def _layer(self, layer):
+        if not 0 <= layer < self.num_layers:
+            raise IndexError(f"layer {layer} out of range [0, {self.num_layers})")
+
+    # ------------------------------------------------------------- append
+    def append(self, layer, ckv_new, kpe_new, n_new=None, stream=None):
+        """Quantize and store new tokens: ckv_new bf16 [B,T,512], kpe_new bf16 [B,T,64].
+
+        n_new: optional per-sequence counts (host sequence of ints, <= T).
+        """
+        self._layer(layer)
+        T = ckv_new.shape[1] if ckv_new.dim() == 3 else -1
+        _need(ckv_new, "ckv_new", torch.bfloat16, (self.batch, T, LATENT), self.device)
+        _need(kpe_new, "kpe_new", torch.bfloat16, (self.batch, T, ROPE), self.device)
+        if n_new is None:
+            counts = np.full(self.batch, T, dtype=np.int64)
+            n_dev = None
+        else:
+            counts = np.asarray(n_new, dtype=np.int64).reshape(-1)
+            if counts.shape != (self.batch,) or (counts < 0).any() or (counts > T).any():
+                raise ValueError("n_new must hold batch counts in [0, T]")
+            n_dev = torch.tensor(counts, dtype=torch.int32, device=self.device)
+        if (self._lens[layer] + counts > self.capacity).any():
+            raise MlaError(_lib.MLA_ERR_CAPACITY, "append")
+        check(_lib.lib().mla_cache_append(ctypes.byref(self.struct), layer, _ptr(ckv_new), _ptr(kpe_new),
+                                          T, _ptr(n_dev), _stream(stream)), "mla_cache_append")
+        self._lens[layer] += counts
+        self._keep = n_dev  # keep the count tensor alive until the stream has used it
+
+    # ------------------------------------------------------------- decode
+    def auto_splits(self, heads):
+        n = ctypes.c_int32(0)
+        check(_lib.lib().mla_decode_auto_splits(ctypes.byref(self.struct), heads, ctypes.byref(n)),
+              "mla_decode_auto_splits")
+        return n.value
+
+    def workspace_bytes(self, heads, num_splits=0):
+        n = ctypes.c_size_t(0)
+        check(_lib.lib().mla_decode_workspace_bytes(ctypes.byref(self.struct), heads, num_splits,
+                                                    ctypes.byref(n)), "mla_decode_workspace_bytes")
+        return n.value
+
+    def workspace(self, heads, num_splits=0):
+        """A device workspace tensor large enough for decode(heads, num_splits)."""
+        return torch.empty(self.workspace_bytes(heads, num_splits), dtype=torch.uint8, device=self.device)
+
+    def decode(self, layer, q_nope, q_pe, w_uk, w_uv, softmax_scale, num_splits=0, out=None,
+               workspace=None, stream=None):
+        """Absorbed decode attention of one layer: returns out fp32 [B, H, 128]."""
+        self._layer(layer)
+        H = q_nope.shape[1] if q_nope.dim() == 3 else -1
+        _need(q_nope, "q_nope", torch.bfloat16, (self.batch, H, NOPE), self.device)
+        _need(q_pe, "q_pe", torch.bfloat16, (self.batch, H, ROPE), self.device)
+        _need(w_uk, "w_uk", torch.bfloat16, (H, NOPE, LATENT), self.device)
+        _need(w_uv, "w_uv", torch.bfloat16, (H, LATENT, VDIM), self.device)
+        if out is None:
+            out = torch.empty((self.batch, H, VDIM), dtype=torch.float32, device=self.device)
+        _need(out, "out", torch.float32, (self.batch, H, VDIM), self.device)
+        if workspace is None:
+            workspace = self.workspace(H, num_splits)
+        check(_lib.lib().mla_decode_attn(ctypes.byref(self.struct), layer, _ptr(q_nope), _ptr(q_pe),
+                                         _ptr(w_uk), _ptr(w_uv), H, float(softmax_scale), num_splits,
+                                         _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream)),
+              "mla_decode_attn")
+        return out
+
+    # ------------------------------------------------ decode, phase by phase
+    def decode_absorb(self, q_nope, q_pe, w_uk, softmax_scale, workspace, num_splits=0, stream=None):
+        """Phase 1 of decode: absorbed, scaled queries into the workspace."""
+        H = q_nope.shape[1] if q_nope.dim() == 3 else -1
+        _need(q_nope, "q_nope", torch.bfloat16, (self.batch, H, NOPE), self.device)
+        _need(q_pe, "q_pe", torch.bfloat16, (self.batch, H, ROPE), self.device)
+        _need(w_uk, "w_uk", torch.bfloat16, (H, NOPE, LATENT), self.device)
+        check(_lib.lib().mla_decode_absorb(ctypes.byref(self.struct), _ptr(q_nope), _ptr(q_pe), _ptr(w_uk), H,
+                                           float(softmax_scale), num_splits, _ptr(workspace),
+                                           workspace.numel(), _stream(stream)), "mla_decode_absorb")
+
+    def decode_partial(self, layer, heads, workspace, num_splits=0, stream=None):
+        """Phase 2 of decode: split-KV attention of every (sequence, split)."""
+        self._layer(layer)
+        check(_lib.lib().mla_decode_partial(ctypes.byref(self.struct), layer, heads, num_splits,
+                                            _ptr(workspace), workspace.numel(), _stream(stream)),
+              "mla_decode_partial")
+
+    def decode_combine(self, w_uv, workspace, num_splits=0, out=None, stream=None):
+        """Phase 3 of decode: merge the splits and project through W_UV."""
+        H = w_uv.shape[0]
+        _need(w_uv, "w_uv", torch.bfloat16, (H, LATENT, VDIM), self.device)
+        if out is None:
+            out = torch.empty((self.batch, H, VDIM), dtype=torch.float32, device=self.device)
+        _need(out, "out", torch.float32, (self.batch, H, VDIM), self.device)
+        check(_lib.lib().mla_decode_combine(ctypes.byref(self.struct), _ptr(w_uv), H, num_splits,
+                                            _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream)),
+              "mla_decode_combine")
+        return out
+
+    # ---------------------------------------------------------------- get
+    def get(self, layer, stream=None):
+        """Dequantized copy of one layer: (ckv fp32 [B,cap,512], kpe fp32 [B,cap,64])."""
+        self._layer(layer)
+        ckv = torch.empty((self.batch, self.capacity, LATENT), dtype=torch.float32, device=self.device)
+        kpe = torch.empty((self.batch, self.capacity, ROPE), dtype=torch.float32, device=self.device)
+        check(_lib.lib().mla_cache_get(ctypes.byref(self.struct), layer, _ptr(ckv), _ptr(kpe),
+                                       _stream(stream)), "mla_cache_get")
+        return ckv, kpe
+
+    def planes(self, layer, b):
+        """The raw cache planes of one sequence (first seq_len rows), as host numpy arrays."""
+        n = int(self._lens[layer, b])
+        out = {"ckv": self.ckv[layer, b, :n].cpu(), "kpe": self.kpe[layer, b, :n].cpu()}
+        if self.scale is not None:
+            out["scale"] = self.scale[layer, b, :n].cpu()
+        if self.zero is not None:
+            out["zero"] = self.zero[layer, b, :n].cpu()
+        return out

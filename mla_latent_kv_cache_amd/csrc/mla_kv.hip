@@ -1,0 +1,1137 @@
+// Absorbed MLA decode over a quantized latent KV cache, for MI355X (gfx950).
+//
+// The operation (one layer, one new query token per sequence) is defined in
+// include/mla_kv.h. Sources on the pages this follows:
+//   * "Absorbed MLA Cache Optimization on DeepSeek-V2-Lite", section 2.1 (the
+//     cache stores the 512-d latent plus the 64-d k_pe per token, quantizing
+//     on store, and projects at compute time), section 3.2 / 4.2 tables
+//     (per-channel INT8 in 32 blocks, k_pe INT8 in 8 blocks, asymmetric INT4
+//     in 32 blocks).
+//   * "DeepSeek的MLA技术", MLA mechanism step 2 (K_i = C W_i^upK,
+//     V_i = C W_i^upV) and MLAttentionWithCache (per-head softmax(q K^T s) V
+//     over every cached token). Absorbing W_UK into the query and applying
+//     W_UV after the softmax-weighted latent sum is the same computation by
+//     associativity; no token is expanded here.
+//
+// Kernels, in launch order:
+//   append_kernel       quantize new bf16 rows into the cache planes
+//   seqlen_kernel       advance seq_lens after an append
+//   absorb_kernel       q_abs = scale*log2(e) * q_nope W_UK[h]  -> fp16 workspace
+//   split_kernel        split-KV partial attention over one token range per
+//                       workgroup: 16-byte loads of codes, in-register dequant
+//                       to fp16, LDS tile, MFMA scores and MFMA value sums,
+//                       online softmax in base 2
+//   reduce_kernel       log-sum-exp merge of the splits, then o_lat W_UV[h]
+//   get_kernel          dequantize a layer to fp32 (inspection aid)
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "mla_kv.h"
+
+namespace {
+
+// ----------------------------------------------------------------- constants
+
+constexpr int kLatent = 512;               // kv_lora_rank
+constexpr int kRope = 64;                  // qk_rope_head_dim
+constexpr int kRow = kLatent + kRope;      // 576 channels scored per token
+constexpr int kNope = 128;                 // qk_nope_head_dim
+constexpr int kVDim = 128;                 // v_head_dim
+constexpr int kGroupL = 16;                // latent channels per quantization group
+constexpr int kGroupR = 8;                 // k_pe channels per quantization group
+constexpr int kNGroupL = kLatent / kGroupL;  // 32
+constexpr int kNGroupR = kRope / kGroupR;    // 8
+constexpr int kNScale = kNGroupL + kNGroupR; // 40 fp16 scales per row
+constexpr int kTile = 16;                  // tokens per MFMA tile
+constexpr int kLdsRow = kRow + 8;          // fp16 per LDS tile row (1168 B, breaks bank aliasing)
+constexpr int kWaves = 4;                  // waves per split workgroup
+constexpr int kThreads = kWaves * 64;
+constexpr int kMrgRow = kLatent + 4;       // fp32 per head row in the merge area
+constexpr int kMaxSplits = 4096;
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <typename To, typename From>
+__device__ __forceinline__ To bitcast(From v) {
+  static_assert(sizeof(To) == sizeof(From), "size");
+  return __builtin_bit_cast(To, v);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
+  return (float)bitcast<_Float16>(b);
+}
+
+// ------------------------------------------------------- exact quantization
+// One IEEE fp32 operation per step, no contraction, correctly rounded
+// division (the compiler default for HIP), rintf = round half to even.
+
+#pragma clang fp contract(off)
+
+// fp32 -> fp16 bits, round to nearest even, saturating at +-65504.
+__device__ __forceinline__ uint16_t f16_rne_sat(float v) {
+  uint16_t b = bitcast<uint16_t>((_Float16)v);
+  if ((b & 0x7FFFu) == 0x7C00u) b = (uint16_t)((b & 0x8000u) | 0x7BFFu);
+  return b;
+}
+
+// fp32 -> fp16 bits, rounded toward -inf, saturating, zero stored as +0.
+__device__ __forceinline__ uint16_t f16_rd_sat(float v) {
+  uint16_t b = bitcast<uint16_t>((_Float16)v);
+  if (b == 0x7C00u) b = 0x7BFFu;  // above the largest finite: round down to it
+  if (f16_bits_to_f32(b) > v) {   // nearest was above v: step one toward -inf
+    if ((b & 0x7FFFu) == 0) b = 0x8001u;
+    else if (b & 0x8000u) b = (uint16_t)(b + 1);
+    else b = (uint16_t)(b - 1);
+  }
+  if (b == 0xFC00u) b = 0xFBFFu;
+  if (b == 0x8000u) b = 0x0000u;
+  return b;
+}
+
+// Symmetric INT8 of n values: returns the fp16 scale bits, writes codes.
+template <int N>
+__device__ __forceinline__ uint16_t quant_sym8(const float (&x)[N], int8_t (&q)[N]) {
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) a = fmaxf(a, fabsf(x[i]));
+  uint16_t sb = f16_rne_sat(__fdiv_rn(a, 127.0f));
+  float s = f16_bits_to_f32(sb);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    float c = 0.0f;
+    if (s != 0.0f) c = fminf(fmaxf(rintf(__fdiv_rn(x[i], s)), -127.0f), 127.0f);
+    q[i] = (int8_t)(int)c;
+  }
+  return sb;
+}
+
+// Asymmetric INT4 of 16 values: writes scale and zero bits and codes 0..15.
+__device__ __forceinline__ void quant_asym4(const float (&x)[kGroupL], uint8_t (&q)[kGroupL],
+                                            uint16_t &sb, uint16_t &zb) {
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int i = 1; i < kGroupL; ++i) {
+    mn = fminf(mn, x[i]);
+    mx = fmaxf(mx, x[i]);
+  }
+  zb = f16_rd_sat(mn);
+  float z = f16_bits_to_f32(zb);
+  sb = f16_rne_sat(__fdiv_rn(__fsub_rn(mx, z), 15.0f));
+  if ((sb & 0x7FFFu) == 0) sb = 0;  // zero scale stored as +0 (sign of max - z is not defined)
+  float s = f16_bits_to_f32(sb);
+#pragma unroll
+  for (int i = 0; i < kGroupL; ++i) {
+    float c = 0.0f;
+    if (s != 0.0f) c = fminf(fmaxf(rintf(__fdiv_rn(__fsub_rn(x[i], z), s)), 0.0f), 15.0f);
+    q[i] = (uint8_t)(int)c;
+  }
+}
+
+#pragma clang fp contract(on)
+
+// ------------------------------------------------------------------ append
+
+struct AppendArgs {
+  void *ckv;            // layer base of the ckv plane
+  void *kpe;
+  uint16_t *scale;
+  uint16_t *zero;
+  const int32_t *seq_lens;  // layer row of seq_lens
+  const uint16_t *ckv_new;  // bf16 [B][T][512]
+  const uint16_t *kpe_new;  // bf16 [B][T][64]
+  const int32_t *n_new;     // optional [B]
+  int B, T, cap;
+};
+
+// One thread per quantization group: 32 latent groups then 8 k_pe groups per token.
+template <int FMT>
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  const int64_t total = (int64_t)a.B * a.T * kNScale;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int grp = (int)(idx % kNScale);
+    const int64_t bt = idx / kNScale;
+    const int t = (int)(bt % a.T);
+    const int b = (int)(bt / a.T);
+    const int n = a.n_new ? a.n_new[b] : a.T;
+    if (t >= n) continue;
+    const int pos = a.seq_lens[b] + t;
+    if (pos < 0 || pos >= a.cap) continue;
+    const int64_t row = (int64_t)b * a.cap + pos;
+    if (grp < kNGroupL) {
+      const uint16_t *src = a.ckv_new + ((int64_t)b * a.T + t) * kLatent + grp * kGroupL;
+      const u32x4 v0 = *(const u32x4 *)src;
+      const u32x4 v1 = *(const u32x4 *)(src + 8);
+      if (FMT == MLA_FMT_BF16) {
+        u32x4 *dst = (u32x4 *)((uint16_t *)a.ckv + row * kLatent + grp * kGroupL);
+        dst[0] = v0;
+        dst[1] = v1;
+        continue;
+      }
+      float x[kGroupL];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = bf16_bits_to_f32(v0[i] & 0xFFFFu);
+        x[2 * i + 1] = bf16_bits_to_f32(v0[i] >> 16);
+        x[8 + 2 * i] = bf16_bits_to_f32(v1[i] & 0xFFFFu);
+        x[8 + 2 * i + 1] = bf16_bits_to_f32(v1[i] >> 16);
+      }
+      if (FMT == MLA_FMT_INT8) {
+        int8_t q[kGroupL];
+        const uint16_t sb = quant_sym8<kGroupL>(x, q);
+        u32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          w[i] = (uint32_t)(uint8_t)q[4 * i] | ((uint32_t)(uint8_t)q[4 * i + 1] << 8) |
+                 ((uint32_t)(uint8_t)q[4 * i + 2] << 16) | ((uint32_t)(uint8_t)q[4 * i + 3] << 24);
+        *(u32x4 *)((int8_t *)a.ckv + row * kLatent + grp * kGroupL) = w;
+        a.scale[row * kNScale + grp] = sb;
+      } else {
+        uint8_t q[kGroupL];
+        uint16_t sb, zb;
+        quant_asym4(x, q, sb, zb);
+        u32x2 w;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          uint32_t v = 0;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v |= (uint32_t)q[8 * i + j] << (4 * j);
+          w[i] = v;
+        }
+        *(u32x2 *)((uint8_t *)a.ckv + row * (kLatent / 2) + grp * (kGroupL / 2)) = w;
+        a.scale[row * kNScale + grp] = sb;
+        a.zero[row * kNGroupL + grp] = zb;
+      }
+    } else {
+      const int g = grp - kNGroupL;
+      const uint16_t *src = a.kpe_new + ((int64_t)b * a.T + t) * kRope + g * kGroupR;
+      const u32x4 v = *(const u32x4 *)src;
+      if (FMT == MLA_FMT_BF16) {
+        *(u32x4 *)((uint16_t *)a.kpe + row * kRope + g * kGroupR) = v;
+        continue;
+      }
+      float x[kGroupR];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = bf16_bits_to_f32(v[i] & 0xFFFFu);
+        x[2 * i + 1] = bf16_bits_to_f32(v[i] >> 16);
+      }
+      int8_t q[kGroupR];
+      const uint16_t sb = quant_sym8<kGroupR>(x, q);
+      u32x2 w;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        w[i] = (uint32_t)(uint8_t)q[4 * i] | ((uint32_t)(uint8_t)q[4 * i + 1] << 8) |
+               ((uint32_t)(uint8_t)q[4 * i + 2] << 16) | ((uint32_t)(uint8_t)q[4 * i + 3] << 24);
+      *(u32x2 *)((int8_t *)a.kpe + row * kRope + g * kGroupR) = w;
+      a.scale[row * kNScale + grp] = sb;
+    }
+  }
+}
+
+// Runs after append_kernel on the same stream, so every block of the append
+// has read the old length before it changes.
+__global__ void seqlen_kernel(int32_t *seq_lens, const int32_t *n_new, int B, int T, int cap) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const int n = n_new ? n_new[b] : T;
+  const int64_t v = (int64_t)seq_lens[b] + n;
+  seq_lens[b] = (int32_t)(v > cap ? cap : v);
+}
+
+// ------------------------------------------------------------------ absorb
+
+constexpr int kAbsorbBT = 8;  // batch rows per absorb / reduce block
+
+// q_abs[b,h,c] = qs * sum_d q_nope[b,h,d] W_UK[h,d,c] for c < 512, and
+// q_abs[b,h,512+d] = qs * q_pe[b,h,d]; qs = softmax_scale * log2(e), so the
+// attention kernels work in base 2. Grid (H, ceil(B/8)), 256 threads.
+__global__ __launch_bounds__(256) void absorb_kernel(const uint16_t *q_nope, const uint16_t *q_pe,
+                                                     const uint16_t *w_uk, int B, int H, float qs,
+                                                     _Float16 *qa) {
+  __shared__ float qsh[kAbsorbBT][kNope];
+  const int h = blockIdx.x;
+  const int b0 = blockIdx.y * kAbsorbBT;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kAbsorbBT * kNope; i += 256) {
+    const int bt = i / kNope, d = i % kNope;
+    const int b = b0 + bt;
+    qsh[bt][d] = b < B ? bf16_bits_to_f32(q_nope[((int64_t)b * H + h) * kNope + d]) : 0.0f;
+  }
+  __syncthreads();
+  float acc[kAbsorbBT][2];
+#pragma unroll
+  for (int bt = 0; bt < kAbsorbBT; ++bt) acc[bt][0] = acc[bt][1] = 0.0f;
+  const uint16_t *w = w_uk + (int64_t)h * kNope * kLatent;
+  for (int d = 0; d < kNope; ++d) {
+    const float w0 = bf16_bits_to_f32(w[d * kLatent + tid]);
+    const float w1 = bf16_bits_to_f32(w[d * kLatent + tid + 256]);
+#pragma unroll
+    for (int bt = 0; bt < kAbsorbBT; ++bt) {
+      acc[bt][0] += qsh[bt][d] * w0;
+      acc[bt][1] += qsh[bt][d] * w1;
+    }
+  }
+#pragma unroll
+  for (int bt = 0; bt < kAbsorbBT; ++bt) {
+    const int b = b0 + bt;
+    if (b >= B) break;
+    _Float16 *o = qa + ((int64_t)b * H + h) * kRow;
+    o[tid] = (_Float16)(acc[bt][0] * qs);
+    o[tid + 256] = (_Float16)(acc[bt][1] * qs);
+    if (tid < kRope) o[kLatent + tid] = (_Float16)(bf16_bits_to_f32(q_pe[((int64_t)b * H + h) * kRope + tid]) * qs);
+  }
+}
+
+// ------------------------------------------------------------- split-KV core
+
+// Raw 16-byte chunks a lane loads for one token tile, before dequantization.
+// Lane l, chunk k of a plane covers the 16 bytes at l + 64*k of the tile's
+// contiguous rows of that plane (perfectly coalesced: a wave reads 1 KB).
+template <int FMT> struct Fmt;
+
+template <> struct Fmt<MLA_FMT_INT8> {
+  static constexpr int kLat = 8;  // latent chunks per lane (16 rows x 512 B)
+  static constexpr int kKpe = 1;  // k_pe chunks per lane (16 rows x 64 B)
+  static constexpr int kLatRowBytes = kLatent;
+  static constexpr int kKpeRowBytes = kRope;
+};
+template <> struct Fmt<MLA_FMT_INT4> {
+  static constexpr int kLat = 4;  // 16 rows x 256 B
+  static constexpr int kKpe = 1;
+  static constexpr int kLatRowBytes = kLatent / 2;
+  static constexpr int kKpeRowBytes = kRope;
+};
+template <> struct Fmt<MLA_FMT_BF16> {
+  static constexpr int kLat = 16;  // 16 rows x 1024 B
+  static constexpr int kKpe = 2;   // 16 rows x 128 B
+  static constexpr int kLatRowBytes = kLatent * 2;
+  static constexpr int kKpeRowBytes = kRope * 2;
+};
+
+// Chunk k of lane l: which tile row it belongs to and where its channels start.
+template <int FMT> __device__ __forceinline__ int lat_row(int lane, int k) {
+  constexpr int per_row = Fmt<FMT>::kLatRowBytes / 16;  // chunks per row
+  return (lane + 64 * k) / per_row;
+}
+template <int FMT> __device__ __forceinline__ int lat_chunk(int lane) {
+  constexpr int per_row = Fmt<FMT>::kLatRowBytes / 16;
+  return lane % per_row;  // (lane + 64k) % per_row == lane % per_row, per_row | 64
+}
+template <int FMT> __device__ __forceinline__ int kpe_row(int lane, int k) {
+  constexpr int per_row = Fmt<FMT>::kKpeRowBytes / 16;
+  return (lane + 64 * k) / per_row;
+}
+template <int FMT> __device__ __forceinline__ int kpe_chunk(int lane) {
+  constexpr int per_row = Fmt<FMT>::kKpeRowBytes / 16;
+  return lane % per_row;
+}
+
+template <int FMT, int NW>  // NW: waves sharing (and splitting) the dequant of one tile
+struct RawTile {
+  static constexpr int kLat = Fmt<FMT>::kLat / NW;
+  static constexpr int kKpe = (Fmt<FMT>::kKpe + NW - 1) / NW;
+  u32x4 lat[kLat];
+  u32x4 kpe[kKpe];
+  uint32_t lsc[kLat];   // latent scale bits (INT8: one group; INT4: two groups packed)
+  uint32_t lzp[kLat];   // INT4 zero-point bits (two groups packed)
+  uint32_t ksc[kKpe];   // k_pe scale bits (two groups packed)
+};
+
+struct SplitArgs {
+  const void *ckv;
+  const void *kpe;
+  const uint16_t *scale;
+  const uint16_t *zero;
+  const int32_t *seq_lens;  // layer row
+  const _Float16 *qa;       // [B][H][576]
+  float *ws_m;              // [B][nsplit][H]
+  float *ws_l;              // [B][nsplit][H]
+  float *ws_acc;            // [B][nsplit][H][512]
+  int B, H, cap, nsplit, chunk, hh_count;
+};
+
+template <int FMT, int NW>
+__device__ __forceinline__ void load_raw(RawTile<FMT, NW> &r, const SplitArgs &a, int b, int t0,
+                                         int tend, int lane, int hw) {
+  const int64_t row0 = (int64_t)b * a.cap + t0;
+#pragma unroll
+  for (int j = 0; j < RawTile<FMT, NW>::kLat; ++j) {
+    const int k = j * NW + hw;
+    const int tr = lat_row<FMT>(lane, k);
+    const int ch = lat_chunk<FMT>(lane);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    uint32_t s = 0u, z = 0u;
+    if (t0 + tr < tend) {
+      const int64_t row = row0 + tr;
+      v = *(const u32x4 *)((const uint8_t *)a.ckv + row * Fmt<FMT>::kLatRowBytes + ch * 16);
+      if (FMT == MLA_FMT_INT8) {
+        s = a.scale[row * kNScale + ch];
+      } else if (FMT == MLA_FMT_INT4) {
+        s = *(const uint32_t *)(a.scale + row * kNScale + 2 * ch);
+        z = *(const uint32_t *)(a.zero + row * kNGroupL + 2 * ch);
+      }
+    }
+    r.lat[j] = v;
+    r.lsc[j] = s;
+    r.lzp[j] = z;
+  }
+#pragma unroll
+  for (int j = 0; j < RawTile<FMT, NW>::kKpe; ++j) {
+    const int k = j * NW + hw;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    uint32_t s = 0u;
+    if (k < Fmt<FMT>::kKpe) {
+      const int tr = kpe_row<FMT>(lane, k);
+      const int ch = kpe_chunk<FMT>(lane);
+      if (t0 + tr < tend) {
+        const int64_t row = row0 + tr;
+        v = *(const u32x4 *)((const uint8_t *)a.kpe + row * Fmt<FMT>::kKpeRowBytes + ch * 16);
+        if (FMT != MLA_FMT_BF16) s = *(const uint32_t *)(a.scale + row * kNScale + kNGroupL + 2 * ch);
+      }
+    }
+    r.kpe[j] = v;
+    r.ksc[j] = s;
+  }
+}
+
+// 4 signed bytes -> 4 fp16 values q*s: bias to unsigned, splice into the
+// mantissa of 1024.0 (exact), subtract 1152 (exact), scale (one rounding).
+__device__ __forceinline__ void deq_i8x4(uint32_t w, f16x2 s2, f16x2 &lo, f16x2 &hi) {
+  const uint32_t u = w ^ 0x80808080u;
+  const uint32_t a = (u & 0xFFu) | ((u << 8) & 0xFF0000u) | 0x64006400u;
+  const uint32_t c = ((u >> 16) & 0xFFu) | ((u >> 8) & 0xFF0000u) | 0x64006400u;
+  const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  lo = (bitcast<f16x2>(a) - bias) * s2;
+  hi = (bitcast<f16x2>(c) - bias) * s2;
+}
+
+// 8 nibbles (channels 0..7, low nibble first) -> 8 fp16 values q*s + z.
+__device__ __forceinline__ void deq_i4x8(uint32_t w, f16x2 s2, f16x2 z2, f16x2 (&o)[4]) {
+  const f16x2 bias = {(_Float16)1024.0f, (_Float16)1024.0f};
+  const f16x2 q04 = bitcast<f16x2>((w & 0x000F000Fu) | 0x64006400u) - bias;          // ch0, ch4
+  const f16x2 q15 = bitcast<f16x2>(((w >> 4) & 0x000F000Fu) | 0x64006400u) - bias;   // ch1, ch5
+  const f16x2 q26 = bitcast<f16x2>(((w >> 8) & 0x000F000Fu) | 0x64006400u) - bias;   // ch2, ch6
+  const f16x2 q37 = bitcast<f16x2>(((w >> 12) & 0x000F000Fu) | 0x64006400u) - bias;  // ch3, ch7
+  const f16x2 v04 = __builtin_elementwise_fma(q04, s2, z2);
+  const f16x2 v15 = __builtin_elementwise_fma(q15, s2, z2);
+  const f16x2 v26 = __builtin_elementwise_fma(q26, s2, z2);
+  const f16x2 v37 = __builtin_elementwise_fma(q37, s2, z2);
+  o[0] = f16x2{v04.x, v15.x};
+  o[1] = f16x2{v26.x, v37.x};
+  o[2] = f16x2{v04.y, v15.y};
+  o[3] = f16x2{v26.y, v37.y};
+}
+
+__device__ __forceinline__ f16x2 bf16x2_to_f16x2(uint32_t w) {
+  return f16x2{(_Float16)bf16_bits_to_f32(w & 0xFFFFu), (_Float16)bf16_bits_to_f32(w >> 16)};
+}
+
+__device__ __forceinline__ f16x2 splat_f16_bits(uint32_t bits16) {
+  const _Float16 h = bitcast<_Float16>((uint16_t)bits16);
+  return f16x2{h, h};
+}
+
+__device__ __forceinline__ void st16(_Float16 *p, f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
+  u32x4 v = {bitcast<uint32_t>(a), bitcast<uint32_t>(b), bitcast<uint32_t>(c), bitcast<uint32_t>(d)};
+  *(u32x4 *)p = v;
+}
+
+// Dequantize this lane's raw chunks into the fp16 LDS tile [16][kLdsRow].
+template <int FMT, int NW>
+__device__ __forceinline__ void dequant_store(const RawTile<FMT, NW> &r, _Float16 *tile, int lane,
+                                              int hw) {
+#pragma unroll
+  for (int j = 0; j < RawTile<FMT, NW>::kLat; ++j) {
+    const int k = j * NW + hw;
+    const int tr = lat_row<FMT>(lane, k);
+    const int ch = lat_chunk<FMT>(lane);
+    const u32x4 v = r.lat[j];
+    if (FMT == MLA_FMT_INT8) {
+      const f16x2 s2 = splat_f16_bits(r.lsc[j]);
+      f16x2 o[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) deq_i8x4(v[i], s2, o[2 * i], o[2 * i + 1]);
+      _Float16 *dst = tile + tr * kLdsRow + ch * 16;
+      st16(dst, o[0], o[1], o[2], o[3]);
+      st16(dst + 8, o[4], o[5], o[6], o[7]);
+    } else if (FMT == MLA_FMT_INT4) {
+      // 32 channels: bytes 0-7 in group 2ch (scale/zero low half), 8-15 in 2ch+1.
+      const f16x2 s0 = splat_f16_bits(r.lsc[j] & 0xFFFFu), s1 = splat_f16_bits(r.lsc[j] >> 16);
+      const f16x2 z0 = splat_f16_bits(r.lzp[j] & 0xFFFFu), z1 = splat_f16_bits(r.lzp[j] >> 16);
+      _Float16 *dst = tile + tr * kLdsRow + ch * 32;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f16x2 o[4];
+        deq_i4x8(v[i], i < 2 ? s0 : s1, i < 2 ? z0 : z1, o);
+        st16(dst + 8 * i, o[0], o[1], o[2], o[3]);
+      }
+    } else {
+      _Float16 *dst = tile + tr * kLdsRow + ch * 8;
+      st16(dst, bf16x2_to_f16x2(v[0]), bf16x2_to_f16x2(v[1]), bf16x2_to_f16x2(v[2]),
+           bf16x2_to_f16x2(v[3]));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < RawTile<FMT, NW>::kKpe; ++j) {
+    const int k = j * NW + hw;
+    if (k >= Fmt<FMT>::kKpe) continue;
+    const int tr = kpe_row<FMT>(lane, k);
+    const int ch = kpe_chunk<FMT>(lane);
+    const u32x4 v = r.kpe[j];
+    if (FMT == MLA_FMT_BF16) {
+      _Float16 *dst = tile + tr * kLdsRow + kLatent + ch * 8;
+      st16(dst, bf16x2_to_f16x2(v[0]), bf16x2_to_f16x2(v[1]), bf16x2_to_f16x2(v[2]),
+           bf16x2_to_f16x2(v[3]));
+    } else {
+      // 16 channels = k_pe groups 2ch (bytes 0-7) and 2ch+1 (bytes 8-15)
+      const f16x2 s0 = splat_f16_bits(r.ksc[j] & 0xFFFFu), s1 = splat_f16_bits(r.ksc[j] >> 16);
+      f16x2 o[8];
+      deq_i8x4(v[0], s0, o[0], o[1]);
+      deq_i8x4(v[1], s0, o[2], o[3]);
+      deq_i8x4(v[2], s1, o[4], o[5]);
+      deq_i8x4(v[3], s1, o[6], o[7]);
+      _Float16 *dst = tile + tr * kLdsRow + kLatent + ch * 16;
+      st16(dst, o[0], o[1], o[2], o[3]);
+      st16(dst + 8, o[4], o[5], o[6], o[7]);
+    }
+  }
+}
+
+constexpr int kTileBytes = kTile * kLdsRow * 2;                    // 18,688
+constexpr int kMergeBytes = kWaves * 16 * kMrgRow * 4;             // 132,096
+constexpr int kSplitLds = kMergeBytes > 4 * kTileBytes ? kMergeBytes : 4 * kTileBytes;
+
+// One workgroup = 4 waves = one (sequence b, split s, head block hh) unit.
+// HGW waves (one per 16 heads) share each token tile; the 4/HGW token groups
+// take interleaved tiles of the split and are merged at the end through LDS.
+//
+// Per wave, with lane = 16*g + i (g = 0..3, i = 0..15):
+//   scores  S^T[t][h] = sum_c C[t][c] Qabs[h][c]: 18 MFMA 16x16x32 f16 per
+//           tile; A = tile row t = i (8 channels per lane group), B = Qabs of
+//           head i held in registers; lane (g, i) gets tokens 4g..4g+3 of head i.
+//   values  O^T[c][h] += sum_t C[t][c] P[t][h]: 32 MFMA 16x16x16 f16 per
+//           tile; B = P exactly as the score MFMA left it in registers,
+//           A = channel 16n+i of tokens 4g..4g+3 read from the LDS tile;
+//           lane (g, i) accumulates channels 16n+4g..16n+4g+3 of head i.
+template <int FMT, int HGW>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+void split_kernel(SplitArgs a) {
+  constexpr int TG = kWaves / HGW;                 // token groups
+  constexpr int NBUF = HGW == 1 ? 1 : 2;           // wave-private tile, or double-buffered shared
+  constexpr int NPF = FMT == MLA_FMT_BF16 ? 1 : 2; // raw tiles in flight per wave
+  static_assert(TG * NBUF * kTileBytes <= kSplitLds, "lds");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kSplitLds];
+  __shared__ float ml_m[kWaves][16], ml_l[kWaves][16];
+
+  const int split = blockIdx.x / a.hh_count;
+  const int hh = blockIdx.x % a.hh_count;
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, li = lane & 15;
+  const int tg = wave / HGW, hw = wave % HGW;
+  const int head0 = (hh * HGW) * 16;              // first head of this workgroup
+  const int head = head0 + hw * 16 + li;          // the head this lane's columns belong to
+
+  const int L = min(max(a.seq_lens[b], 0), a.cap);
+  const int t_begin = split * a.chunk;
+  const int t_end = min(t_begin + a.chunk, L);
+  const int64_t ws_row = ((int64_t)b * a.nsplit + split) * a.H;
+  if (t_begin >= t_end) {  // empty unit: identity of the merge
+    if (tid < HGW * 16) {
+      a.ws_m[ws_row + head0 + tid] = -INFINITY;
+      a.ws_l[ws_row + head0 + tid] = 0.0f;
+    }
+    return;
+  }
+  const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
+  const int niters = (ntiles + TG - 1) / TG;
+
+  // Qabs of head `head` in the MFMA B layout: k-step s holds channels 32s+8g..+7.
+  f16x8 qb[kRow / 32];
+  {
+    const _Float16 *q = a.qa + ((int64_t)b * a.H + head) * kRow + 8 * g;
+#pragma unroll
+    for (int s = 0; s < kRow / 32; ++s) qb[s] = *(const f16x8 *)(q + 32 * s);
+  }
+
+  f32x4 acc[kLatent / 16];
+#pragma unroll
+  for (int n = 0; n < kLatent / 16; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  _Float16 *tiles = (_Float16 *)lds + (int64_t)tg * NBUF * kTile * kLdsRow;
+
+  RawTile<FMT, HGW> raw[NPF];
+#pragma unroll
+  for (int p = 0; p < NPF; ++p) {
+    const int tile = tg + p * TG;
+    if (tile < ntiles) load_raw<FMT, HGW>(raw[p], a, b, t_begin + tile * kTile, t_end, lane, hw);
+  }
+
+  for (int it0 = 0; it0 < niters; it0 += NPF) {
+#pragma unroll
+    for (int p = 0; p < NPF; ++p) {
+      const int it = it0 + p;
+      if (HGW == 1 && it >= niters) break;
+      if (HGW > 1 && it >= niters) break;  // uniform across the workgroup
+      const int tile = tg + it * TG;
+      const bool valid = tile < ntiles;
+      _Float16 *tb = tiles + (NBUF == 1 ? 0 : (it & 1)) * kTile * kLdsRow;
+      if (valid) dequant_store<FMT, HGW>(raw[p], tb, lane, hw);
+      const int nxt = tile + NPF * TG;
+      if (nxt < ntiles) load_raw<FMT, HGW>(raw[p], a, b, t_begin + nxt * kTile, t_end, lane, hw);
+      if (HGW > 1) {
+        __syncthreads();
+      } else {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+      if (!valid) continue;
+      const int t0 = t_begin + tile * kTile;
+
+      // ---- scores
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+      const _Float16 *arow = tb + li * kLdsRow + 8 * g;
+#pragma unroll
+      for (int s = 0; s < kRow / 32; ++s) {
+        const f16x8 av = *(const f16x8 *)(arow + 32 * s);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qb[s], sc, 0, 0, 0);
+      }
+      // ---- online softmax (base 2); lane (g, i) holds tokens t0+4g+r of head i
+      float p4[4];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p4[r] = (t0 + 4 * g + r < t_end) ? sc[r] : -INFINITY;
+        tmax = fmaxf(tmax, p4[r]);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      float psum = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p4[r] = __builtin_amdgcn_exp2f(p4[r] - m_new);
+        psum += p4[r];
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+#pragma unroll
+      for (int n = 0; n < kLatent / 16; ++n) acc[n] *= alpha;
+      const f16x4 pb = {(_Float16)p4[0], (_Float16)p4[1], (_Float16)p4[2], (_Float16)p4[3]};
+
+      // ---- values
+      const _Float16 *vcol = tb + (4 * g) * kLdsRow + li;
+#pragma unroll
+      for (int n = 0; n < kLatent / 16; ++n) {
+        const _Float16 *c = vcol + 16 * n;
+        const f16x4 av = {c[0], c[kLdsRow], c[2 * kLdsRow], c[3 * kLdsRow]};
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pb, acc[n], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- merge the token groups of this workgroup through LDS, write the partial
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  __syncthreads();  // every wave is done with the tiles; the area becomes the merge area
+  float *mrg = (float *)lds;
+  if (g == 0) {
+    ml_m[wave][li] = m_run;
+    ml_l[wave][li] = l_run;
+  }
+  {
+    float *dst = mrg + ((int64_t)wave * 16 + li) * kMrgRow + 4 * g;
+#pragma unroll
+    for (int n = 0; n < kLatent / 16; ++n) *(f32x4 *)(dst + 16 * n) = acc[n];
+  }
+  __syncthreads();
+  // HGW*16 heads x 512 channels, 256 threads: thread -> (head-in-block, channel)
+  for (int e = tid; e < HGW * 16 * kLatent; e += kThreads) {
+    const int c = e % kLatent;
+    const int hb = e / kLatent;  // 0 .. HGW*16-1
+    const int w_hw = hb / 16, w_li = hb % 16;
+    float M = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < TG; ++q) M = fmaxf(M, ml_m[q * HGW + w_hw][w_li]);
+    float o = 0.0f, l = 0.0f;
+#pragma unroll
+    for (int q = 0; q < TG; ++q) {
+      const float mq = ml_m[q * HGW + w_hw][w_li];
+      const float w = mq == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mq - M);
+      o += w * mrg[((int64_t)(q * HGW + w_hw) * 16 + w_li) * kMrgRow + c];
+      l += w * ml_l[q * HGW + w_hw][w_li];
+    }
+    a.ws_acc[(ws_row + head0 + hb) * kLatent + c] = o;
+    if (c == 0) {
+      a.ws_m[ws_row + head0 + hb] = M;
+      a.ws_l[ws_row + head0 + hb] = l;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ reduce
+
+// Per (head h, 8 batch rows): merge the splits, normalize, project by W_UV[h].
+__global__ __launch_bounds__(256) void reduce_kernel(const float *ws_m, const float *ws_l,
+                                                     const float *ws_acc, const uint16_t *w_uv,
+                                                     int B, int H, int nsplit, float *out) {
+  __shared__ float olat[kAbsorbBT][kLatent];
+  __shared__ float part[kAbsorbBT][kVDim];
+  const int h = blockIdx.x;
+  const int b0 = blockIdx.y * kAbsorbBT;
+  const int tid = threadIdx.x;
+  for (int bt = 0; bt < kAbsorbBT; ++bt) {
+    const int b = b0 + bt;
+    if (b >= B) {
+      olat[bt][tid] = 0.0f;
+      olat[bt][tid + 256] = 0.0f;
+      continue;
+    }
+    const int64_t base = (int64_t)b * nsplit * H + h;
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s)
+      if (ws_l[base + (int64_t)s * H] > 0.0f) M = fmaxf(M, ws_m[base + (int64_t)s * H]);
+    float Ls = 0.0f, o0 = 0.0f, o1 = 0.0f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float l = ws_l[base + (int64_t)s * H];
+      if (!(l > 0.0f)) continue;
+      const float w = exp2f(ws_m[base + (int64_t)s * H] - M);
+      Ls += w * l;
+      const float *acc = ws_acc + (base + (int64_t)s * H) * kLatent;
+      o0 += w * acc[tid];
+      o1 += w * acc[tid + 256];
+    }
+    const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+    olat[bt][tid] = o0 * inv;
+    olat[bt][tid + 256] = o1 * inv;
+  }
+  __syncthreads();
+  const int e = tid % kVDim, half = tid / kVDim;
+  float acc[kAbsorbBT];
+#pragma unroll
+  for (int bt = 0; bt < kAbsorbBT; ++bt) acc[bt] = 0.0f;
+  const uint16_t *w = w_uv + (int64_t)h * kLatent * kVDim + e;
+  for (int c = half * 256; c < half * 256 + 256; ++c) {
+    const float wv = bf16_bits_to_f32(w[(int64_t)c * kVDim]);
+#pragma unroll
+    for (int bt = 0; bt < kAbsorbBT; ++bt) acc[bt] += olat[bt][c] * wv;
+  }
+  if (half == 1) {
+#pragma unroll
+    for (int bt = 0; bt < kAbsorbBT; ++bt) part[bt][e] = acc[bt];
+  }
+  __syncthreads();
+  if (half == 0) {
+#pragma unroll
+    for (int bt = 0; bt < kAbsorbBT; ++bt) {
+      const int b = b0 + bt;
+      if (b < B) out[((int64_t)b * H + h) * kVDim + e] = acc[bt] + part[bt][e];
+    }
+  }
+}
+
+// --------------------------------------------------------------------- get
+
+template <int FMT>
+__global__ __launch_bounds__(256) void get_kernel(const void *ckv, const void *kpe,
+                                                  const uint16_t *scale, const uint16_t *zero,
+                                                  const int32_t *seq_lens, int B, int cap,
+                                                  float *ckv_out, float *kpe_out) {
+  const int64_t total = (int64_t)B * cap * kRow;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(idx % kRow);
+    const int64_t row = idx / kRow;
+    const int b = (int)(row / cap), t = (int)(row % cap);
+    float v = 0.0f;
+    if (t < seq_lens[b]) {
+      if (c < kLatent) {
+        if (FMT == MLA_FMT_BF16) {
+          v = bf16_bits_to_f32(((const uint16_t *)ckv)[row * kLatent + c]);
+        } else if (FMT == MLA_FMT_INT8) {
+          v = (float)((const int8_t *)ckv)[row * kLatent + c] *
+              f16_bits_to_f32(scale[row * kNScale + c / kGroupL]);
+        } else {
+          const uint8_t byte = ((const uint8_t *)ckv)[row * (kLatent / 2) + c / 2];
+          const float q = (float)((c & 1) ? (byte >> 4) : (byte & 15));
+          v = fmaf(q, f16_bits_to_f32(scale[row * kNScale + c / kGroupL]),
+                   f16_bits_to_f32(zero[row * kNGroupL + c / kGroupL]));
+        }
+      } else {
+        const int d = c - kLatent;
+        if (FMT == MLA_FMT_BF16)
+          v = bf16_bits_to_f32(((const uint16_t *)kpe)[row * kRope + d]);
+        else
+          v = (float)((const int8_t *)kpe)[row * kRope + d] *
+              f16_bits_to_f32(scale[row * kNScale + kNGroupL + d / kGroupR]);
+      }
+    }
+    if (c < kLatent) {
+      if (ckv_out) ckv_out[row * kLatent + c] = v;
+    } else if (kpe_out) {
+      kpe_out[row * kRope + (c - kLatent)] = v;
+    }
+  }
+}
+
+// -------------------------------------------------------------- host side
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_cache(const mla_cache *c) {
+  if (!c) return MLA_ERR_INVALID_ARG;
+  if (c->format < MLA_FMT_BF16 || c->format > MLA_FMT_INT4) return MLA_ERR_INVALID_ARG;
+  if (c->num_layers < 1 || c->batch < 1 || c->capacity < 1) return MLA_ERR_INVALID_ARG;
+  if (c->kv_lora_rank != kLatent || c->rope_dim != kRope || c->group_latent != kGroupL ||
+      c->group_rope != kGroupR)
+    return MLA_ERR_UNSUPPORTED;
+  if (!c->ckv || !c->kpe || !c->seq_lens) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(c->ckv) || !aligned16(c->kpe) || ((uintptr_t)c->seq_lens & 3u)) return MLA_ERR_INVALID_ARG;
+  const bool quant = c->format != MLA_FMT_BF16;
+  if (quant != (c->scale != nullptr)) return MLA_ERR_INVALID_ARG;
+  if ((c->format == MLA_FMT_INT4) != (c->zero != nullptr)) return MLA_ERR_INVALID_ARG;
+  if (c->scale && !aligned16(c->scale)) return MLA_ERR_INVALID_ARG;
+  if (c->zero && !aligned16(c->zero)) return MLA_ERR_INVALID_ARG;
+  return MLA_OK;
+}
+
+int64_t ckv_row_bytes(int fmt) {
+  return fmt == MLA_FMT_BF16 ? kLatent * 2 : fmt == MLA_FMT_INT8 ? kLatent : kLatent / 2;
+}
+int64_t kpe_row_bytes(int fmt) { return fmt == MLA_FMT_BF16 ? kRope * 2 : kRope; }
+
+struct LayerPlanes {
+  void *ckv, *kpe;
+  uint16_t *scale, *zero;
+  int32_t *seq_lens;
+};
+
+LayerPlanes layer_planes(const mla_cache *c, int layer) {
+  const int64_t rows = (int64_t)layer * c->batch * c->capacity;
+  LayerPlanes p;
+  p.ckv = (uint8_t *)c->ckv + rows * ckv_row_bytes(c->format);
+  p.kpe = (uint8_t *)c->kpe + rows * kpe_row_bytes(c->format);
+  p.scale = c->scale ? c->scale + rows * kNScale : nullptr;
+  p.zero = c->zero ? c->zero + rows * kNGroupL : nullptr;
+  p.seq_lens = c->seq_lens + (int64_t)layer * c->batch;
+  return p;
+}
+
+bool heads_ok(int heads) { return heads == 16 || heads == 32 || heads == 64 || heads == 128; }
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct WsLayout {
+  size_t qa, m, l, acc, total;
+};
+
+WsLayout ws_layout(int B, int H, int nsplit) {
+  WsLayout w;
+  size_t off = 0;
+  w.qa = off;
+  off = align256(off + (size_t)B * H * kRow * 2);
+  w.m = off;
+  off = align256(off + (size_t)B * nsplit * H * 4);
+  w.l = off;
+  off = align256(off + (size_t)B * nsplit * H * 4);
+  w.acc = off;
+  off = align256(off + (size_t)B * nsplit * H * kLatent * 4);
+  w.total = off;
+  return w;
+}
+
+int auto_splits(const mla_cache *c, int heads, int *out) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return MLA_ERR_HIP;
+  if (cus < 1) cus = 1;
+  const int hh = heads <= 64 ? 1 : heads / 64;
+  const int64_t units = (int64_t)c->batch * hh;
+  int64_t want = (2 * (int64_t)cus + units - 1) / units;     // about two workgroups per CU
+  const int64_t by_len = (c->capacity + 255) / 256;           // keep >= 256 tokens per split
+  int64_t ns = want < by_len ? want : by_len;
+  if (ns < 1) ns = 1;
+  if (ns > kMaxSplits) ns = kMaxSplits;
+  *out = (int)ns;
+  return MLA_OK;
+}
+
+int chunk_for(int cap, int nsplit) {
+  int chunk = (cap + nsplit - 1) / nsplit;
+  return (chunk + kTile - 1) / kTile * kTile;
+}
+
+template <int FMT>
+hipError_t launch_split_fmt(const SplitArgs &a, int heads, dim3 grid, hipStream_t st) {
+  if (heads == 16) hipLaunchKernelGGL((split_kernel<FMT, 1>), grid, dim3(kThreads), 0, st, a);
+  else if (heads == 32) hipLaunchKernelGGL((split_kernel<FMT, 2>), grid, dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL((split_kernel<FMT, 4>), grid, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// ================================================================== C ABI
+
+extern "C" const char *mla_status_str(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported dimension or head count";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_CAPACITY: return "append exceeds cache capacity";
+    case MLA_ERR_HIP: return "HIP runtime or launch error";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int mla_cache_append(const mla_cache *cache, int32_t layer, const void *ckv_new,
+                                const void *kpe_new, int32_t t_new, const int32_t *n_new,
+                                void *hip_stream) {
+  int st = check_cache(cache);
+  if (st != MLA_OK) return st;
+  if (layer < 0 || layer >= cache->num_layers || t_new < 0) return MLA_ERR_INVALID_ARG;
+  if (t_new == 0) return MLA_OK;
+  if (!ckv_new || !kpe_new || !aligned16(ckv_new) || !aligned16(kpe_new)) return MLA_ERR_INVALID_ARG;
+  if (n_new && ((uintptr_t)n_new & 3u)) return MLA_ERR_INVALID_ARG;
+  const LayerPlanes p = layer_planes(cache, layer);
+  AppendArgs a;
+  a.ckv = p.ckv;
+  a.kpe = p.kpe;
+  a.scale = p.scale;
+  a.zero = p.zero;
+  a.seq_lens = p.seq_lens;
+  a.ckv_new = (const uint16_t *)ckv_new;
+  a.kpe_new = (const uint16_t *)kpe_new;
+  a.n_new = n_new;
+  a.B = cache->batch;
+  a.T = t_new;
+  a.cap = cache->capacity;
+  hipStream_t s = (hipStream_t)hip_stream;
+  const int64_t items = (int64_t)a.B * a.T * kNScale;
+  int64_t blocks = (items + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (cache->format == MLA_FMT_INT8)
+    hipLaunchKernelGGL(append_kernel<MLA_FMT_INT8>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  else if (cache->format == MLA_FMT_INT4)
+    hipLaunchKernelGGL(append_kernel<MLA_FMT_INT4>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(append_kernel<MLA_FMT_BF16>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
+  hipLaunchKernelGGL(seqlen_kernel, dim3((a.B + 255) / 256), dim3(256), 0, s, p.seq_lens, n_new, a.B,
+                     a.T, a.cap);
+  if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+extern "C" int mla_decode_auto_splits(const mla_cache *cache, int32_t heads, int32_t *num_splits) {
+  int st = check_cache(cache);
+  if (st != MLA_OK) return st;
+  if (!num_splits) return MLA_ERR_INVALID_ARG;
+  if (!heads_ok(heads)) return MLA_ERR_UNSUPPORTED;
+  return auto_splits(cache, heads, num_splits);
+}
+
+extern "C" int mla_decode_workspace_bytes(const mla_cache *cache, int32_t heads, int32_t num_splits,
+                                          size_t *bytes) {
+  int st = check_cache(cache);
+  if (st != MLA_OK) return st;
+  if (!bytes) return MLA_ERR_INVALID_ARG;
+  if (!heads_ok(heads)) return MLA_ERR_UNSUPPORTED;
+  if (num_splits < 0 || num_splits > kMaxSplits) return MLA_ERR_INVALID_ARG;
+  int ns = num_splits;
+  if (ns == 0) {
+    st = auto_splits(cache, heads, &ns);
+    if (st != MLA_OK) return st;
+  }
+  *bytes = ws_layout(cache->batch, heads, ns).total;
+  return MLA_OK;
+}
+
+namespace {
+
+struct DecodePlan {
+  int ns;
+  WsLayout wl;
+};
+
+// Validation shared by the decode entry points: cache, heads, split count and
+// workspace. Fills the plan (split count, workspace layout) on success.
+int plan_decode(const mla_cache *cache, int heads, int num_splits, const void *workspace,
+                size_t workspace_bytes, DecodePlan *plan) {
+  int st = check_cache(cache);
+  if (st != MLA_OK) return st;
+  if (!heads_ok(heads)) return MLA_ERR_UNSUPPORTED;
+  if (num_splits < 0 || num_splits > kMaxSplits) return MLA_ERR_INVALID_ARG;
+  int ns = num_splits;
+  if (ns == 0) {
+    st = auto_splits(cache, heads, &ns);
+    if (st != MLA_OK) return st;
+  }
+  plan->ns = ns;
+  plan->wl = ws_layout(cache->batch, heads, ns);
+  if (!workspace || workspace_bytes < plan->wl.total || ((uintptr_t)workspace & 255u))
+    return MLA_ERR_WORKSPACE;
+  return MLA_OK;
+}
+
+int check_absorb_args(const void *q_nope, const void *q_pe, const void *w_uk, float softmax_scale) {
+  if (!q_nope || !q_pe || !w_uk) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(w_uk)) return MLA_ERR_INVALID_ARG;
+  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return MLA_ERR_INVALID_ARG;
+  return MLA_OK;
+}
+
+int check_combine_args(const void *w_uv, const float *out) {
+  if (!w_uv || !out || !aligned16(w_uv) || !aligned16(out)) return MLA_ERR_INVALID_ARG;
+  return MLA_OK;
+}
+
+int run_absorb(const mla_cache *cache, const DecodePlan &pl, const void *q_nope, const void *q_pe,
+               const void *w_uk, int heads, float softmax_scale, void *workspace, hipStream_t s) {
+  const int B = cache->batch;
+  _Float16 *qa = (_Float16 *)((uint8_t *)workspace + pl.wl.qa);
+  hipLaunchKernelGGL(absorb_kernel, dim3(heads, (B + kAbsorbBT - 1) / kAbsorbBT), dim3(256), 0, s,
+                     (const uint16_t *)q_nope, (const uint16_t *)q_pe, (const uint16_t *)w_uk, B, heads,
+                     softmax_scale * kLog2e, qa);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int run_partial(const mla_cache *cache, const DecodePlan &pl, int layer, int heads, void *workspace,
+                hipStream_t s) {
+  const LayerPlanes p = layer_planes(cache, layer);
+  uint8_t *ws = (uint8_t *)workspace;
+  SplitArgs a;
+  a.ckv = p.ckv;
+  a.kpe = p.kpe;
+  a.scale = p.scale;
+  a.zero = p.zero;
+  a.seq_lens = p.seq_lens;
+  a.qa = (const _Float16 *)(ws + pl.wl.qa);
+  a.ws_m = (float *)(ws + pl.wl.m);
+  a.ws_l = (float *)(ws + pl.wl.l);
+  a.ws_acc = (float *)(ws + pl.wl.acc);
+  a.B = cache->batch;
+  a.H = heads;
+  a.cap = cache->capacity;
+  a.nsplit = pl.ns;
+  a.chunk = chunk_for(cache->capacity, pl.ns);
+  a.hh_count = heads <= 64 ? 1 : heads / 64;
+  const dim3 grid((unsigned)(pl.ns * a.hh_count), (unsigned)cache->batch);
+  hipError_t e;
+  if (cache->format == MLA_FMT_INT8) e = launch_split_fmt<MLA_FMT_INT8>(a, heads, grid, s);
+  else if (cache->format == MLA_FMT_INT4) e = launch_split_fmt<MLA_FMT_INT4>(a, heads, grid, s);
+  else e = launch_split_fmt<MLA_FMT_BF16>(a, heads, grid, s);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int run_combine(const mla_cache *cache, const DecodePlan &pl, const void *w_uv, int heads,
+                void *workspace, float *out, hipStream_t s) {
+  const int B = cache->batch;
+  uint8_t *ws = (uint8_t *)workspace;
+  hipLaunchKernelGGL(reduce_kernel, dim3(heads, (B + kAbsorbBT - 1) / kAbsorbBT), dim3(256), 0, s,
+                     (const float *)(ws + pl.wl.m), (const float *)(ws + pl.wl.l),
+                     (const float *)(ws + pl.wl.acc), (const uint16_t *)w_uv, B, heads, pl.ns, out);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int mla_decode_attn(const mla_cache *cache, int32_t layer, const void *q_nope,
+                               const void *q_pe, const void *w_uk, const void *w_uv, int32_t heads,
+                               float softmax_scale, int32_t num_splits, void *workspace,
+                               size_t workspace_bytes, float *out, void *hip_stream) {
+  int st = check_cache(cache);
+  if (st != MLA_OK) return st;
+  if (layer < 0 || layer >= cache->num_layers) return MLA_ERR_INVALID_ARG;
+  if (!heads_ok(heads)) return MLA_ERR_UNSUPPORTED;
+  if ((st = check_absorb_args(q_nope, q_pe, w_uk, softmax_scale)) != MLA_OK) return st;
+  if ((st = check_combine_args(w_uv, out)) != MLA_OK) return st;
+  DecodePlan pl;
+  if ((st = plan_decode(cache, heads, num_splits, workspace, workspace_bytes, &pl)) != MLA_OK) return st;
+  hipStream_t s = (hipStream_t)hip_stream;
+  if ((st = run_absorb(cache, pl, q_nope, q_pe, w_uk, heads, softmax_scale, workspace, s)) != MLA_OK)
+    return st;
+  if ((st = run_partial(cache, pl, layer, heads, workspace, s)) != MLA_OK) return st;
+  return run_combine(cache, pl, w_uv, heads, workspace, out, s);
+}
+
+extern "C" int mla_decode_absorb(const mla_cache *cache, const void *q_nope, const void *q_pe,
+                                 const void *w_uk, int32_t heads, float softmax_scale,
+                                 int32_t num_splits, void *workspace, size_t workspace_bytes,
+                                 void *hip_stream) {
+  int st = check_cache(cache);
+  if (st != MLA_OK) return st;
+  if (!heads_ok(heads)) return MLA_ERR_UNSUPPORTED;
+  if ((st = check_absorb_args(q_nope, q_pe, w_uk, softmax_scale)) != MLA_OK) return st;
+  DecodePlan pl;
+  if ((st = plan_decode(cache, heads, num_splits, workspace, workspace_bytes, &pl)) != MLA_OK) return st;
+  return run_absorb(cache, pl, q_nope, q_pe, w_uk, heads, softmax_scale, workspace,
+                    (hipStream_t)hip_stream);
+}
+
+extern "C" int mla_decode_partial(const mla_cache *cache, int32_t layer, int32_t heads,
+                                  int32_t num_splits, void *workspace, size_t workspace_bytes,
+                                  void *hip_stream) {
+  int st = check_cache(cache);
+  if (st != MLA_OK) return st;
+  if (layer < 0 || layer >= cache->num_layers) return MLA_ERR_INVALID_ARG;
+  DecodePlan pl;
+  if ((st = plan_decode(cache, heads, num_splits, workspace, workspace_bytes, &pl)) != MLA_OK) return st;
+  return run_partial(cache, pl, layer, heads, workspace, (hipStream_t)hip_stream);
+}
+
+extern "C" int mla_decode_combine(const mla_cache *cache, const void *w_uv, int32_t heads,
+                                  int32_t num_splits, void *workspace, size_t workspace_bytes,
+                                  float *out, void *hip_stream) {
+  int st = check_cache(cache);
+  if (st != MLA_OK) return st;
+  if (!heads_ok(heads)) return MLA_ERR_UNSUPPORTED;
+  if ((st = check_combine_args(w_uv, out)) != MLA_OK) return st;
+  DecodePlan pl;
+  if ((st = plan_decode(cache, heads, num_splits, workspace, workspace_bytes, &pl)) != MLA_OK) return st;
+  return run_combine(cache, pl, w_uv, heads, workspace, out, (hipStream_t)hip_stream);
+}
+
+extern "C" int mla_cache_get(const mla_cache *cache, int32_t layer, float *ckv_out, float *kpe_out,
+                             void *hip_stream) {
+  int st = check_cache(cache);
+  if (st != MLA_OK) return st;
+  if (layer < 0 || layer >= cache->num_layers) return MLA_ERR_INVALID_ARG;
+  if (!ckv_out && !kpe_out) return MLA_OK;
+  const LayerPlanes p = layer_planes(cache, layer);
+  hipStream_t s = (hipStream_t)hip_stream;
+  const int64_t total = (int64_t)cache->batch * cache->capacity * kRow;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  const dim3 g((unsigned)blocks), bl(256);
+  if (cache->format == MLA_FMT_INT8)
+    hipLaunchKernelGGL(get_kernel<MLA_FMT_INT8>, g, bl, 0, s, p.ckv, p.kpe, p.scale, p.zero, p.seq_lens,
+                       cache->batch, cache->capacity, ckv_out, kpe_out);
+  else if (cache->format == MLA_FMT_INT4)
+    hipLaunchKernelGGL(get_kernel<MLA_FMT_INT4>, g, bl, 0, s, p.ckv, p.kpe, p.scale, p.zero, p.seq_lens,
+                       cache->batch, cache->capacity, ckv_out, kpe_out);
+  else
+    hipLaunchKernelGGL(get_kernel<MLA_FMT_BF16>, g, bl, 0, s, p.ckv, p.kpe, p.scale, p.zero, p.seq_lens,
+                       cache->batch, cache->capacity, ckv_out, kpe_out);
+  if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
+  return MLA_OK;
+}

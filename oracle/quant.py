@@ -18,8 +18,8 @@ What the pages fix, and the reading taken where they leave it open:
   by the STORED scale, so dequantization uses exactly the value quantization
   used; round() is round-half-to-even; codes are clamped to [-127, 127].
 * Asymmetric INT4 (report section 3.2, "非对称"): reading: a float offset z
-  (fp16, the group minimum rounded toward -inf, a zero stored as +0) and an fp16 scale
-  s = (max - z) / 15; codes = clamp(rne((x - z) / s), 0, 15); x_hat = q*s + z.
+  (fp16, the group minimum rounded toward -inf) and an fp16 scale
+  s = (max - z) / 15, each stored as +0 when zero; codes = clamp(rne((x - z) / s), 0, 15); x_hat = q*s + z.
   Two codes per byte, the even channel in the low nibble.
 
 Arithmetic: inputs are bf16 values widened to fp32 (exact). Every step below is
@@ -124,6 +124,9 @@ def quantize_asym_int4(x, group):
     z = fp16_round_down(mn)
     zf = z.astype(np.float32)
     s = fp16_rne((mx - zf) / F32(15.0))
+    # a zero scale is stored as +0: for a group of zeros of both signs, the
+    # sign of max - z would depend on which zero min and max happen to pick
+    s = np.where(s == 0, np.float16(0.0), s).astype(np.float16)
     sf = s.astype(np.float32)[..., None]
     nonzero = sf != 0
     with np.errstate(divide="ignore", invalid="ignore"):

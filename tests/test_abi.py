@@ -1,0 +1,162 @@
+"""The C ABI without a GPU: the library loads, exports what include/mla_kv.h
+declares, and rejects bad arguments on the host before launching anything.
+
+Device pointers below are fake (never dereferenced): every call here returns
+from host-side validation.
+"""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from mla_latent_kv_cache_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7F0000000000  # 256-byte aligned, never dereferenced
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "mla_kv.h")).read()
+    return sorted(set(re.findall(r"^(?:int|size_t|const char \*)\s*\**\s*(mla_\w+)\s*\(", src, re.M)))
+
+
+def cache_struct(fmt="int8", L=2, B=3, cap=100, **over):
+    f = _lib.FORMATS[fmt]
+    s = _lib.MlaCacheStruct(f, L, B, cap, 512, 64, 16, 8, FAKE, FAKE + 0x100000,
+                            FAKE + 0x200000 if fmt != "bf16" else 0,
+                            FAKE + 0x300000 if fmt == "int4" else 0, FAKE + 0x400000)
+    for k, v in over.items():
+        setattr(s, k, v)
+    return s
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = _lib.lib()
+    declared = header_functions()
+    assert set(declared) == set(_lib.SYMBOLS), declared
+    for name in declared:
+        assert hasattr(L, name)
+
+
+def test_status_strings():
+    for st in (0, -1, -2, -3, -4, -5):
+        assert _lib.status_str(st) and _lib.status_str(st) != "unknown status"
+    assert _lib.status_str(-99) == "unknown status"
+
+
+def _ws(s, heads=16, splits=4):
+    n = ctypes.c_size_t(0)
+    st = _lib.lib().mla_decode_workspace_bytes(ctypes.byref(s), heads, splits, ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_size_formula():
+    s = cache_struct(B=3)
+    st, n = _ws(s, 16, 4)
+    assert st == 0
+
+    def a256(v):
+        return (v + 255) // 256 * 256
+    B, H, ns = 3, 16, 4
+    expect = a256(B * H * 576 * 2) + 2 * a256(B * ns * H * 4) + a256(B * ns * H * 512 * 4)
+    assert n == expect
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("format", 7, _lib.MLA_ERR_INVALID_ARG),
+    ("num_layers", 0, _lib.MLA_ERR_INVALID_ARG),
+    ("batch", 0, _lib.MLA_ERR_INVALID_ARG),
+    ("capacity", 0, _lib.MLA_ERR_INVALID_ARG),
+    ("kv_lora_rank", 256, _lib.MLA_ERR_UNSUPPORTED),
+    ("rope_dim", 32, _lib.MLA_ERR_UNSUPPORTED),
+    ("group_latent", 32, _lib.MLA_ERR_UNSUPPORTED),
+    ("group_rope", 16, _lib.MLA_ERR_UNSUPPORTED),
+    ("ckv", 0, _lib.MLA_ERR_INVALID_ARG),
+    ("seq_lens", 0, _lib.MLA_ERR_INVALID_ARG),
+    ("ckv", FAKE + 8, _lib.MLA_ERR_INVALID_ARG),  # not 16-byte aligned
+    ("scale", 0, _lib.MLA_ERR_INVALID_ARG),       # quantized format needs scales
+    ("zero", FAKE, _lib.MLA_ERR_INVALID_ARG),     # INT8 has no zero-points
+])
+def test_cache_descriptor_validation(field, value, status):
+    s = cache_struct("int8", **{field: value})
+    assert _ws(s)[0] == status
+
+
+def test_format_plane_rules():
+    assert _ws(cache_struct("bf16"))[0] == 0
+    assert _ws(cache_struct("bf16", scale=FAKE))[0] == _lib.MLA_ERR_INVALID_ARG
+    assert _ws(cache_struct("int4"))[0] == 0
+    assert _ws(cache_struct("int4", zero=0))[0] == _lib.MLA_ERR_INVALID_ARG
+
+
+def test_null_cache_and_outputs():
+    L = _lib.lib()
+    n = ctypes.c_size_t(0)
+    assert L.mla_decode_workspace_bytes(None, 16, 1, ctypes.byref(n)) == _lib.MLA_ERR_INVALID_ARG
+    s = cache_struct()
+    assert L.mla_decode_workspace_bytes(ctypes.byref(s), 16, 1, None) == _lib.MLA_ERR_INVALID_ARG
+    assert L.mla_cache_append(None, 0, FAKE, FAKE, 1, None, None) == _lib.MLA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("heads", [0, 8, 17, 48, 96, 256])
+def test_unsupported_head_counts(heads):
+    assert _ws(cache_struct(), heads=heads)[0] == _lib.MLA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("splits", [-1, 4097])
+def test_split_count_range(splits):
+    assert _ws(cache_struct(), splits=splits)[0] == _lib.MLA_ERR_INVALID_ARG
+
+
+def _decode(s, layer=0, heads=16, scale=0.07, splits=4, ws=FAKE, ws_bytes=None, q=FAKE, out=FAKE):
+    if ws_bytes is None:
+        ws_bytes = _ws(s, heads, splits)[1]
+    return _lib.lib().mla_decode_attn(ctypes.byref(s), layer, q, FAKE, FAKE, FAKE, heads, scale, splits,
+                                      ws, ws_bytes, out, None)
+
+
+def test_decode_argument_validation_before_launch():
+    s = cache_struct()
+    assert _decode(s, layer=2) == _lib.MLA_ERR_INVALID_ARG
+    assert _decode(s, layer=-1) == _lib.MLA_ERR_INVALID_ARG
+    assert _decode(s, heads=24) == _lib.MLA_ERR_UNSUPPORTED
+    assert _decode(s, scale=math.nan) == _lib.MLA_ERR_INVALID_ARG
+    assert _decode(s, scale=math.inf) == _lib.MLA_ERR_INVALID_ARG
+    assert _decode(s, q=0) == _lib.MLA_ERR_INVALID_ARG
+    assert _decode(s, q=FAKE + 4) == _lib.MLA_ERR_INVALID_ARG
+    assert _decode(s, out=0) == _lib.MLA_ERR_INVALID_ARG
+    assert _decode(s, ws=0) == _lib.MLA_ERR_WORKSPACE
+    assert _decode(s, ws=FAKE + 16) == _lib.MLA_ERR_WORKSPACE  # workspace must be 256-byte aligned
+    need = _ws(s, 16, 4)[1]
+    assert _decode(s, ws_bytes=need - 1) == _lib.MLA_ERR_WORKSPACE
+
+
+def test_append_argument_validation_before_launch():
+    L = _lib.lib()
+    s = cache_struct()
+    b = ctypes.byref(s)
+    assert L.mla_cache_append(b, 5, FAKE, FAKE, 1, None, None) == _lib.MLA_ERR_INVALID_ARG
+    assert L.mla_cache_append(b, 0, FAKE, FAKE, -1, None, None) == _lib.MLA_ERR_INVALID_ARG
+    assert L.mla_cache_append(b, 0, 0, FAKE, 1, None, None) == _lib.MLA_ERR_INVALID_ARG
+    assert L.mla_cache_append(b, 0, FAKE, FAKE + 2, 1, None, None) == _lib.MLA_ERR_INVALID_ARG
+    assert L.mla_cache_append(b, 0, FAKE, FAKE, 1, FAKE + 2, None) == _lib.MLA_ERR_INVALID_ARG
+    # zero new tokens is a no-op that launches nothing
+    assert L.mla_cache_append(b, 0, 0, 0, 0, None, None) == _lib.MLA_OK
+
+
+def test_get_argument_validation_before_launch():
+    L = _lib.lib()
+    s = cache_struct()
+    assert L.mla_cache_get(ctypes.byref(s), 2, FAKE, FAKE, None) == _lib.MLA_ERR_INVALID_ARG
+    assert L.mla_cache_get(ctypes.byref(s), 0, None, None, None) == _lib.MLA_OK
+
+
+def test_python_binding_has_no_fallback(monkeypatch, tmp_path):
+    # With the library missing the binding raises instead of computing anything.
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.lib()

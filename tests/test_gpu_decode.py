@@ -1,0 +1,101 @@
+"""Absorbed decode on the GPU against the fp64 oracle, on small problems that
+still span several tiles and splits and have ragged tails."""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import assert_close, f32, oracle_decode, random_problem
+
+pytestmark = pytest.mark.gpu
+TAU = 1.0 / np.sqrt(192.0)
+
+
+def check_all(cache, rows, q_nope, q_pe, w_uk, w_uv, out, fmt, what):
+    for b, (c, k) in enumerate(rows):
+        ref = oracle_decode(c, k, fmt, q_nope[b], q_pe[b], w_uk, w_uv, TAU)
+        assert_close(f32(out[b]), ref, f"{what} seq {b} (len {c.shape[0]})")
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "int8", "int4"])
+@pytest.mark.parametrize("heads", [16, 32, 64, 128])
+def test_decode_formats_and_heads(fmt, heads):
+    lens = [1, 17, 600, 0]
+    cache, rows, qn, qp, wuk, wuv = random_problem(fmt, 4, heads, lens, seed=heads + len(fmt))
+    for splits in (1, 3, 0):
+        out = cache.decode(0, qn, qp, wuk, wuv, TAU, num_splits=splits)
+        torch.cuda.synchronize()
+        check_all(cache, rows, qn, qp, wuk, wuv, out, fmt, f"{fmt} H{heads} splits {splits}")
+        assert not out[3].any()  # empty sequence -> zeros
+
+
+@pytest.mark.parametrize("fmt", ["int8", "int4"])
+def test_tile_and_split_boundaries(fmt):
+    lens = [15, 16, 17, 31, 32, 33, 63, 64, 65, 255, 256, 257]
+    cache, rows, qn, qp, wuk, wuv = random_problem(fmt, len(lens), 16, lens, seed=5, cap=272)
+    for splits in (1, 2, 4, 17):
+        out = cache.decode(0, qn, qp, wuk, wuv, TAU, num_splits=splits)
+        torch.cuda.synchronize()
+        check_all(cache, rows, qn, qp, wuk, wuv, out, fmt, f"{fmt} splits {splits}")
+
+
+def test_split_count_invariance_and_determinism():
+    lens = [3000, 1234]
+    cache, rows, qn, qp, wuk, wuv = random_problem("int8", 2, 16, lens, seed=9)
+    outs = {}
+    for splits in (1, 2, 7, 64, 188, 0):
+        o1 = cache.decode(0, qn, qp, wuk, wuv, TAU, num_splits=splits)
+        o2 = cache.decode(0, qn, qp, wuk, wuv, TAU, num_splits=splits)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2), f"splits {splits}: two runs differ"
+        check_all(cache, rows, qn, qp, wuk, wuv, o1, "int8", f"splits {splits}")
+        outs[splits] = f32(o1)
+    base = outs[1]
+    for s, o in outs.items():
+        assert np.max(np.abs(o - base)) <= 1e-3 * (1 + np.abs(base).max()), s
+
+
+def test_workspace_contents_do_not_matter():
+    cache, rows, qn, qp, wuk, wuv = random_problem("int4", 3, 16, [100, 700, 5], seed=13)
+    ws = cache.workspace(16, 5)
+    ws.fill_(0xFF)  # NaN patterns everywhere
+    out = cache.decode(0, qn, qp, wuk, wuv, TAU, num_splits=5, workspace=ws)
+    ws.zero_()
+    out2 = cache.decode(0, qn, qp, wuk, wuv, TAU, num_splits=5, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    check_all(cache, rows, qn, qp, wuk, wuv, out, "int4", "garbage workspace")
+
+
+def test_decode_sees_appended_tokens():
+    # decode after an append attends to the new rows too
+    cache, rows, qn, qp, wuk, wuv = random_problem("int8", 2, 16, [40, 40], seed=21, cap=48)
+    from gpu_util import random_rows
+    c, k = random_rows(8, 999)
+    cache.append(0, torch.stack([c, c]).contiguous(), torch.stack([k, k]).contiguous())
+    out = cache.decode(0, qn, qp, wuk, wuv, TAU)
+    torch.cuda.synchronize()
+    rows2 = [(torch.cat([rc, c]), torch.cat([rk, k])) for rc, rk in rows]
+    check_all(cache, rows2, qn, qp, wuk, wuv, out, "int8", "after append")
+
+
+def test_extreme_scores_stay_finite():
+    # large query norms give large score gaps; the online softmax must not overflow
+    cache, rows, qn, qp, wuk, wuv = random_problem("int8", 2, 16, [500, 70], seed=31)
+    qn = (qn.float() * 4).to(torch.bfloat16)
+    qp = (qp.float() * 4).to(torch.bfloat16)
+    out = cache.decode(0, qn, qp, wuk, wuv, TAU, num_splits=3)
+    torch.cuda.synchronize()
+    check_all(cache, rows, qn, qp, wuk, wuv, out, "int8", "large scores")
+
+
+def test_three_phases_equal_one_call():
+    cache, rows, qn, qp, wuk, wuv = random_problem("int4", 3, 32, [333, 18, 1000], seed=41)
+    ws = cache.workspace(32, 6)
+    ref = cache.decode(0, qn, qp, wuk, wuv, TAU, num_splits=6, workspace=ws)
+    ws2 = cache.workspace(32, 6)
+    cache.decode_absorb(qn, qp, wuk, TAU, ws2, num_splits=6)
+    cache.decode_partial(0, 32, ws2, num_splits=6)
+    out = cache.decode_combine(wuv, ws2, num_splits=6)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)

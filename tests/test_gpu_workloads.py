@@ -1,0 +1,129 @@
+"""The five named workloads at their full sizes, in the launch configuration
+the benchmark times: caches prefilled through mla_cache_append, codes checked
+bit-exactly on sampled sequences, and decode outputs of sampled sequences
+checked against the fp64 oracle one by one."""
+
+import numpy as np
+import pytest
+import torch
+
+from mla_latent_kv_cache_amd import workloads as W
+
+from gpu_util import (assert_close, assert_planes_equal, build_workload, f32, oracle_decode,
+                      oracle_planes)
+
+pytestmark = pytest.mark.gpu
+
+
+def rows_of(wid, layer, b, n):
+    return W.latent_rows(wid, layer, b, n, device="cuda")
+
+
+def check_sequences(wid, cache, layer, samples, out, q_nope, q_pe, w_uk, w_uv, extra=None):
+    w = W.WORKLOADS[wid]
+    lens = cache.lengths(layer)
+    for b in samples:
+        c, k = rows_of(wid, layer, b, int(W.lengths(wid)[b]))
+        if extra is not None:
+            c = torch.cat([c, extra[0][b]])
+            k = torch.cat([k, extra[1][b]])
+        assert c.shape[0] == lens[b]
+        ref = oracle_decode(c, k, w.fmt, q_nope[b], q_pe[b], w_uk, w_uv)
+        err = assert_close(f32(out[b]), ref, f"{w.name} layer {layer} seq {b}")
+        print(f"  {w.name} layer {layer} seq {b} len {lens[b]}: max abs err {err:.2e}", flush=True)
+
+
+def check_codes(wid, cache, layer, b, nrows=None):
+    w = W.WORKLOADS[wid]
+    n = int(W.lengths(wid)[b])
+    c, k = rows_of(wid, layer, b, n)
+    got = cache.planes(layer, b)
+    if nrows is not None:  # a sample of rows spread over the sequence
+        idx = np.unique(np.linspace(0, n - 1, nrows).astype(int))
+        got = {key: v[idx] for key, v in got.items()}
+        c, k = c[idx], k[idx]
+    assert_planes_equal(got, oracle_planes(c, k, w.fmt), w.fmt, f"{w.name} layer {layer} seq {b}")
+
+
+def test_workload0_bf16_full():
+    wid = 0
+    cache, lens = build_workload(wid)
+    check_codes(wid, cache, 0, 0)
+    qn, qp = W.queries(wid, 0, "cuda")
+    wuk, wuv = W.weights(wid, 0, "cuda")
+    out = cache.decode(0, qn, qp, wuk, wuv, W.SOFTMAX_SCALE, num_splits=W.WORKLOADS[wid].num_splits)
+    torch.cuda.synchronize()
+    check_sequences(wid, cache, 0, range(1), out, qn, qp, wuk, wuv)
+
+
+def test_workload1_int8_append64_full():
+    wid = 1
+    w = W.WORKLOADS[wid]
+    cache, lens = build_workload(wid)
+    for b in (0, 7):
+        check_codes(wid, cache, 0, b)
+    qn, qp = W.queries(wid, 0, "cuda")
+    wuk, wuv = W.weights(wid, 0, "cuda")
+    out = cache.decode(0, qn, qp, wuk, wuv, W.SOFTMAX_SCALE, num_splits=w.num_splits)
+    torch.cuda.synchronize()
+    check_sequences(wid, cache, 0, range(w.batch), out, qn, qp, wuk, wuv)
+    # quantize-on-append of 64 tokens per sequence, then decode over 4160
+    new = W.latent_batch(wid, 0, w.append, device="cuda", kind="append")
+    cache.append(0, *new)
+    out = cache.decode(0, qn, qp, wuk, wuv, W.SOFTMAX_SCALE, num_splits=w.num_splits)
+    torch.cuda.synchronize()
+    assert cache.lengths(0).tolist() == [4096 + 64] * w.batch
+    check_sequences(wid, cache, 0, range(w.batch), out, qn, qp, wuk, wuv, extra=new)
+    got = cache.planes(0, 3)
+    tail = {key: v[4096:] for key, v in got.items()}
+    assert_planes_equal(tail, oracle_planes(new[0][3], new[1][3], "int8"), "int8", "appended rows")
+
+
+def test_workload2_int4_full_sampled():
+    wid = 2
+    w = W.WORKLOADS[wid]
+    cache, lens = build_workload(wid)
+    check_codes(wid, cache, 0, 0)
+    check_codes(wid, cache, 0, 31, nrows=2000)
+    qn, qp = W.queries(wid, 0, "cuda")
+    wuk, wuv = W.weights(wid, 0, "cuda")
+    out = cache.decode(0, qn, qp, wuk, wuv, W.SOFTMAX_SCALE, num_splits=w.num_splits)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    check_sequences(wid, cache, 0, (0, 13, 31), out, qn, qp, wuk, wuv)
+
+
+def test_workload3_int8_full_stack_ragged_sampled():
+    wid = 3
+    w = W.WORKLOADS[wid]
+    cache, lens = build_workload(wid)
+    assert cache.lengths().shape == (27, 64)
+    assert (cache.lengths() == lens[None]).all()
+    samples = {0: (0, 63), 13: (int(np.argmax(lens)),), 26: (int(np.argmin(lens)), 40)}
+    wuk_all, wuv_all, q_all, outs = {}, {}, {}, {}
+    for layer in range(w.layers):
+        qn, qp = W.queries(wid, layer, "cuda")
+        wuk, wuv = W.weights(wid, layer, "cuda")
+        outs[layer] = cache.decode(layer, qn, qp, wuk, wuv, W.SOFTMAX_SCALE, num_splits=w.num_splits)
+        if layer in samples:
+            q_all[layer], wuk_all[layer], wuv_all[layer] = (qn, qp), wuk, wuv
+    torch.cuda.synchronize()
+    for layer in range(w.layers):
+        assert torch.isfinite(outs[layer]).all(), layer
+    for layer, bs in samples.items():
+        check_codes(wid, cache, layer, bs[0], nrows=500)
+        qn, qp = q_all[layer]
+        check_sequences(wid, cache, layer, bs, outs[layer], qn, qp, wuk_all[layer], wuv_all[layer])
+
+
+def test_workload4_int4_wide_heads_64_splits_sampled():
+    wid = 4
+    w = W.WORKLOADS[wid]
+    cache, lens = build_workload(wid)
+    check_codes(wid, cache, 0, 5, nrows=3000)
+    qn, qp = W.queries(wid, 0, "cuda")
+    wuk, wuv = W.weights(wid, 0, "cuda")
+    out = cache.decode(0, qn, qp, wuk, wuv, W.SOFTMAX_SCALE, num_splits=w.num_splits)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    check_sequences(wid, cache, 0, (0, 11), out, qn, qp, wuk, wuv)

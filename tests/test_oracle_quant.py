@@ -275,3 +275,11 @@ def test_zero_point_of_negative_zero_is_positive_zero():
     x = np.array([-0.0] + [1.0] * 15, np.float32)
     q, s, z = Q.quantize_asym_int4(x, 16)
     assert int(z.view(np.uint16)[0]) == 0
+
+
+def test_zero_scale_is_positive_zero():
+    # groups of signed zeros: neither the scale nor the zero-point may carry a sign
+    for vals in ([-0.0] * 16, [0.0, -0.0] * 8, [-0.0] * 15 + [0.0]):
+        q, s, z = Q.quantize_asym_int4(np.array(vals, np.float32), 16)
+        assert int(s.view(np.uint16)[0]) == 0 and int(z.view(np.uint16)[0]) == 0
+        assert not q.any()
