@@ -148,14 +148,91 @@ struct AppendArgs {
   void *kpe;
   uint16_t *scale;
   uint16_t *zero;
-  const int32_t *seq_lens;  // layer row of seq_lens
+  int32_t *seq_lens;        // layer row of seq_lens
   const uint16_t *ckv_new;  // bf16 [B][T][512]
   const uint16_t *kpe_new;  // bf16 [B][T][64]
   const int32_t *n_new;     // optional [B]
   int B, T, cap;
 };
 
-// One thread per quantization group: 32 latent groups then 8 k_pe groups per token.
+// Quantize and store one group (grp < 32: latent group, else k_pe group) of
+// new token t of sequence b at row `pos` of the cache.
+template <int FMT>
+__device__ __forceinline__ void append_group(const AppendArgs &a, int b, int t, int grp, int pos) {
+  const int64_t row = (int64_t)b * a.cap + pos;
+  if (grp < kNGroupL) {
+    const uint16_t *src = a.ckv_new + ((int64_t)b * a.T + t) * kLatent + grp * kGroupL;
+    const u32x4 v0 = *(const u32x4 *)src;
+    const u32x4 v1 = *(const u32x4 *)(src + 8);
+    if (FMT == MLA_FMT_BF16) {
+      u32x4 *dst = (u32x4 *)((uint16_t *)a.ckv + row * kLatent + grp * kGroupL);
+      dst[0] = v0;
+      dst[1] = v1;
+      return;
+    }
+    float x[kGroupL];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf16_bits_to_f32(v0[i] & 0xFFFFu);
+      x[2 * i + 1] = bf16_bits_to_f32(v0[i] >> 16);
+      x[8 + 2 * i] = bf16_bits_to_f32(v1[i] & 0xFFFFu);
+      x[8 + 2 * i + 1] = bf16_bits_to_f32(v1[i] >> 16);
+    }
+    if (FMT == MLA_FMT_INT8) {
+      int8_t q[kGroupL];
+      const uint16_t sb = quant_sym8<kGroupL>(x, q);
+      u32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = (uint32_t)(uint8_t)q[4 * i] | ((uint32_t)(uint8_t)q[4 * i + 1] << 8) |
+               ((uint32_t)(uint8_t)q[4 * i + 2] << 16) | ((uint32_t)(uint8_t)q[4 * i + 3] << 24);
+      *(u32x4 *)((int8_t *)a.ckv + row * kLatent + grp * kGroupL) = w;
+      a.scale[row * kNScale + grp] = sb;
+    } else {
+      uint8_t q[kGroupL];
+      uint16_t sb, zb;
+      quant_asym4(x, q, sb, zb);
+      u32x2 w;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v |= (uint32_t)q[8 * i + j] << (4 * j);
+        w[i] = v;
+      }
+      *(u32x2 *)((uint8_t *)a.ckv + row * (kLatent / 2) + grp * (kGroupL / 2)) = w;
+      a.scale[row * kNScale + grp] = sb;
+      a.zero[row * kNGroupL + grp] = zb;
+    }
+  } else {
+    const int g = grp - kNGroupL;
+    const uint16_t *src = a.kpe_new + ((int64_t)b * a.T + t) * kRope + g * kGroupR;
+    const u32x4 v = *(const u32x4 *)src;
+    if (FMT == MLA_FMT_BF16) {
+      *(u32x4 *)((uint16_t *)a.kpe + row * kRope + g * kGroupR) = v;
+      return;
+    }
+    float x[kGroupR];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf16_bits_to_f32(v[i] & 0xFFFFu);
+      x[2 * i + 1] = bf16_bits_to_f32(v[i] >> 16);
+    }
+    int8_t q[kGroupR];
+    const uint16_t sb = quant_sym8<kGroupR>(x, q);
+    u32x2 w;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      w[i] = (uint32_t)(uint8_t)q[4 * i] | ((uint32_t)(uint8_t)q[4 * i + 1] << 8) |
+             ((uint32_t)(uint8_t)q[4 * i + 2] << 16) | ((uint32_t)(uint8_t)q[4 * i + 3] << 24);
+    *(u32x2 *)((int8_t *)a.kpe + row * kRope + g * kGroupR) = w;
+    a.scale[row * kNScale + grp] = sb;
+  }
+}
+
+// Bulk append: one thread per quantization group, grid-stride over B*T*40.
+// seq_lens advances in seqlen_kernel, launched after it on the same stream,
+// so every block reads the old length.
 template <int FMT>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int64_t total = (int64_t)a.B * a.T * kNScale;
@@ -169,80 +246,10 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     if (t >= n) continue;
     const int pos = a.seq_lens[b] + t;
     if (pos < 0 || pos >= a.cap) continue;
-    const int64_t row = (int64_t)b * a.cap + pos;
-    if (grp < kNGroupL) {
-      const uint16_t *src = a.ckv_new + ((int64_t)b * a.T + t) * kLatent + grp * kGroupL;
-      const u32x4 v0 = *(const u32x4 *)src;
-      const u32x4 v1 = *(const u32x4 *)(src + 8);
-      if (FMT == MLA_FMT_BF16) {
-        u32x4 *dst = (u32x4 *)((uint16_t *)a.ckv + row * kLatent + grp * kGroupL);
-        dst[0] = v0;
-        dst[1] = v1;
-        continue;
-      }
-      float x[kGroupL];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[2 * i] = bf16_bits_to_f32(v0[i] & 0xFFFFu);
-        x[2 * i + 1] = bf16_bits_to_f32(v0[i] >> 16);
-        x[8 + 2 * i] = bf16_bits_to_f32(v1[i] & 0xFFFFu);
-        x[8 + 2 * i + 1] = bf16_bits_to_f32(v1[i] >> 16);
-      }
-      if (FMT == MLA_FMT_INT8) {
-        int8_t q[kGroupL];
-        const uint16_t sb = quant_sym8<kGroupL>(x, q);
-        u32x4 w;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          w[i] = (uint32_t)(uint8_t)q[4 * i] | ((uint32_t)(uint8_t)q[4 * i + 1] << 8) |
-                 ((uint32_t)(uint8_t)q[4 * i + 2] << 16) | ((uint32_t)(uint8_t)q[4 * i + 3] << 24);
-        *(u32x4 *)((int8_t *)a.ckv + row * kLatent + grp * kGroupL) = w;
-        a.scale[row * kNScale + grp] = sb;
-      } else {
-        uint8_t q[kGroupL];
-        uint16_t sb, zb;
-        quant_asym4(x, q, sb, zb);
-        u32x2 w;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          uint32_t v = 0;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) v |= (uint32_t)q[8 * i + j] << (4 * j);
-          w[i] = v;
-        }
-        *(u32x2 *)((uint8_t *)a.ckv + row * (kLatent / 2) + grp * (kGroupL / 2)) = w;
-        a.scale[row * kNScale + grp] = sb;
-        a.zero[row * kNGroupL + grp] = zb;
-      }
-    } else {
-      const int g = grp - kNGroupL;
-      const uint16_t *src = a.kpe_new + ((int64_t)b * a.T + t) * kRope + g * kGroupR;
-      const u32x4 v = *(const u32x4 *)src;
-      if (FMT == MLA_FMT_BF16) {
-        *(u32x4 *)((uint16_t *)a.kpe + row * kRope + g * kGroupR) = v;
-        continue;
-      }
-      float x[kGroupR];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[2 * i] = bf16_bits_to_f32(v[i] & 0xFFFFu);
-        x[2 * i + 1] = bf16_bits_to_f32(v[i] >> 16);
-      }
-      int8_t q[kGroupR];
-      const uint16_t sb = quant_sym8<kGroupR>(x, q);
-      u32x2 w;
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        w[i] = (uint32_t)(uint8_t)q[4 * i] | ((uint32_t)(uint8_t)q[4 * i + 1] << 8) |
-               ((uint32_t)(uint8_t)q[4 * i + 2] << 16) | ((uint32_t)(uint8_t)q[4 * i + 3] << 24);
-      *(u32x2 *)((int8_t *)a.kpe + row * kRope + g * kGroupR) = w;
-      a.scale[row * kNScale + grp] = sb;
-    }
+    append_group<FMT>(a, b, t, grp, pos);
   }
 }
 
-// Runs after append_kernel on the same stream, so every block of the append
-// has read the old length before it changes.
 __global__ void seqlen_kernel(int32_t *seq_lens, const int32_t *n_new, int B, int T, int cap) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= B) return;
@@ -251,13 +258,49 @@ __global__ void seqlen_kernel(int32_t *seq_lens, const int32_t *n_new, int B, in
   seq_lens[b] = (int32_t)(v > cap ? cap : v);
 }
 
+// Small appends (a decode step): one block per sequence stores its T*40 groups,
+// then advances its own length after a block barrier. One launch.
+constexpr int kStepAppendMaxT = 8;
+
+template <int FMT>
+__global__ __launch_bounds__(128) void append_step_kernel(AppendArgs a) {
+  const int b = blockIdx.x;
+  const int n = a.n_new ? a.n_new[b] : a.T;
+  const int base = a.seq_lens[b];
+  for (int i = threadIdx.x; i < a.T * kNScale; i += blockDim.x) {
+    const int t = i / kNScale, grp = i % kNScale;
+    const int pos = base + t;
+    if (t < n && pos >= 0 && pos < a.cap) append_group<FMT>(a, b, t, grp, pos);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int64_t v = (int64_t)base + n;
+    a.seq_lens[b] = (int32_t)(v > a.cap ? a.cap : v);
+  }
+}
+
 // ------------------------------------------------------------------ absorb
 
 constexpr int kAbsorbBT = 8;  // batch rows per absorb / reduce block
 
+// Per (sequence, head) record of absorbed queries, in fp16, each value v kept
+// as hi = fp16(v) and lo = fp16(v - hi), so that hi + lo carries ~22 bits:
+//   [0, 576)          hi of (q_abs | q_pe) * softmax_scale * log2(e)
+//   [576, 1152)       lo of the same
+//   [1152, 1184)      hi of the 32 latent-group sums of q_abs (INT4 zero-points)
+//   [1184, 1216)      lo of those sums
+constexpr int kQHi = 0, kQLo = kRow, kQSumHi = 2 * kRow, kQSumLo = 2 * kRow + kNGroupL;
+constexpr int kQRec = 2 * kRow + 2 * kNGroupL;  // 1216 halves
+
+__device__ __forceinline__ void split_store(_Float16 *hi, _Float16 *lo, float v) {
+  const _Float16 h = (_Float16)v;
+  *hi = h;
+  *lo = (_Float16)(v - (float)h);
+}
+
 // q_abs[b,h,c] = qs * sum_d q_nope[b,h,d] W_UK[h,d,c] for c < 512, and
-// q_abs[b,h,512+d] = qs * q_pe[b,h,d]; qs = softmax_scale * log2(e), so the
-// attention kernels work in base 2. Grid (H, ceil(B/8)), 256 threads.
+// qs * q_pe[b,h,d] for the 64 RoPE channels; qs = softmax_scale * log2(e),
+// so the attention kernels work in base 2. Grid (H, ceil(B/8)), 256 threads.
 __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t *q_nope, const uint16_t *q_pe,
                                                      const uint16_t *w_uk, int B, int H, float qs,
                                                      _Float16 *qa) {
@@ -287,11 +330,26 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t *q_nope, con
 #pragma unroll
   for (int bt = 0; bt < kAbsorbBT; ++bt) {
     const int b = b0 + bt;
-    if (b >= B) break;
-    _Float16 *o = qa + ((int64_t)b * H + h) * kRow;
-    o[tid] = (_Float16)(acc[bt][0] * qs);
-    o[tid + 256] = (_Float16)(acc[bt][1] * qs);
-    if (tid < kRope) o[kLatent + tid] = (_Float16)(bf16_bits_to_f32(q_pe[((int64_t)b * H + h) * kRope + tid]) * qs);
+    if (b >= B) break;  // uniform across the block
+    _Float16 *o = qa + ((int64_t)b * H + h) * kQRec;
+    const float v0 = acc[bt][0] * qs, v1 = acc[bt][1] * qs;
+    split_store(o + kQHi + tid, o + kQLo + tid, v0);
+    split_store(o + kQHi + tid + 256, o + kQLo + tid + 256, v1);
+    // sums over each 16-channel group: 16 consecutive threads hold one group
+    float g0 = v0, g1 = v1;
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) {
+      g0 += __shfl_xor(g0, off);
+      g1 += __shfl_xor(g1, off);
+    }
+    if ((tid & 15) == 0) {
+      split_store(o + kQSumHi + tid / 16, o + kQSumLo + tid / 16, g0);
+      split_store(o + kQSumHi + (tid + 256) / 16, o + kQSumLo + (tid + 256) / 16, g1);
+    }
+    if (tid < kRope) {
+      const float v = bf16_bits_to_f32(q_pe[((int64_t)b * H + h) * kRope + tid]) * qs;
+      split_store(o + kQHi + kLatent + tid, o + kQLo + kLatent + tid, v);
+    }
   }
 }
 
@@ -356,7 +414,7 @@ struct SplitArgs {
   const uint16_t *scale;
   const uint16_t *zero;
   const int32_t *seq_lens;  // layer row
-  const _Float16 *qa;       // [B][H][576]
+  const _Float16 *qa;       // [B][H][kQRec]
   float *ws_m;              // [B][nsplit][H]
   float *ws_l;              // [B][nsplit][H]
   float *ws_acc;            // [B][nsplit][H][512]
@@ -407,32 +465,22 @@ __device__ __forceinline__ void load_raw(RawTile<FMT, NW> &r, const SplitArgs &a
   }
 }
 
-// 4 signed bytes -> 4 fp16 values q*s: bias to unsigned, splice into the
-// mantissa of 1024.0 (exact), subtract 1152 (exact), scale (one rounding).
-__device__ __forceinline__ void deq_i8x4(uint32_t w, f16x2 s2, f16x2 &lo, f16x2 &hi) {
+// 4 signed bytes -> the 4 codes as exact fp16: bias to unsigned, splice into
+// the mantissa of 1024.0, subtract 1152 (both exact).
+__device__ __forceinline__ void codes_i8x4(uint32_t w, f16x2 &lo, f16x2 &hi) {
   const uint32_t u = w ^ 0x80808080u;
   const uint32_t a = (u & 0xFFu) | ((u << 8) & 0xFF0000u) | 0x64006400u;
   const uint32_t c = ((u >> 16) & 0xFFu) | ((u >> 8) & 0xFF0000u) | 0x64006400u;
   const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-  lo = (bitcast<f16x2>(a) - bias) * s2;
-  hi = (bitcast<f16x2>(c) - bias) * s2;
+  lo = bitcast<f16x2>(a) - bias;
+  hi = bitcast<f16x2>(c) - bias;
 }
 
-// 8 nibbles (channels 0..7, low nibble first) -> 8 fp16 values q*s + z.
-__device__ __forceinline__ void deq_i4x8(uint32_t w, f16x2 s2, f16x2 z2, f16x2 (&o)[4]) {
-  const f16x2 bias = {(_Float16)1024.0f, (_Float16)1024.0f};
-  const f16x2 q04 = bitcast<f16x2>((w & 0x000F000Fu) | 0x64006400u) - bias;          // ch0, ch4
-  const f16x2 q15 = bitcast<f16x2>(((w >> 4) & 0x000F000Fu) | 0x64006400u) - bias;   // ch1, ch5
-  const f16x2 q26 = bitcast<f16x2>(((w >> 8) & 0x000F000Fu) | 0x64006400u) - bias;   // ch2, ch6
-  const f16x2 q37 = bitcast<f16x2>(((w >> 12) & 0x000F000Fu) | 0x64006400u) - bias;  // ch3, ch7
-  const f16x2 v04 = __builtin_elementwise_fma(q04, s2, z2);
-  const f16x2 v15 = __builtin_elementwise_fma(q15, s2, z2);
-  const f16x2 v26 = __builtin_elementwise_fma(q26, s2, z2);
-  const f16x2 v37 = __builtin_elementwise_fma(q37, s2, z2);
-  o[0] = f16x2{v04.x, v15.x};
-  o[1] = f16x2{v26.x, v37.x};
-  o[2] = f16x2{v04.y, v15.y};
-  o[3] = f16x2{v26.y, v37.y};
+// x = q*s as hi + lo in fp16: hi = fp16(q*s), lo = q*s - hi, which a fused
+// multiply-add gives exactly (q has at most 8 significant bits, s 11).
+__device__ __forceinline__ void scale_split(f16x2 q, f16x2 s, f16x2 &hi, f16x2 &lo) {
+  hi = q * s;
+  lo = __builtin_elementwise_fma(q, s, -hi);
 }
 
 __device__ __forceinline__ f16x2 bf16x2_to_f16x2(uint32_t w) {
@@ -449,10 +497,23 @@ __device__ __forceinline__ void st16(_Float16 *p, f16x2 a, f16x2 b, f16x2 c, f16
   *(u32x4 *)p = v;
 }
 
-// Dequantize this lane's raw chunks into the fp16 LDS tile [16][kLdsRow].
+// LDS tile of one token group: dequantized latent+k_pe rows as fp16 hi
+// ([16][kLdsRow]), their exact fp16 residuals lo (quantized formats), and the
+// per-group zero-points ([16][kZRow], INT4).
+constexpr int kZRow = 40;  // fp16 per zero-point row (80 B: 16-byte aligned rows)
+template <int FMT> struct TileLayout {
+  static constexpr int kHi = 0;
+  static constexpr int kLo = kTile * kLdsRow;
+  static constexpr int kZ = kLo + (FMT == MLA_FMT_BF16 ? 0 : kTile * kLdsRow);
+  static constexpr int kHalves = kZ + (FMT == MLA_FMT_INT4 ? kTile * kZRow : 0);
+  static constexpr int kBytes = kHalves * 2;
+};
+
+// Dequantize this lane's raw chunks into the LDS tile.
 template <int FMT, int NW>
 __device__ __forceinline__ void dequant_store(const RawTile<FMT, NW> &r, _Float16 *tile, int lane,
                                               int hw) {
+  using TL = TileLayout<FMT>;
 #pragma unroll
   for (int j = 0; j < RawTile<FMT, NW>::kLat; ++j) {
     const int k = j * NW + hw;
@@ -461,25 +522,50 @@ __device__ __forceinline__ void dequant_store(const RawTile<FMT, NW> &r, _Float1
     const u32x4 v = r.lat[j];
     if (FMT == MLA_FMT_INT8) {
       const f16x2 s2 = splat_f16_bits(r.lsc[j]);
-      f16x2 o[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) deq_i8x4(v[i], s2, o[2 * i], o[2 * i + 1]);
-      _Float16 *dst = tile + tr * kLdsRow + ch * 16;
-      st16(dst, o[0], o[1], o[2], o[3]);
-      st16(dst + 8, o[4], o[5], o[6], o[7]);
-    } else if (FMT == MLA_FMT_INT4) {
-      // 32 channels: bytes 0-7 in group 2ch (scale/zero low half), 8-15 in 2ch+1.
-      const f16x2 s0 = splat_f16_bits(r.lsc[j] & 0xFFFFu), s1 = splat_f16_bits(r.lsc[j] >> 16);
-      const f16x2 z0 = splat_f16_bits(r.lzp[j] & 0xFFFFu), z1 = splat_f16_bits(r.lzp[j] >> 16);
-      _Float16 *dst = tile + tr * kLdsRow + ch * 32;
+      f16x2 hi[8], lo[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        f16x2 o[4];
-        deq_i4x8(v[i], i < 2 ? s0 : s1, i < 2 ? z0 : z1, o);
-        st16(dst + 8 * i, o[0], o[1], o[2], o[3]);
+        f16x2 q0, q1;
+        codes_i8x4(v[i], q0, q1);
+        scale_split(q0, s2, hi[2 * i], lo[2 * i]);
+        scale_split(q1, s2, hi[2 * i + 1], lo[2 * i + 1]);
       }
+      _Float16 *dh = tile + TL::kHi + tr * kLdsRow + ch * 16;
+      _Float16 *dl = tile + TL::kLo + tr * kLdsRow + ch * 16;
+      st16(dh, hi[0], hi[1], hi[2], hi[3]);
+      st16(dh + 8, hi[4], hi[5], hi[6], hi[7]);
+      st16(dl, lo[0], lo[1], lo[2], lo[3]);
+      st16(dl + 8, lo[4], lo[5], lo[6], lo[7]);
+    } else if (FMT == MLA_FMT_INT4) {
+      // 32 channels: bytes 0-7 in group 2ch (scale/zero low half), 8-15 in 2ch+1.
+      // The tile holds q*s; the zero-points go to their own rows and enter
+      // the scores and the value sums through separate exact products.
+      const f16x2 s0 = splat_f16_bits(r.lsc[j] & 0xFFFFu), s1 = splat_f16_bits(r.lsc[j] >> 16);
+      _Float16 *dh = tile + TL::kHi + tr * kLdsRow + ch * 32;
+      _Float16 *dl = tile + TL::kLo + tr * kLdsRow + ch * 32;
+      const f16x2 bias = {(_Float16)1024.0f, (_Float16)1024.0f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w = v[i];
+        const f16x2 s2 = i < 2 ? s0 : s1;
+        // nibble j of w is channel 8i + j; pairs (0,4), (1,5), (2,6), (3,7)
+        const f16x2 q04 = bitcast<f16x2>((w & 0x000F000Fu) | 0x64006400u) - bias;
+        const f16x2 q15 = bitcast<f16x2>(((w >> 4) & 0x000F000Fu) | 0x64006400u) - bias;
+        const f16x2 q26 = bitcast<f16x2>(((w >> 8) & 0x000F000Fu) | 0x64006400u) - bias;
+        const f16x2 q37 = bitcast<f16x2>(((w >> 12) & 0x000F000Fu) | 0x64006400u) - bias;
+        f16x2 h04, l04, h15, l15, h26, l26, h37, l37;
+        scale_split(q04, s2, h04, l04);
+        scale_split(q15, s2, h15, l15);
+        scale_split(q26, s2, h26, l26);
+        scale_split(q37, s2, h37, l37);
+        st16(dh + 8 * i, f16x2{h04.x, h15.x}, f16x2{h26.x, h37.x}, f16x2{h04.y, h15.y},
+             f16x2{h26.y, h37.y});
+        st16(dl + 8 * i, f16x2{l04.x, l15.x}, f16x2{l26.x, l37.x}, f16x2{l04.y, l15.y},
+             f16x2{l26.y, l37.y});
+      }
+      *(uint32_t *)(tile + TL::kZ + tr * kZRow + 2 * ch) = r.lzp[j];
     } else {
-      _Float16 *dst = tile + tr * kLdsRow + ch * 8;
+      _Float16 *dst = tile + TL::kHi + tr * kLdsRow + ch * 8;
       st16(dst, bf16x2_to_f16x2(v[0]), bf16x2_to_f16x2(v[1]), bf16x2_to_f16x2(v[2]),
            bf16x2_to_f16x2(v[3]));
     }
@@ -492,48 +578,78 @@ __device__ __forceinline__ void dequant_store(const RawTile<FMT, NW> &r, _Float1
     const int ch = kpe_chunk<FMT>(lane);
     const u32x4 v = r.kpe[j];
     if (FMT == MLA_FMT_BF16) {
-      _Float16 *dst = tile + tr * kLdsRow + kLatent + ch * 8;
+      _Float16 *dst = tile + TL::kHi + tr * kLdsRow + kLatent + ch * 8;
       st16(dst, bf16x2_to_f16x2(v[0]), bf16x2_to_f16x2(v[1]), bf16x2_to_f16x2(v[2]),
            bf16x2_to_f16x2(v[3]));
     } else {
       // 16 channels = k_pe groups 2ch (bytes 0-7) and 2ch+1 (bytes 8-15)
       const f16x2 s0 = splat_f16_bits(r.ksc[j] & 0xFFFFu), s1 = splat_f16_bits(r.ksc[j] >> 16);
-      f16x2 o[8];
-      deq_i8x4(v[0], s0, o[0], o[1]);
-      deq_i8x4(v[1], s0, o[2], o[3]);
-      deq_i8x4(v[2], s1, o[4], o[5]);
-      deq_i8x4(v[3], s1, o[6], o[7]);
-      _Float16 *dst = tile + tr * kLdsRow + kLatent + ch * 16;
-      st16(dst, o[0], o[1], o[2], o[3]);
-      st16(dst + 8, o[4], o[5], o[6], o[7]);
+      f16x2 hi[8], lo[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f16x2 q0, q1;
+        codes_i8x4(v[i], q0, q1);
+        scale_split(q0, i < 2 ? s0 : s1, hi[2 * i], lo[2 * i]);
+        scale_split(q1, i < 2 ? s0 : s1, hi[2 * i + 1], lo[2 * i + 1]);
+      }
+      _Float16 *dh = tile + TL::kHi + tr * kLdsRow + kLatent + ch * 16;
+      _Float16 *dl = tile + TL::kLo + tr * kLdsRow + kLatent + ch * 16;
+      st16(dh, hi[0], hi[1], hi[2], hi[3]);
+      st16(dh + 8, hi[4], hi[5], hi[6], hi[7]);
+      st16(dl, lo[0], lo[1], lo[2], lo[3]);
+      st16(dl + 8, lo[4], lo[5], lo[6], lo[7]);
     }
   }
 }
 
-constexpr int kTileBytes = kTile * kLdsRow * 2;                    // 18,688
+typedef __fp16 fp16x4_lds __attribute__((__vector_size__(4 * sizeof(__fp16))));
+
+// LDS transpose read (gfx950 ds_read_b64_tr_b16): in each 16-lane group g,
+// lane 4r+c points at row r, columns 4c..4c+3 of a 4x16 block of fp16, and
+// lane i of the group receives column i, rows 0..3.
+__device__ __forceinline__ f16x4 lds_read_tr16(const _Float16 *p) {
+  const fp16x4_lds v = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+      (__attribute__((address_space(3))) fp16x4_lds *)(p));
+  return bitcast<f16x4>(v);
+}
+
 constexpr int kMergeBytes = kWaves * 16 * kMrgRow * 4;             // 132,096
-constexpr int kSplitLds = kMergeBytes > 4 * kTileBytes ? kMergeBytes : 4 * kTileBytes;
+constexpr int kOzBytes = kWaves * 16 * kNGroupL * 4;               // 8,192
+template <int FMT, int HGW> struct SplitLds {
+  static constexpr int TG = kWaves / HGW;
+  static constexpr int NBUF = HGW == 1 ? 1 : 2;
+  static constexpr int kTiles = TG * NBUF * TileLayout<FMT>::kBytes;
+  static constexpr int kEnd = kMergeBytes + kOzBytes;
+  static constexpr int kBytes = kTiles > kEnd ? kTiles : kEnd;
+};
 
 // One workgroup = 4 waves = one (sequence b, split s, head block hh) unit.
 // HGW waves (one per 16 heads) share each token tile; the 4/HGW token groups
 // take interleaved tiles of the split and are merged at the end through LDS.
 //
 // Per wave, with lane = 16*g + i (g = 0..3, i = 0..15):
-//   scores  S^T[t][h] = sum_c C[t][c] Qabs[h][c]: 18 MFMA 16x16x32 f16 per
-//           tile; A = tile row t = i (8 channels per lane group), B = Qabs of
-//           head i held in registers; lane (g, i) gets tokens 4g..4g+3 of head i.
-//   values  O^T[c][h] += sum_t C[t][c] P[t][h]: 32 MFMA 16x16x16 f16 per
+//   scores  S^T[t][h] = sum_c C[t][c] Q[h][c], as C_hi Q_hi + C_hi Q_lo +
+//           C_lo Q_hi with 16x16x32 f16 MFMAs (fp32 accumulation), which keeps
+//           the scores to about fp32 accuracy although every operand is fp16;
+//           A = tile row t = i, B = this lane's head i held in registers;
+//           lane (g, i) gets tokens 4g..4g+3 of head i. INT4 adds
+//           sum_g z[t][g] Qsum[h][g] for the zero-points.
+//   values  O^T[c][h] += sum_t C_hi[t][c] P[t][h]: 32 MFMA 16x16x16 f16 per
 //           tile; B = P exactly as the score MFMA left it in registers,
-//           A = channel 16n+i of tokens 4g..4g+3 read from the LDS tile;
+//           A = channel 16n+i of tokens 4g..4g+3 by an LDS transpose read;
 //           lane (g, i) accumulates channels 16n+4g..16n+4g+3 of head i.
+//           INT4 accumulates sum_t P[t][h] z[t][g] beside it.
 template <int FMT, int HGW>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void split_kernel(SplitArgs a) {
-  constexpr int TG = kWaves / HGW;                 // token groups
-  constexpr int NBUF = HGW == 1 ? 1 : 2;           // wave-private tile, or double-buffered shared
-  constexpr int NPF = FMT == MLA_FMT_BF16 ? 1 : 2; // raw tiles in flight per wave
-  static_assert(TG * NBUF * kTileBytes <= kSplitLds, "lds");
-  __shared__ __attribute__((aligned(16))) unsigned char lds[kSplitLds];
+  using TL = TileLayout<FMT>;
+  using LD = SplitLds<FMT, HGW>;
+  constexpr int TG = LD::TG;                        // token groups
+  constexpr int NBUF = LD::NBUF;                    // wave-private tile, or double-buffered shared
+  constexpr int NPF = 1;                            // raw tiles in flight per wave
+  constexpr bool kLo = FMT != MLA_FMT_BF16;
+  constexpr bool kZp = FMT == MLA_FMT_INT4;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[LD::kBytes];
   __shared__ float ml_m[kWaves][16], ml_l[kWaves][16];
 
   const int split = blockIdx.x / a.hh_count;
@@ -560,20 +676,26 @@ void split_kernel(SplitArgs a) {
   const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
   const int niters = (ntiles + TG - 1) / TG;
 
-  // Qabs of head `head` in the MFMA B layout: k-step s holds channels 32s+8g..+7.
-  f16x8 qb[kRow / 32];
+  // Queries of head `head` in the MFMA B layout: k-step s holds channels 32s+8g..+7.
+  f16x8 qh[kRow / 32], ql[kRow / 32], qsh, qsl;
   {
-    const _Float16 *q = a.qa + ((int64_t)b * a.H + head) * kRow + 8 * g;
+    const _Float16 *q = a.qa + ((int64_t)b * a.H + head) * kQRec + 8 * g;
 #pragma unroll
-    for (int s = 0; s < kRow / 32; ++s) qb[s] = *(const f16x8 *)(q + 32 * s);
+    for (int s = 0; s < kRow / 32; ++s) {
+      qh[s] = *(const f16x8 *)(q + kQHi + 32 * s);
+      ql[s] = *(const f16x8 *)(q + kQLo + 32 * s);
+    }
+    qsh = *(const f16x8 *)(q + kQSumHi);
+    qsl = *(const f16x8 *)(q + kQSumLo);
   }
 
   f32x4 acc[kLatent / 16];
 #pragma unroll
   for (int n = 0; n < kLatent / 16; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 accz[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
   float m_run = -INFINITY, l_run = 0.0f;
 
-  _Float16 *tiles = (_Float16 *)lds + (int64_t)tg * NBUF * kTile * kLdsRow;
+  _Float16 *tiles = (_Float16 *)lds + (int64_t)tg * NBUF * TL::kHalves;
 
   RawTile<FMT, HGW> raw[NPF];
 #pragma unroll
@@ -586,11 +708,10 @@ void split_kernel(SplitArgs a) {
 #pragma unroll
     for (int p = 0; p < NPF; ++p) {
       const int it = it0 + p;
-      if (HGW == 1 && it >= niters) break;
-      if (HGW > 1 && it >= niters) break;  // uniform across the workgroup
+      if (it >= niters) break;  // uniform across the workgroup
       const int tile = tg + it * TG;
       const bool valid = tile < ntiles;
-      _Float16 *tb = tiles + (NBUF == 1 ? 0 : (it & 1)) * kTile * kLdsRow;
+      _Float16 *tb = tiles + (NBUF == 1 ? 0 : (it & 1)) * TL::kHalves;
       if (valid) dequant_store<FMT, HGW>(raw[p], tb, lane, hw);
       const int nxt = tile + NPF * TG;
       if (nxt < ntiles) load_raw<FMT, HGW>(raw[p], a, b, t_begin + nxt * kTile, t_end, lane, hw);
@@ -604,14 +725,26 @@ void split_kernel(SplitArgs a) {
       if (!valid) continue;
       const int t0 = t_begin + tile * kTile;
 
-      // ---- scores
-      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-      const _Float16 *arow = tb + li * kLdsRow + 8 * g;
+      // ---- scores (three fp16 products keep about fp32 accuracy)
+      f32x4 sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
+      const _Float16 *rh = tb + TL::kHi + li * kLdsRow + 8 * g;
+      const _Float16 *rl = tb + TL::kLo + li * kLdsRow + 8 * g;
 #pragma unroll
       for (int s = 0; s < kRow / 32; ++s) {
-        const f16x8 av = *(const f16x8 *)(arow + 32 * s);
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qb[s], sc, 0, 0, 0);
+        const f16x8 ah = *(const f16x8 *)(rh + 32 * s);
+        sc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, qh[s], sc0, 0, 0, 0);
+        sc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, ql[s], sc1, 0, 0, 0);
+        if (kLo) {
+          const f16x8 al = *(const f16x8 *)(rl + 32 * s);
+          sc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, qh[s], sc1, 0, 0, 0);
+        }
       }
+      if (kZp) {
+        const f16x8 az = *(const f16x8 *)(tb + TL::kZ + li * kZRow + 8 * g);
+        sc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, qsh, sc1, 0, 0, 0);
+        sc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, qsl, sc1, 0, 0, 0);
+      }
+      const f32x4 sc = sc0 + sc1;
       // ---- online softmax (base 2); lane (g, i) holds tokens t0+4g+r of head i
       float p4[4];
       float tmax = -INFINITY;
@@ -634,15 +767,26 @@ void split_kernel(SplitArgs a) {
       m_run = m_new;
 #pragma unroll
       for (int n = 0; n < kLatent / 16; ++n) acc[n] *= alpha;
+      if (kZp) {
+        accz[0] *= alpha;
+        accz[1] *= alpha;
+      }
       const f16x4 pb = {(_Float16)p4[0], (_Float16)p4[1], (_Float16)p4[2], (_Float16)p4[3]};
 
       // ---- values
-      const _Float16 *vcol = tb + (4 * g) * kLdsRow + li;
+      const _Float16 *vb = tb + TL::kHi + (4 * g + (li >> 2)) * kLdsRow + 4 * (li & 3);
 #pragma unroll
       for (int n = 0; n < kLatent / 16; ++n) {
-        const _Float16 *c = vcol + 16 * n;
-        const f16x4 av = {c[0], c[kLdsRow], c[2 * kLdsRow], c[3 * kLdsRow]};
+        const f16x4 av = lds_read_tr16(vb + 16 * n);
         acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pb, acc[n], 0, 0, 0);
+      }
+      if (kZp) {
+        const _Float16 *zb = tb + TL::kZ + (4 * g + (li >> 2)) * kZRow + 4 * (li & 3);
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          const f16x4 az = lds_read_tr16(zb + 16 * n);
+          accz[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(az, pb, accz[n], 0, 0, 0);
+        }
       }
     }
   }
@@ -652,6 +796,19 @@ void split_kernel(SplitArgs a) {
   l_run += __shfl_xor(l_run, 32);
   __syncthreads();  // every wave is done with the tiles; the area becomes the merge area
   float *mrg = (float *)lds;
+  if (kZp) {
+    // add sum_t p_t z[t][g(c)] to every channel c of group g(c) = n
+    float *oz = (float *)(lds + kMergeBytes) + (int64_t)wave * 16 * kNGroupL;
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) oz[li * kNGroupL + 16 * n + 4 * g + r] = accz[n][r];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int n = 0; n < kLatent / 16; ++n) acc[n] += oz[li * kNGroupL + n];
+  }
   if (g == 0) {
     ml_m[wave][li] = m_run;
     ml_l[wave][li] = l_run;
@@ -683,6 +840,187 @@ void split_kernel(SplitArgs a) {
       a.ws_m[ws_row + head0 + hb] = M;
       a.ws_l[ws_row + head0 + hb] = l;
     }
+  }
+}
+
+// ------------------------------------------------- split-KV core, 16 heads
+
+// For 16 heads the four waves of a workgroup work on the same token tile and
+// divide the contractions instead of the tiles:
+//   scores  wave w sums the 576 channels of k-steps [kKb[w], kKb[w+1]) (three
+//           fp16 products each, as above); the four partial 16x16 score tiles
+//           meet in LDS and every wave adds them in the same order, so all
+//           waves hold the same scores and the same softmax state.
+//   values  wave w accumulates latent channels [128w, 128w+128) only.
+// Per wave that is 32 accumulator registers instead of 128 and at most 5
+// k-steps of queries, which leaves room for two workgroups per CU and four
+// tiles of loads in flight per workgroup.
+constexpr int kKb[5] = {0, 5, 10, 14, 18};  // k-step ranges (of 32 channels) per wave
+constexpr int kPartBytes = kWaves * 64 * 16;  // one float4 per lane per wave
+
+template <int FMT> struct Split16Lds {
+  static constexpr int kTiles = 2 * TileLayout<FMT>::kBytes;
+  static constexpr int kBytes = kTiles + kPartBytes;
+};
+
+template <int FMT>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+void split16_kernel(SplitArgs a) {
+  using TL = TileLayout<FMT>;
+  constexpr int NPF = 4;  // raw tiles in flight per workgroup (a quarter tile per wave)
+  constexpr bool kLo = FMT != MLA_FMT_BF16;
+  constexpr bool kZp = FMT == MLA_FMT_INT4;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[Split16Lds<FMT>::kBytes];
+  float *part = (float *)(lds + Split16Lds<FMT>::kTiles);
+
+  const int split = blockIdx.x;
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, li = lane & 15;
+
+  const int L = min(max(a.seq_lens[b], 0), a.cap);
+  const int t_begin = split * a.chunk;
+  const int t_end = min(t_begin + a.chunk, L);
+  const int64_t ws_row = ((int64_t)b * a.nsplit + split) * a.H;
+  if (t_begin >= t_end) {  // empty unit: identity of the merge
+    if (tid < 16) {
+      a.ws_m[ws_row + tid] = -INFINITY;
+      a.ws_l[ws_row + tid] = 0.0f;
+    }
+    return;
+  }
+  const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
+  const int kb = kKb[wave], nk = kKb[wave + 1] - kKb[wave];
+
+  // this wave's k-steps of the queries of head li (MFMA B layout)
+  f16x8 qh[5], ql[5], qsh, qsl;
+  {
+    const _Float16 *q = a.qa + ((int64_t)b * a.H + li) * kQRec + 8 * g;
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      if (j < nk) {
+        qh[j] = *(const f16x8 *)(q + kQHi + 32 * (kb + j));
+        ql[j] = *(const f16x8 *)(q + kQLo + 32 * (kb + j));
+      }
+    }
+    qsh = *(const f16x8 *)(q + kQSumHi);
+    qsl = *(const f16x8 *)(q + kQSumLo);
+  }
+
+  f32x4 acc[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 accz = {0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  RawTile<FMT, kWaves> raw[NPF];
+#pragma unroll
+  for (int p = 0; p < NPF; ++p)
+    if (p < ntiles) load_raw<FMT, kWaves>(raw[p], a, b, t_begin + p * kTile, t_end, lane, wave);
+
+  for (int it0 = 0; it0 < ntiles; it0 += NPF) {
+#pragma unroll
+    for (int p = 0; p < NPF; ++p) {
+      const int it = it0 + p;
+      if (it >= ntiles) break;  // uniform across the workgroup
+      _Float16 *tb = (_Float16 *)lds + (it & 1) * TL::kHalves;
+      dequant_store<FMT, kWaves>(raw[p], tb, lane, wave);
+      if (it + NPF < ntiles)
+        load_raw<FMT, kWaves>(raw[p], a, b, t_begin + (it + NPF) * kTile, t_end, lane, wave);
+      __syncthreads();  // the tile is complete
+      const int t0 = t_begin + it * kTile;
+
+      // ---- partial scores over this wave's k-steps
+      f32x4 sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
+      const _Float16 *rh = tb + TL::kHi + li * kLdsRow + 8 * g + 32 * kb;
+      const _Float16 *rl = tb + TL::kLo + li * kLdsRow + 8 * g + 32 * kb;
+#pragma unroll
+      for (int j = 0; j < 5; ++j) {
+        if (j < nk) {
+          const f16x8 ah = *(const f16x8 *)(rh + 32 * j);
+          sc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, qh[j], sc0, 0, 0, 0);
+          sc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, ql[j], sc1, 0, 0, 0);
+          if (kLo) {
+            const f16x8 al = *(const f16x8 *)(rl + 32 * j);
+            sc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, qh[j], sc1, 0, 0, 0);
+          }
+        }
+      }
+      if (kZp && wave == kWaves - 1) {
+        const f16x8 az = *(const f16x8 *)(tb + TL::kZ + li * kZRow + 8 * g);
+        sc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, qsh, sc1, 0, 0, 0);
+        sc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, qsl, sc1, 0, 0, 0);
+      }
+      *(f32x4 *)(part + (wave * 64 + lane) * 4) = sc0 + sc1;
+      __syncthreads();  // all partial scores are in LDS
+      f32x4 sc = *(const f32x4 *)(part + lane * 4);
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) sc += *(const f32x4 *)(part + (w * 64 + lane) * 4);
+
+      // ---- online softmax (base 2), identical in every wave
+      float p4[4];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p4[r] = (t0 + 4 * g + r < t_end) ? sc[r] : -INFINITY;
+        tmax = fmaxf(tmax, p4[r]);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      float psum = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p4[r] = __builtin_amdgcn_exp2f(p4[r] - m_new);
+        psum += p4[r];
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) acc[n] *= alpha;
+      if (kZp) accz *= alpha;
+      const f16x4 pb = {(_Float16)p4[0], (_Float16)p4[1], (_Float16)p4[2], (_Float16)p4[3]};
+
+      // ---- values of this wave's 128 channels
+      const _Float16 *vb = tb + TL::kHi + (4 * g + (li >> 2)) * kLdsRow + 4 * (li & 3) + 128 * wave;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const f16x4 av = lds_read_tr16(vb + 16 * n);
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pb, acc[n], 0, 0, 0);
+      }
+      if (kZp) {  // zero-point groups 16*(wave/2) .. +15
+        const f16x4 az = lds_read_tr16(tb + TL::kZ + (4 * g + (li >> 2)) * kZRow + 4 * (li & 3) +
+                                       16 * (wave >> 1));
+        accz = __builtin_amdgcn_mfma_f32_16x16x16f16(az, pb, accz, 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- write this unit's partial: m and l (same in every wave), channels of this wave
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (kZp) {
+    // channel block n of this wave is zero-point group 8*wave + n; the wave
+    // holds sums for groups 16*(wave/2) + 4g + r
+    __syncthreads();  // everyone is done reading the partial-score area
+    float *oz = part + wave * 256;  // [16 heads][16 groups]
+#pragma unroll
+    for (int r = 0; r < 4; ++r) oz[li * 16 + 4 * g + r] = accz[r];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int gofs = (wave & 1) * 8;  // group 8*wave + n within the wave's 16-group block
+#pragma unroll
+    for (int n = 0; n < 8; ++n) acc[n] += oz[li * 16 + gofs + n];
+  }
+  float *dst = a.ws_acc + (ws_row + li) * kLatent + 128 * wave + 4 * g;
+#pragma unroll
+  for (int n = 0; n < 8; ++n) *(f32x4 *)(dst + 16 * n) = acc[n];
+  if (wave == 0 && g == 0) {
+    a.ws_m[ws_row + li] = m_run;
+    a.ws_l[ws_row + li] = l_run;
   }
 }
 
@@ -846,7 +1184,7 @@ WsLayout ws_layout(int B, int H, int nsplit) {
   WsLayout w;
   size_t off = 0;
   w.qa = off;
-  off = align256(off + (size_t)B * H * kRow * 2);
+  off = align256(off + (size_t)B * H * kQRec * 2);
   w.m = off;
   off = align256(off + (size_t)B * nsplit * H * 4);
   w.l = off;
@@ -881,7 +1219,7 @@ int chunk_for(int cap, int nsplit) {
 
 template <int FMT>
 hipError_t launch_split_fmt(const SplitArgs &a, int heads, dim3 grid, hipStream_t st) {
-  if (heads == 16) hipLaunchKernelGGL((split_kernel<FMT, 1>), grid, dim3(kThreads), 0, st, a);
+  if (heads == 16) hipLaunchKernelGGL((split16_kernel<FMT>), grid, dim3(kThreads), 0, st, a);
   else if (heads == 32) hipLaunchKernelGGL((split_kernel<FMT, 2>), grid, dim3(kThreads), 0, st, a);
   else hipLaunchKernelGGL((split_kernel<FMT, 4>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
@@ -926,6 +1264,16 @@ extern "C" int mla_cache_append(const mla_cache *cache, int32_t layer, const voi
   a.T = t_new;
   a.cap = cache->capacity;
   hipStream_t s = (hipStream_t)hip_stream;
+  if (t_new <= kStepAppendMaxT) {  // a decode step: one launch, lengths advanced in-kernel
+    const dim3 g((unsigned)a.B), bl(128);
+    if (cache->format == MLA_FMT_INT8)
+      hipLaunchKernelGGL(append_step_kernel<MLA_FMT_INT8>, g, bl, 0, s, a);
+    else if (cache->format == MLA_FMT_INT4)
+      hipLaunchKernelGGL(append_step_kernel<MLA_FMT_INT4>, g, bl, 0, s, a);
+    else
+      hipLaunchKernelGGL(append_step_kernel<MLA_FMT_BF16>, g, bl, 0, s, a);
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  }
   const int64_t items = (int64_t)a.B * a.T * kNScale;
   int64_t blocks = (items + 255) / 256;
   if (blocks > 65536) blocks = 65536;
