@@ -141,6 +141,16 @@ __device__ __forceinline__ void quant_asym4(const float (&x)[kGroupL], uint8_t (
 
 #pragma clang fp contract(on)
 
+// Wait until every LDS instruction this wave issued has completed, with no
+// instruction moved across. An LDS store may read its data registers well
+// after it issues; the registers of the stores above are reused right after
+// (as MFMA results, by returning loads), so they must have been read first.
+__device__ __forceinline__ void lds_stores_done() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left at their maxima
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // ------------------------------------------------------------------ append
 
 struct AppendArgs {
@@ -281,7 +291,8 @@ __global__ __launch_bounds__(128) void append_step_kernel(AppendArgs a) {
 
 // ------------------------------------------------------------------ absorb
 
-constexpr int kAbsorbBT = 8;  // batch rows per absorb / reduce block
+constexpr int kAbsorbBT = 8;   // batch rows per absorb block
+constexpr int kAbsorbCB = 64;  // channels per absorb block
 
 // Per (sequence, head) record of absorbed queries, in fp16, each value v kept
 // as hi = fp16(v) and lo = fp16(v - hi), so that hi + lo carries ~22 bits:
@@ -300,55 +311,57 @@ __device__ __forceinline__ void split_store(_Float16 *hi, _Float16 *lo, float v)
 
 // q_abs[b,h,c] = qs * sum_d q_nope[b,h,d] W_UK[h,d,c] for c < 512, and
 // qs * q_pe[b,h,d] for the 64 RoPE channels; qs = softmax_scale * log2(e),
-// so the attention kernels work in base 2. Grid (H, ceil(B/8)), 256 threads.
+// so the attention kernels work in base 2.
+// Grid (H, 512/64 channel blocks, ceil(B/8)), 256 threads: thread = (channel
+// c of the block, quarter of the 128 d), quarters summed through LDS.
 __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t *q_nope, const uint16_t *q_pe,
                                                      const uint16_t *w_uk, int B, int H, float qs,
                                                      _Float16 *qa) {
   __shared__ float qsh[kAbsorbBT][kNope];
-  const int h = blockIdx.x;
-  const int b0 = blockIdx.y * kAbsorbBT;
+  __shared__ float red[4][kAbsorbBT][kAbsorbCB];
+  const int h = blockIdx.x, cb = blockIdx.y;
+  const int b0 = blockIdx.z * kAbsorbBT;
   const int tid = threadIdx.x;
-  for (int i = tid; i < kAbsorbBT * kNope; i += 256) {
-    const int bt = i / kNope, d = i % kNope;
+  for (int e = tid; e < kAbsorbBT * kNope; e += 256) {
+    const int bt = e / kNope, d = e % kNope;
     const int b = b0 + bt;
     qsh[bt][d] = b < B ? bf16_bits_to_f32(q_nope[((int64_t)b * H + h) * kNope + d]) : 0.0f;
   }
   __syncthreads();
-  float acc[kAbsorbBT][2];
+  const int cl = tid & 63, ds = tid >> 6;
+  const int c = cb * kAbsorbCB + cl;
+  const uint16_t *w = w_uk + ((int64_t)h * kNope + ds * 32) * kLatent + c;
+  float acc[kAbsorbBT];
 #pragma unroll
-  for (int bt = 0; bt < kAbsorbBT; ++bt) acc[bt][0] = acc[bt][1] = 0.0f;
-  const uint16_t *w = w_uk + (int64_t)h * kNope * kLatent;
-  for (int d = 0; d < kNope; ++d) {
-    const float w0 = bf16_bits_to_f32(w[d * kLatent + tid]);
-    const float w1 = bf16_bits_to_f32(w[d * kLatent + tid + 256]);
+  for (int bt = 0; bt < kAbsorbBT; ++bt) acc[bt] = 0.0f;
+#pragma unroll 8
+  for (int d = 0; d < 32; ++d) {
+    const float wv = bf16_bits_to_f32(w[d * kLatent]);
 #pragma unroll
-    for (int bt = 0; bt < kAbsorbBT; ++bt) {
-      acc[bt][0] += qsh[bt][d] * w0;
-      acc[bt][1] += qsh[bt][d] * w1;
-    }
+    for (int bt = 0; bt < kAbsorbBT; ++bt) acc[bt] += qsh[bt][ds * 32 + d] * wv;
   }
 #pragma unroll
-  for (int bt = 0; bt < kAbsorbBT; ++bt) {
-    const int b = b0 + bt;
-    if (b >= B) break;  // uniform across the block
-    _Float16 *o = qa + ((int64_t)b * H + h) * kQRec;
-    const float v0 = acc[bt][0] * qs, v1 = acc[bt][1] * qs;
-    split_store(o + kQHi + tid, o + kQLo + tid, v0);
-    split_store(o + kQHi + tid + 256, o + kQLo + tid + 256, v1);
-    // sums over each 16-channel group: 16 consecutive threads hold one group
-    float g0 = v0, g1 = v1;
+  for (int bt = 0; bt < kAbsorbBT; ++bt) red[ds][bt][cl] = acc[bt];
+  lds_stores_done();
+  __syncthreads();
 #pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) {
-      g0 += __shfl_xor(g0, off);
-      g1 += __shfl_xor(g1, off);
-    }
-    if ((tid & 15) == 0) {
-      split_store(o + kQSumHi + tid / 16, o + kQSumLo + tid / 16, g0);
-      split_store(o + kQSumHi + (tid + 256) / 16, o + kQSumLo + (tid + 256) / 16, g1);
-    }
-    if (tid < kRope) {
-      const float v = bf16_bits_to_f32(q_pe[((int64_t)b * H + h) * kRope + tid]) * qs;
-      split_store(o + kQHi + kLatent + tid, o + kQLo + kLatent + tid, v);
+  for (int k = 0; k < 2; ++k) {
+    const int o = tid + 256 * k;  // (bt, channel of the block); lanes of one wave share bt
+    const int bt = o / kAbsorbCB, ol = o % kAbsorbCB;
+    const float v = (red[0][bt][ol] + red[1][bt][ol] + red[2][bt][ol] + red[3][bt][ol]) * qs;
+    float gsum = v;  // sums over each 16-channel group: 16 consecutive lanes
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) gsum += __shfl_xor(gsum, off);
+    const int b = b0 + bt;
+    if (b < B) {
+      _Float16 *rec = qa + ((int64_t)b * H + h) * kQRec;
+      const int oc = cb * kAbsorbCB + ol;
+      split_store(rec + kQHi + oc, rec + kQLo + oc, v);
+      if ((ol & 15) == 0) split_store(rec + kQSumHi + oc / 16, rec + kQSumLo + oc / 16, gsum);
+      if (cb == 0) {  // this block also scales the RoPE part of the query
+        const float vp = bf16_bits_to_f32(q_pe[((int64_t)b * H + h) * kRope + ol]) * qs;
+        split_store(rec + kQHi + kLatent + ol, rec + kQLo + kLatent + ol, vp);
+      }
     }
   }
 }
@@ -421,47 +434,65 @@ struct SplitArgs {
   int B, H, cap, nsplit, chunk, hh_count;
 };
 
+// Buffer descriptors over one split's rows of each plane. A buffer load past
+// the descriptor's byte count returns zero without touching memory, so rows
+// past the split or the sequence need no branch, and every load of a tile is
+// issued unconditionally (which lets the compiler count outstanding loads
+// exactly instead of draining the queue before each use).
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9 buffer resource dword 3
+constexpr int kOffNone = 0x7FFFFFF0;        // an offset past any descriptor
+
+struct SplitRsrc {
+  __amdgpu_buffer_rsrc_t ckv, kpe, scale, zero;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, (int)kRsrcWord3);
+}
+
+template <int FMT>
+__device__ __forceinline__ SplitRsrc split_rsrc(const SplitArgs &a, int b, int t_begin, int t_end) {
+  const int64_t row0 = (int64_t)b * a.cap + t_begin;
+  const int64_t n = t_end - t_begin;
+  SplitRsrc r;
+  r.ckv = make_rsrc((const uint8_t *)a.ckv + row0 * Fmt<FMT>::kLatRowBytes, n * Fmt<FMT>::kLatRowBytes);
+  r.kpe = make_rsrc((const uint8_t *)a.kpe + row0 * Fmt<FMT>::kKpeRowBytes, n * Fmt<FMT>::kKpeRowBytes);
+  r.scale = make_rsrc(FMT == MLA_FMT_BF16 ? a.kpe : (const void *)(a.scale + row0 * kNScale),
+                      FMT == MLA_FMT_BF16 ? 0 : n * kNScale * 2);
+  r.zero = make_rsrc(FMT == MLA_FMT_INT4 ? (const void *)(a.zero + row0 * kNGroupL) : a.kpe,
+                     FMT == MLA_FMT_INT4 ? n * kNGroupL * 2 : 0);
+  return r;
+}
+
+// Raw chunks of the tile whose first row is row `r0` of the split.
 template <int FMT, int NW>
-__device__ __forceinline__ void load_raw(RawTile<FMT, NW> &r, const SplitArgs &a, int b, int t0,
-                                         int tend, int lane, int hw) {
-  const int64_t row0 = (int64_t)b * a.cap + t0;
+__device__ __forceinline__ void load_raw(RawTile<FMT, NW> &r, const SplitRsrc &rs, int r0, int lane,
+                                         int hw) {
 #pragma unroll
   for (int j = 0; j < RawTile<FMT, NW>::kLat; ++j) {
     const int k = j * NW + hw;
-    const int tr = lat_row<FMT>(lane, k);
+    const int row = r0 + lat_row<FMT>(lane, k);
     const int ch = lat_chunk<FMT>(lane);
-    u32x4 v = {0u, 0u, 0u, 0u};
-    uint32_t s = 0u, z = 0u;
-    if (t0 + tr < tend) {
-      const int64_t row = row0 + tr;
-      v = *(const u32x4 *)((const uint8_t *)a.ckv + row * Fmt<FMT>::kLatRowBytes + ch * 16);
-      if (FMT == MLA_FMT_INT8) {
-        s = a.scale[row * kNScale + ch];
-      } else if (FMT == MLA_FMT_INT4) {
-        s = *(const uint32_t *)(a.scale + row * kNScale + 2 * ch);
-        z = *(const uint32_t *)(a.zero + row * kNGroupL + 2 * ch);
-      }
+    r.lat[j] = bitcast<u32x4>(
+        __builtin_amdgcn_raw_buffer_load_b128(rs.ckv, row * Fmt<FMT>::kLatRowBytes + ch * 16, 0, 0));
+    if (FMT == MLA_FMT_INT8) {
+      r.lsc[j] = __builtin_amdgcn_raw_buffer_load_b16(rs.scale, row * kNScale * 2 + ch * 2, 0, 0);
+    } else if (FMT == MLA_FMT_INT4) {
+      r.lsc[j] = __builtin_amdgcn_raw_buffer_load_b32(rs.scale, row * kNScale * 2 + ch * 4, 0, 0);
+      r.lzp[j] = __builtin_amdgcn_raw_buffer_load_b32(rs.zero, row * kNGroupL * 2 + ch * 4, 0, 0);
     }
-    r.lat[j] = v;
-    r.lsc[j] = s;
-    r.lzp[j] = z;
   }
 #pragma unroll
   for (int j = 0; j < RawTile<FMT, NW>::kKpe; ++j) {
     const int k = j * NW + hw;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    uint32_t s = 0u;
-    if (k < Fmt<FMT>::kKpe) {
-      const int tr = kpe_row<FMT>(lane, k);
-      const int ch = kpe_chunk<FMT>(lane);
-      if (t0 + tr < tend) {
-        const int64_t row = row0 + tr;
-        v = *(const u32x4 *)((const uint8_t *)a.kpe + row * Fmt<FMT>::kKpeRowBytes + ch * 16);
-        if (FMT != MLA_FMT_BF16) s = *(const uint32_t *)(a.scale + row * kNScale + kNGroupL + 2 * ch);
-      }
-    }
-    r.kpe[j] = v;
-    r.ksc[j] = s;
+    const bool have = k < Fmt<FMT>::kKpe;  // waves past the last chunk read nothing (zeros)
+    const int row = r0 + kpe_row<FMT>(lane, have ? k : 0);
+    const int ch = kpe_chunk<FMT>(lane);
+    const int off = have ? row * Fmt<FMT>::kKpeRowBytes + ch * 16 : kOffNone;
+    r.kpe[j] = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rs.kpe, off, 0, 0));
+    if (FMT != MLA_FMT_BF16)
+      r.ksc[j] = __builtin_amdgcn_raw_buffer_load_b32(
+          rs.scale, have ? row * kNScale * 2 + kNGroupL * 2 + ch * 4 : kOffNone, 0, 0);
   }
 }
 
@@ -697,12 +728,10 @@ void split_kernel(SplitArgs a) {
 
   _Float16 *tiles = (_Float16 *)lds + (int64_t)tg * NBUF * TL::kHalves;
 
+  const SplitRsrc rs = split_rsrc<FMT>(a, b, t_begin, t_end);
   RawTile<FMT, HGW> raw[NPF];
 #pragma unroll
-  for (int p = 0; p < NPF; ++p) {
-    const int tile = tg + p * TG;
-    if (tile < ntiles) load_raw<FMT, HGW>(raw[p], a, b, t_begin + tile * kTile, t_end, lane, hw);
-  }
+  for (int p = 0; p < NPF; ++p) load_raw<FMT, HGW>(raw[p], rs, (tg + p * TG) * kTile, lane, hw);
 
   for (int it0 = 0; it0 < niters; it0 += NPF) {
 #pragma unroll
@@ -713,8 +742,8 @@ void split_kernel(SplitArgs a) {
       const bool valid = tile < ntiles;
       _Float16 *tb = tiles + (NBUF == 1 ? 0 : (it & 1)) * TL::kHalves;
       if (valid) dequant_store<FMT, HGW>(raw[p], tb, lane, hw);
-      const int nxt = tile + NPF * TG;
-      if (nxt < ntiles) load_raw<FMT, HGW>(raw[p], a, b, t_begin + nxt * kTile, t_end, lane, hw);
+      lds_stores_done();
+      load_raw<FMT, HGW>(raw[p], rs, (tile + NPF * TG) * kTile, lane, hw);
       if (HGW > 1) {
         __syncthreads();
       } else {
@@ -803,9 +832,7 @@ void split_kernel(SplitArgs a) {
     for (int n = 0; n < 2; ++n)
 #pragma unroll
       for (int r = 0; r < 4; ++r) oz[li * kNGroupL + 16 * n + 4 * g + r] = accz[n][r];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    lds_stores_done();
 #pragma unroll
     for (int n = 0; n < kLatent / 16; ++n) acc[n] += oz[li * kNGroupL + n];
   }
@@ -818,6 +845,7 @@ void split_kernel(SplitArgs a) {
 #pragma unroll
     for (int n = 0; n < kLatent / 16; ++n) *(f32x4 *)(dst + 16 * n) = acc[n];
   }
+  lds_stores_done();
   __syncthreads();
   // HGW*16 heads x 512 channels, 256 threads: thread -> (head-in-block, channel)
   for (int e = tid; e < HGW * 16 * kLatent; e += kThreads) {
@@ -845,39 +873,174 @@ void split_kernel(SplitArgs a) {
 
 // ------------------------------------------------- split-KV core, 16 heads
 
-// For 16 heads the four waves of a workgroup work on the same token tile and
-// divide the contractions instead of the tiles:
-//   scores  wave w sums the 576 channels of k-steps [kKb[w], kKb[w+1]) (three
-//           fp16 products each, as above); the four partial 16x16 score tiles
-//           meet in LDS and every wave adds them in the same order, so all
-//           waves hold the same scores and the same softmax state.
-//   values  wave w accumulates latent channels [128w, 128w+128) only.
-// Per wave that is 32 accumulator registers instead of 128 and at most 5
-// k-steps of queries, which leaves room for two workgroups per CU and four
-// tiles of loads in flight per workgroup.
-constexpr int kKb[5] = {0, 5, 10, 14, 18};  // k-step ranges (of 32 channels) per wave
-constexpr int kPartBytes = kWaves * 64 * 16;  // one float4 per lane per wave
+// For 16 heads the four waves of a workgroup share each 32-token tile and
+// divide the channels: wave w owns latent channels [128w, 128w+128) and k_pe
+// channels [16w, 16w+16). Each wave loads its channels of the tile straight
+// into the MFMA operand layout, dequantizes them in registers (as fp16 hi and
+// exact residual lo), and
+//   scores  adds its share of S^T[t][h] = sum_c C[t][c] Q[h][c] as
+//           C_hi Q_hi + C_hi Q_lo + C_lo Q_hi (16x16x32 f16 MFMA, fp32
+//           accumulation); the four partial score tiles meet in LDS and every
+//           wave adds them in the same order, so all waves hold the same
+//           scores and the same softmax state;
+//   values  accumulates O^T[c][h] = sum_t C_hi[t][c] P[t][h] for its own 128
+//           channels: its C_hi goes to a wave-private LDS block and comes back
+//           transposed (ds_read_b64_tr_b16) as the A operand, P is the B
+//           operand exactly as the score MFMA left it in registers.
+// Lane l = 16g + i: in the score, row i of each 16-token half of the tile and
+// channels 32g..32g+31 of the wave's block (two quantization groups); in the
+// accumulators, head i.
+constexpr int kT16 = 32;             // tokens per tile
+constexpr int kVRow = 128 + 8;       // fp16 per row of a wave's value block: 128 channels, then
+                                     // (INT4) the 8 zero-points of the wave's groups
+constexpr int kWBlk = kT16 * kVRow;  // fp16 per wave block
+constexpr int kPart16 = 2 * kWaves * 64 * 8;          // floats: 2 buffers x 4 waves x 64 lanes x 8
 
-template <int FMT> struct Split16Lds {
-  static constexpr int kTiles = 2 * TileLayout<FMT>::kBytes;
-  static constexpr int kBytes = kTiles + kPartBytes;
+template <int FMT> struct Raw16;
+template <> struct Raw16<MLA_FMT_INT8> {
+  static constexpr int kLat = 2;  // 16-byte loads per half-tile row: 32 codes
+  u32x4 lat[2][2];
+  uint32_t sc[2], zp[2];
+  u32x2 kq[2];
+  uint32_t ks[2];
+};
+template <> struct Raw16<MLA_FMT_INT4> {
+  static constexpr int kLat = 1;  // 32 nibbles
+  u32x4 lat[2][1];
+  uint32_t sc[2], zp[2];
+  u32x2 kq[2];
+  uint32_t ks[2];
+};
+template <> struct Raw16<MLA_FMT_BF16> {
+  static constexpr int kLat = 4;  // 32 bf16
+  u32x4 lat[2][4];
+  uint32_t sc[2], zp[2];
+  u32x2 kq[2];
+  uint32_t ks[2];
 };
 
+// Raw data of this lane for the tile starting at split row r0: rows r0+i and
+// r0+16+i, channels 128w+32g..+31 and k_pe channels 16w+4g..+3.
 template <int FMT>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+__device__ __forceinline__ void load16(Raw16<FMT> &r, const SplitRsrc &rs, int r0, int w, int g, int i) {
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int row = r0 + 16 * rb + i;
+#pragma unroll
+    for (int j = 0; j < Raw16<FMT>::kLat; ++j) {
+      int off;
+      if (FMT == MLA_FMT_INT8) off = row * kLatent + 128 * w + 32 * g + 16 * j;
+      else if (FMT == MLA_FMT_INT4) off = row * (kLatent / 2) + 64 * w + 16 * g;
+      else off = row * (kLatent * 2) + 2 * (128 * w + 32 * g) + 16 * j;
+      r.lat[rb][j] = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rs.ckv, off, 0, 0));
+    }
+    if (FMT != MLA_FMT_BF16) {
+      r.sc[rb] = __builtin_amdgcn_raw_buffer_load_b32(rs.scale, row * kNScale * 2 + (8 * w + 2 * g) * 2, 0, 0);
+      r.kq[rb].x = __builtin_amdgcn_raw_buffer_load_b32(rs.kpe, row * kRope + 16 * w + 4 * g, 0, 0);
+      r.ks[rb] = __builtin_amdgcn_raw_buffer_load_b16(
+          rs.scale, row * kNScale * 2 + (kNGroupL + 2 * w + (g >> 1)) * 2, 0, 0);
+    } else {
+      r.kq[rb] = bitcast<u32x2>(
+          __builtin_amdgcn_raw_buffer_load_b64(rs.kpe, row * (kRope * 2) + 2 * (16 * w + 4 * g), 0, 0));
+    }
+    if (FMT == MLA_FMT_INT4)
+      r.zp[rb] = __builtin_amdgcn_raw_buffer_load_b32(rs.zero, row * kNGroupL * 2 + (8 * w + 2 * g) * 2, 0, 0);
+  }
+}
+
+__device__ __forceinline__ f16x8 cat8(f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
+  return f16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+// Dequantize one half-tile row of this lane: hi/lo operands of the 4 latent
+// k-steps (8 channels each) and of the k_pe k-step (4 channels), and the hi
+// values in channel order, stored to the value block row `vrow`.
+//
+// INT4 operands keep the channel order in which the nibbles come out of a
+// dword, (0,4,1,5,2,6,3,7) within each 8 channels, and the queries are
+// permuted to match once per workgroup; only the copy for LDS is re-paired
+// into channel order. The MFMA operands are then whole registers straight
+// from the packed multiply-adds, as in the other formats.
+template <int FMT>
+__device__ __forceinline__ void dequant16(const Raw16<FMT> &r, int rb, f16x8 (&hi)[4], f16x8 (&lo)[4],
+                                          _Float16 *vrow, f16x4 &khi, f16x4 &klo) {
+  if (FMT == MLA_FMT_INT8) {
+    const f16x2 s0 = splat_f16_bits(r.sc[rb] & 0xFFFFu), s1 = splat_f16_bits(r.sc[rb] >> 16);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const u32x4 v = r.lat[rb][kk >> 1];
+      const f16x2 s2 = kk < 2 ? s0 : s1;
+      f16x2 q0, q1, q2, q3, h0, h1, h2, h3, l0, l1, l2, l3;
+      codes_i8x4(v[2 * (kk & 1)], q0, q1);
+      codes_i8x4(v[2 * (kk & 1) + 1], q2, q3);
+      scale_split(q0, s2, h0, l0);
+      scale_split(q1, s2, h1, l1);
+      scale_split(q2, s2, h2, l2);
+      scale_split(q3, s2, h3, l3);
+      hi[kk] = cat8(h0, h1, h2, h3);
+      lo[kk] = cat8(l0, l1, l2, l3);
+      *(f16x8 *)(vrow + 8 * kk) = hi[kk];
+    }
+  } else if (FMT == MLA_FMT_INT4) {
+    const f16x2 s0 = splat_f16_bits(r.sc[rb] & 0xFFFFu), s1 = splat_f16_bits(r.sc[rb] >> 16);
+    const f16x2 bias = {(_Float16)1024.0f, (_Float16)1024.0f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const uint32_t w = r.lat[rb][0][kk];
+      const f16x2 s2 = kk < 2 ? s0 : s1;
+      const f16x2 q04 = bitcast<f16x2>((w & 0x000F000Fu) | 0x64006400u) - bias;
+      const f16x2 q15 = bitcast<f16x2>(((w >> 4) & 0x000F000Fu) | 0x64006400u) - bias;
+      const f16x2 q26 = bitcast<f16x2>(((w >> 8) & 0x000F000Fu) | 0x64006400u) - bias;
+      const f16x2 q37 = bitcast<f16x2>(((w >> 12) & 0x000F000Fu) | 0x64006400u) - bias;
+      f16x2 h04, l04, h15, l15, h26, l26, h37, l37;
+      scale_split(q04, s2, h04, l04);
+      scale_split(q15, s2, h15, l15);
+      scale_split(q26, s2, h26, l26);
+      scale_split(q37, s2, h37, l37);
+      hi[kk] = cat8(h04, h15, h26, h37);  // channels 0,4,1,5,2,6,3,7
+      lo[kk] = cat8(l04, l15, l26, l37);
+      *(f16x8 *)(vrow + 8 * kk) = f16x8{h04.x, h15.x, h26.x, h37.x, h04.y, h15.y, h26.y, h37.y};
+    }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const u32x4 v = r.lat[rb][kk];
+      hi[kk] = cat8(bf16x2_to_f16x2(v[0]), bf16x2_to_f16x2(v[1]), bf16x2_to_f16x2(v[2]),
+                    bf16x2_to_f16x2(v[3]));
+      lo[kk] = f16x8{};
+      *(f16x8 *)(vrow + 8 * kk) = hi[kk];
+    }
+  }
+  if (FMT != MLA_FMT_BF16) {
+    const f16x2 ks = splat_f16_bits(r.ks[rb]);
+    f16x2 q0, q1, h0, h1, l0, l1;
+    codes_i8x4(r.kq[rb].x, q0, q1);
+    scale_split(q0, ks, h0, l0);
+    scale_split(q1, ks, h1, l1);
+    khi = f16x4{h0.x, h0.y, h1.x, h1.y};
+    klo = f16x4{l0.x, l0.y, l1.x, l1.y};
+  } else {
+    const f16x2 a = bf16x2_to_f16x2(r.kq[rb].x), b = bf16x2_to_f16x2(r.kq[rb].y);
+    khi = f16x4{a.x, a.y, b.x, b.y};
+    klo = f16x4{};
+  }
+}
+
+template <int FMT>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(3, 3)))
 void split16_kernel(SplitArgs a) {
-  using TL = TileLayout<FMT>;
-  constexpr int NPF = 4;  // raw tiles in flight per workgroup (a quarter tile per wave)
+  constexpr int NPF = 1;  // tiles of loads in flight per wave (issued a whole tile ahead)
   constexpr bool kLo = FMT != MLA_FMT_BF16;
   constexpr bool kZp = FMT == MLA_FMT_INT4;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[Split16Lds<FMT>::kBytes];
-  float *part = (float *)(lds + Split16Lds<FMT>::kTiles);
+  // +16: the zero-point read of the last row runs 8 fp16 past its block (unused slots)
+  __shared__ __attribute__((aligned(16))) _Float16 wblk[kWaves * kWBlk + 16];
+  __shared__ __attribute__((aligned(16))) float part[kPart16];
 
   const int split = blockIdx.x;
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int g = lane >> 4, li = lane & 15;
+  const int w = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, i = lane & 15;
 
   const int L = min(max(a.seq_lens[b], 0), a.cap);
   const int t_begin = split * a.chunk;
@@ -890,23 +1053,31 @@ void split16_kernel(SplitArgs a) {
     }
     return;
   }
-  const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
-  const int kb = kKb[wave], nk = kKb[wave + 1] - kKb[wave];
+  const int ntiles = (t_end - t_begin + kT16 - 1) / kT16;
 
-  // this wave's k-steps of the queries of head li (MFMA B layout)
-  f16x8 qh[5], ql[5], qsh, qsl;
+  // queries of head i for this wave's channels, in the MFMA B layout
+  f16x8 qh[4], ql[4];
+  f16x4 kqh, kql, zqh, zql;
   {
-    const _Float16 *q = a.qa + ((int64_t)b * a.H + li) * kQRec + 8 * g;
+    const _Float16 *q = a.qa + ((int64_t)b * a.H + i) * kQRec;
 #pragma unroll
-    for (int j = 0; j < 5; ++j) {
-      if (j < nk) {
-        qh[j] = *(const f16x8 *)(q + kQHi + 32 * (kb + j));
-        ql[j] = *(const f16x8 *)(q + kQLo + 32 * (kb + j));
+    for (int kk = 0; kk < 4; ++kk) {
+      qh[kk] = *(const f16x8 *)(q + kQHi + 128 * w + 32 * g + 8 * kk);
+      ql[kk] = *(const f16x8 *)(q + kQLo + 128 * w + 32 * g + 8 * kk);
+      if (FMT == MLA_FMT_INT4) {  // the INT4 operand order: channels 0,4,1,5,2,6,3,7
+        qh[kk] = f16x8{qh[kk][0], qh[kk][4], qh[kk][1], qh[kk][5], qh[kk][2], qh[kk][6], qh[kk][3], qh[kk][7]};
+        ql[kk] = f16x8{ql[kk][0], ql[kk][4], ql[kk][1], ql[kk][5], ql[kk][2], ql[kk][6], ql[kk][3], ql[kk][7]};
       }
     }
-    qsh = *(const f16x8 *)(q + kQSumHi);
-    qsl = *(const f16x8 *)(q + kQSumLo);
+    kqh = *(const f16x4 *)(q + kQHi + kLatent + 16 * w + 4 * g);
+    kql = *(const f16x4 *)(q + kQLo + kLatent + 16 * w + 4 * g);
+    const f16x2 sh = *(const f16x2 *)(q + kQSumHi + 8 * w + 2 * g);
+    const f16x2 sl = *(const f16x2 *)(q + kQSumLo + 8 * w + 2 * g);
+    zqh = f16x4{sh.x, sh.y, (_Float16)0.0f, (_Float16)0.0f};
+    zql = f16x4{sl.x, sl.y, (_Float16)0.0f, (_Float16)0.0f};
   }
+
+  _Float16 *vblk = wblk + w * kWBlk;  // [32][kVRow] C_hi of this wave's channels (+ zero-points)
 
   f32x4 acc[8];
 #pragma unroll
@@ -914,174 +1085,258 @@ void split16_kernel(SplitArgs a) {
   f32x4 accz = {0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.0f;
 
-  RawTile<FMT, kWaves> raw[NPF];
+  const SplitRsrc rs = split_rsrc<FMT>(a, b, t_begin, t_end);
+  Raw16<FMT> raw[NPF];
 #pragma unroll
-  for (int p = 0; p < NPF; ++p)
-    if (p < ntiles) load_raw<FMT, kWaves>(raw[p], a, b, t_begin + p * kTile, t_end, lane, wave);
+  for (int p = 0; p < NPF; ++p) load16<FMT>(raw[p], rs, p * kT16, w, g, i);
 
   for (int it0 = 0; it0 < ntiles; it0 += NPF) {
 #pragma unroll
     for (int p = 0; p < NPF; ++p) {
       const int it = it0 + p;
-      if (it >= ntiles) break;  // uniform across the workgroup
-      _Float16 *tb = (_Float16 *)lds + (it & 1) * TL::kHalves;
-      dequant_store<FMT, kWaves>(raw[p], tb, lane, wave);
-      if (it + NPF < ntiles)
-        load_raw<FMT, kWaves>(raw[p], a, b, t_begin + (it + NPF) * kTile, t_end, lane, wave);
-      __syncthreads();  // the tile is complete
-      const int t0 = t_begin + it * kTile;
-
-      // ---- partial scores over this wave's k-steps
-      f32x4 sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
-      const _Float16 *rh = tb + TL::kHi + li * kLdsRow + 8 * g + 32 * kb;
-      const _Float16 *rl = tb + TL::kLo + li * kLdsRow + 8 * g + 32 * kb;
+      const bool valid = it < ntiles;  // uniform across the workgroup
+      f32x4 sc[2];
+      if (valid) {
+        // ---- dequantize in registers; partial scores; C_hi to the value block
 #pragma unroll
-      for (int j = 0; j < 5; ++j) {
-        if (j < nk) {
-          const f16x8 ah = *(const f16x8 *)(rh + 32 * j);
-          sc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, qh[j], sc0, 0, 0, 0);
-          sc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, ql[j], sc1, 0, 0, 0);
-          if (kLo) {
-            const f16x8 al = *(const f16x8 *)(rl + 32 * j);
-            sc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, qh[j], sc1, 0, 0, 0);
+        for (int rb = 0; rb < 2; ++rb) {
+          f16x8 hi[4], lo[4];
+          f16x4 khi, klo;
+          // C_hi of this wave's channels goes to its value block as it is made
+          dequant16<FMT>(raw[p], rb, hi, lo, vblk + (16 * rb + i) * kVRow + 32 * g, khi, klo);
+          if (kZp) *(uint32_t *)(vblk + (16 * rb + i) * kVRow + 128 + 2 * g) = raw[p].zp[rb];
+          lds_stores_done();
+          f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi[kk], qh[kk], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi[kk], ql[kk], s1, 0, 0, 0);
+            if (kLo) s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo[kk], qh[kk], s1, 0, 0, 0);
           }
+          s0 = __builtin_amdgcn_mfma_f32_16x16x16f16(khi, kqh, s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_16x16x16f16(khi, kql, s1, 0, 0, 0);
+          if (kLo) s1 = __builtin_amdgcn_mfma_f32_16x16x16f16(klo, kqh, s1, 0, 0, 0);
+          if (kZp) {
+            const f16x2 z = bitcast<f16x2>(raw[p].zp[rb]);
+            const f16x4 az = {z.x, z.y, (_Float16)0.0f, (_Float16)0.0f};
+            s1 = __builtin_amdgcn_mfma_f32_16x16x16f16(az, zqh, s1, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x16f16(az, zql, s1, 0, 0, 0);
+          }
+          sc[rb] = s0 + s1;
         }
       }
-      if (kZp && wave == kWaves - 1) {
-        const f16x8 az = *(const f16x8 *)(tb + TL::kZ + li * kZRow + 8 * g);
-        sc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, qsh, sc1, 0, 0, 0);
-        sc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, qsl, sc1, 0, 0, 0);
-      }
-      *(f32x4 *)(part + (wave * 64 + lane) * 4) = sc0 + sc1;
-      __syncthreads();  // all partial scores are in LDS
-      f32x4 sc = *(const f32x4 *)(part + lane * 4);
-#pragma unroll
-      for (int w = 1; w < kWaves; ++w) sc += *(const f32x4 *)(part + (w * 64 + lane) * 4);
+      // always issued (past the split it reads zeros), so load counting stays exact
+      load16<FMT>(raw[p], rs, (it + NPF) * kT16, w, g, i);
+      if (!valid) continue;
 
-      // ---- online softmax (base 2), identical in every wave
-      float p4[4];
+      float *pb_out = part + ((it & 1) * kWaves * 64 + w * 64 + lane) * 8;
+      *(f32x4 *)pb_out = sc[0];
+      *(f32x4 *)(pb_out + 4) = sc[1];
+      lds_stores_done();
+      __syncthreads();  // every wave's partial scores of this tile are in LDS
+      const float *pb_in = part + ((it & 1) * kWaves * 64 + lane) * 8;
+      f32x4 t0 = *(const f32x4 *)pb_in, t1 = *(const f32x4 *)(pb_in + 4);
+#pragma unroll
+      for (int v = 1; v < kWaves; ++v) {
+        t0 += *(const f32x4 *)(pb_in + v * 64 * 8);
+        t1 += *(const f32x4 *)(pb_in + v * 64 * 8 + 4);
+      }
+
+      // ---- online softmax (base 2), identical in every wave; lane (g, i)
+      // holds tokens 4g+r and 16+4g+r of head i
+      const int tok0 = t_begin + it * kT16 + 4 * g;
+      float p8[8];
       float tmax = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p4[r] = (t0 + 4 * g + r < t_end) ? sc[r] : -INFINITY;
-        tmax = fmaxf(tmax, p4[r]);
+        p8[r] = (tok0 + r < t_end) ? t0[r] : -INFINITY;
+        p8[4 + r] = (tok0 + 16 + r < t_end) ? t1[r] : -INFINITY;
       }
+#pragma unroll
+      for (int r = 0; r < 8; ++r) tmax = fmaxf(tmax, p8[r]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
       const float m_new = fmaxf(m_run, tmax);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       float psum = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p4[r] = __builtin_amdgcn_exp2f(p4[r] - m_new);
-        psum += p4[r];
+      for (int r = 0; r < 8; ++r) {
+        p8[r] = __builtin_amdgcn_exp2f(p8[r] - m_new);
+        psum += p8[r];
       }
       l_run = l_run * alpha + psum;
       m_run = m_new;
 #pragma unroll
       for (int n = 0; n < 8; ++n) acc[n] *= alpha;
       if (kZp) accz *= alpha;
-      const f16x4 pb = {(_Float16)p4[0], (_Float16)p4[1], (_Float16)p4[2], (_Float16)p4[3]};
+      f16x8 pb;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) pb[r] = (_Float16)p8[r];
 
-      // ---- values of this wave's 128 channels
-      const _Float16 *vb = tb + TL::kHi + (4 * g + (li >> 2)) * kLdsRow + 4 * (li & 3) + 128 * wave;
+      // ---- values of this wave's 128 channels (its own block, no barrier needed)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const _Float16 *v0 = vblk + (4 * g + (i >> 2)) * kVRow + 4 * (i & 3);
+      const _Float16 *v1 = v0 + 16 * kVRow;
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
-        const f16x4 av = lds_read_tr16(vb + 16 * n);
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pb, acc[n], 0, 0, 0);
+        const f16x4 a0 = lds_read_tr16(v0 + 16 * n);
+        const f16x4 a1 = lds_read_tr16(v1 + 16 * n);
+        const f16x8 av = f16x8{a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb, acc[n], 0, 0, 0);
       }
-      if (kZp) {  // zero-point groups 16*(wave/2) .. +15
-        const f16x4 az = lds_read_tr16(tb + TL::kZ + (4 * g + (li >> 2)) * kZRow + 4 * (li & 3) +
-                                       16 * (wave >> 1));
-        accz = __builtin_amdgcn_mfma_f32_16x16x16f16(az, pb, accz, 0, 0, 0);
+      if (kZp) {
+        // columns 128..135 of the block are the 8 groups; lanes reading past
+        // them fill the unused slots 8..15 of this product
+        const _Float16 *z0 = vblk + (4 * g + (i >> 2)) * kVRow + 128 + 4 * (i & 3);
+        const f16x4 a0 = lds_read_tr16(z0);
+        const f16x4 a1 = lds_read_tr16(z0 + 16 * kVRow);
+        const f16x8 az = f16x8{a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        accz = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, pb, accz, 0, 0, 0);
       }
     }
   }
 
-  // ---- write this unit's partial: m and l (same in every wave), channels of this wave
+  // ---- write this unit's partial: m and l (same in every wave), this wave's channels
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
   if (kZp) {
-    // channel block n of this wave is zero-point group 8*wave + n; the wave
-    // holds sums for groups 16*(wave/2) + 4g + r
-    __syncthreads();  // everyone is done reading the partial-score area
-    float *oz = part + wave * 256;  // [16 heads][16 groups]
-#pragma unroll
-    for (int r = 0; r < 4; ++r) oz[li * 16 + 4 * g + r] = accz[r];
+    // accz lane (g, i) holds zero-point group 4g+r of this wave (slots 8..15 are
+    // padding); channel block n of the wave is group n
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int gofs = (wave & 1) * 8;  // group 8*wave + n within the wave's 16-group block
+    float *oz = (float *)vblk;  // [16 heads][16 slots], the value block is free now
 #pragma unroll
-    for (int n = 0; n < 8; ++n) acc[n] += oz[li * 16 + gofs + n];
+    for (int r = 0; r < 4; ++r) oz[i * 16 + 4 * g + r] = accz[r];
+    lds_stores_done();
+#pragma unroll
+    for (int n = 0; n < 8; ++n) acc[n] += oz[i * 16 + n];
   }
-  float *dst = a.ws_acc + (ws_row + li) * kLatent + 128 * wave + 4 * g;
+  float *dst = a.ws_acc + (ws_row + i) * kLatent + 128 * w + 4 * g;
 #pragma unroll
   for (int n = 0; n < 8; ++n) *(f32x4 *)(dst + 16 * n) = acc[n];
-  if (wave == 0 && g == 0) {
-    a.ws_m[ws_row + li] = m_run;
-    a.ws_l[ws_row + li] = l_run;
+  if (w == 0 && g == 0) {
+    a.ws_m[ws_row + i] = m_run;
+    a.ws_l[ws_row + i] = l_run;
   }
 }
 
 // ------------------------------------------------------------------ reduce
 
-// Per (head h, 8 batch rows): merge the splits, normalize, project by W_UV[h].
+constexpr int kReduceBT = 4;  // batch rows per combine block
+
+__device__ __forceinline__ float block_max256(float v, float *sh) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  v = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+  __syncthreads();
+  return v;
+}
+
+__device__ __forceinline__ float block_sum256(float v, float *sh) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  v = (sh[0] + sh[1]) + (sh[2] + sh[3]);
+  __syncthreads();
+  return v;
+}
+
+// Per (head h, 4 batch rows): merge the splits with log-sum-exp weights,
+// normalize, then out[b,h,:] = o_lat W_UV[h]. The split weights are formed in
+// parallel into LDS first, so the loads of the partial sums that follow are
+// independent of each other (no branch on a loaded value). Grid (H, ceil(B/4)).
 __global__ __launch_bounds__(256) void reduce_kernel(const float *ws_m, const float *ws_l,
                                                      const float *ws_acc, const uint16_t *w_uv,
                                                      int B, int H, int nsplit, float *out) {
-  __shared__ float olat[kAbsorbBT][kLatent];
-  __shared__ float part[kAbsorbBT][kVDim];
+  __shared__ float olat[kReduceBT][kLatent];
+  __shared__ float red[16][kReduceBT][kVDim];
+  __shared__ float wts[kMaxSplits];
+  __shared__ float sh[4];
   const int h = blockIdx.x;
-  const int b0 = blockIdx.y * kAbsorbBT;
+  const int b0 = blockIdx.y * kReduceBT;
   const int tid = threadIdx.x;
-  for (int bt = 0; bt < kAbsorbBT; ++bt) {
-    const int b = b0 + bt;
+  for (int bt = 0; bt < kReduceBT; ++bt) {
+    const int b = b0 + bt;  // uniform across the block
     if (b >= B) {
       olat[bt][tid] = 0.0f;
       olat[bt][tid + 256] = 0.0f;
       continue;
     }
     const int64_t base = (int64_t)b * nsplit * H + h;
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s)
-      if (ws_l[base + (int64_t)s * H] > 0.0f) M = fmaxf(M, ws_m[base + (int64_t)s * H]);
-    float Ls = 0.0f, o0 = 0.0f, o1 = 0.0f;
-    for (int s = 0; s < nsplit; ++s) {
+    float mloc = -INFINITY;
+    for (int s = tid; s < nsplit; s += 256)
+      if (ws_l[base + (int64_t)s * H] > 0.0f) mloc = fmaxf(mloc, ws_m[base + (int64_t)s * H]);
+    const float M = block_max256(mloc, sh);
+    float lloc = 0.0f;
+    for (int s = tid; s < nsplit; s += 256) {
       const float l = ws_l[base + (int64_t)s * H];
-      if (!(l > 0.0f)) continue;
-      const float w = exp2f(ws_m[base + (int64_t)s * H] - M);
-      Ls += w * l;
-      const float *acc = ws_acc + (base + (int64_t)s * H) * kLatent;
-      o0 += w * acc[tid];
-      o1 += w * acc[tid + 256];
+      const float wgt = l > 0.0f ? exp2f(ws_m[base + (int64_t)s * H] - M) : 0.0f;
+      wts[s] = wgt;
+      lloc += wgt * l;
+    }
+    const float Ls = block_sum256(lloc, sh);  // its barriers also publish wts
+    float o0 = 0.0f, o1 = 0.0f;
+    const float *acc = ws_acc + base * kLatent;
+#pragma unroll 4
+    for (int s = 0; s < nsplit; ++s) {
+      const float wgt = wts[s];
+      const float a0 = acc[(int64_t)s * H * kLatent + tid];
+      const float a1 = acc[(int64_t)s * H * kLatent + tid + 256];
+      // an empty split's sums are never written: select, do not multiply
+      o0 += wgt != 0.0f ? wgt * a0 : 0.0f;
+      o1 += wgt != 0.0f ? wgt * a1 : 0.0f;
     }
     const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
     olat[bt][tid] = o0 * inv;
     olat[bt][tid + 256] = o1 * inv;
+    __syncthreads();  // wts is rewritten for the next row
   }
   __syncthreads();
-  const int e = tid % kVDim, half = tid / kVDim;
-  float acc[kAbsorbBT];
+  // o_lat W_UV[h]: thread = (8 output columns, a slice of 32 latent rows)
+  const int eg = tid & 15, cs = tid >> 4;
+  float acc[kReduceBT][8];
 #pragma unroll
-  for (int bt = 0; bt < kAbsorbBT; ++bt) acc[bt] = 0.0f;
-  const uint16_t *w = w_uv + (int64_t)h * kLatent * kVDim + e;
-  for (int c = half * 256; c < half * 256 + 256; ++c) {
-    const float wv = bf16_bits_to_f32(w[(int64_t)c * kVDim]);
+  for (int bt = 0; bt < kReduceBT; ++bt)
 #pragma unroll
-    for (int bt = 0; bt < kAbsorbBT; ++bt) acc[bt] += olat[bt][c] * wv;
-  }
-  if (half == 1) {
+    for (int k = 0; k < 8; ++k) acc[bt][k] = 0.0f;
+  const uint16_t *w = w_uv + ((int64_t)h * kLatent + cs * 32) * kVDim + 8 * eg;
+#pragma unroll 4
+  for (int cc = 0; cc < 32; ++cc) {
+    const u32x4 wv = *(const u32x4 *)(w + cc * kVDim);
+    float wf[8];
 #pragma unroll
-    for (int bt = 0; bt < kAbsorbBT; ++bt) part[bt][e] = acc[bt];
-  }
-  __syncthreads();
-  if (half == 0) {
-#pragma unroll
-    for (int bt = 0; bt < kAbsorbBT; ++bt) {
-      const int b = b0 + bt;
-      if (b < B) out[((int64_t)b * H + h) * kVDim + e] = acc[bt] + part[bt][e];
+    for (int k = 0; k < 4; ++k) {
+      wf[2 * k] = bf16_bits_to_f32(wv[k] & 0xFFFFu);
+      wf[2 * k + 1] = bf16_bits_to_f32(wv[k] >> 16);
     }
+#pragma unroll
+    for (int bt = 0; bt < kReduceBT; ++bt) {
+      const float ov = olat[bt][cs * 32 + cc];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[bt][k] += ov * wf[k];
+    }
+  }
+#pragma unroll
+  for (int bt = 0; bt < kReduceBT; ++bt)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) red[cs][bt][8 * eg + k] = acc[bt][k];
+  lds_stores_done();
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int o = tid + 256 * k;
+    const int bt = o / kVDim, e = o % kVDim;
+    const int b = b0 + bt;
+    float v = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) v += red[q][bt][e];
+    if (b < B) out[((int64_t)b * H + h) * kVDim + e] = v;
   }
 }
 
@@ -1214,7 +1469,7 @@ int auto_splits(const mla_cache *c, int heads, int *out) {
 
 int chunk_for(int cap, int nsplit) {
   int chunk = (cap + nsplit - 1) / nsplit;
-  return (chunk + kTile - 1) / kTile * kTile;
+  return (chunk + kT16 - 1) / kT16 * kT16;  // whole 32-token tiles (two 16-token tiles)
 }
 
 template <int FMT>
@@ -1357,7 +1612,8 @@ int run_absorb(const mla_cache *cache, const DecodePlan &pl, const void *q_nope,
                const void *w_uk, int heads, float softmax_scale, void *workspace, hipStream_t s) {
   const int B = cache->batch;
   _Float16 *qa = (_Float16 *)((uint8_t *)workspace + pl.wl.qa);
-  hipLaunchKernelGGL(absorb_kernel, dim3(heads, (B + kAbsorbBT - 1) / kAbsorbBT), dim3(256), 0, s,
+  hipLaunchKernelGGL(absorb_kernel, dim3(heads, kLatent / kAbsorbCB, (B + kAbsorbBT - 1) / kAbsorbBT),
+                     dim3(256), 0, s,
                      (const uint16_t *)q_nope, (const uint16_t *)q_pe, (const uint16_t *)w_uk, B, heads,
                      softmax_scale * kLog2e, qa);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
@@ -1395,7 +1651,7 @@ int run_combine(const mla_cache *cache, const DecodePlan &pl, const void *w_uv, 
                 void *workspace, float *out, hipStream_t s) {
   const int B = cache->batch;
   uint8_t *ws = (uint8_t *)workspace;
-  hipLaunchKernelGGL(reduce_kernel, dim3(heads, (B + kAbsorbBT - 1) / kAbsorbBT), dim3(256), 0, s,
+  hipLaunchKernelGGL(reduce_kernel, dim3(heads, (B + kReduceBT - 1) / kReduceBT), dim3(256), 0, s,
                      (const float *)(ws + pl.wl.m), (const float *)(ws + pl.wl.l),
                      (const float *)(ws + pl.wl.acc), (const uint16_t *)w_uv, B, heads, pl.ns, out);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;

@@ -61,7 +61,9 @@ def test_workspace_size_formula():
     def a256(v):
         return (v + 255) // 256 * 256
     B, H, ns = 3, 16, 4
-    expect = a256(B * H * 576 * 2) + 2 * a256(B * ns * H * 4) + a256(B * ns * H * 512 * 4)
+    # absorbed queries: per (sequence, head) 576 channels as fp16 hi and lo, plus
+    # 32 group sums as hi and lo
+    expect = a256(B * H * (2 * 576 + 2 * 32) * 2) + 2 * a256(B * ns * H * 4) + a256(B * ns * H * 512 * 4)
     assert n == expect
 
 
