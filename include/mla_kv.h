@@ -142,8 +142,10 @@ int mla_decode_auto_splits(const mla_cache *cache, int32_t heads, int32_t *num_s
  *   heads    16, 32, 64 or 128
  *   softmax_scale   multiplies q.k before the softmax (e.g. 1/sqrt(192))
  *   num_splits      KV splits per sequence, 0 = auto, else 1..4096. Split s
- *                   covers tokens [s*chunk, (s+1)*chunk) with chunk =
- *                   ceil(capacity / num_splits) rounded up to 32.
+ *                   of sequence b covers tokens [s*chunk, (s+1)*chunk) with
+ *                   chunk = ceil(seq_len / num_splits) rounded up to 32, and
+ *                   for num_splits = 0 at least 256 (short sequences use
+ *                   fewer splits).
  *   workspace       device scratch of at least mla_decode_workspace_bytes;
  *                   its contents on entry do not matter
  *   out      fp32 [batch][heads][128]

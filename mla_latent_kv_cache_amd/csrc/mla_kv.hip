@@ -52,6 +52,7 @@ constexpr int kWaves = 4;                  // waves per split workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kMrgRow = kLatent + 4;       // fp32 per head row in the merge area
 constexpr int kMaxSplits = 4096;
+constexpr int kAutoMinChunk = 256;         // fewest tokens per split in the automatic plan
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -431,8 +432,15 @@ struct SplitArgs {
   float *ws_m;              // [B][nsplit][H]
   float *ws_l;              // [B][nsplit][H]
   float *ws_acc;            // [B][nsplit][H][512]
-  int B, H, cap, nsplit, chunk, hh_count;
+  int B, H, cap, nsplit, min_chunk, hh_count;
 };
+
+// Tokens per split of a sequence of length L: ceil(L / nsplit) rounded up to a
+// whole 32-token tile, and at least min_chunk. Splits past the sequence are empty.
+__device__ __forceinline__ int split_chunk(int L, int nsplit, int min_chunk) {
+  const int c = ((L + nsplit - 1) / nsplit + 31) / 32 * 32;
+  return max(c, min_chunk);
+}
 
 // Buffer descriptors over one split's rows of each plane. A buffer load past
 // the descriptor's byte count returns zero without touching memory, so rows
@@ -500,8 +508,9 @@ __device__ __forceinline__ void load_raw(RawTile<FMT, NW> &r, const SplitRsrc &r
 // the mantissa of 1024.0, subtract 1152 (both exact).
 __device__ __forceinline__ void codes_i8x4(uint32_t w, f16x2 &lo, f16x2 &hi) {
   const uint32_t u = w ^ 0x80808080u;
-  const uint32_t a = (u & 0xFFu) | ((u << 8) & 0xFF0000u) | 0x64006400u;
-  const uint32_t c = ((u >> 16) & 0xFFu) | ((u >> 8) & 0xFF0000u) | 0x64006400u;
+  // v_perm_b32: bytes 0-3 of the pair come from the second operand, 4-7 from the first
+  const uint32_t a = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);  // u0, 0x64, u1, 0x64
+  const uint32_t c = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);  // u2, 0x64, u3, 0x64
   const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
   lo = bitcast<f16x2>(a) - bias;
   hi = bitcast<f16x2>(c) - bias;
@@ -694,8 +703,9 @@ void split_kernel(SplitArgs a) {
   const int head = head0 + hw * 16 + li;          // the head this lane's columns belong to
 
   const int L = min(max(a.seq_lens[b], 0), a.cap);
-  const int t_begin = split * a.chunk;
-  const int t_end = min(t_begin + a.chunk, L);
+  const int chunk = split_chunk(L, a.nsplit, a.min_chunk);
+  const int t_begin = min(split * chunk, L);
+  const int t_end = min(t_begin + chunk, L);
   const int64_t ws_row = ((int64_t)b * a.nsplit + split) * a.H;
   if (t_begin >= t_end) {  // empty unit: identity of the merge
     if (tid < HGW * 16) {
@@ -891,61 +901,163 @@ void split_kernel(SplitArgs a) {
 // channels 32g..32g+31 of the wave's block (two quantization groups); in the
 // accumulators, head i.
 constexpr int kT16 = 32;             // tokens per tile
+constexpr float kLazy = 8.0f;         // log2 of the largest softmax weight before a rescale
 constexpr int kVRow = 128 + 8;       // fp16 per row of a wave's value block: 128 channels, then
                                      // (INT4) the 8 zero-points of the wave's groups
 constexpr int kWBlk = kT16 * kVRow;  // fp16 per wave block
-constexpr int kPart16 = 2 * kWaves * 64 * 8;          // floats: 2 buffers x 4 waves x 64 lanes x 8
+constexpr int kPart16 = kWaves * 64 * 8;              // floats: 4 waves x 64 lanes x 8
+
+// The small planes of a tile (latent scales, k_pe codes and scales, INT4
+// zero-points) are few bytes per row, and loading each lane's few bytes
+// straight from its row costs one memory request per row and instruction.
+// Instead the workgroup loads a tile's rows of each small plane as whole
+// 16-byte chunks (consecutive lanes, consecutive chunks), stages them in LDS,
+// and every lane then reads its own bytes from there.
+constexpr int kAuxRow = 80;      // staged row stride (bytes) of the scale, k_pe and zero blocks
+constexpr int kAuxRowBf16 = 144; // staged k_pe row stride for bf16 (128-byte rows, padded)
+
+template <int FMT> struct Aux16 {
+  static constexpr int kScale = 0;                                         // block offsets (bytes)
+  static constexpr int kKpe = FMT == MLA_FMT_BF16 ? 0 : kT16 * kAuxRow;
+  static constexpr int kZero = 2 * kT16 * kAuxRow;
+  static constexpr int kBytes = FMT == MLA_FMT_BF16 ? kT16 * kAuxRowBf16
+                                : FMT == MLA_FMT_INT4 ? 3 * kT16 * kAuxRow : 2 * kT16 * kAuxRow;
+};
 
 template <int FMT> struct Raw16;
 template <> struct Raw16<MLA_FMT_INT8> {
   static constexpr int kLat = 2;  // 16-byte loads per half-tile row: 32 codes
   u32x4 lat[2][2];
-  uint32_t sc[2], zp[2];
-  u32x2 kq[2];
-  uint32_t ks[2];
+  u32x4 sa, sb;                   // this lane's chunks of the small planes
 };
 template <> struct Raw16<MLA_FMT_INT4> {
   static constexpr int kLat = 1;  // 32 nibbles
   u32x4 lat[2][1];
-  uint32_t sc[2], zp[2];
-  u32x2 kq[2];
-  uint32_t ks[2];
+  u32x4 sa, sb;
 };
 template <> struct Raw16<MLA_FMT_BF16> {
   static constexpr int kLat = 4;  // 32 bf16
   u32x4 lat[2][4];
-  uint32_t sc[2], zp[2];
-  u32x2 kq[2];
-  uint32_t ks[2];
+  u32x4 sa, sb;
 };
 
-// Raw data of this lane for the tile starting at split row r0: rows r0+i and
-// r0+16+i, channels 128w+32g..+31 and k_pe channels 16w+4g..+3.
+// What a lane reads back from the staged small planes for rows i and 16+i.
+struct Meta16 {
+  uint32_t sc[2], ks[2], zp[2];
+  u32x2 kq[2];
+};
+
+// Byte offsets of this lane's data within a tile (the same for every tile).
+//   latent: rows i and 16+i, channels 128w+32g..+31
+//   small planes: chunk plan of the staging loads. Wave w (uniform) loads
+//     slot A: scale chunks 64w+l (w < 3; 160 chunks = 32 rows x 80 B), or for
+//             bf16 k_pe chunks 64w+l (256 chunks = 32 rows x 128 B);
+//     slot B: k_pe chunks 64w+l (w < 2; 128 chunks = 32 rows x 64 B), and for
+//             INT4 zero-point chunks 64(w-2)+l (w >= 2; 128 chunks).
+//   A chunk past its plane's tile reads nothing (kOffNone) and is not staged.
+template <int FMT> struct Off16 {
+  int lat[2][Raw16<FMT>::kLat];
+  int ga, gb;    // byte offsets in the tile (or kOffNone)
+  int la, lb;    // LDS byte offsets in the staging area (or -1: not staged)
+  bool b_zero;   // slot B reads the zero-point plane (INT4, waves 2 and 3)
+};
+
 template <int FMT>
-__device__ __forceinline__ void load16(Raw16<FMT> &r, const SplitRsrc &rs, int r0, int w, int g, int i) {
+__device__ __forceinline__ Off16<FMT> offsets16(int w, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  Off16<FMT> o;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    const int row = r0 + 16 * rb + i;
+    const int row = 16 * rb + i;
 #pragma unroll
     for (int j = 0; j < Raw16<FMT>::kLat; ++j) {
-      int off;
-      if (FMT == MLA_FMT_INT8) off = row * kLatent + 128 * w + 32 * g + 16 * j;
-      else if (FMT == MLA_FMT_INT4) off = row * (kLatent / 2) + 64 * w + 16 * g;
-      else off = row * (kLatent * 2) + 2 * (128 * w + 32 * g) + 16 * j;
-      r.lat[rb][j] = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rs.ckv, off, 0, 0));
+      if (FMT == MLA_FMT_INT8) o.lat[rb][j] = row * kLatent + 128 * w + 32 * g + 16 * j;
+      else if (FMT == MLA_FMT_INT4) o.lat[rb][j] = row * (kLatent / 2) + 64 * w + 16 * g;
+      else o.lat[rb][j] = row * (kLatent * 2) + 2 * (128 * w + 32 * g) + 16 * j;
     }
-    if (FMT != MLA_FMT_BF16) {
-      r.sc[rb] = __builtin_amdgcn_raw_buffer_load_b32(rs.scale, row * kNScale * 2 + (8 * w + 2 * g) * 2, 0, 0);
-      r.kq[rb].x = __builtin_amdgcn_raw_buffer_load_b32(rs.kpe, row * kRope + 16 * w + 4 * g, 0, 0);
-      r.ks[rb] = __builtin_amdgcn_raw_buffer_load_b16(
-          rs.scale, row * kNScale * 2 + (kNGroupL + 2 * w + (g >> 1)) * 2, 0, 0);
-    } else {
-      r.kq[rb] = bitcast<u32x2>(
-          __builtin_amdgcn_raw_buffer_load_b64(rs.kpe, row * (kRope * 2) + 2 * (16 * w + 4 * g), 0, 0));
-    }
-    if (FMT == MLA_FMT_INT4)
-      r.zp[rb] = __builtin_amdgcn_raw_buffer_load_b32(rs.zero, row * kNGroupL * 2 + (8 * w + 2 * g) * 2, 0, 0);
   }
+  o.ga = o.gb = kOffNone;
+  o.la = o.lb = -1;
+  o.b_zero = false;
+  if (FMT == MLA_FMT_BF16) {
+    const int c = 64 * w + lane;  // < 256
+    o.ga = 16 * c;
+    o.la = (c >> 3) * kAuxRowBf16 + 16 * (c & 7);
+  } else {
+    const int ca = 64 * w + lane;
+    if (ca < kT16 * kAuxRow / 16) {
+      o.ga = 16 * ca;
+      o.la = Aux16<FMT>::kScale + 16 * ca;
+    }
+    if (w < 2) {
+      const int cb = 64 * w + lane;  // k_pe chunk, 4 per 64-byte row
+      o.gb = 16 * cb;
+      o.lb = Aux16<FMT>::kKpe + (cb >> 2) * kAuxRow + 16 * (cb & 3);
+    } else if (FMT == MLA_FMT_INT4) {
+      const int cb = 64 * (w - 2) + lane;  // zero-point chunk, 4 per 64-byte row
+      o.gb = 16 * cb;
+      o.lb = Aux16<FMT>::kZero + (cb >> 2) * kAuxRow + 16 * (cb & 3);
+      o.b_zero = true;
+    }
+  }
+  return o;
+}
+
+// Descriptors over rows [r0, t_end) of the split (empty when r0 >= t_end):
+// the tile's own base, so per-lane offsets stay constant across tiles and
+// the range check still covers every byte read. All scalar arithmetic.
+template <int FMT>
+__device__ __forceinline__ SplitRsrc tile_rsrc(const SplitArgs &a, int b, int r0, int t_end) {
+  const int r = min(r0, t_end);
+  return split_rsrc<FMT>(a, b, r, t_end);
+}
+
+// Issue every load of one tile. `zero_b` is wave-uniform: it selects the
+// descriptor of slot B. Rows past the descriptor read as zeros.
+template <int FMT>
+__device__ __forceinline__ void load16(Raw16<FMT> &r, const SplitRsrc &rs, const Off16<FMT> &o, bool zero_b) {
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int j = 0; j < Raw16<FMT>::kLat; ++j)
+      r.lat[rb][j] = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rs.ckv, o.lat[rb][j], 0, 0));
+  if (FMT == MLA_FMT_BF16) {
+    r.sa = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rs.kpe, o.ga, 0, 0));
+  } else {
+    r.sa = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rs.scale, o.ga, 0, 0));
+    r.sb = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(zero_b ? rs.zero : rs.kpe, o.gb, 0, 0));
+  }
+}
+
+// This lane's chunks into the staging area.
+template <int FMT>
+__device__ __forceinline__ void stage16(const Raw16<FMT> &r, const Off16<FMT> &o, uint8_t *aux) {
+  if (o.la >= 0) *(u32x4 *)(aux + o.la) = r.sa;
+  if (FMT != MLA_FMT_BF16 && o.lb >= 0) *(u32x4 *)(aux + o.lb) = r.sb;
+}
+
+// This lane's small-plane values of rows i and 16+i from the staging area.
+template <int FMT>
+__device__ __forceinline__ Meta16 meta16(const uint8_t *aux, int w, int g, int i) {
+  Meta16 m;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int row = 16 * rb + i;
+    if (FMT == MLA_FMT_BF16) {
+      m.kq[rb] = *(const u32x2 *)(aux + row * kAuxRowBf16 + 2 * (16 * w + 4 * g));
+      m.sc[rb] = m.ks[rb] = m.zp[rb] = 0;
+    } else {
+      const uint8_t *srow = aux + Aux16<FMT>::kScale + row * kAuxRow;
+      m.sc[rb] = *(const uint32_t *)(srow + 2 * (8 * w + 2 * g));
+      m.ks[rb] = *(const uint16_t *)(srow + 2 * (kNGroupL + 2 * w + (g >> 1)));
+      m.kq[rb].x = *(const uint32_t *)(aux + Aux16<FMT>::kKpe + row * kAuxRow + 16 * w + 4 * g);
+      m.kq[rb].y = 0;
+      m.zp[rb] = FMT == MLA_FMT_INT4
+                     ? *(const uint32_t *)(aux + Aux16<FMT>::kZero + row * kAuxRow + 2 * (8 * w + 2 * g))
+                     : 0u;
+    }
+  }
+  return m;
 }
 
 __device__ __forceinline__ f16x8 cat8(f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
@@ -962,10 +1074,10 @@ __device__ __forceinline__ f16x8 cat8(f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
 // into channel order. The MFMA operands are then whole registers straight
 // from the packed multiply-adds, as in the other formats.
 template <int FMT>
-__device__ __forceinline__ void dequant16(const Raw16<FMT> &r, int rb, f16x8 (&hi)[4], f16x8 (&lo)[4],
-                                          _Float16 *vrow, f16x4 &khi, f16x4 &klo) {
+__device__ __forceinline__ void dequant16(const Raw16<FMT> &r, const Meta16 &m, int rb, f16x8 (&hi)[4],
+                                          f16x8 (&lo)[4], _Float16 *vrow, f16x4 &khi, f16x4 &klo) {
   if (FMT == MLA_FMT_INT8) {
-    const f16x2 s0 = splat_f16_bits(r.sc[rb] & 0xFFFFu), s1 = splat_f16_bits(r.sc[rb] >> 16);
+    const f16x2 s0 = splat_f16_bits(m.sc[rb] & 0xFFFFu), s1 = splat_f16_bits(m.sc[rb] >> 16);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const u32x4 v = r.lat[rb][kk >> 1];
@@ -982,7 +1094,7 @@ __device__ __forceinline__ void dequant16(const Raw16<FMT> &r, int rb, f16x8 (&h
       *(f16x8 *)(vrow + 8 * kk) = hi[kk];
     }
   } else if (FMT == MLA_FMT_INT4) {
-    const f16x2 s0 = splat_f16_bits(r.sc[rb] & 0xFFFFu), s1 = splat_f16_bits(r.sc[rb] >> 16);
+    const f16x2 s0 = splat_f16_bits(m.sc[rb] & 0xFFFFu), s1 = splat_f16_bits(m.sc[rb] >> 16);
     const f16x2 bias = {(_Float16)1024.0f, (_Float16)1024.0f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -1012,39 +1124,53 @@ __device__ __forceinline__ void dequant16(const Raw16<FMT> &r, int rb, f16x8 (&h
     }
   }
   if (FMT != MLA_FMT_BF16) {
-    const f16x2 ks = splat_f16_bits(r.ks[rb]);
+    const f16x2 ks = splat_f16_bits(m.ks[rb]);
     f16x2 q0, q1, h0, h1, l0, l1;
-    codes_i8x4(r.kq[rb].x, q0, q1);
+    codes_i8x4(m.kq[rb].x, q0, q1);
     scale_split(q0, ks, h0, l0);
     scale_split(q1, ks, h1, l1);
     khi = f16x4{h0.x, h0.y, h1.x, h1.y};
     klo = f16x4{l0.x, l0.y, l1.x, l1.y};
   } else {
-    const f16x2 a = bf16x2_to_f16x2(r.kq[rb].x), b = bf16x2_to_f16x2(r.kq[rb].y);
+    const f16x2 a = bf16x2_to_f16x2(m.kq[rb].x), b = bf16x2_to_f16x2(m.kq[rb].y);
     khi = f16x4{a.x, a.y, b.x, b.y};
     klo = f16x4{};
   }
 }
 
+// Per tile, every wave:
+//   1. stages its chunks of the tile's small planes, barrier (the staging
+//      area and the partial-score slots of the previous tile are then free);
+//   2. reads its scales, k_pe codes and zero-points back, dequantizes its
+//      latent channels in registers, stores C_hi to its value block, and
+//      issues the MFMAs of its partial scores;
+//   3. issues all loads of the next tile (after the score sums are read back
+//      from the MFMA results);
+//   4. stores its partial scores, barrier, and adds the four waves' partials
+//      in a fixed order;
+//   5. online softmax and the value MFMAs of its channels.
 template <int FMT>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(3, 3)))
 void split16_kernel(SplitArgs a) {
-  constexpr int NPF = 1;  // tiles of loads in flight per wave (issued a whole tile ahead)
   constexpr bool kLo = FMT != MLA_FMT_BF16;
   constexpr bool kZp = FMT == MLA_FMT_INT4;
   // +16: the zero-point read of the last row runs 8 fp16 past its block (unused slots)
   __shared__ __attribute__((aligned(16))) _Float16 wblk[kWaves * kWBlk + 16];
   __shared__ __attribute__((aligned(16))) float part[kPart16];
+  // read only between the two barriers of a tile (the next tile's staging
+  // writes come after the second)
+  __shared__ __attribute__((aligned(16))) uint8_t aux[Aux16<FMT>::kBytes];
 
   const int split = blockIdx.x;
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 4, i = lane & 15;
 
   const int L = min(max(a.seq_lens[b], 0), a.cap);
-  const int t_begin = split * a.chunk;
-  const int t_end = min(t_begin + a.chunk, L);
+  const int chunk = split_chunk(L, a.nsplit, a.min_chunk);
+  const int t_begin = min(split * chunk, L);
+  const int t_end = min(t_begin + chunk, L);
   const int64_t ws_row = ((int64_t)b * a.nsplit + split) * a.H;
   if (t_begin >= t_end) {  // empty unit: identity of the merge
     if (tid < 16) {
@@ -1077,7 +1203,7 @@ void split16_kernel(SplitArgs a) {
     zql = f16x4{sl.x, sl.y, (_Float16)0.0f, (_Float16)0.0f};
   }
 
-  _Float16 *vblk = wblk + w * kWBlk;  // [32][kVRow] C_hi of this wave's channels (+ zero-points)
+  _Float16 *vblk = wblk + w * kWBlk;  // [32][kVRow] C_hi of this wave's channels
 
   f32x4 acc[8];
 #pragma unroll
@@ -1085,116 +1211,138 @@ void split16_kernel(SplitArgs a) {
   f32x4 accz = {0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.0f;
 
-  const SplitRsrc rs = split_rsrc<FMT>(a, b, t_begin, t_end);
-  Raw16<FMT> raw[NPF];
-#pragma unroll
-  for (int p = 0; p < NPF; ++p) load16<FMT>(raw[p], rs, p * kT16, w, g, i);
+  const Off16<FMT> off = offsets16<FMT>(w, lane);
+  const bool zero_b = off.b_zero;  // uniform: depends on the wave only
+  Raw16<FMT> raw;
+  load16<FMT>(raw, tile_rsrc<FMT>(a, b, t_begin, t_end), off, zero_b);
 
-  for (int it0 = 0; it0 < ntiles; it0 += NPF) {
-#pragma unroll
-    for (int p = 0; p < NPF; ++p) {
-      const int it = it0 + p;
-      const bool valid = it < ntiles;  // uniform across the workgroup
-      f32x4 sc[2];
-      if (valid) {
-        // ---- dequantize in registers; partial scores; C_hi to the value block
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          f16x8 hi[4], lo[4];
-          f16x4 khi, klo;
-          // C_hi of this wave's channels goes to its value block as it is made
-          dequant16<FMT>(raw[p], rb, hi, lo, vblk + (16 * rb + i) * kVRow + 32 * g, khi, klo);
-          if (kZp) *(uint32_t *)(vblk + (16 * rb + i) * kVRow + 128 + 2 * g) = raw[p].zp[rb];
-          lds_stores_done();
-          f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi[kk], qh[kk], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi[kk], ql[kk], s1, 0, 0, 0);
-            if (kLo) s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo[kk], qh[kk], s1, 0, 0, 0);
-          }
-          s0 = __builtin_amdgcn_mfma_f32_16x16x16f16(khi, kqh, s0, 0, 0, 0);
-          s1 = __builtin_amdgcn_mfma_f32_16x16x16f16(khi, kql, s1, 0, 0, 0);
-          if (kLo) s1 = __builtin_amdgcn_mfma_f32_16x16x16f16(klo, kqh, s1, 0, 0, 0);
-          if (kZp) {
-            const f16x2 z = bitcast<f16x2>(raw[p].zp[rb]);
-            const f16x4 az = {z.x, z.y, (_Float16)0.0f, (_Float16)0.0f};
-            s1 = __builtin_amdgcn_mfma_f32_16x16x16f16(az, zqh, s1, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_16x16x16f16(az, zql, s1, 0, 0, 0);
-          }
-          sc[rb] = s0 + s1;
-        }
-      }
-      // always issued (past the split it reads zeros), so load counting stays exact
-      load16<FMT>(raw[p], rs, (it + NPF) * kT16, w, g, i);
-      if (!valid) continue;
+  for (int it = 0; it < ntiles; ++it) {
+    // ---- 1. the tile's small planes into the shared staging area
+    stage16<FMT>(raw, off, aux);
+    lds_stores_done();
+    __syncthreads();
+    const Meta16 mt = meta16<FMT>(aux, w, g, i);
 
-      float *pb_out = part + ((it & 1) * kWaves * 64 + w * 64 + lane) * 8;
-      *(f32x4 *)pb_out = sc[0];
-      *(f32x4 *)(pb_out + 4) = sc[1];
+    // ---- 2. dequantize in registers; partial scores; C_hi to the value block
+    f32x4 sc[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      f16x8 hi[4], lo[4];
+      f16x4 khi, klo;
+      dequant16<FMT>(raw, mt, rb, hi, lo, vblk + (16 * rb + i) * kVRow + 32 * g, khi, klo);
+      // INT4: the zero-points of the wave's 8 groups go to columns 128..135 of
+      // its value block, for the value-side zero-point product
+      if (kZp) *(uint32_t *)(vblk + (16 * rb + i) * kVRow + 128 + 2 * g) = mt.zp[rb];
       lds_stores_done();
-      __syncthreads();  // every wave's partial scores of this tile are in LDS
-      const float *pb_in = part + ((it & 1) * kWaves * 64 + lane) * 8;
-      f32x4 t0 = *(const f32x4 *)pb_in, t1 = *(const f32x4 *)(pb_in + 4);
+      // Each accumulator is fed by one MFMA shape only: a 16x16x16 MFMA that
+      // takes as its accumulator the result of a 16x16x32 MFMA issued just
+      // before it reads a stale value on this GPU (the matrix unit forwards
+      // a result only to an identical instruction), and the compiler does not
+      // separate the two. The k_pe and zero-point products (K = 16) therefore
+      // build their own sum s2, and the three sums meet in VALU adds.
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f}, s2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int v = 1; v < kWaves; ++v) {
-        t0 += *(const f32x4 *)(pb_in + v * 64 * 8);
-        t1 += *(const f32x4 *)(pb_in + v * 64 * 8 + 4);
+      for (int kk = 0; kk < 4; ++kk) {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi[kk], qh[kk], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi[kk], ql[kk], s1, 0, 0, 0);
+        if (kLo) s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo[kk], qh[kk], s1, 0, 0, 0);
       }
+      s2 = __builtin_amdgcn_mfma_f32_16x16x16f16(khi, kqh, s2, 0, 0, 0);
+      s2 = __builtin_amdgcn_mfma_f32_16x16x16f16(khi, kql, s2, 0, 0, 0);
+      if (kLo) s2 = __builtin_amdgcn_mfma_f32_16x16x16f16(klo, kqh, s2, 0, 0, 0);
+      if (kZp) {
+        const f16x2 z = bitcast<f16x2>(mt.zp[rb]);
+        const f16x4 az = {z.x, z.y, (_Float16)0.0f, (_Float16)0.0f};
+        s2 = __builtin_amdgcn_mfma_f32_16x16x16f16(az, zqh, s2, 0, 0, 0);
+        s2 = __builtin_amdgcn_mfma_f32_16x16x16f16(az, zql, s2, 0, 0, 0);
+      }
+      sc[rb] = (s0 + s1) + s2;
+    }
 
-      // ---- online softmax (base 2), identical in every wave; lane (g, i)
-      // holds tokens 4g+r and 16+4g+r of head i
-      const int tok0 = t_begin + it * kT16 + 4 * g;
-      float p8[8];
-      float tmax = -INFINITY;
+    // ---- 3. the next tile's loads. They go out only after the score sums
+    // above have been read back from the MFMA results, so no matrix
+    // instruction is still pending when they are issued: a load that falls
+    // wholly past the split returns (zeros) within a few cycles, and must not
+    // land in a register that a queued MFMA of this tile has yet to read.
+    // Always issued, so the count of outstanding loads is the same on every
+    // path.
+    __builtin_amdgcn_sched_barrier(0);
+    load16<FMT>(raw, tile_rsrc<FMT>(a, b, t_begin + (it + 1) * kT16, t_end), off, zero_b);
+
+    // ---- 4. partial scores of the four waves
+    float *pb_out = part + (w * 64 + lane) * 8;
+    *(f32x4 *)pb_out = sc[0];
+    *(f32x4 *)(pb_out + 4) = sc[1];
+    lds_stores_done();
+    __syncthreads();  // every wave's partial scores of this tile are in LDS
+    const float *pb_in = part + lane * 8;
+    f32x4 t0 = *(const f32x4 *)pb_in, t1 = *(const f32x4 *)(pb_in + 4);
+#pragma unroll
+    for (int v = 1; v < kWaves; ++v) {
+      t0 += *(const f32x4 *)(pb_in + v * 64 * 8);
+      t1 += *(const f32x4 *)(pb_in + v * 64 * 8 + 4);
+    }
+
+    // ---- 5. online softmax (base 2), identical in every wave; lane (g, i)
+    // holds tokens 4g+r and 16+4g+r of head i
+    float p8[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+    const int left = t_end - (t_begin + it * kT16);  // uniform
+    if (left < kT16) {  // only the last tile of a split is partial
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p8[r] = (tok0 + r < t_end) ? t0[r] : -INFINITY;
-        p8[4 + r] = (tok0 + 16 + r < t_end) ? t1[r] : -INFINITY;
+        if (4 * g + r >= left) p8[r] = -INFINITY;
+        if (16 + 4 * g + r >= left) p8[4 + r] = -INFINITY;
       }
-#pragma unroll
-      for (int r = 0; r < 8; ++r) tmax = fmaxf(tmax, p8[r]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    }
+    float tmax = fmaxf(fmaxf(fmaxf(p8[0], p8[1]), fmaxf(p8[2], p8[3])),
+                       fmaxf(fmaxf(p8[4], p8[5]), fmaxf(p8[6], p8[7])));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    // Lazy running max: the reference point moves only when some head's tile
+    // maximum exceeds it by more than 2^kLazy, so weights stay below 2^kLazy
+    // (exact in fp16 relative terms) and most tiles skip the rescale.
+    // Every wave holds the same scores and takes the same decision.
+    if (__builtin_amdgcn_ballot_w64(tmax > m_run + kLazy)) {
       const float m_new = fmaxf(m_run, tmax);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      float psum = 0.0f;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        p8[r] = __builtin_amdgcn_exp2f(p8[r] - m_new);
-        psum += p8[r];
-      }
-      l_run = l_run * alpha + psum;
+      l_run *= alpha;
       m_run = m_new;
 #pragma unroll
       for (int n = 0; n < 8; ++n) acc[n] *= alpha;
       if (kZp) accz *= alpha;
-      f16x8 pb;
+    }
+    float psum = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) pb[r] = (_Float16)p8[r];
+    for (int r = 0; r < 8; ++r) {
+      p8[r] = __builtin_amdgcn_exp2f(p8[r] - m_run);
+      psum += p8[r];
+    }
+    l_run += psum;
+    f16x8 pb;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) pb[r] = (_Float16)p8[r];
 
-      // ---- values of this wave's 128 channels (its own block, no barrier needed)
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const _Float16 *v0 = vblk + (4 * g + (i >> 2)) * kVRow + 4 * (i & 3);
-      const _Float16 *v1 = v0 + 16 * kVRow;
+    // values of this wave's 128 channels (its own block, no barrier needed)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const _Float16 *v0 = vblk + (4 * g + (i >> 2)) * kVRow + 4 * (i & 3);
+    const _Float16 *v1 = v0 + 16 * kVRow;
 #pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        const f16x4 a0 = lds_read_tr16(v0 + 16 * n);
-        const f16x4 a1 = lds_read_tr16(v1 + 16 * n);
-        const f16x8 av = f16x8{a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb, acc[n], 0, 0, 0);
-      }
-      if (kZp) {
-        // columns 128..135 of the block are the 8 groups; lanes reading past
-        // them fill the unused slots 8..15 of this product
-        const _Float16 *z0 = vblk + (4 * g + (i >> 2)) * kVRow + 128 + 4 * (i & 3);
-        const f16x4 a0 = lds_read_tr16(z0);
-        const f16x4 a1 = lds_read_tr16(z0 + 16 * kVRow);
-        const f16x8 az = f16x8{a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        accz = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, pb, accz, 0, 0, 0);
-      }
+    for (int n = 0; n < 8; ++n) {
+      const f16x4 a0 = lds_read_tr16(v0 + 16 * n);
+      const f16x4 a1 = lds_read_tr16(v1 + 16 * n);
+      const f16x8 av = f16x8{a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb, acc[n], 0, 0, 0);
+    }
+    if (kZp) {
+      // columns 128..135 of the block are the 8 groups; lanes reading past
+      // them fill the unused slots 8..15 of this product
+      const _Float16 *z0 = vblk + (4 * g + (i >> 2)) * kVRow + 128 + 4 * (i & 3);
+      const f16x4 a0 = lds_read_tr16(z0);
+      const f16x4 a1 = lds_read_tr16(z0 + 16 * kVRow);
+      const f16x8 az = f16x8{a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      accz = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, pb, accz, 0, 0, 0);
     }
   }
 
@@ -1274,17 +1422,21 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float *ws_m, const fl
       if (ws_l[base + (int64_t)s * H] > 0.0f) mloc = fmaxf(mloc, ws_m[base + (int64_t)s * H]);
     const float M = block_max256(mloc, sh);
     float lloc = 0.0f;
+    int last = -1;
     for (int s = tid; s < nsplit; s += 256) {
       const float l = ws_l[base + (int64_t)s * H];
       const float wgt = l > 0.0f ? exp2f(ws_m[base + (int64_t)s * H] - M) : 0.0f;
       wts[s] = wgt;
       lloc += wgt * l;
+      if (l > 0.0f) last = s;
     }
+    // the splits holding tokens are a prefix; the rest are never read
+    const int nact = (int)block_max256((float)last, sh) + 1;
     const float Ls = block_sum256(lloc, sh);  // its barriers also publish wts
     float o0 = 0.0f, o1 = 0.0f;
     const float *acc = ws_acc + base * kLatent;
 #pragma unroll 4
-    for (int s = 0; s < nsplit; ++s) {
+    for (int s = 0; s < nact; ++s) {
       const float wgt = wts[s];
       const float a0 = acc[(int64_t)s * H * kLatent + tid];
       const float a1 = acc[(int64_t)s * H * kLatent + tid + 256];
@@ -1458,8 +1610,11 @@ int auto_splits(const mla_cache *c, int heads, int *out) {
   if (cus < 1) cus = 1;
   const int hh = heads <= 64 ? 1 : heads / 64;
   const int64_t units = (int64_t)c->batch * hh;
-  int64_t want = (2 * (int64_t)cus + units - 1) / units;     // about two workgroups per CU
-  const int64_t by_len = (c->capacity + 255) / 256;           // keep >= 256 tokens per split
+  // About eight workgroups per CU when every sequence is full, so ragged batches
+  // still keep the chip busy; splits of the automatic plan hold at least
+  // kAutoMinChunk tokens, so short sequences use fewer of them.
+  int64_t want = (8 * (int64_t)cus + units - 1) / units;
+  const int64_t by_len = (c->capacity + kAutoMinChunk - 1) / kAutoMinChunk;
   int64_t ns = want < by_len ? want : by_len;
   if (ns < 1) ns = 1;
   if (ns > kMaxSplits) ns = kMaxSplits;
@@ -1467,10 +1622,6 @@ int auto_splits(const mla_cache *c, int heads, int *out) {
   return MLA_OK;
 }
 
-int chunk_for(int cap, int nsplit) {
-  int chunk = (cap + nsplit - 1) / nsplit;
-  return (chunk + kT16 - 1) / kT16 * kT16;  // whole 32-token tiles (two 16-token tiles)
-}
 
 template <int FMT>
 hipError_t launch_split_fmt(const SplitArgs &a, int heads, dim3 grid, hipStream_t st) {
@@ -1573,6 +1724,7 @@ namespace {
 
 struct DecodePlan {
   int ns;
+  int min_chunk;  // kAutoMinChunk for the automatic split count, else one tile
   WsLayout wl;
 };
 
@@ -1590,6 +1742,7 @@ int plan_decode(const mla_cache *cache, int heads, int num_splits, const void *w
     if (st != MLA_OK) return st;
   }
   plan->ns = ns;
+  plan->min_chunk = num_splits == 0 ? kAutoMinChunk : kT16;
   plan->wl = ws_layout(cache->batch, heads, ns);
   if (!workspace || workspace_bytes < plan->wl.total || ((uintptr_t)workspace & 255u))
     return MLA_ERR_WORKSPACE;
@@ -1637,7 +1790,7 @@ int run_partial(const mla_cache *cache, const DecodePlan &pl, int layer, int hea
   a.H = heads;
   a.cap = cache->capacity;
   a.nsplit = pl.ns;
-  a.chunk = chunk_for(cache->capacity, pl.ns);
+  a.min_chunk = pl.min_chunk;
   a.hh_count = heads <= 64 ? 1 : heads / 64;
   const dim3 grid((unsigned)(pl.ns * a.hh_count), (unsigned)cache->batch);
   hipError_t e;
