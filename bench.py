@@ -217,7 +217,7 @@ def roofline(res):
         "bound": "hbm", "achieved": round(res["partial_gb_per_s"], 1), "peak": HBM_PEAK_GBS,
         "unit": "GB/s", "frac": round(res["partial_gb_per_s"] / HBM_PEAK_GBS, 4),
         "traffic": stored_traffic(res["workload"]),
-        "kernel": "split_kernel (mla_decode_partial)",
+        "kernel": ("split16_kernel" if res["heads"] == 16 else "split_kernel") + " (mla_decode_partial)",
         "per_launch_bytes": res["partial_bytes_per_launch"],
         "avg_launch_us": round(res["partial_avg_us"], 2),
     }
@@ -268,6 +268,94 @@ def cpu_baseline(wid, seconds):
     }
 
 
+PMC_COPY_BYTES = 1 << 30  # the calibration copy: 1 GiB read, 1 GiB written
+
+
+def pmc_run(wid):
+    """Launches for counter collection (no timing): one step's partial-attention
+    launches of the workload, then a plain device copy of PMC_COPY_BYTES twice.
+    Run under `rocprofv3 --pmc FETCH_SIZE` and again under `--pmc WRITE_SIZE`."""
+    import torch
+    r = Runner(wid, 2)
+    r.step()
+    torch.cuda.synchronize()
+    L = r.lib
+    for layer in range(r.w.layers):
+        qn, qp = r.args_q[layer]
+        wuk, _ = r.args_w[layer]
+        r.check(L.mla_decode_absorb(r.cref, qn, qp, wuk, r.H, r.scale, r.splits, r.ws_p, r.ws_n, r.sp), "absorb")
+        r.check(L.mla_decode_partial(r.cref, layer, r.H, r.splits, r.ws_p, r.ws_n, r.sp), "partial")
+    torch.cuda.synchronize()
+    a = torch.ones(PMC_COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"pmc run: {r.w.layers} partial launches of {r.w.name}, 2 copies of {PMC_COPY_BYTES} bytes")
+
+
+def _pmc_means(csv_path, counter):
+    """Mean counter value (KiB) per dispatch for the partial kernel and the copy."""
+    import csv
+    vals = {"partial": {}, "copy": {}}
+    with open(csv_path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            name = row["Kernel_Name"]
+            kind = "partial" if "split16_kernel" in name or "split_kernel" in name else \
+                "copy" if "copyBuffer" in name or "copy" in name.lower() else None
+            if kind is None:
+                continue
+            d = vals[kind]
+            d[row["Dispatch_Id"]] = d.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
+    out = {}
+    for kind, d in vals.items():
+        v = sorted(d.values())
+        if kind == "copy":  # the two large copies are the largest copy dispatches
+            v = v[-2:]
+        out[kind] = (float(np.mean(v)) if v else None, len(d))
+    return out
+
+
+def summarize_pmc(wid, fetch_csv, write_csv, out_path):
+    """Write the profiles/ summary that roofline() reads: HBM bytes per partial
+    launch from FETCH_SIZE and WRITE_SIZE, each scaled by what the same counter
+    reads for the calibration copy of known size."""
+    from mla_latent_kv_cache_amd import workloads as W
+    w = W.WORKLOADS[wid]
+    fe = _pmc_means(fetch_csv, "FETCH_SIZE")
+    wr = _pmc_means(write_csv, "WRITE_SIZE")
+    f_fetch = PMC_COPY_BYTES / (fe["copy"][0] * 1024.0)
+    f_write = PMC_COPY_BYTES / (wr["copy"][0] * 1024.0)
+    hbm = fe["partial"][0] * 1024.0 * f_fetch + wr["partial"][0] * 1024.0 * f_write
+    lens = W.lengths(wid)
+    algo = float(np.sum(lens + 1)) * row_bytes(w.fmt)  # the cache rows one launch attends
+    text = f"""# HBM traffic of the partial-attention kernel, {w.name}
+# Commands (from the repository root, on one MI355X; each pass is its own run):
+#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir_fetch> -o run -- python3 bench.py --pmc-run --workload {wid}
+#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir_write> -o run -- python3 bench.py --pmc-run --workload {wid}
+#   python3 bench.py --summarize-pmc <dir_fetch>/run_counter_collection.csv <dir_write>/run_counter_collection.csv --workload {wid}
+# Calibration: a device copy of {PMC_COPY_BYTES} bytes reads FETCH_SIZE {fe['copy'][0]:.1f} KiB and
+# WRITE_SIZE {wr['copy'][0]:.1f} KiB per dispatch; the partial kernel's counters are scaled by
+# bytes/(KiB*1024) of the copy.
+workload: {w.name}
+partial_dispatches: {fe['partial'][1]}
+fetch_kib_per_launch: {fe['partial'][0]:.1f}
+write_kib_per_launch: {wr['partial'][0]:.1f}
+copy_fetch_factor: {f_fetch:.4f}
+copy_write_factor: {f_write:.4f}
+algorithmic_bytes_per_launch: {algo:.0f}
+hbm_bytes_per_launch: {hbm:.0f}
+traffic_over_algorithmic: {hbm / algo:.3f}
+kernel_source_sha256_16: {kernel_sha()}
+"""
+    os.makedirs(os.path.dirname(out_path), exist_ok=True)
+    with open(out_path, "w") as f:
+        f.write(text)
+    log(f"wrote {out_path}: {hbm:.0f} HBM bytes per launch ({hbm / algo:.3f} x algorithmic)")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -276,7 +364,17 @@ def main():
     ap.add_argument("--workload", type=int, default=3, help="index into workloads.WORKLOADS")
     ap.add_argument("--int4-workload", type=int, default=2, help="-1 to skip")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="0 to skip the CPU baseline")
+    ap.add_argument("--pmc-run", action="store_true",
+                    help="only issue the launches that the HBM counter summary is taken from")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/pmc_partial_<workload>.txt from two rocprofv3 counter runs")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        from mla_latent_kv_cache_amd import workloads as W
+        name = W.WORKLOADS[args.workload].name
+        summarize_pmc(args.workload, args.summarize_pmc[0], args.summarize_pmc[1],
+                      os.path.join(ROOT, "profiles", f"pmc_partial_{name}.txt"))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the decode path here is single-GPU "
               "(see DESIGN.md for how it would shard). Run with --gpus 1.", file=sys.stderr)
@@ -286,6 +384,9 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     from mla_latent_kv_cache_amd import workloads as W
+    if args.pmc_run:
+        pmc_run(args.workload)
+        return
 
     main_res = measure(args.workload, args.steps, args.warmup)
     int4 = None
