@@ -143,9 +143,8 @@ __device__ __forceinline__ void quant_asym4(const float (&x)[kGroupL], uint8_t (
 #pragma clang fp contract(on)
 
 // Wait until every LDS instruction this wave issued has completed, with no
-// instruction moved across. An LDS store may read its data registers well
-// after it issues; the registers of the stores above are reused right after
-// (as MFMA results, by returning loads), so they must have been read first.
+// instruction moved across: a conservative fence, used at a few places off
+// the per-tile path of the 16-head kernel.
 __device__ __forceinline__ void lds_stores_done() {
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left at their maxima
@@ -901,6 +900,10 @@ void split_kernel(SplitArgs a) {
 // channels 32g..32g+31 of the wave's block (two quantization groups); in the
 // accumulators, head i.
 constexpr int kT16 = 32;             // tokens per tile
+#ifndef MLA_NPF16
+#define MLA_NPF16 1
+#endif
+constexpr int kNpf16 = MLA_NPF16;    // tiles of loads in flight per wave
 constexpr float kLazy = 8.0f;         // log2 of the largest softmax weight before a rescale
 constexpr int kVRow = 128 + 8;       // fp16 per row of a wave's value block: 128 channels, then
                                      // (INT4) the 8 zero-points of the wave's groups
@@ -1213,13 +1216,18 @@ void split16_kernel(SplitArgs a) {
 
   const Off16<FMT> off = offsets16<FMT>(w, lane);
   const bool zero_b = off.b_zero;  // uniform: depends on the wave only
-  Raw16<FMT> raw;
-  load16<FMT>(raw, tile_rsrc<FMT>(a, b, t_begin, t_end), off, zero_b);
+  Raw16<FMT> raw[kNpf16];
+#pragma unroll
+  for (int p = 0; p < kNpf16; ++p)
+    load16<FMT>(raw[p], tile_rsrc<FMT>(a, b, t_begin + p * kT16, t_end), off, zero_b);
 
-  for (int it = 0; it < ntiles; ++it) {
+  for (int it0 = 0; it0 < ntiles; it0 += kNpf16) {
+#pragma unroll
+  for (int p = 0; p < kNpf16; ++p) {
+    const int it = it0 + p;
+    if (it >= ntiles) break;  // uniform across the workgroup
     // ---- 1. the tile's small planes into the shared staging area
-    stage16<FMT>(raw, off, aux);
-    lds_stores_done();
+    stage16<FMT>(raw[p], off, aux);
     __syncthreads();
     const Meta16 mt = meta16<FMT>(aux, w, g, i);
 
@@ -1229,11 +1237,10 @@ void split16_kernel(SplitArgs a) {
     for (int rb = 0; rb < 2; ++rb) {
       f16x8 hi[4], lo[4];
       f16x4 khi, klo;
-      dequant16<FMT>(raw, mt, rb, hi, lo, vblk + (16 * rb + i) * kVRow + 32 * g, khi, klo);
+      dequant16<FMT>(raw[p], mt, rb, hi, lo, vblk + (16 * rb + i) * kVRow + 32 * g, khi, klo);
       // INT4: the zero-points of the wave's 8 groups go to columns 128..135 of
       // its value block, for the value-side zero-point product
       if (kZp) *(uint32_t *)(vblk + (16 * rb + i) * kVRow + 128 + 2 * g) = mt.zp[rb];
-      lds_stores_done();
       // Each accumulator is fed by one MFMA shape only: a 16x16x16 MFMA that
       // takes as its accumulator the result of a 16x16x32 MFMA issued just
       // before it reads a stale value on this GPU (the matrix unit forwards
@@ -1267,20 +1274,19 @@ void split16_kernel(SplitArgs a) {
     // Always issued, so the count of outstanding loads is the same on every
     // path.
     __builtin_amdgcn_sched_barrier(0);
-    load16<FMT>(raw, tile_rsrc<FMT>(a, b, t_begin + (it + 1) * kT16, t_end), off, zero_b);
+    load16<FMT>(raw[p], tile_rsrc<FMT>(a, b, t_begin + (it + kNpf16) * kT16, t_end), off, zero_b);
 
     // ---- 4. partial scores of the four waves
-    float *pb_out = part + (w * 64 + lane) * 8;
-    *(f32x4 *)pb_out = sc[0];
-    *(f32x4 *)(pb_out + 4) = sc[1];
-    lds_stores_done();
+    // [wave][half][lane][4]: consecutive lanes use consecutive 16 bytes
+    *(f32x4 *)(part + ((2 * w) * 64 + lane) * 4) = sc[0];
+    *(f32x4 *)(part + ((2 * w + 1) * 64 + lane) * 4) = sc[1];
     __syncthreads();  // every wave's partial scores of this tile are in LDS
-    const float *pb_in = part + lane * 8;
-    f32x4 t0 = *(const f32x4 *)pb_in, t1 = *(const f32x4 *)(pb_in + 4);
+    const float *pb_in = part + lane * 4;
+    f32x4 t0 = *(const f32x4 *)pb_in, t1 = *(const f32x4 *)(pb_in + 64 * 4);
 #pragma unroll
     for (int v = 1; v < kWaves; ++v) {
-      t0 += *(const f32x4 *)(pb_in + v * 64 * 8);
-      t1 += *(const f32x4 *)(pb_in + v * 64 * 8 + 4);
+      t0 += *(const f32x4 *)(pb_in + (2 * v) * 64 * 4);
+      t1 += *(const f32x4 *)(pb_in + (2 * v + 1) * 64 * 4);
     }
 
     // ---- 5. online softmax (base 2), identical in every wave; lane (g, i)
@@ -1346,6 +1352,7 @@ void split16_kernel(SplitArgs a) {
     }
   }
 
+  }
   // ---- write this unit's partial: m and l (same in every wave), this wave's channels
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
@@ -1375,79 +1382,90 @@ void split16_kernel(SplitArgs a) {
 
 constexpr int kReduceBT = 4;  // batch rows per combine block
 
-__device__ __forceinline__ float block_max256(float v, float *sh) {
+__device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
-  __syncthreads();
-  v = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
-  __syncthreads();
   return v;
 }
 
-__device__ __forceinline__ float block_sum256(float v, float *sh) {
+__device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
-  __syncthreads();
-  v = (sh[0] + sh[1]) + (sh[2] + sh[3]);
-  __syncthreads();
   return v;
 }
 
-// Per (head h, 4 batch rows): merge the splits with log-sum-exp weights,
-// normalize, then out[b,h,:] = o_lat W_UV[h]. The split weights are formed in
-// parallel into LDS first, so the loads of the partial sums that follow are
-// independent of each other (no branch on a loaded value). Grid (H, ceil(B/4)).
+constexpr int kWtsChunk = 256;  // split weights staged per wave at a time
+
+// Per (head h, 4 batch rows), one wave per row: merge the splits with
+// log-sum-exp weights and normalize, then all four waves form
+// out[b,h,:] = o_lat W_UV[h]. In the merge each lane owns 8 latent channels
+// and keeps 16 independent 16-byte loads in flight; the weights of a chunk of
+// splits are formed first (one per lane) into the wave's LDS row, so no load
+// waits on another. Only the splits holding tokens (a prefix) are read.
+// Grid (H, ceil(B/4)).
 __global__ __launch_bounds__(256) void reduce_kernel(const float *ws_m, const float *ws_l,
                                                      const float *ws_acc, const uint16_t *w_uv,
                                                      int B, int H, int nsplit, float *out) {
   __shared__ float olat[kReduceBT][kLatent];
   __shared__ float red[16][kReduceBT][kVDim];
-  __shared__ float wts[kMaxSplits];
-  __shared__ float sh[4];
+  __shared__ float wts[kReduceBT][kWtsChunk];
   const int h = blockIdx.x;
   const int b0 = blockIdx.y * kReduceBT;
   const int tid = threadIdx.x;
-  for (int bt = 0; bt < kReduceBT; ++bt) {
-    const int b = b0 + bt;  // uniform across the block
-    if (b >= B) {
-      olat[bt][tid] = 0.0f;
-      olat[bt][tid + 256] = 0.0f;
-      continue;
-    }
+  const int bt = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int b = b0 + bt;  // uniform across the wave
+  if (b < B) {
     const int64_t base = (int64_t)b * nsplit * H + h;
     float mloc = -INFINITY;
-    for (int s = tid; s < nsplit; s += 256)
-      if (ws_l[base + (int64_t)s * H] > 0.0f) mloc = fmaxf(mloc, ws_m[base + (int64_t)s * H]);
-    const float M = block_max256(mloc, sh);
-    float lloc = 0.0f;
     int last = -1;
-    for (int s = tid; s < nsplit; s += 256) {
+    for (int s = lane; s < nsplit; s += 64) {
       const float l = ws_l[base + (int64_t)s * H];
-      const float wgt = l > 0.0f ? exp2f(ws_m[base + (int64_t)s * H] - M) : 0.0f;
-      wts[s] = wgt;
-      lloc += wgt * l;
-      if (l > 0.0f) last = s;
+      if (l > 0.0f) {
+        mloc = fmaxf(mloc, ws_m[base + (int64_t)s * H]);
+        last = s;
+      }
     }
-    // the splits holding tokens are a prefix; the rest are never read
-    const int nact = (int)block_max256((float)last, sh) + 1;
-    const float Ls = block_sum256(lloc, sh);  // its barriers also publish wts
-    float o0 = 0.0f, o1 = 0.0f;
-    const float *acc = ws_acc + base * kLatent;
-#pragma unroll 4
-    for (int s = 0; s < nact; ++s) {
-      const float wgt = wts[s];
-      const float a0 = acc[(int64_t)s * H * kLatent + tid];
-      const float a1 = acc[(int64_t)s * H * kLatent + tid + 256];
-      // an empty split's sums are never written: select, do not multiply
-      o0 += wgt != 0.0f ? wgt * a0 : 0.0f;
-      o1 += wgt != 0.0f ? wgt * a1 : 0.0f;
+    const float M = wave_max(mloc);
+    const int nact = (int)wave_max((float)last) + 1;  // the splits holding tokens are a prefix
+    float lloc = 0.0f;
+    f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+    const float *acc = ws_acc + base * kLatent + 8 * lane;
+    for (int c0 = 0; c0 < nact; c0 += kWtsChunk) {
+      const int cn = min(kWtsChunk, nact - c0);
+      for (int j = lane; j < cn; j += 64) {
+        const int64_t s = c0 + j;
+        const float l = ws_l[base + s * H];
+        const float wgt = l > 0.0f ? __builtin_amdgcn_exp2f(ws_m[base + s * H] - M) : 0.0f;
+        wts[bt][j] = wgt;
+        lloc += wgt * l;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll 8
+      for (int j = 0; j < cn; ++j) {
+        const float wgt = wts[bt][j];
+        const float *src = acc + (int64_t)(c0 + j) * H * kLatent;
+        const f32x4 a0 = *(const f32x4 *)src, a1 = *(const f32x4 *)(src + 4);
+        // an empty split's sums are never written: select, do not multiply
+        const bool use = wgt != 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          o0[k] = use ? fmaf(wgt, a0[k], o0[k]) : o0[k];
+          o1[k] = use ? fmaf(wgt, a1[k], o1[k]) : o1[k];
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();  // wts is rewritten for the next chunk
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
+    const float Ls = wave_sum(lloc);
     const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
-    olat[bt][tid] = o0 * inv;
-    olat[bt][tid + 256] = o1 * inv;
-    __syncthreads();  // wts is rewritten for the next row
+    *(f32x4 *)&olat[bt][8 * lane] = o0 * inv;
+    *(f32x4 *)&olat[bt][8 * lane + 4] = o1 * inv;
+  } else {
+    *(f32x4 *)&olat[bt][8 * lane] = f32x4{0.f, 0.f, 0.f, 0.f};
+    *(f32x4 *)&olat[bt][8 * lane + 4] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   __syncthreads();
   // o_lat W_UV[h]: thread = (8 output columns, a slice of 32 latent rows)
