@@ -1063,6 +1063,27 @@ __device__ __forceinline__ Meta16 meta16(const uint8_t *aux, int w, int g, int i
   return m;
 }
 
+// Max and sum over the four 16-lane groups (lanes i, i+16, i+32, i+48) with the
+// gfx950 lane-swap instructions: VALU only, no LDS round trip. A swap of x with
+// itself leaves, in the two results, the lane's own value and its partner's.
+__device__ __forceinline__ float max_across_groups(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t v = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float sum_across_groups(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t v = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ f16x8 cat8(f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
   return f16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
@@ -1186,7 +1207,7 @@ void split16_kernel(SplitArgs a) {
 
   // queries of head i for this wave's channels, in the MFMA B layout
   f16x8 qh[4], ql[4];
-  f16x4 kqh, kql, zqh, zql;
+  f16x8 kzh, kzl;  // k_pe channels 16w+4g..+3, then (INT4) the sums of groups 8w+2g, +1, then 0
   {
     const _Float16 *q = a.qa + ((int64_t)b * a.H + i) * kQRec;
 #pragma unroll
@@ -1198,12 +1219,18 @@ void split16_kernel(SplitArgs a) {
         ql[kk] = f16x8{ql[kk][0], ql[kk][4], ql[kk][1], ql[kk][5], ql[kk][2], ql[kk][6], ql[kk][3], ql[kk][7]};
       }
     }
-    kqh = *(const f16x4 *)(q + kQHi + kLatent + 16 * w + 4 * g);
-    kql = *(const f16x4 *)(q + kQLo + kLatent + 16 * w + 4 * g);
-    const f16x2 sh = *(const f16x2 *)(q + kQSumHi + 8 * w + 2 * g);
-    const f16x2 sl = *(const f16x2 *)(q + kQSumLo + 8 * w + 2 * g);
-    zqh = f16x4{sh.x, sh.y, (_Float16)0.0f, (_Float16)0.0f};
-    zql = f16x4{sl.x, sl.y, (_Float16)0.0f, (_Float16)0.0f};
+    const f16x4 kh = *(const f16x4 *)(q + kQHi + kLatent + 16 * w + 4 * g);
+    const f16x4 kl = *(const f16x4 *)(q + kQLo + kLatent + 16 * w + 4 * g);
+    const _Float16 z0 = (_Float16)0.0f;
+    if (FMT == MLA_FMT_INT4) {
+      const f16x2 sh = *(const f16x2 *)(q + kQSumHi + 8 * w + 2 * g);
+      const f16x2 sl = *(const f16x2 *)(q + kQSumLo + 8 * w + 2 * g);
+      kzh = f16x8{kh.x, kh.y, kh.z, kh.w, sh.x, sh.y, z0, z0};
+      kzl = f16x8{kl.x, kl.y, kl.z, kl.w, sl.x, sl.y, z0, z0};
+    } else {
+      kzh = f16x8{kh.x, kh.y, kh.z, kh.w, z0, z0, z0, z0};
+      kzl = f16x8{kl.x, kl.y, kl.z, kl.w, z0, z0, z0, z0};
+    }
   }
 
   _Float16 *vblk = wblk + w * kWBlk;  // [32][kVRow] C_hi of this wave's channels
@@ -1241,29 +1268,29 @@ void split16_kernel(SplitArgs a) {
       // INT4: the zero-points of the wave's 8 groups go to columns 128..135 of
       // its value block, for the value-side zero-point product
       if (kZp) *(uint32_t *)(vblk + (16 * rb + i) * kVRow + 128 + 2 * g) = mt.zp[rb];
-      // Each accumulator is fed by one MFMA shape only: a 16x16x16 MFMA that
-      // takes as its accumulator the result of a 16x16x32 MFMA issued just
-      // before it reads a stale value on this GPU (the matrix unit forwards
-      // a result only to an identical instruction), and the compiler does not
-      // separate the two. The k_pe and zero-point products (K = 16) therefore
-      // build their own sum s2, and the three sums meet in VALU adds.
-      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f}, s2 = {0.f, 0.f, 0.f, 0.f};
+      // Every score product is a 16x16x32 MFMA, so each accumulator is fed
+      // by one MFMA shape only: on this GPU a 16x16x16 MFMA that takes as its
+      // accumulator the result of a 16x16x32 MFMA issued just before it reads
+      // a stale value (the matrix unit forwards a result only to an identical
+      // instruction), and the compiler does not separate the two. The k_pe
+      // channels and (INT4) the zero-points share one k-step: slots 0..3 of
+      // each lane group hold k_pe, slots 4..5 the zero-points, 6..7 zeros.
+      const _Float16 z0 = (_Float16)0.0f;
+      f16x2 z = {z0, z0};
+      if (kZp) z = bitcast<f16x2>(mt.zp[rb]);
+      const f16x8 akh = {khi.x, khi.y, khi.z, khi.w, z.x, z.y, z0, z0};
+      const f16x8 akl = {klo.x, klo.y, klo.z, klo.w, z0, z0, z0, z0};
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi[kk], qh[kk], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi[kk], ql[kk], s1, 0, 0, 0);
         if (kLo) s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo[kk], qh[kk], s1, 0, 0, 0);
       }
-      s2 = __builtin_amdgcn_mfma_f32_16x16x16f16(khi, kqh, s2, 0, 0, 0);
-      s2 = __builtin_amdgcn_mfma_f32_16x16x16f16(khi, kql, s2, 0, 0, 0);
-      if (kLo) s2 = __builtin_amdgcn_mfma_f32_16x16x16f16(klo, kqh, s2, 0, 0, 0);
-      if (kZp) {
-        const f16x2 z = bitcast<f16x2>(mt.zp[rb]);
-        const f16x4 az = {z.x, z.y, (_Float16)0.0f, (_Float16)0.0f};
-        s2 = __builtin_amdgcn_mfma_f32_16x16x16f16(az, zqh, s2, 0, 0, 0);
-        s2 = __builtin_amdgcn_mfma_f32_16x16x16f16(az, zql, s2, 0, 0, 0);
-      }
-      sc[rb] = (s0 + s1) + s2;
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(akh, kzh, s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(akh, kzl, s1, 0, 0, 0);
+      if (kLo) s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(akl, kzh, s1, 0, 0, 0);
+      sc[rb] = s0 + s1;
     }
 
     // ---- 3. the next tile's loads. They go out only after the score sums
@@ -1302,8 +1329,7 @@ void split16_kernel(SplitArgs a) {
     }
     float tmax = fmaxf(fmaxf(fmaxf(p8[0], p8[1]), fmaxf(p8[2], p8[3])),
                        fmaxf(fmaxf(p8[4], p8[5]), fmaxf(p8[6], p8[7])));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = max_across_groups(tmax);
     // Lazy running max: the reference point moves only when some head's tile
     // maximum exceeds it by more than 2^kLazy, so weights stay below 2^kLazy
     // (exact in fp16 relative terms) and most tiles skip the rescale.
@@ -1354,8 +1380,7 @@ void split16_kernel(SplitArgs a) {
 
   }
   // ---- write this unit's partial: m and l (same in every wave), this wave's channels
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = sum_across_groups(l_run);
   if (kZp) {
     // accz lane (g, i) holds zero-point group 4g+r of this wave (slots 8..15 are
     // padding); channel block n of the wave is group n
