@@ -434,6 +434,37 @@ struct SplitArgs {
   int B, H, cap, nsplit, min_chunk, hh_count;
 };
 
+// Dispatch order of the partial kernels: grid row r (blockIdx.y) serves the
+// sequence of rank r when sequences are ranked by decreasing length (ties by
+// index). Workgroups are dispatched in grid order, so the longest splits start
+// first and the short ones fill the compute units behind them, instead of a
+// long split starting last and running alone at the end. The rank is found by
+// the workgroup itself from the lengths (one compare per pair of sequences) for
+// batches of up to kRankMaxB; larger batches keep the identity order.
+constexpr int kRankMaxB = 256;
+static_assert(kThreads >= kRankMaxB, "one thread per ranked sequence");
+
+// Call with every thread of a 256-thread workgroup (it holds barriers).
+// Returns the sequence of this workgroup's grid row, uniform across it.
+__device__ __forceinline__ int seq_of_row(const int *seq_lens, int B, int cap, int *lens_sh, int *sel) {
+  const int row = blockIdx.y;
+  if (B > kRankMaxB) return row;
+  const int tid = threadIdx.x;
+  if (tid < B) lens_sh[tid] = min(max(seq_lens[tid], 0), cap);
+  __syncthreads();
+  if (tid < B) {
+    const int lt = lens_sh[tid];
+    int r = 0;
+    for (int j = 0; j < B; ++j) {
+      const int lj = lens_sh[j];
+      r += (lj > lt) | ((lj == lt) & (j < tid));
+    }
+    if (r == row) *sel = tid;  // ranks are a permutation: exactly one thread writes
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(*sel);
+}
+
 // Tokens per split of a sequence of length L: ceil(L / nsplit) rounded up to a
 // whole 32-token tile, and at least min_chunk. Splits past the sequence are empty.
 __device__ __forceinline__ int split_chunk(int L, int nsplit, int min_chunk) {
@@ -690,10 +721,11 @@ void split_kernel(SplitArgs a) {
   constexpr bool kZp = FMT == MLA_FMT_INT4;
   __shared__ __attribute__((aligned(16))) unsigned char lds[LD::kBytes];
   __shared__ float ml_m[kWaves][16], ml_l[kWaves][16];
+  __shared__ int rank_lens[kRankMaxB], rank_sel;
 
   const int split = blockIdx.x / a.hh_count;
   const int hh = blockIdx.x % a.hh_count;
-  const int b = blockIdx.y;
+  const int b = seq_of_row(a.seq_lens, a.B, a.cap, rank_lens, &rank_sel);
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, li = lane & 15;
@@ -1184,9 +1216,10 @@ void split16_kernel(SplitArgs a) {
   // read only between the two barriers of a tile (the next tile's staging
   // writes come after the second)
   __shared__ __attribute__((aligned(16))) uint8_t aux[Aux16<FMT>::kBytes];
+  __shared__ int rank_lens[kRankMaxB], rank_sel;
 
   const int split = blockIdx.x;
-  const int b = blockIdx.y;
+  const int b = seq_of_row(a.seq_lens, a.B, a.cap, rank_lens, &rank_sel);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 4, i = lane & 15;
@@ -1653,10 +1686,11 @@ int auto_splits(const mla_cache *c, int heads, int *out) {
   if (cus < 1) cus = 1;
   const int hh = heads <= 64 ? 1 : heads / 64;
   const int64_t units = (int64_t)c->batch * hh;
-  // About eight workgroups per CU when every sequence is full, so ragged batches
-  // still keep the chip busy; splits of the automatic plan hold at least
-  // kAutoMinChunk tokens, so short sequences use fewer of them.
-  int64_t want = (8 * (int64_t)cus + units - 1) / units;
+  // About four workgroups per CU when every sequence is full (the partial
+  // kernels dispatch the longest sequences first, so ragged batches still
+  // balance); splits of the automatic plan hold at least kAutoMinChunk tokens,
+  // so short sequences use fewer of them.
+  int64_t want = (4 * (int64_t)cus + units - 1) / units;
   const int64_t by_len = (c->capacity + kAutoMinChunk - 1) / kAutoMinChunk;
   int64_t ns = want < by_len ? want : by_len;
   if (ns < 1) ns = 1;

@@ -39,6 +39,22 @@ def test_tile_and_split_boundaries(fmt):
         check_all(cache, rows, qn, qp, wuk, wuv, out, fmt, f"{fmt} splits {splits}")
 
 
+@pytest.mark.parametrize("fmt,heads", [("int8", 16), ("int4", 16), ("int8", 32)])
+def test_dispatch_order_ties_and_large_batch(fmt, heads):
+    # The partial kernels serve sequences in order of decreasing length (ties
+    # by index) for batches of up to 256 and in batch order above that: many
+    # tied lengths, and a batch past that bound, both against the oracle.
+    rng = np.random.default_rng(7)
+    tied = rng.choice([0, 5, 33, 96, 129], size=40).tolist()
+    large = rng.integers(0, 70, size=260).tolist()
+    for lens, seed in ((tied, 51), (large, 52)):
+        cache, rows, qn, qp, wuk, wuv = random_problem(fmt, len(lens), heads, lens, seed=seed)
+        for splits in (0, 3):
+            out = cache.decode(0, qn, qp, wuk, wuv, TAU, num_splits=splits)
+            torch.cuda.synchronize()
+            check_all(cache, rows, qn, qp, wuk, wuv, out, fmt, f"B{len(lens)} H{heads} splits {splits}")
+
+
 def test_split_count_invariance_and_determinism():
     lens = [3000, 1234]
     cache, rows, qn, qp, wuk, wuv = random_problem("int8", 2, 16, lens, seed=9)
