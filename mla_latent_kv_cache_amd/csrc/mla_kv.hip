@@ -61,6 +61,9 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 template <typename To, typename From>
 __device__ __forceinline__ To bitcast(From v) {
@@ -291,8 +294,9 @@ __global__ __launch_bounds__(128) void append_step_kernel(AppendArgs a) {
 
 // ------------------------------------------------------------------ absorb
 
-constexpr int kAbsorbBT = 8;   // batch rows per absorb block
-constexpr int kAbsorbCB = 64;  // channels per absorb block
+constexpr int kAbsorbBT = 64;              // batch rows per absorb block (four MFMA column blocks)
+constexpr int kAbsorbCB = 64;              // latent channels per absorb block, 16 per wave
+constexpr int kAbsorbWRow = kAbsorbCB + 16;  // bf16 per LDS row of the staged W_UK tile (see below)
 
 // Per (sequence, head) record of absorbed queries, in fp16, each value v kept
 // as hi = fp16(v) and lo = fp16(v - hi), so that hi + lo carries ~22 bits:
@@ -303,6 +307,13 @@ constexpr int kAbsorbCB = 64;  // channels per absorb block
 constexpr int kQHi = 0, kQLo = kRow, kQSumHi = 2 * kRow, kQSumLo = 2 * kRow + kNGroupL;
 constexpr int kQRec = 2 * kRow + 2 * kNGroupL;  // 1216 halves
 
+// Transposed LDS read (ds_read_b64_tr_b16): the 16 lanes of a lane group
+// each give the address of 4 consecutive 16-bit values, together a block of 4
+// rows x 16 columns; lane i receives column i of those 4 rows.
+__device__ __forceinline__ i16x4 lds_read_tr16_i16(const uint16_t *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(p));
+}
+
 __device__ __forceinline__ void split_store(_Float16 *hi, _Float16 *lo, float v) {
   const _Float16 h = (_Float16)v;
   *hi = h;
@@ -312,55 +323,115 @@ __device__ __forceinline__ void split_store(_Float16 *hi, _Float16 *lo, float v)
 // q_abs[b,h,c] = qs * sum_d q_nope[b,h,d] W_UK[h,d,c] for c < 512, and
 // qs * q_pe[b,h,d] for the 64 RoPE channels; qs = softmax_scale * log2(e),
 // so the attention kernels work in base 2.
-// Grid (H, 512/64 channel blocks, ceil(B/8)), 256 threads: thread = (channel
-// c of the block, quarter of the 128 d), quarters summed through LDS.
+// Grid (H, 512/64 channel blocks, ceil(B/64)), 256 threads. The block stages
+// its W_UK tile (128 d x 64 c, rows padded to 80 bf16 = 40 dwords so the four
+// rows of a transposed read start 8 banks apart) in LDS once. Wave w owns
+// channels 16w..16w+15 of the block and computes them for the block's batch
+// rows as [16 c x 32 d] x [32 d x 16 b] bf16 MFMAs with fp32 accumulation
+// (bf16 products are exact in fp32). The W_UK operand comes from LDS through
+// transposed reads, 8 consecutive d per lane; the query operand is those same
+// 8 d of one batch row, one 16-byte load.
 __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t *q_nope, const uint16_t *q_pe,
                                                      const uint16_t *w_uk, int B, int H, float qs,
                                                      _Float16 *qa) {
-  __shared__ float qsh[kAbsorbBT][kNope];
-  __shared__ float red[4][kAbsorbBT][kAbsorbCB];
+  __shared__ __attribute__((aligned(16))) uint16_t wt[kNope * kAbsorbWRow];
   const int h = blockIdx.x, cb = blockIdx.y;
   const int b0 = blockIdx.z * kAbsorbBT;
   const int tid = threadIdx.x;
-  for (int e = tid; e < kAbsorbBT * kNope; e += 256) {
-    const int bt = e / kNope, d = e % kNope;
-    const int b = b0 + bt;
-    qsh[bt][d] = b < B ? bf16_bits_to_f32(q_nope[((int64_t)b * H + h) * kNope + d]) : 0.0f;
+  const int w = tid >> 6, lane = tid & 63, g = lane >> 4, i = lane & 15;
+
+  // W_UK[h][:, 64cb .. 64cb+63]: 128 rows of 128 bytes, 16 bytes per lane
+  const uint16_t *wsrc = w_uk + (int64_t)h * kNope * kLatent + cb * kAbsorbCB;
+  constexpr int kWLoads = kNope * kAbsorbCB / 8 / 256;
+  u32x4 wl[kWLoads];
+#pragma unroll
+  for (int j = 0; j < kWLoads; ++j) {
+    const int k = tid + 256 * j, row = k >> 3, c8 = k & 7;
+    wl[j] = *(const u32x4 *)(wsrc + (int64_t)row * kLatent + 8 * c8);
+  }
+  // every query operand of the block, in flight together with the tile
+  // (rows past the batch repeat its last row and are not stored)
+  constexpr int kBB = kAbsorbBT / 16;
+  u32x4 qv[kBB][kNope / 32];
+#pragma unroll
+  for (int bb = 0; bb < kBB; ++bb) {
+    const int b = min(b0 + 16 * bb + i, B - 1);
+    const uint16_t *qrow = q_nope + ((int64_t)b * H + h) * kNope + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < kNope / 32; ++kk) qv[bb][kk] = *(const u32x4 *)(qrow + 32 * kk);
+  }
+  // blocks of channel block 0 also scale the RoPE part: 8 values per 16-byte
+  // chunk, 64 rows of 8 chunks
+  constexpr int kPLoads = kAbsorbBT * kRope / 8 / 256;
+  u32x4 qpv[kPLoads];
+  if (cb == 0) {
+#pragma unroll
+    for (int j = 0; j < kPLoads; ++j) {
+      const int k = tid + 256 * j, b = min(b0 + (k >> 3), B - 1);
+      qpv[j] = *(const u32x4 *)(q_pe + ((int64_t)b * H + h) * kRope + 8 * (k & 7));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kWLoads; ++j) {
+    const int k = tid + 256 * j, row = k >> 3, c8 = k & 7;
+    *(u32x4 *)(wt + row * kAbsorbWRow + 8 * c8) = wl[j];
   }
   __syncthreads();
-  const int cl = tid & 63, ds = tid >> 6;
-  const int c = cb * kAbsorbCB + cl;
-  const uint16_t *w = w_uk + ((int64_t)h * kNope + ds * 32) * kLatent + c;
-  float acc[kAbsorbBT];
+  // lane (i, g) of k-step kk: column 16w + i, rows 32kk + 8g .. +7 (two
+  // transposed reads of four rows each)
+  bf16x8 wa[kNope / 32];
 #pragma unroll
-  for (int bt = 0; bt < kAbsorbBT; ++bt) acc[bt] = 0.0f;
-#pragma unroll 8
-  for (int d = 0; d < 32; ++d) {
-    const float wv = bf16_bits_to_f32(w[d * kLatent]);
-#pragma unroll
-    for (int bt = 0; bt < kAbsorbBT; ++bt) acc[bt] += qsh[bt][ds * 32 + d] * wv;
+  for (int kk = 0; kk < kNope / 32; ++kk) {
+    const uint16_t *p = wt + (32 * kk + 8 * g + (i >> 2)) * kAbsorbWRow + 16 * w + 4 * (i & 3);
+    const i16x4 r0 = lds_read_tr16_i16(p), r1 = lds_read_tr16_i16(p + 4 * kAbsorbWRow);
+    wa[kk] = bitcast<bf16x8>(i16x8{r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w});
   }
+
+  const int c = cb * kAbsorbCB + 16 * w + 4 * g;  // this lane's 4 output channels
 #pragma unroll
-  for (int bt = 0; bt < kAbsorbBT; ++bt) red[ds][bt][cl] = acc[bt];
-  lds_stores_done();
-  __syncthreads();
+  for (int bb = 0; bb < kBB; ++bb) {
+    if (b0 + 16 * bb >= B) break;  // uniform
+    const int b = b0 + 16 * bb + i;
+    f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int o = tid + 256 * k;  // (bt, channel of the block); lanes of one wave share bt
-    const int bt = o / kAbsorbCB, ol = o % kAbsorbCB;
-    const float v = (red[0][bt][ol] + red[1][bt][ol] + red[2][bt][ol] + red[3][bt][ol]) * qs;
-    float gsum = v;  // sums over each 16-channel group: 16 consecutive lanes
+    for (int kk = 0; kk < kNope / 32; ++kk)
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[kk], bitcast<bf16x8>(qv[bb][kk]), d, 0, 0, 0);
+    // lane (i, g) holds channels c .. c+3 of batch row b
+    f16x4 vh, vl;
+    float gsum = 0.0f;
 #pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) gsum += __shfl_xor(gsum, off);
-    const int b = b0 + bt;
+    for (int r = 0; r < 4; ++r) {
+      const float v = d[r] * qs;
+      vh[r] = (_Float16)v;
+      vl[r] = (_Float16)(v - (float)vh[r]);
+      gsum += v;
+    }
+    // the wave's 16 channels are one latent group: add the four lane groups
+    gsum += __shfl_xor(gsum, 16);
+    gsum += __shfl_xor(gsum, 32);
     if (b < B) {
       _Float16 *rec = qa + ((int64_t)b * H + h) * kQRec;
-      const int oc = cb * kAbsorbCB + ol;
-      split_store(rec + kQHi + oc, rec + kQLo + oc, v);
-      if ((ol & 15) == 0) split_store(rec + kQSumHi + oc / 16, rec + kQSumLo + oc / 16, gsum);
-      if (cb == 0) {  // this block also scales the RoPE part of the query
-        const float vp = bf16_bits_to_f32(q_pe[((int64_t)b * H + h) * kRope + ol]) * qs;
-        split_store(rec + kQHi + kLatent + ol, rec + kQLo + kLatent + ol, vp);
+      *(f16x4 *)(rec + kQHi + c) = vh;
+      *(f16x4 *)(rec + kQLo + c) = vl;
+      if (g == 0) split_store(rec + kQSumHi + c / 16, rec + kQSumLo + c / 16, gsum);
+    }
+  }
+  if (cb == 0) {
+#pragma unroll
+    for (int j = 0; j < kPLoads; ++j) {
+      const int k = tid + 256 * j, b = b0 + (k >> 3);
+      if (b < B) {
+        f16x8 vh, vl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t bits = (qpv[j][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+          const float v = bf16_bits_to_f32(bits) * qs;
+          vh[e] = (_Float16)v;
+          vl[e] = (_Float16)(v - (float)vh[e]);
+        }
+        _Float16 *rec = qa + ((int64_t)b * H + h) * kQRec + kLatent + 8 * (k & 7);
+        *(f16x8 *)(rec + kQHi) = vh;
+        *(f16x8 *)(rec + kQLo) = vl;
       }
     }
   }
@@ -937,9 +1008,16 @@ constexpr int kT16 = 32;             // tokens per tile
 #endif
 constexpr int kNpf16 = MLA_NPF16;    // tiles of loads in flight per wave
 constexpr float kLazy = 8.0f;         // log2 of the largest softmax weight before a rescale
-constexpr int kVRow = 128 + 8;       // fp16 per row of a wave's value block: 128 channels, then
-                                     // (INT4) the 8 zero-points of the wave's groups
+// A wave's value block: 32 rows (tokens) of 128 channels, then (INT4) the 8
+// zero-points of the wave's groups, padded to 144 fp16 (72 dwords, 8 banks
+// apart), so the four rows a transposed read spans start 8 banks apart and
+// never share a bank. Writes go row per lane, 16 bytes at a time; there the
+// 16-byte chunks of rows with bit 2 xor bit 3 of the row set are swapped in
+// pairs (chunk c stored at c ^ 1), which puts rows r, r + 4 and r + 8 on
+// different banks too.
+constexpr int kVRow = 144;           // fp16 per row
 constexpr int kWBlk = kT16 * kVRow;  // fp16 per wave block
+__device__ __forceinline__ int vswz(int row) { return ((row >> 2) ^ (row >> 3)) & 1; }
 constexpr int kPart16 = kWaves * 64 * 8;              // floats: 4 waves x 64 lanes x 8
 
 // The small planes of a tile (latent scales, k_pe codes and scales, INT4
@@ -1131,7 +1209,8 @@ __device__ __forceinline__ f16x8 cat8(f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
 // from the packed multiply-adds, as in the other formats.
 template <int FMT>
 __device__ __forceinline__ void dequant16(const Raw16<FMT> &r, const Meta16 &m, int rb, f16x8 (&hi)[4],
-                                          f16x8 (&lo)[4], _Float16 *vrow, f16x4 &khi, f16x4 &klo) {
+                                          f16x8 (&lo)[4], _Float16 *vrow, int swz, f16x4 &khi,
+                                          f16x4 &klo) {
   if (FMT == MLA_FMT_INT8) {
     const f16x2 s0 = splat_f16_bits(m.sc[rb] & 0xFFFFu), s1 = splat_f16_bits(m.sc[rb] >> 16);
 #pragma unroll
@@ -1147,7 +1226,7 @@ __device__ __forceinline__ void dequant16(const Raw16<FMT> &r, const Meta16 &m, 
       scale_split(q3, s2, h3, l3);
       hi[kk] = cat8(h0, h1, h2, h3);
       lo[kk] = cat8(l0, l1, l2, l3);
-      *(f16x8 *)(vrow + 8 * kk) = hi[kk];
+      *(f16x8 *)(vrow + 8 * (kk ^ swz)) = hi[kk];
     }
   } else if (FMT == MLA_FMT_INT4) {
     const f16x2 s0 = splat_f16_bits(m.sc[rb] & 0xFFFFu), s1 = splat_f16_bits(m.sc[rb] >> 16);
@@ -1167,7 +1246,7 @@ __device__ __forceinline__ void dequant16(const Raw16<FMT> &r, const Meta16 &m, 
       scale_split(q37, s2, h37, l37);
       hi[kk] = cat8(h04, h15, h26, h37);  // channels 0,4,1,5,2,6,3,7
       lo[kk] = cat8(l04, l15, l26, l37);
-      *(f16x8 *)(vrow + 8 * kk) = f16x8{h04.x, h15.x, h26.x, h37.x, h04.y, h15.y, h26.y, h37.y};
+      *(f16x8 *)(vrow + 8 * (kk ^ swz)) = f16x8{h04.x, h15.x, h26.x, h37.x, h04.y, h15.y, h26.y, h37.y};
     }
   } else {
 #pragma unroll
@@ -1176,7 +1255,7 @@ __device__ __forceinline__ void dequant16(const Raw16<FMT> &r, const Meta16 &m, 
       hi[kk] = cat8(bf16x2_to_f16x2(v[0]), bf16x2_to_f16x2(v[1]), bf16x2_to_f16x2(v[2]),
                     bf16x2_to_f16x2(v[3]));
       lo[kk] = f16x8{};
-      *(f16x8 *)(vrow + 8 * kk) = hi[kk];
+      *(f16x8 *)(vrow + 8 * (kk ^ swz)) = hi[kk];
     }
   }
   if (FMT != MLA_FMT_BF16) {
@@ -1211,7 +1290,7 @@ void split16_kernel(SplitArgs a) {
   constexpr bool kLo = FMT != MLA_FMT_BF16;
   constexpr bool kZp = FMT == MLA_FMT_INT4;
   // +16: the zero-point read of the last row runs 8 fp16 past its block (unused slots)
-  __shared__ __attribute__((aligned(16))) _Float16 wblk[kWaves * kWBlk + 16];
+  __shared__ __attribute__((aligned(16))) _Float16 wblk[kWaves * kWBlk];
   __shared__ __attribute__((aligned(16))) float part[kPart16];
   // read only between the two barriers of a tile (the next tile's staging
   // writes come after the second)
@@ -1297,10 +1376,11 @@ void split16_kernel(SplitArgs a) {
     for (int rb = 0; rb < 2; ++rb) {
       f16x8 hi[4], lo[4];
       f16x4 khi, klo;
-      dequant16<FMT>(raw[p], mt, rb, hi, lo, vblk + (16 * rb + i) * kVRow + 32 * g, khi, klo);
+      dequant16<FMT>(raw[p], mt, rb, hi, lo, vblk + (16 * rb + i) * kVRow + 32 * g, vswz(i), khi, klo);
       // INT4: the zero-points of the wave's 8 groups go to columns 128..135 of
-      // its value block, for the value-side zero-point product
-      if (kZp) *(uint32_t *)(vblk + (16 * rb + i) * kVRow + 128 + 2 * g) = mt.zp[rb];
+      // its value block (chunk 16, swapped with 17 like the others), for the
+      // value-side zero-point product
+      if (kZp) *(uint32_t *)(vblk + (16 * rb + i) * kVRow + 128 + 8 * vswz(i) + 2 * g) = mt.zp[rb];
       // Every score product is a 16x16x32 MFMA, so each accumulator is fed
       // by one MFMA shape only: on this GPU a 16x16x16 MFMA that takes as its
       // accumulator the result of a 16x16x32 MFMA issued just before it reads
@@ -1391,7 +1471,10 @@ void split16_kernel(SplitArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const _Float16 *v0 = vblk + (4 * g + (i >> 2)) * kVRow + 4 * (i & 3);
+    // rows 4g..4g+3 (and 16 more) share bits 2 and 3, so one swap bit per lane group
+    const int sg = vswz(4 * g);
+    const int col = 8 * (((i >> 1) & 1) ^ sg) + 4 * (i & 1);  // this lane's 4 fp16 of 16
+    const _Float16 *v0 = vblk + (4 * g + (i >> 2)) * kVRow + col;
     const _Float16 *v1 = v0 + 16 * kVRow;
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
@@ -1401,9 +1484,9 @@ void split16_kernel(SplitArgs a) {
       acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb, acc[n], 0, 0, 0);
     }
     if (kZp) {
-      // columns 128..135 of the block are the 8 groups; lanes reading past
-      // them fill the unused slots 8..15 of this product
-      const _Float16 *z0 = vblk + (4 * g + (i >> 2)) * kVRow + 128 + 4 * (i & 3);
+      // columns 128..135 of the block are the 8 groups; the lanes that read
+      // columns 136..143 fill the unused slots 8..15 of this product
+      const _Float16 *z0 = vblk + (4 * g + (i >> 2)) * kVRow + 128 + col;
       const f16x4 a0 = lds_read_tr16(z0);
       const f16x4 a1 = lds_read_tr16(z0 + 16 * kVRow);
       const f16x8 az = f16x8{a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
@@ -1452,119 +1535,126 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-constexpr int kWtsChunk = 256;  // split weights staged per wave at a time
+constexpr int kMergeChunk = 16;  // splits merged per round of loads
 
 // Per (head h, 4 batch rows), one wave per row: merge the splits with
 // log-sum-exp weights and normalize, then all four waves form
-// out[b,h,:] = o_lat W_UV[h]. In the merge each lane owns 8 latent channels
-// and keeps 16 independent 16-byte loads in flight; the weights of a chunk of
-// splits are formed first (one per lane) into the wave's LDS row, so no load
-// waits on another. Only the splits holding tokens (a prefix) are read.
-// Grid (H, ceil(B/4)).
+// out[b,h,:] = o_lat W_UV[h]. The merge takes the splits 16 at a time: lane s
+// loads m and l of split s while every lane loads its 8 latent channels of all
+// 16 splits, in one round of loads. The chunk's maximum updates a running
+// maximum (what was merged before is rescaled by 2^(M_old - M_new)), and each
+// split's weight 2^(m_s - M) is taken from its lane as a scalar. A split with
+// l = 0 holds no tokens and its sums were never written: it gets weight zero
+// and its sums are skipped, not multiplied. Grid (H, ceil(B/4)).
 __global__ __launch_bounds__(256) void reduce_kernel(const float *ws_m, const float *ws_l,
                                                      const float *ws_acc, const uint16_t *w_uv,
                                                      int B, int H, int nsplit, float *out) {
   __shared__ float olat[kReduceBT][kLatent];
   __shared__ float red[16][kReduceBT][kVDim];
-  __shared__ float wts[kReduceBT][kWtsChunk];
   const int h = blockIdx.x;
   const int b0 = blockIdx.y * kReduceBT;
   const int tid = threadIdx.x;
   const int bt = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int b = b0 + bt;  // uniform across the wave
+  f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
   if (b < B) {
     const int64_t base = (int64_t)b * nsplit * H + h;
-    float mloc = -INFINITY;
-    int last = -1;
-    for (int s = lane; s < nsplit; s += 64) {
-      const float l = ws_l[base + (int64_t)s * H];
-      if (l > 0.0f) {
-        mloc = fmaxf(mloc, ws_m[base + (int64_t)s * H]);
-        last = s;
-      }
-    }
-    const float M = wave_max(mloc);
-    const int nact = (int)wave_max((float)last) + 1;  // the splits holding tokens are a prefix
-    float lloc = 0.0f;
-    f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
     const float *acc = ws_acc + base * kLatent + 8 * lane;
-    for (int c0 = 0; c0 < nact; c0 += kWtsChunk) {
-      const int cn = min(kWtsChunk, nact - c0);
-      for (int j = lane; j < cn; j += 64) {
-        const int64_t s = c0 + j;
-        const float l = ws_l[base + s * H];
-        const float wgt = l > 0.0f ? __builtin_amdgcn_exp2f(ws_m[base + s * H] - M) : 0.0f;
-        wts[bt][j] = wgt;
-        lloc += wgt * l;
+    float M = -INFINITY, Ls = 0.0f;
+    for (int c0 = 0; c0 < nsplit; c0 += kMergeChunk) {
+      const int cn = min(kMergeChunk, nsplit - c0);  // uniform
+      float ml = -INFINITY, ll = 0.0f;
+      if (lane < cn) {
+        ll = ws_l[base + (int64_t)(c0 + lane) * H];
+        ml = ws_m[base + (int64_t)(c0 + lane) * H];
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll 8
-      for (int j = 0; j < cn; ++j) {
-        const float wgt = wts[bt][j];
-        const float *src = acc + (int64_t)(c0 + j) * H * kLatent;
-        const f32x4 a0 = *(const f32x4 *)src, a1 = *(const f32x4 *)(src + 4);
-        // an empty split's sums are never written: select, do not multiply
-        const bool use = wgt != 0.0f;
+      f32x4 a0[kMergeChunk], a1[kMergeChunk];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          o0[k] = use ? fmaf(wgt, a0[k], o0[k]) : o0[k];
-          o1[k] = use ? fmaf(wgt, a1[k], o1[k]) : o1[k];
+      for (int j = 0; j < kMergeChunk; ++j) {
+        if (j < cn) {
+          const float *src = acc + (int64_t)(c0 + j) * H * kLatent;
+          a0[j] = *(const f32x4 *)src;
+          a1[j] = *(const f32x4 *)(src + 4);
         }
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();  // wts is rewritten for the next chunk
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const float mc = wave_max(ll > 0.0f ? ml : -INFINITY);
+      if (mc == -INFINITY) continue;  // no split of the chunk holds tokens
+      const float mn = fmaxf(M, mc);
+      const float alpha = __builtin_amdgcn_exp2f(M - mn);  // 0 while nothing is merged
+      o0 *= alpha;
+      o1 *= alpha;
+      Ls *= alpha;
+      M = mn;
+      const float wl = ll > 0.0f ? __builtin_amdgcn_exp2f(ml - M) : 0.0f;
+      Ls += wave_sum(wl * ll);
+#pragma unroll
+      for (int j = 0; j < kMergeChunk; ++j) {
+        if (j < cn) {
+          const float wgt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j));
+          if (wgt != 0.0f) {  // uniform
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              o0[k] = fmaf(wgt, a0[j][k], o0[k]);
+              o1[k] = fmaf(wgt, a1[j][k], o1[k]);
+            }
+          }
+        }
+      }
     }
-    const float Ls = wave_sum(lloc);
     const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
-    *(f32x4 *)&olat[bt][8 * lane] = o0 * inv;
-    *(f32x4 *)&olat[bt][8 * lane + 4] = o1 * inv;
-  } else {
-    *(f32x4 *)&olat[bt][8 * lane] = f32x4{0.f, 0.f, 0.f, 0.f};
-    *(f32x4 *)&olat[bt][8 * lane + 4] = f32x4{0.f, 0.f, 0.f, 0.f};
+    o0 *= inv;
+    o1 *= inv;
   }
-  __syncthreads();
-  // o_lat W_UV[h]: thread = (8 output columns, a slice of 32 latent rows)
+  // this thread's W_UV rows for the projection (8 output columns of 32 latent
+  // rows), in flight while the merged rows go through LDS
   const int eg = tid & 15, cs = tid >> 4;
+  const uint16_t *w = w_uv + ((int64_t)h * kLatent + cs * 32) * kVDim + 8 * eg;
+  u32x4 wv[32];
+#pragma unroll
+  for (int cc = 0; cc < 32; ++cc) wv[cc] = *(const u32x4 *)(w + cc * kVDim);
+  *(f32x4 *)&olat[bt][8 * lane] = o0;
+  *(f32x4 *)&olat[bt][8 * lane + 4] = o1;
+  __syncthreads();
   float acc[kReduceBT][8];
 #pragma unroll
-  for (int bt = 0; bt < kReduceBT; ++bt)
+  for (int r = 0; r < kReduceBT; ++r)
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc[bt][k] = 0.0f;
-  const uint16_t *w = w_uv + ((int64_t)h * kLatent + cs * 32) * kVDim + 8 * eg;
-#pragma unroll 4
-  for (int cc = 0; cc < 32; ++cc) {
-    const u32x4 wv = *(const u32x4 *)(w + cc * kVDim);
-    float wf[8];
+    for (int k = 0; k < 8; ++k) acc[r][k] = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      wf[2 * k] = bf16_bits_to_f32(wv[k] & 0xFFFFu);
-      wf[2 * k + 1] = bf16_bits_to_f32(wv[k] >> 16);
-    }
+  for (int c4 = 0; c4 < 8; ++c4) {
+    f32x4 ov[kReduceBT];
 #pragma unroll
-    for (int bt = 0; bt < kReduceBT; ++bt) {
-      const float ov = olat[bt][cs * 32 + cc];
+    for (int r = 0; r < kReduceBT; ++r) ov[r] = *(const f32x4 *)&olat[r][cs * 32 + 4 * c4];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc[bt][k] += ov * wf[k];
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 wq = wv[4 * c4 + q];
+      float wf[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        wf[2 * k] = bf16_bits_to_f32(wq[k] & 0xFFFFu);
+        wf[2 * k + 1] = bf16_bits_to_f32(wq[k] >> 16);
+      }
+#pragma unroll
+      for (int r = 0; r < kReduceBT; ++r)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[r][k] += ov[r][q] * wf[k];
     }
   }
 #pragma unroll
-  for (int bt = 0; bt < kReduceBT; ++bt)
+  for (int r = 0; r < kReduceBT; ++r)
 #pragma unroll
-    for (int k = 0; k < 8; ++k) red[cs][bt][8 * eg + k] = acc[bt][k];
+    for (int k = 0; k < 8; ++k) red[cs][r][8 * eg + k] = acc[r][k];
   lds_stores_done();
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int o = tid + 256 * k;
-    const int bt = o / kVDim, e = o % kVDim;
-    const int b = b0 + bt;
+    const int r = o / kVDim, e = o % kVDim;
+    const int bo = b0 + r;
     float v = 0.0f;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) v += red[q][bt][e];
-    if (b < B) out[((int64_t)b * H + h) * kVDim + e] = v;
+    for (int q = 0; q < 16; ++q) v += red[q][r][e];
+    if (bo < B) out[((int64_t)bo * H + h) * kVDim + e] = v;
   }
 }
 
