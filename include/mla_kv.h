@@ -161,6 +161,40 @@ int mla_decode_attn(const mla_cache *cache, int32_t layer, const void *q_nope,
                     size_t workspace_bytes, float *out, void *hip_stream);
 
 /*
+ * The fused decode step of one layer: store one new token per sequence, then
+ * attend over every stored token, the new one included ("DeepSeek的MLA技术",
+ * optimization 2: the RoPE key is cached already rotated by its position;
+ * "Absorbed MLA Cache Optimization", section 2.1: store, then attend).
+ *
+ *   ckv_new   bf16 [batch][512]   the new token's latent
+ *   kpe_new   bf16 [batch][64]    its RoPE key, NOT yet rotated
+ *   q_nope, q_pe                  as for mla_decode_attn, but q_pe NOT yet rotated
+ *   rope_cos, rope_sin  fp32 [rope_rows][32] angle tables, row p holding
+ *                   cos / sin of p * theta_i for channel pair (2i, 2i+1);
+ *                   rope_rows >= capacity + 1. Both NULL: nothing is rotated.
+ *   the rest        as for mla_decode_attn
+ *
+ * For sequence b with length p = seq_lens[layer][b] (before the step):
+ *   1. k_pe turns by table row p: y[2i] = x[2i] c - x[2i+1] s and
+ *      y[2i+1] = x[2i] s + x[2i+1] c in fp32 (each product and sum rounded,
+ *      no fused multiply-add), rounded to bf16 (nearest even); the token is
+ *      then quantized and stored at row p exactly as mla_cache_append stores
+ *      that bf16 input, and seq_lens[layer][b] becomes p + 1. A full sequence
+ *      (p = capacity) stores nothing and keeps its length.
+ *   2. q_pe of every head turns by the same row (fp32).
+ *   3. Absorbed decode over the sequence's (now p + 1) tokens into out.
+ * Three launches on hip_stream; the same workspace and split rules as
+ * mla_decode_attn. Errors: as mla_cache_append and mla_decode_attn, plus
+ * MLA_ERR_INVALID_ARG for one table NULL and the other not, tables not 4-byte
+ * aligned, or rope_rows < capacity + 1; nothing is launched then.
+ */
+int mla_decode_step(const mla_cache *cache, int32_t layer, const void *ckv_new, const void *kpe_new,
+                    const void *q_nope, const void *q_pe, const float *rope_cos,
+                    const float *rope_sin, int32_t rope_rows, const void *w_uk, const void *w_uv,
+                    int32_t heads, float softmax_scale, int32_t num_splits, void *workspace,
+                    size_t workspace_bytes, float *out, void *hip_stream);
+
+/*
  * The three phases of mla_decode_attn, for callers that schedule them
  * separately (for example to time or overlap them). Calling, on one stream and
  * with one workspace, mla_decode_absorb, then mla_decode_partial, then

@@ -21,6 +21,16 @@ N_SCALES = 40
 N_ZEROS = 32
 
 
+def rope_tables(rows, base=10000.0, device="cuda"):
+    """RoPE angle tables for decode_step: (cos, sin), fp32 [rows, 32], row p
+    holding cos / sin of p * base^(-2i/64) for channel pair (2i, 2i+1),
+    each evaluated in fp64 and rounded to fp32 (host-side set-up, once)."""
+    i = torch.arange(ROPE // 2, dtype=torch.float64)
+    ang = torch.arange(rows, dtype=torch.float64)[:, None] * (float(base) ** (-2.0 * i / ROPE))[None, :]
+    return (torch.cos(ang).to(torch.float32).to(device).contiguous(),
+            torch.sin(ang).to(torch.float32).to(device).contiguous())
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
@@ -156,6 +166,41 @@ class LatentCache:
                                          _ptr(w_uk), _ptr(w_uv), H, float(softmax_scale), num_splits,
                                          _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream)),
               "mla_decode_attn")
+        return out
+
+    def decode_step(self, layer, ckv_new, kpe_new, q_nope, q_pe, w_uk, w_uv, softmax_scale, rope=None,
+                    num_splits=0, out=None, workspace=None, stream=None):
+        """Fused decode step of one layer: store one new token per sequence (its
+        k_pe turned by RoPE at its position), then attend over every stored
+        token. ckv_new bf16 [B,512], kpe_new bf16 [B,64] (not turned); q_pe not
+        turned; rope: (cos, sin) fp32 [rows >= capacity + 1, 32] device tensors
+        (see rope_tables), or None for no turn. Returns out fp32 [B, H, 128].
+        A full sequence stores nothing and keeps its length."""
+        self._layer(layer)
+        H = q_nope.shape[1] if q_nope.dim() == 3 else -1
+        _need(ckv_new, "ckv_new", torch.bfloat16, (self.batch, LATENT), self.device)
+        _need(kpe_new, "kpe_new", torch.bfloat16, (self.batch, ROPE), self.device)
+        _need(q_nope, "q_nope", torch.bfloat16, (self.batch, H, NOPE), self.device)
+        _need(q_pe, "q_pe", torch.bfloat16, (self.batch, H, ROPE), self.device)
+        _need(w_uk, "w_uk", torch.bfloat16, (H, NOPE, LATENT), self.device)
+        _need(w_uv, "w_uv", torch.bfloat16, (H, LATENT, VDIM), self.device)
+        cos = sin = None
+        rows = 0
+        if rope is not None:
+            cos, sin = rope
+            rows = cos.shape[0] if cos.dim() == 2 else -1
+            _need(cos, "rope cos", torch.float32, (rows, ROPE // 2), self.device)
+            _need(sin, "rope sin", torch.float32, (rows, ROPE // 2), self.device)
+        if out is None:
+            out = torch.empty((self.batch, H, VDIM), dtype=torch.float32, device=self.device)
+        _need(out, "out", torch.float32, (self.batch, H, VDIM), self.device)
+        if workspace is None:
+            workspace = self.workspace(H, num_splits)
+        check(_lib.lib().mla_decode_step(ctypes.byref(self.struct), layer, _ptr(ckv_new), _ptr(kpe_new),
+                                         _ptr(q_nope), _ptr(q_pe), _ptr(cos), _ptr(sin), rows, _ptr(w_uk),
+                                         _ptr(w_uv), H, float(softmax_scale), num_splits, _ptr(workspace),
+                                         workspace.numel(), _ptr(out), _stream(stream)), "mla_decode_step")
+        self._lens[layer] = np.minimum(self._lens[layer] + 1, self.capacity)
         return out
 
     # ------------------------------------------------ decode, phase by phase

@@ -165,8 +165,26 @@ struct AppendArgs {
   const uint16_t *ckv_new;  // bf16 [B][T][512]
   const uint16_t *kpe_new;  // bf16 [B][T][64]
   const int32_t *n_new;     // optional [B]
+  const float *rope_cos;    // optional fp32 [rows][32]: the k_pe of new tokens turns by its row
+  const float *rope_sin;    // (fused decode step only; plain appends store k_pe as given)
   int B, T, cap;
 };
+
+// One RoPE turn of a channel pair by a table angle, in fp32 with every
+// product and every sum rounded (no contraction into a fused multiply-add),
+// so that the turned value is the same on any IEEE fp32 machine.
+__device__ __forceinline__ void rope_pair_exact(float x0, float x1, float c, float s, float &y0, float &y1) {
+#pragma clang fp contract(off)
+  const float a = x0 * c, b = x1 * s, d = x0 * s, e = x1 * c;
+  y0 = a - b;
+  y1 = d + e;
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
 
 // Quantize and store one group (grp < 32: latent group, else k_pe group) of
 // new token t of sequence b at row `pos` of the cache.
@@ -220,7 +238,18 @@ __device__ __forceinline__ void append_group(const AppendArgs &a, int b, int t, 
   } else {
     const int g = grp - kNGroupL;
     const uint16_t *src = a.kpe_new + ((int64_t)b * a.T + t) * kRope + g * kGroupR;
-    const u32x4 v = *(const u32x4 *)src;
+    u32x4 v = *(const u32x4 *)src;
+    if (a.rope_cos) {
+      // turn the group's 4 channel pairs by the row's angles, round to bf16
+      const float *cr = a.rope_cos + (int64_t)pos * (kRope / 2) + g * (kGroupR / 2);
+      const float *sr = a.rope_sin + (int64_t)pos * (kRope / 2) + g * (kGroupR / 2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float y0, y1;
+        rope_pair_exact(bf16_bits_to_f32(v[j] & 0xFFFFu), bf16_bits_to_f32(v[j] >> 16), cr[j], sr[j], y0, y1);
+        v[j] = f32_to_bf16_rne(y0) | (f32_to_bf16_rne(y1) << 16);
+      }
+    }
     if (FMT == MLA_FMT_BF16) {
       *(u32x4 *)((uint16_t *)a.kpe + row * kRope + g * kGroupR) = v;
       return;
@@ -331,12 +360,13 @@ __device__ __forceinline__ void split_store(_Float16 *hi, _Float16 *lo, float v)
 // (bf16 products are exact in fp32). The W_UK operand comes from LDS through
 // transposed reads, 8 consecutive d per lane; the query operand is those same
 // 8 d of one batch row, one 16-byte load.
-__global__ __launch_bounds__(256) void absorb_kernel(const uint16_t *q_nope, const uint16_t *q_pe,
-                                                     const uint16_t *w_uk, int B, int H, float qs,
-                                                     _Float16 *qa) {
+// One block of the absorption: head h, channel block cb, batch block bz. With
+// with_pe, the blocks of channel block 0 also write the scaled RoPE part.
+__device__ __forceinline__ void absorb_block(const uint16_t *q_nope, const uint16_t *q_pe,
+                                             const uint16_t *w_uk, int B, int H, float qs, _Float16 *qa,
+                                             int h, int cb, int bz, bool with_pe) {
   __shared__ __attribute__((aligned(16))) uint16_t wt[kNope * kAbsorbWRow];
-  const int h = blockIdx.x, cb = blockIdx.y;
-  const int b0 = blockIdx.z * kAbsorbBT;
+  const int b0 = bz * kAbsorbBT;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, g = lane >> 4, i = lane & 15;
 
@@ -364,7 +394,8 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t *q_nope, con
   // chunk, 64 rows of 8 chunks
   constexpr int kPLoads = kAbsorbBT * kRope / 8 / 256;
   u32x4 qpv[kPLoads];
-  if (cb == 0) {
+  const bool pe = with_pe && cb == 0;
+  if (pe) {
 #pragma unroll
     for (int j = 0; j < kPLoads; ++j) {
       const int k = tid + 256 * j, b = min(b0 + (k >> 3), B - 1);
@@ -416,7 +447,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t *q_nope, con
       if (g == 0) split_store(rec + kQSumHi + c / 16, rec + kQSumLo + c / 16, gsum);
     }
   }
-  if (cb == 0) {
+  if (pe) {
 #pragma unroll
     for (int j = 0; j < kPLoads; ++j) {
       const int k = tid + 256 * j, b = b0 + (k >> 3);
@@ -435,6 +466,63 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t *q_nope, con
       }
     }
   }
+}
+
+__global__ __launch_bounds__(256) void absorb_kernel(const uint16_t *q_nope, const uint16_t *q_pe,
+                                                     const uint16_t *w_uk, int B, int H, float qs,
+                                                     _Float16 *qa) {
+  absorb_block(q_nope, q_pe, w_uk, B, H, qs, qa, blockIdx.x, blockIdx.y, blockIdx.z, true);
+}
+
+// ------------------------------------------------------------ fused step
+
+// First launch of the fused decode step (append one token, then attend). The
+// grid holds n_absorb absorption blocks (head-major over (h, cb, bz)) and then
+// one block per sequence b, which
+//   * reads its length pos (the new token's position), quantizes and stores
+//     the new token at row pos with its k_pe turned by table row pos
+//     (unless the sequence is full), and advances the length after a barrier;
+//   * turns every head's q_pe by the same row (fp32), scales it and writes the
+//     RoPE part of the query records, which the absorption blocks leave alone.
+// No block reads a length another block writes.
+struct StepArgs {
+  AppendArgs ap;            // T = 1; rope tables optional
+  const uint16_t *q_nope, *q_pe, *w_uk;
+  _Float16 *qa;
+  float qs;
+  int H, n_absorb;
+};
+
+template <int FMT>
+__global__ __launch_bounds__(256) void step_kernel(StepArgs s) {
+  const int blk = blockIdx.x;
+  if (blk < s.n_absorb) {  // uniform
+    const int h = blk % s.H, cb = (blk / s.H) % (kLatent / kAbsorbCB), bz = blk / (s.H * (kLatent / kAbsorbCB));
+    absorb_block(s.q_nope, s.q_pe, s.w_uk, s.ap.B, s.H, s.qs, s.qa, h, cb, bz, false);
+    return;
+  }
+  const int b = blk - s.n_absorb;
+  const int tid = threadIdx.x;
+  const int pos = s.ap.seq_lens[b];
+  if (tid < kNScale && pos >= 0 && pos < s.ap.cap) append_group<FMT>(s.ap, b, 0, tid, pos);
+  const int row = min(max(pos, 0), s.ap.cap);  // tables hold cap + 1 rows
+  for (int e = tid; e < s.H * (kRope / 2); e += 256) {
+    const int h = e / (kRope / 2), i = e % (kRope / 2);
+    const uint32_t v = *(const uint32_t *)(s.q_pe + ((int64_t)b * s.H + h) * kRope + 2 * i);
+    float x0 = bf16_bits_to_f32(v & 0xFFFFu), x1 = bf16_bits_to_f32(v >> 16);
+    if (s.ap.rope_cos) {
+      const float c = s.ap.rope_cos[(int64_t)row * (kRope / 2) + i];
+      const float sn = s.ap.rope_sin[(int64_t)row * (kRope / 2) + i];
+      const float y0 = x0 * c - x1 * sn, y1 = x0 * sn + x1 * c;
+      x0 = y0;
+      x1 = y1;
+    }
+    _Float16 *rec = s.qa + ((int64_t)b * s.H + h) * kQRec + kLatent + 2 * i;
+    split_store(rec + kQHi, rec + kQLo, x0 * s.qs);
+    split_store(rec + kQHi + 1, rec + kQLo + 1, x1 * s.qs);
+  }
+  __syncthreads();
+  if (tid == 0 && pos >= 0) s.ap.seq_lens[b] = min(pos + 1, s.ap.cap);
 }
 
 // ------------------------------------------------------------- split-KV core
@@ -1833,6 +1921,7 @@ extern "C" int mla_cache_append(const mla_cache *cache, int32_t layer, const voi
   a.ckv_new = (const uint16_t *)ckv_new;
   a.kpe_new = (const uint16_t *)kpe_new;
   a.n_new = n_new;
+  a.rope_cos = a.rope_sin = nullptr;
   a.B = cache->batch;
   a.T = t_new;
   a.cap = cache->capacity;
@@ -1994,6 +2083,60 @@ extern "C" int mla_decode_attn(const mla_cache *cache, int32_t layer, const void
   hipStream_t s = (hipStream_t)hip_stream;
   if ((st = run_absorb(cache, pl, q_nope, q_pe, w_uk, heads, softmax_scale, workspace, s)) != MLA_OK)
     return st;
+  if ((st = run_partial(cache, pl, layer, heads, workspace, s)) != MLA_OK) return st;
+  return run_combine(cache, pl, w_uv, heads, workspace, out, s);
+}
+
+extern "C" int mla_decode_step(const mla_cache *cache, int32_t layer, const void *ckv_new,
+                               const void *kpe_new, const void *q_nope, const void *q_pe,
+                               const float *rope_cos, const float *rope_sin, int32_t rope_rows,
+                               const void *w_uk, const void *w_uv, int32_t heads, float softmax_scale,
+                               int32_t num_splits, void *workspace, size_t workspace_bytes, float *out,
+                               void *hip_stream) {
+  int st = check_cache(cache);
+  if (st != MLA_OK) return st;
+  if (layer < 0 || layer >= cache->num_layers) return MLA_ERR_INVALID_ARG;
+  if (!ckv_new || !kpe_new || !aligned16(ckv_new) || !aligned16(kpe_new)) return MLA_ERR_INVALID_ARG;
+  if ((rope_cos == nullptr) != (rope_sin == nullptr)) return MLA_ERR_INVALID_ARG;
+  if (rope_cos && (((uintptr_t)rope_cos & 3u) || ((uintptr_t)rope_sin & 3u) ||
+                   (int64_t)rope_rows < (int64_t)cache->capacity + 1))
+    return MLA_ERR_INVALID_ARG;
+  if (!heads_ok(heads)) return MLA_ERR_UNSUPPORTED;
+  if ((st = check_absorb_args(q_nope, q_pe, w_uk, softmax_scale)) != MLA_OK) return st;
+  if ((st = check_combine_args(w_uv, out)) != MLA_OK) return st;
+  DecodePlan pl;
+  if ((st = plan_decode(cache, heads, num_splits, workspace, workspace_bytes, &pl)) != MLA_OK) return st;
+  const LayerPlanes p = layer_planes(cache, layer);
+  StepArgs sa;
+  sa.ap.ckv = p.ckv;
+  sa.ap.kpe = p.kpe;
+  sa.ap.scale = p.scale;
+  sa.ap.zero = p.zero;
+  sa.ap.seq_lens = p.seq_lens;
+  sa.ap.ckv_new = (const uint16_t *)ckv_new;
+  sa.ap.kpe_new = (const uint16_t *)kpe_new;
+  sa.ap.n_new = nullptr;
+  sa.ap.rope_cos = rope_cos;
+  sa.ap.rope_sin = rope_sin;
+  sa.ap.B = cache->batch;
+  sa.ap.T = 1;
+  sa.ap.cap = cache->capacity;
+  sa.q_nope = (const uint16_t *)q_nope;
+  sa.q_pe = (const uint16_t *)q_pe;
+  sa.w_uk = (const uint16_t *)w_uk;
+  sa.qa = (_Float16 *)((uint8_t *)workspace + pl.wl.qa);
+  sa.qs = softmax_scale * kLog2e;
+  sa.H = heads;
+  const int64_t n_absorb =
+      (int64_t)heads * (kLatent / kAbsorbCB) * ((cache->batch + kAbsorbBT - 1) / kAbsorbBT);
+  if (n_absorb + cache->batch > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  sa.n_absorb = (int)n_absorb;
+  hipStream_t s = (hipStream_t)hip_stream;
+  const dim3 g((unsigned)(n_absorb + cache->batch)), bl(256);
+  if (cache->format == MLA_FMT_INT8) hipLaunchKernelGGL(step_kernel<MLA_FMT_INT8>, g, bl, 0, s, sa);
+  else if (cache->format == MLA_FMT_INT4) hipLaunchKernelGGL(step_kernel<MLA_FMT_INT4>, g, bl, 0, s, sa);
+  else hipLaunchKernelGGL(step_kernel<MLA_FMT_BF16>, g, bl, 0, s, sa);
+  if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
   if ((st = run_partial(cache, pl, layer, heads, workspace, s)) != MLA_OK) return st;
   return run_combine(cache, pl, w_uv, heads, workspace, out, s);
 }

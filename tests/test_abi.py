@@ -136,6 +136,30 @@ def test_decode_argument_validation_before_launch():
     assert _decode(s, ws_bytes=need - 1) == _lib.MLA_ERR_WORKSPACE
 
 
+def _step(s, layer=0, ckv=FAKE, kpe=FAKE, cos=FAKE + 0x500000, sin=FAKE + 0x600000, rows=101, heads=16,
+          scale=0.1, splits=4, ws=FAKE + 0x700000, ws_bytes=None, out=FAKE + 0x800000):
+    if ws_bytes is None:
+        ws_bytes = _ws(s, heads, splits)[1]
+    return _lib.lib().mla_decode_step(ctypes.byref(s), layer, ckv, kpe, FAKE, FAKE, cos, sin, rows, FAKE,
+                                      FAKE, heads, scale, splits, ws, ws_bytes, out, None)
+
+
+def test_step_argument_validation_before_launch():
+    s = cache_struct(cap=100)
+    assert _step(s, layer=2) == _lib.MLA_ERR_INVALID_ARG
+    assert _step(s, ckv=0) == _lib.MLA_ERR_INVALID_ARG
+    assert _step(s, kpe=FAKE + 8) == _lib.MLA_ERR_INVALID_ARG
+    assert _step(s, cos=0) == _lib.MLA_ERR_INVALID_ARG          # one table without the other
+    assert _step(s, sin=0) == _lib.MLA_ERR_INVALID_ARG
+    assert _step(s, cos=FAKE + 2) == _lib.MLA_ERR_INVALID_ARG   # tables are fp32
+    assert _step(s, rows=100) == _lib.MLA_ERR_INVALID_ARG       # rows must reach position = capacity
+    assert _step(s, heads=24) == _lib.MLA_ERR_UNSUPPORTED
+    assert _step(s, scale=math.nan) == _lib.MLA_ERR_INVALID_ARG
+    assert _step(s, out=0) == _lib.MLA_ERR_INVALID_ARG
+    assert _step(s, ws=0) == _lib.MLA_ERR_WORKSPACE
+    assert _step(s, ws_bytes=_ws(s, 16, 4)[1] - 1) == _lib.MLA_ERR_WORKSPACE
+
+
 def test_append_argument_validation_before_launch():
     L = _lib.lib()
     s = cache_struct()

@@ -1,0 +1,112 @@
+"""The fused decode step on the GPU (RoPE on the new token, append, attend
+over L+1) against oracle.rope.decode_step: stored rows bit-exact, lengths
+advanced, outputs within the attention tolerance."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import quant as Q
+from oracle import rope as R
+
+from gpu_util import assert_close, assert_planes_equal, f32, oracle_planes, random_problem, random_rows
+
+pytestmark = pytest.mark.gpu
+TAU = 1.0 / np.sqrt(192.0)
+
+
+def new_tokens(B, H, seed, fmt):
+    ckv = torch.empty((B, 512), dtype=torch.bfloat16, device="cuda")
+    kpe = torch.empty((B, 64), dtype=torch.bfloat16, device="cuda")
+    for b in range(B):
+        c, k = random_rows(1, seed * 31 + b, "skew" if fmt == "int4" else "outlier")
+        ckv[b], kpe[b] = c[0], k[0]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed + 7)
+    qn = torch.randn((B, H, 128), generator=g, device="cuda").to(torch.bfloat16)
+    qp = (torch.randn((B, H, 64), generator=g, device="cuda") * 2).to(torch.bfloat16)
+    return ckv, kpe, qn, qp
+
+
+def oracle_rows(rows, fmt):
+    """Dequantized oracle rows of each sequence's cached bf16 tokens."""
+    out = []
+    for c, k in rows:
+        if c.shape[0] == 0:
+            out.append((np.zeros((0, 512)), np.zeros((0, 64))))
+        else:
+            out.append(Q.dequantize_rows(oracle_planes(c, k, fmt), fmt))
+    return out
+
+
+def tables(rows_needed):
+    cos, sin = R.rope_tables(rows_needed)
+    return cos, sin, (torch.from_numpy(cos).cuda(), torch.from_numpy(sin).cuda())
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "int8", "int4"])
+@pytest.mark.parametrize("heads", [16, 32])
+def test_step_with_rope_against_oracle(fmt, heads):
+    cap = 320
+    lens = [0, 1, 37, 319, 320]  # the last sequence is full: nothing is stored
+    B = len(lens)
+    cache, rows, qn, qp, wuk, wuv = random_problem(fmt, B, heads, lens, seed=61 + heads, cap=cap)
+    ckv_new, kpe_new, qn, qp = new_tokens(B, heads, 62 + heads, fmt)
+    cos, sin, rope = tables(cap + 1)
+    before = oracle_rows(rows, fmt)
+    for splits in (0, 3):
+        c2, rows2, _, _, _, _ = random_problem(fmt, B, heads, lens, seed=61 + heads, cap=cap)
+        out = c2.decode_step(0, ckv_new, kpe_new, qn, qp, wuk, wuv, TAU, rope=rope, num_splits=splits)
+        torch.cuda.synchronize()
+        assert c2.seq_lens[0].tolist() == [1, 2, 38, 320, 320]
+        for b in range(B):
+            planes, n, ref = R.decode_step(before[b][0], before[b][1], lens[b], cap, f32(ckv_new[b]),
+                                           f32(kpe_new[b]), f32(qn[b]), f32(qp[b]), f32(wuk), f32(wuv), TAU,
+                                           fmt, cos, sin)
+            assert n == int(c2.seq_lens[0, b])
+            assert_close(f32(out[b]), ref, f"{fmt} H{heads} splits {splits} seq {b} (len {lens[b]})")
+            if planes is not None:
+                got = {k: v[-1:] for k, v in c2.planes(0, b).items()}
+                assert_planes_equal(got, {k: v[None] for k, v in planes.items()}, fmt,
+                                    f"{fmt} seq {b} stored row")
+
+
+@pytest.mark.parametrize("fmt", ["int8", "int4"])
+def test_step_without_rope_is_append_then_decode(fmt):
+    lens = [5, 130, 64]
+    B, H = len(lens), 16
+    a, _, qn, qp, wuk, wuv = random_problem(fmt, B, H, lens, seed=71, cap=200)
+    b_, _, _, _, _, _ = random_problem(fmt, B, H, lens, seed=71, cap=200)
+    ckv_new, kpe_new, qn, qp = new_tokens(B, H, 72, fmt)
+    out_step = a.decode_step(0, ckv_new, kpe_new, qn, qp, wuk, wuv, TAU, rope=None)
+    b_.append(0, ckv_new[:, None].contiguous(), kpe_new[:, None].contiguous())
+    out_ref = b_.decode(0, qn, qp, wuk, wuv, TAU)
+    torch.cuda.synchronize()
+    assert torch.equal(a.seq_lens, b_.seq_lens)
+    assert torch.equal(out_step, out_ref)
+    for s in range(B):
+        pa, pb = a.planes(0, s), b_.planes(0, s)
+        for k in pa:
+            assert torch.equal(pa[k], pb[k]), (s, k)
+
+
+def test_consecutive_steps_turn_by_each_position():
+    fmt, H, cap = "int8", 16, 64
+    lens = [0, 9, 40]
+    B = len(lens)
+    cache, rows, _, _, wuk, wuv = random_problem(fmt, B, H, lens, seed=81, cap=cap)
+    cos, sin, rope = tables(cap + 1)
+    cur = oracle_rows(rows, fmt)
+    L = list(lens)
+    for step in range(3):
+        ckv_new, kpe_new, qn, qp = new_tokens(B, H, 90 + step, fmt)
+        out = cache.decode_step(0, ckv_new, kpe_new, qn, qp, wuk, wuv, TAU, rope=rope)
+        torch.cuda.synchronize()
+        for b in range(B):
+            planes, n, ref = R.decode_step(cur[b][0], cur[b][1], L[b], cap, f32(ckv_new[b]), f32(kpe_new[b]),
+                                           f32(qn[b]), f32(qp[b]), f32(wuk), f32(wuv), TAU, fmt, cos, sin)
+            assert_close(f32(out[b]), ref, f"step {step} seq {b}")
+            c_hat, k_hat = Q.dequantize_rows({k: v[None] for k, v in planes.items()}, fmt)
+            cur[b] = (np.concatenate([cur[b][0], c_hat]), np.concatenate([cur[b][1], k_hat]))
+            L[b] = n
+    assert cache.seq_lens[0].tolist() == [3, 12, 43]
