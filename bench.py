@@ -2,9 +2,11 @@
 """Absorbed MLA decode on one MI355X: KV-tokens/s and achieved HBM GB/s.
 
 A step is one decode step of the whole hot path over every layer of the
-workload: quantize-on-append of one new token per sequence, then absorbed
-decode attention (absorb through W_UK, split-KV partial attention over the
-quantized cache, merge and W_UV projection), all through libmla_kv.so.
+workload, through libmla_kv.so's fused decode step in its three launches:
+(1) every sequence's new token is stored, its k_pe turned by RoPE at its
+position and quantized, while the turned query is absorbed through W_UK;
+(2) split-KV partial attention over the quantized cache, the new token
+included; (3) merge of the splits and W_UV projection.
 
 Default workload: DeepSeek-V2-Lite-shaped, 27 layers, 16 heads, batch 64,
 ragged lengths uniform in [1024, 16384], INT8 latent + INT8 k_pe cache. The
@@ -84,6 +86,8 @@ class Runner:
         self.new = [[(steps_new[l][0][:, i:i + 1].contiguous(), steps_new[l][1][:, i:i + 1].contiguous())
                      for l in range(w.layers)] for i in range(extra_steps)]
         self.ws = cache.workspace(self.H, self.splits)
+        from mla_latent_kv_cache_amd import rope_tables
+        self.rope = rope_tables(cap + 1, device=dev)  # positions 0 .. capacity
         self.out = torch.empty((w.batch, self.H, 128), dtype=torch.float32, device=dev)
         self.lib = _lib.lib()
         self.check = _lib.check
@@ -96,6 +100,7 @@ class Runner:
         self.args_w = [(vp(wuk), vp(wuv)) for wuk, wuv in self.wts]
         self.args_new = [[(vp(c), vp(k)) for c, k in step] for step in self.new]
         self.ws_p, self.ws_n = vp(self.ws), ctypes.c_size_t(self.ws.numel())
+        self.rope_p = (vp(self.rope[0]), vp(self.rope[1]), self.rope[0].shape[0])
         self.out_p = vp(self.out)
         self.steps_done = 0
         self.ns = cache.auto_splits(self.H) if self.splits == 0 else self.splits
@@ -105,17 +110,15 @@ class Runner:
         recorded around each partial-attention launch."""
         L = self.lib
         i = self.steps_done
+        cos_p, sin_p, rows = self.rope_p
         for layer in range(self.w.layers):
             c, k = self.args_new[i][layer]
-            st = L.mla_cache_append(self.cref, layer, c, k, 1, None, self.sp)
-            if st:
-                self.check(st, "append")
             qn, qp = self.args_q[layer]
             wuk, wuv = self.args_w[layer]
-            st = L.mla_decode_absorb(self.cref, qn, qp, wuk, self.H, self.scale, self.splits, self.ws_p,
-                                     self.ws_n, self.sp)
+            st = L.mla_decode_step_begin(self.cref, layer, c, k, qn, qp, cos_p, sin_p, rows, wuk, self.H,
+                                         self.scale, self.splits, self.ws_p, self.ws_n, self.sp)
             if st:
-                self.check(st, "absorb")
+                self.check(st, "step_begin")
             if events is not None:
                 e0 = self.torch.cuda.Event(enable_timing=True)
                 e1 = self.torch.cuda.Event(enable_timing=True)
@@ -227,14 +230,16 @@ def roofline(res):
 
 def cpu_baseline(wid, seconds):
     """The oracle as it stands, on the host cores, over a bounded sample of the
-    workload: whole sequences of layer 0, one decode step each (quantize the new
-    token, dequantize the cache rows, absorbed decode in float64)."""
+    workload: whole sequences of layer 0, one fused decode step each (dequantize
+    the cache rows; turn, quantize and append the new token; absorbed decode
+    with the turned query in float64)."""
     import torch
     from mla_latent_kv_cache_amd import workloads as W
-    from oracle import attention as A
     from oracle import quant as Q
+    from oracle import rope as R
     w = W.WORKLOADS[wid]
     lens = W.lengths(wid)
+    cos, sin = R.rope_tables(int(lens.max()) + 1)
     wuk, wuv = (t.float().numpy() for t in W.weights(wid, 0, "cpu"))
     qn, qp = (t.float().numpy() for t in W.queries(wid, 0, "cpu"))
     tokens, elapsed, seqs = 0, 0.0, 0
@@ -245,10 +250,9 @@ def cpu_baseline(wid, seconds):
         nc, nk = W.latent_rows(wid, 0, b, 1, "cpu", kind="step")
         nc, nk = nc.float().numpy(), nk.float().numpy()
         t0 = time.perf_counter()
-        new = Q.quantize_rows(nc, nk, w.fmt)
-        full = {key: np.concatenate([planes[key], new[key]]) for key in planes}
-        ch, kh = Q.dequantize_rows(full, w.fmt)
-        A.decode_absorbed(qn[b], qp[b], wuk, wuv, ch, kh, W.SOFTMAX_SCALE)
+        ch, kh = Q.dequantize_rows(planes, w.fmt)
+        R.decode_step(ch, kh, int(lens[b]), int(lens[b]) + 1, nc[0], nk[0], qn[b], qp[b], wuk, wuv,
+                      W.SOFTMAX_SCALE, w.fmt, cos, sin)
         elapsed += time.perf_counter() - t0
         tokens += int(lens[b]) + 1
         seqs += 1
@@ -262,8 +266,9 @@ def cpu_baseline(wid, seconds):
     return {
         "value": tokens / elapsed, "unit": "KV-tokens/s",
         "cores": threads if threads else cores, "kind": "oracle",
-        "sample": f"{seqs} sequences of layer 0 of {w.name} ({tokens} KV tokens), one decode step "
-                  f"each: oracle quantize of the new token, fp64 dequantize and absorbed decode; "
+        "sample": f"{seqs} sequences of layer 0 of {w.name} ({tokens} KV tokens), one fused decode "
+                  f"step each: oracle RoPE, quantize and append of the new token, fp64 dequantize "
+                  f"and absorbed decode; "
                   f"{elapsed:.1f}s on {cores} host cores visible, BLAS threads {threads}",
     }
 

@@ -195,6 +195,19 @@ int mla_decode_step(const mla_cache *cache, int32_t layer, const void *ckv_new, 
                     size_t workspace_bytes, float *out, void *hip_stream);
 
 /*
+ * The first launch of mla_decode_step on its own: store the new tokens (k_pe
+ * turned), advance the lengths, and write the turned, absorbed queries into
+ * the workspace. Calling it, then mla_decode_partial and mla_decode_combine
+ * (same cache, layer, heads, num_splits and workspace, one stream) is exactly
+ * mla_decode_step. Arguments and errors as there (w_uv and out are not taken).
+ */
+int mla_decode_step_begin(const mla_cache *cache, int32_t layer, const void *ckv_new,
+                          const void *kpe_new, const void *q_nope, const void *q_pe,
+                          const float *rope_cos, const float *rope_sin, int32_t rope_rows,
+                          const void *w_uk, int32_t heads, float softmax_scale, int32_t num_splits,
+                          void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
  * The three phases of mla_decode_attn, for callers that schedule them
  * separately (for example to time or overlap them). Calling, on one stream and
  * with one workspace, mla_decode_absorb, then mla_decode_partial, then

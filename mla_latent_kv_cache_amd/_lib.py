@@ -27,6 +27,7 @@ SYMBOLS = (
     "mla_decode_auto_splits",
     "mla_decode_attn",
     "mla_decode_step",
+    "mla_decode_step_begin",
     "mla_decode_absorb",
     "mla_decode_partial",
     "mla_decode_combine",
@@ -84,6 +85,9 @@ def lib():
         L.mla_decode_step.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, ctypes.c_float, i32,
                                       vp, sz, vp, vp]
         L.mla_decode_step.restype = ctypes.c_int
+        L.mla_decode_step_begin.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, i32, vp, i32, ctypes.c_float, i32,
+                                            vp, sz, vp]
+        L.mla_decode_step_begin.restype = ctypes.c_int
         L.mla_decode_absorb.argtypes = [P, vp, vp, vp, i32, ctypes.c_float, i32, vp, sz, vp]
         L.mla_decode_absorb.restype = ctypes.c_int
         L.mla_decode_partial.argtypes = [P, i32, i32, i32, vp, sz, vp]

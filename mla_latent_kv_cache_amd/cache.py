@@ -168,6 +168,34 @@ class LatentCache:
               "mla_decode_attn")
         return out
 
+    def _step_args(self, layer, ckv_new, kpe_new, q_nope, q_pe, w_uk, rope):
+        self._layer(layer)
+        H = q_nope.shape[1] if q_nope.dim() == 3 else -1
+        _need(ckv_new, "ckv_new", torch.bfloat16, (self.batch, LATENT), self.device)
+        _need(kpe_new, "kpe_new", torch.bfloat16, (self.batch, ROPE), self.device)
+        _need(q_nope, "q_nope", torch.bfloat16, (self.batch, H, NOPE), self.device)
+        _need(q_pe, "q_pe", torch.bfloat16, (self.batch, H, ROPE), self.device)
+        _need(w_uk, "w_uk", torch.bfloat16, (H, NOPE, LATENT), self.device)
+        cos = sin = None
+        rows = 0
+        if rope is not None:
+            cos, sin = rope
+            rows = cos.shape[0] if cos.dim() == 2 else -1
+            _need(cos, "rope cos", torch.float32, (rows, ROPE // 2), self.device)
+            _need(sin, "rope sin", torch.float32, (rows, ROPE // 2), self.device)
+        return H, cos, sin, rows
+
+    def decode_step_begin(self, layer, ckv_new, kpe_new, q_nope, q_pe, w_uk, softmax_scale, workspace,
+                          rope=None, num_splits=0, stream=None):
+        """Phase 1 of decode_step: store the new tokens and absorb the turned
+        queries into the workspace; decode_partial and decode_combine follow."""
+        H, cos, sin, rows = self._step_args(layer, ckv_new, kpe_new, q_nope, q_pe, w_uk, rope)
+        check(_lib.lib().mla_decode_step_begin(ctypes.byref(self.struct), layer, _ptr(ckv_new), _ptr(kpe_new),
+                                               _ptr(q_nope), _ptr(q_pe), _ptr(cos), _ptr(sin), rows, _ptr(w_uk),
+                                               H, float(softmax_scale), num_splits, _ptr(workspace),
+                                               workspace.numel(), _stream(stream)), "mla_decode_step_begin")
+        self._lens[layer] = np.minimum(self._lens[layer] + 1, self.capacity)
+
     def decode_step(self, layer, ckv_new, kpe_new, q_nope, q_pe, w_uk, w_uv, softmax_scale, rope=None,
                     num_splits=0, out=None, workspace=None, stream=None):
         """Fused decode step of one layer: store one new token per sequence (its
@@ -176,21 +204,8 @@ class LatentCache:
         turned; rope: (cos, sin) fp32 [rows >= capacity + 1, 32] device tensors
         (see rope_tables), or None for no turn. Returns out fp32 [B, H, 128].
         A full sequence stores nothing and keeps its length."""
-        self._layer(layer)
-        H = q_nope.shape[1] if q_nope.dim() == 3 else -1
-        _need(ckv_new, "ckv_new", torch.bfloat16, (self.batch, LATENT), self.device)
-        _need(kpe_new, "kpe_new", torch.bfloat16, (self.batch, ROPE), self.device)
-        _need(q_nope, "q_nope", torch.bfloat16, (self.batch, H, NOPE), self.device)
-        _need(q_pe, "q_pe", torch.bfloat16, (self.batch, H, ROPE), self.device)
-        _need(w_uk, "w_uk", torch.bfloat16, (H, NOPE, LATENT), self.device)
+        H, cos, sin, rows = self._step_args(layer, ckv_new, kpe_new, q_nope, q_pe, w_uk, rope)
         _need(w_uv, "w_uv", torch.bfloat16, (H, LATENT, VDIM), self.device)
-        cos = sin = None
-        rows = 0
-        if rope is not None:
-            cos, sin = rope
-            rows = cos.shape[0] if cos.dim() == 2 else -1
-            _need(cos, "rope cos", torch.float32, (rows, ROPE // 2), self.device)
-            _need(sin, "rope sin", torch.float32, (rows, ROPE // 2), self.device)
         if out is None:
             out = torch.empty((self.batch, H, VDIM), dtype=torch.float32, device=self.device)
         _need(out, "out", torch.float32, (self.batch, H, VDIM), self.device)

@@ -2087,12 +2087,14 @@ extern "C" int mla_decode_attn(const mla_cache *cache, int32_t layer, const void
   return run_combine(cache, pl, w_uv, heads, workspace, out, s);
 }
 
-extern "C" int mla_decode_step(const mla_cache *cache, int32_t layer, const void *ckv_new,
-                               const void *kpe_new, const void *q_nope, const void *q_pe,
-                               const float *rope_cos, const float *rope_sin, int32_t rope_rows,
-                               const void *w_uk, const void *w_uv, int32_t heads, float softmax_scale,
-                               int32_t num_splits, void *workspace, size_t workspace_bytes, float *out,
-                               void *hip_stream) {
+namespace {
+
+// Validation and first launch of the fused decode step (store the new
+// token, turn and absorb the query). Fills the plan on success.
+int step_begin(const mla_cache *cache, int32_t layer, const void *ckv_new, const void *kpe_new,
+               const void *q_nope, const void *q_pe, const float *rope_cos, const float *rope_sin,
+               int32_t rope_rows, const void *w_uk, int32_t heads, float softmax_scale, int32_t num_splits,
+               void *workspace, size_t workspace_bytes, hipStream_t s, DecodePlan *pl) {
   int st = check_cache(cache);
   if (st != MLA_OK) return st;
   if (layer < 0 || layer >= cache->num_layers) return MLA_ERR_INVALID_ARG;
@@ -2103,9 +2105,10 @@ extern "C" int mla_decode_step(const mla_cache *cache, int32_t layer, const void
     return MLA_ERR_INVALID_ARG;
   if (!heads_ok(heads)) return MLA_ERR_UNSUPPORTED;
   if ((st = check_absorb_args(q_nope, q_pe, w_uk, softmax_scale)) != MLA_OK) return st;
-  if ((st = check_combine_args(w_uv, out)) != MLA_OK) return st;
-  DecodePlan pl;
-  if ((st = plan_decode(cache, heads, num_splits, workspace, workspace_bytes, &pl)) != MLA_OK) return st;
+  if ((st = plan_decode(cache, heads, num_splits, workspace, workspace_bytes, pl)) != MLA_OK) return st;
+  const int64_t n_absorb =
+      (int64_t)heads * (kLatent / kAbsorbCB) * ((cache->batch + kAbsorbBT - 1) / kAbsorbBT);
+  if (n_absorb + cache->batch > INT32_MAX) return MLA_ERR_UNSUPPORTED;
   const LayerPlanes p = layer_planes(cache, layer);
   StepArgs sa;
   sa.ap.ckv = p.ckv;
@@ -2124,21 +2127,45 @@ extern "C" int mla_decode_step(const mla_cache *cache, int32_t layer, const void
   sa.q_nope = (const uint16_t *)q_nope;
   sa.q_pe = (const uint16_t *)q_pe;
   sa.w_uk = (const uint16_t *)w_uk;
-  sa.qa = (_Float16 *)((uint8_t *)workspace + pl.wl.qa);
+  sa.qa = (_Float16 *)((uint8_t *)workspace + pl->wl.qa);
   sa.qs = softmax_scale * kLog2e;
   sa.H = heads;
-  const int64_t n_absorb =
-      (int64_t)heads * (kLatent / kAbsorbCB) * ((cache->batch + kAbsorbBT - 1) / kAbsorbBT);
-  if (n_absorb + cache->batch > INT32_MAX) return MLA_ERR_UNSUPPORTED;
   sa.n_absorb = (int)n_absorb;
-  hipStream_t s = (hipStream_t)hip_stream;
   const dim3 g((unsigned)(n_absorb + cache->batch)), bl(256);
   if (cache->format == MLA_FMT_INT8) hipLaunchKernelGGL(step_kernel<MLA_FMT_INT8>, g, bl, 0, s, sa);
   else if (cache->format == MLA_FMT_INT4) hipLaunchKernelGGL(step_kernel<MLA_FMT_INT4>, g, bl, 0, s, sa);
   else hipLaunchKernelGGL(step_kernel<MLA_FMT_BF16>, g, bl, 0, s, sa);
-  if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int mla_decode_step(const mla_cache *cache, int32_t layer, const void *ckv_new,
+                               const void *kpe_new, const void *q_nope, const void *q_pe,
+                               const float *rope_cos, const float *rope_sin, int32_t rope_rows,
+                               const void *w_uk, const void *w_uv, int32_t heads, float softmax_scale,
+                               int32_t num_splits, void *workspace, size_t workspace_bytes, float *out,
+                               void *hip_stream) {
+  // everything the later launches need is validated before the first one
+  if (check_combine_args(w_uv, out) != MLA_OK) return MLA_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)hip_stream;
+  DecodePlan pl;
+  int st = step_begin(cache, layer, ckv_new, kpe_new, q_nope, q_pe, rope_cos, rope_sin, rope_rows, w_uk,
+                      heads, softmax_scale, num_splits, workspace, workspace_bytes, s, &pl);
+  if (st != MLA_OK) return st;
   if ((st = run_partial(cache, pl, layer, heads, workspace, s)) != MLA_OK) return st;
   return run_combine(cache, pl, w_uv, heads, workspace, out, s);
+}
+
+extern "C" int mla_decode_step_begin(const mla_cache *cache, int32_t layer, const void *ckv_new,
+                                     const void *kpe_new, const void *q_nope, const void *q_pe,
+                                     const float *rope_cos, const float *rope_sin, int32_t rope_rows,
+                                     const void *w_uk, int32_t heads, float softmax_scale,
+                                     int32_t num_splits, void *workspace, size_t workspace_bytes,
+                                     void *hip_stream) {
+  DecodePlan pl;
+  return step_begin(cache, layer, ckv_new, kpe_new, q_nope, q_pe, rope_cos, rope_sin, rope_rows, w_uk, heads,
+                    softmax_scale, num_splits, workspace, workspace_bytes, (hipStream_t)hip_stream, &pl);
 }
 
 extern "C" int mla_decode_absorb(const mla_cache *cache, const void *q_nope, const void *q_pe,

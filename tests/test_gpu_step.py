@@ -110,3 +110,22 @@ def test_consecutive_steps_turn_by_each_position():
             cur[b] = (np.concatenate([cur[b][0], c_hat]), np.concatenate([cur[b][1], k_hat]))
             L[b] = n
     assert cache.seq_lens[0].tolist() == [3, 12, 43]
+
+
+def test_step_phases_equal_one_call():
+    fmt, H = "int4", 16
+    lens = [300, 2, 77]
+    B = len(lens)
+    a, _, qn, qp, wuk, wuv = random_problem(fmt, B, H, lens, seed=101, cap=400)
+    b_, _, _, _, _, _ = random_problem(fmt, B, H, lens, seed=101, cap=400)
+    ckv_new, kpe_new, qn, qp = new_tokens(B, H, 102, fmt)
+    _, _, rope = tables(401)
+    ws = a.workspace(H, 5)
+    ref = a.decode_step(0, ckv_new, kpe_new, qn, qp, wuk, wuv, TAU, rope=rope, num_splits=5, workspace=ws)
+    ws2 = b_.workspace(H, 5)
+    b_.decode_step_begin(0, ckv_new, kpe_new, qn, qp, wuk, TAU, ws2, rope=rope, num_splits=5)
+    b_.decode_partial(0, H, ws2, num_splits=5)
+    out = b_.decode_combine(wuv, ws2, num_splits=5)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    assert torch.equal(a.seq_lens, b_.seq_lens)
