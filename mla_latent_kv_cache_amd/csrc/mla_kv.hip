@@ -1292,13 +1292,15 @@ __device__ __forceinline__ f16x8 cat8(f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
 //
 // INT4 operands keep the channel order in which the nibbles come out of a
 // dword, (0,4,1,5,2,6,3,7) within each 8 channels, and the queries are
-// permuted to match once per workgroup; only the copy for LDS is re-paired
-// into channel order. The MFMA operands are then whole registers straight
-// from the packed multiply-adds, as in the other formats.
+// permuted to match once per workgroup. The value block in LDS keeps that
+// order too, so the value product's output channels come out in it and are
+// re-paired once, when the unit's sums are stored. The MFMA operands and the
+// LDS copy are then whole registers straight from the packed multiply-adds,
+// as in the other formats.
 template <int FMT>
 __device__ __forceinline__ void dequant16(const Raw16<FMT> &r, const Meta16 &m, int rb, f16x8 (&hi)[4],
-                                          f16x8 (&lo)[4], _Float16 *vrow, int swz, f16x4 &khi,
-                                          f16x4 &klo) {
+                                          f16x8 (&lo)[4], _Float16 *vrow, int swz, uint32_t magic,
+                                          f16x4 &khi, f16x4 &klo) {
   if (FMT == MLA_FMT_INT8) {
     const f16x2 s0 = splat_f16_bits(m.sc[rb] & 0xFFFFu), s1 = splat_f16_bits(m.sc[rb] >> 16);
 #pragma unroll
@@ -1319,14 +1321,18 @@ __device__ __forceinline__ void dequant16(const Raw16<FMT> &r, const Meta16 &m, 
   } else if (FMT == MLA_FMT_INT4) {
     const f16x2 s0 = splat_f16_bits(m.sc[rb] & 0xFFFFu), s1 = splat_f16_bits(m.sc[rb] >> 16);
     const f16x2 bias = {(_Float16)1024.0f, (_Float16)1024.0f};
+    // (x & 0x000F000F) | magic as one bit-field insert: magic (the fp16
+    // exponent bits of 1024 in both halves) sits in a register the compiler
+    // cannot see through, so the pattern stays a v_bfi_b32
+    const auto nib = [magic](uint32_t x) { return (x & 0x000F000Fu) | (magic & ~0x000F000Fu); };
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const uint32_t w = r.lat[rb][0][kk];
       const f16x2 s2 = kk < 2 ? s0 : s1;
-      const f16x2 q04 = bitcast<f16x2>((w & 0x000F000Fu) | 0x64006400u) - bias;
-      const f16x2 q15 = bitcast<f16x2>(((w >> 4) & 0x000F000Fu) | 0x64006400u) - bias;
-      const f16x2 q26 = bitcast<f16x2>(((w >> 8) & 0x000F000Fu) | 0x64006400u) - bias;
-      const f16x2 q37 = bitcast<f16x2>(((w >> 12) & 0x000F000Fu) | 0x64006400u) - bias;
+      const f16x2 q04 = bitcast<f16x2>(nib(w)) - bias;
+      const f16x2 q15 = bitcast<f16x2>(nib(w >> 4)) - bias;
+      const f16x2 q26 = bitcast<f16x2>(nib(w >> 8)) - bias;
+      const f16x2 q37 = bitcast<f16x2>(nib(w >> 12)) - bias;
       f16x2 h04, l04, h15, l15, h26, l26, h37, l37;
       scale_split(q04, s2, h04, l04);
       scale_split(q15, s2, h15, l15);
@@ -1334,7 +1340,7 @@ __device__ __forceinline__ void dequant16(const Raw16<FMT> &r, const Meta16 &m, 
       scale_split(q37, s2, h37, l37);
       hi[kk] = cat8(h04, h15, h26, h37);  // channels 0,4,1,5,2,6,3,7
       lo[kk] = cat8(l04, l15, l26, l37);
-      *(f16x8 *)(vrow + 8 * (kk ^ swz)) = f16x8{h04.x, h15.x, h26.x, h37.x, h04.y, h15.y, h26.y, h37.y};
+      *(f16x8 *)(vrow + 8 * (kk ^ swz)) = hi[kk];  // same order; re-paired at the final store
     }
   } else {
 #pragma unroll
@@ -1434,6 +1440,8 @@ void split16_kernel(SplitArgs a) {
   }
 
   _Float16 *vblk = wblk + w * kWBlk;  // [32][kVRow] C_hi of this wave's channels
+  uint32_t magic = 0;  // INT4: 0x64006400 in a VGPR, opaque to the optimizer
+  if constexpr (FMT == MLA_FMT_INT4) asm("v_mov_b32 %0, 0x64006400" : "=v"(magic));
 
   f32x4 acc[8];
 #pragma unroll
@@ -1464,7 +1472,7 @@ void split16_kernel(SplitArgs a) {
     for (int rb = 0; rb < 2; ++rb) {
       f16x8 hi[4], lo[4];
       f16x4 khi, klo;
-      dequant16<FMT>(raw[p], mt, rb, hi, lo, vblk + (16 * rb + i) * kVRow + 32 * g, vswz(i), khi, klo);
+      dequant16<FMT>(raw[p], mt, rb, hi, lo, vblk + (16 * rb + i) * kVRow + 32 * g, vswz(i), magic, khi, klo);
       // INT4: the zero-points of the wave's 8 groups go to columns 128..135 of
       // its value block (chunk 16, swapped with 17 like the others), for the
       // value-side zero-point product
@@ -1598,9 +1606,21 @@ void split16_kernel(SplitArgs a) {
 #pragma unroll
     for (int n = 0; n < 8; ++n) acc[n] += oz[i * 16 + n];
   }
-  float *dst = a.ws_acc + (ws_row + i) * kLatent + 128 * w + 4 * g;
+  if (kZp) {
+    // INT4 value blocks hold each 8 channels in the order 0,4,1,5,2,6,3,7, so
+    // lane group g holds channels {0,4,1,5} (g even) or {2,6,3,7} (g odd) of
+    // its 8: slots 0 and 2 are a channel pair, and so are slots 1 and 3
+    float *dst = a.ws_acc + (ws_row + i) * kLatent + 128 * w + 8 * (g >> 1) + 2 * (g & 1);
 #pragma unroll
-  for (int n = 0; n < 8; ++n) *(f32x4 *)(dst + 16 * n) = acc[n];
+    for (int n = 0; n < 8; ++n) {
+      *(float2 *)(dst + 16 * n) = float2{acc[n][0], acc[n][2]};
+      *(float2 *)(dst + 16 * n + 4) = float2{acc[n][1], acc[n][3]};
+    }
+  } else {
+    float *dst = a.ws_acc + (ws_row + i) * kLatent + 128 * w + 4 * g;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) *(f32x4 *)(dst + 16 * n) = acc[n];
+  }
   if (w == 0 && g == 0) {
     a.ws_m[ws_row + i] = m_run;
     a.ws_l[ws_row + i] = l_run;
