@@ -75,12 +75,19 @@ def cache_row_bytes(fmt):
     int8: 512 codes + 64 k_pe codes + 40 fp16 scales (32 latent groups of 16,
           8 k_pe groups of 8) = 656
     int4: 256 packed + 64 k_pe codes + 40 fp16 scales + 32 fp16 zero-points = 464
+    int8_kbf16: 512 codes + 64 bf16 k_pe + 32 fp16 latent scales = 704
+    int4_kint4: 256 packed + 32 packed k_pe + 40 fp16 scales + 32 fp16 zero-points = 432
     """
     if fmt == "bf16":
         return LATENT * 2 + QK_ROPE * 2
     scales = (LATENT // 16 + QK_ROPE // 8) * 2
+    zeros = (LATENT // 16) * 2
     if fmt == "int8":
         return LATENT + QK_ROPE + scales
     if fmt == "int4":
-        return LATENT // 2 + QK_ROPE + scales + (LATENT // 16) * 2
+        return LATENT // 2 + QK_ROPE + scales + zeros
+    if fmt == "int8_kbf16":
+        return LATENT + QK_ROPE * 2 + (LATENT // 16) * 2
+    if fmt == "int4_kint4":
+        return LATENT // 2 + QK_ROPE // 2 + scales + zeros
     raise ValueError(fmt)

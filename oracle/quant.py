@@ -17,6 +17,13 @@ What the pages fix, and the reading taken where they leave it open:
   Reading: the scale is stored as fp16 and the codes are computed by dividing
   by the STORED scale, so dequantization uses exactly the value quantization
   used; round() is round-half-to-even; codes are clamped to [-127, 127].
+* INT4 k_pe ("Absorbed MLA Cache Optimization", section 3.2: the 7.6 KB per
+  token of the INT4 configuration needs k_pe in 4 bits as well; symmetric, 8
+  groups). Reading: the INT8 rule with 7 in place of 127: s = fp16(max|x| / 7),
+  codes = clamp(rne(x / s), -7, 7), stored as the nibble code + 8 (1..15),
+  the even channel in the low nibble; x_hat = code * s.
+* latent INT8 with k_pe kept in bf16 (the report's configuration "B",
+  section 3.2 table): latent as INT8 above, k_pe copied.
 * Asymmetric INT4 (report section 3.2, "非对称"): reading: a float offset z
   (fp16, the group minimum rounded toward -inf) and an fp16 scale
   s = (max - z) / 15, each stored as +0 when zero; codes = clamp(rne((x - z) / s), 0, 15); x_hat = q*s + z.
@@ -41,7 +48,7 @@ GROUP_ROPE = 8
 N_GROUPS_LATENT = LATENT_DIM // GROUP_LATENT  # 32
 N_GROUPS_ROPE = ROPE_DIM // GROUP_ROPE  # 8
 
-FORMATS = ("bf16", "int8", "int4")
+FORMATS = ("bf16", "int8", "int4", "int8_kbf16", "int4_kint4")
 
 
 def _f32(x):
@@ -110,6 +117,34 @@ def dequantize_sym_int8(codes, scales, group):
     return (qg * np.asarray(scales).astype(np.float64)[..., None]).reshape(q.shape)
 
 
+def quantize_sym_int4(x, group):
+    """Symmetric INT4 per contiguous channel group (the k_pe of int4_kint4).
+
+    Per group: a = max|x|; s = fp16(a / 7); q = clamp(rne(x / s), -7, 7); a
+    group whose stored scale is 0 gets all-zero codes.
+    Returns (codes int8 in -7..7 [..., n], scales fp16 [..., n/group]).
+    """
+    xg = _groups(x, group)
+    a = np.max(np.abs(xg), axis=-1)
+    s = fp16_rne(a / F32(7.0))
+    sf = s.astype(np.float32)[..., None]
+    nonzero = sf != 0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(nonzero, xg / np.where(nonzero, sf, F32(1.0)), F32(0.0))
+    q = np.clip(np.rint(r), -7, 7)
+    q = np.where(nonzero, q, 0).astype(np.int8)
+    return q.reshape(_f32(x).shape), s
+
+
+def pack_sym_int4(codes):
+    """Codes -7..7 as nibbles code + 8, two per byte, the even channel low."""
+    return pack_nibbles((np.asarray(codes).astype(np.int16) + 8).astype(np.uint8))
+
+
+def unpack_sym_int4(packed):
+    return unpack_nibbles(packed).astype(np.int8) - 8
+
+
 def quantize_asym_int4(x, group):
     """Asymmetric INT4 per contiguous channel group, codes not yet packed.
 
@@ -174,6 +209,14 @@ def quantize_rows(ckv, kpe, fmt):
     kpe = _f32(kpe)
     if fmt == "bf16":
         return {"ckv": ckv, "kpe": kpe}
+    if fmt == "int8_kbf16":
+        cq, cs = quantize_sym_int8(ckv, GROUP_LATENT)
+        return {"ckv": cq, "kpe": kpe, "scale": cs}
+    if fmt == "int4_kint4":
+        cq, cs, cz = quantize_asym_int4(ckv, GROUP_LATENT)
+        kq, ks = quantize_sym_int4(kpe, GROUP_ROPE)
+        return {"ckv": pack_nibbles(cq), "kpe": pack_sym_int4(kq),
+                "scale": np.concatenate([cs, ks], axis=-1), "zero": cz}
     kq, ks = quantize_sym_int8(kpe, GROUP_ROPE)
     if fmt == "int8":
         cq, cs = quantize_sym_int8(ckv, GROUP_LATENT)
@@ -193,6 +236,13 @@ def dequantize_rows(planes, fmt):
     scale = np.asarray(planes["scale"])
     s_lat = scale[..., :N_GROUPS_LATENT]
     s_rope = scale[..., N_GROUPS_LATENT:]
+    if fmt == "int8_kbf16":
+        return (dequantize_sym_int8(planes["ckv"], s_lat, GROUP_LATENT),
+                np.asarray(planes["kpe"]).astype(np.float64))
+    if fmt == "int4_kint4":
+        kpe_hat = dequantize_sym_int8(unpack_sym_int4(planes["kpe"]), s_rope, GROUP_ROPE)
+        codes = unpack_nibbles(planes["ckv"])
+        return dequantize_asym_int4(codes, s_lat, planes["zero"], GROUP_LATENT), kpe_hat
     kpe_hat = dequantize_sym_int8(planes["kpe"], s_rope, GROUP_ROPE)
     if fmt == "int8":
         return dequantize_sym_int8(planes["ckv"], s_lat, GROUP_LATENT), kpe_hat

@@ -62,6 +62,12 @@ def test_cache_row_bytes_with_metadata():
     assert acc.cache_row_bytes("bf16") == 1152
     assert acc.cache_row_bytes("int8") == 656
     assert acc.cache_row_bytes("int4") == 464
+    assert acc.cache_row_bytes("int8_kbf16") == 704
+    assert acc.cache_row_bytes("int4_kint4") == 432
+    # payloads of the two: 640 and 288 bytes per layer, the report's "B" and
+    # headline INT4 configurations
+    assert acc.cache_row_bytes("int8_kbf16") - 64 == acc.payload_bytes_per_layer(8, 16)
+    assert acc.cache_row_bytes("int4_kint4") - 144 == acc.payload_bytes_per_layer(4, 4)
     # every cache row plane is a whole number of 16-byte vectors
     for nbytes in (512, 256, 64, 128, 80, 64):
         assert nbytes % 16 == 0

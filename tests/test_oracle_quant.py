@@ -283,3 +283,57 @@ def test_zero_scale_is_positive_zero():
         q, s, z = Q.quantize_asym_int4(np.array(vals, np.float32), 16)
         assert int(s.view(np.uint16)[0]) == 0 and int(z.view(np.uint16)[0]) == 0
         assert not q.any()
+
+
+# ------------------------------------------------ the formats of the next rows
+
+def test_sym_int4_hand_case():
+    # max|x| = 1.75 -> s = 1.75 / 7 = 0.25 exactly; x / s = 7, -2, 0.5, 1.5,
+    # -4, 2.5, -3.5, 0 -> nearest, ties to even: 7, -2, 0, 2, -4, 2, -4, 0
+    x = np.array([1.75, -0.5, 0.125, 0.375, -1.0, 0.625, -0.875, 0.0], np.float32)
+    q, s = Q.quantize_sym_int4(x, 8)
+    assert s.dtype == np.float16 and float(s[0]) == 0.25
+    assert q.tolist() == [7, -2, 0, 2, -4, 2, -4, 0]
+    # nibbles are code + 8 (15, 6, 8, 10, 4, 10, 4, 8), the even channel low
+    packed = Q.pack_sym_int4(q)
+    assert packed.tolist() == [(15 | (6 << 4)), (8 | (10 << 4)), (4 | (10 << 4)), (4 | (8 << 4))]
+    assert Q.unpack_sym_int4(packed).tolist() == q.tolist()
+
+
+def test_sym_int4_bounds_and_extremes():
+    x = bf16(rng(21).standard_normal((300, 64)) * 3)
+    q, s = Q.quantize_sym_int4(x, 8)
+    assert q.min() >= -7 and q.max() <= 7
+    xh = Q.dequantize_sym_int8(q, s, 8)
+    sg = np.repeat(s.astype(np.float64), 8, axis=-1)
+    assert np.all(np.abs(xh - x) <= sg / 2 + 1e-12 * np.abs(x))
+    # the element of largest magnitude of each group maps to +-7
+    xg, qg = x.reshape(300, 8, 8), q.reshape(300, 8, 8)
+    i = np.abs(xg).argmax(-1)
+    top = np.take_along_axis(qg, i[..., None], -1)[..., 0]
+    assert np.all(np.abs(top) == 7)
+    q0, s0 = Q.quantize_sym_int4(np.zeros(8, np.float32), 8)
+    assert not q0.any() and float(s0[0]) == 0.0
+
+
+@pytest.mark.parametrize("fmt", ["int8_kbf16", "int4_kint4"])
+def test_new_formats_compose_the_existing_quantizers(fmt):
+    r = rng(22)
+    c = bf16(r.standard_normal((5, 512)) * 4)
+    k = bf16(r.standard_normal((5, 64)))
+    p = Q.quantize_rows(c, k, fmt)
+    ch, kh = Q.dequantize_rows(p, fmt)
+    if fmt == "int8_kbf16":
+        ref = Q.quantize_rows(c, k, "int8")
+        assert np.array_equal(p["ckv"], ref["ckv"]) and np.array_equal(p["scale"], ref["scale"][:, :32])
+        assert np.array_equal(kh, k.astype(np.float64))  # k_pe kept exactly
+        assert p["scale"].shape == (5, 32)
+    else:
+        ref = Q.quantize_rows(c, k, "int4")
+        for key in ("ckv", "zero"):
+            assert np.array_equal(p[key], ref[key])
+        assert np.array_equal(p["scale"][:, :32], ref["scale"][:, :32])
+        assert p["kpe"].shape == (5, 32) and p["kpe"].dtype == np.uint8
+        kq, ks = Q.quantize_sym_int4(k, 8)
+        assert np.array_equal(p["scale"][:, 32:], ks)
+        assert np.allclose(kh, Q.dequantize_sym_int8(kq, ks, 8), rtol=0, atol=0)
