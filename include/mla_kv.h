@@ -51,23 +51,29 @@ typedef enum {
   MLA_ERR_HIP = -5          /* a HIP launch or runtime call failed */
 } mla_status;
 
-/* Latent storage format. k_pe is bf16 for MLA_FMT_BF16 and INT8 otherwise. */
+/* Storage format of a cache row (latent c_kv and RoPE key k_pe). */
 typedef enum {
-  MLA_FMT_BF16 = 0, /* c_kv and k_pe copied as bf16 */
-  MLA_FMT_INT8 = 1, /* c_kv symmetric INT8 per 16 channels, k_pe INT8 per 8 channels */
-  MLA_FMT_INT4 = 2  /* c_kv asymmetric INT4 per 16 channels (2 codes/byte), k_pe INT8 */
+  MLA_FMT_BF16 = 0,       /* c_kv and k_pe copied as bf16 */
+  MLA_FMT_INT8 = 1,       /* c_kv symmetric INT8 per 16 channels, k_pe INT8 per 8 channels */
+  MLA_FMT_INT4 = 2,       /* c_kv asymmetric INT4 per 16 channels (2 codes/byte), k_pe INT8 */
+  MLA_FMT_INT8_KBF16 = 3, /* c_kv INT8 as MLA_FMT_INT8, k_pe copied as bf16 (the report's
+                             configuration "B", section 3.2) */
+  MLA_FMT_INT4_KINT4 = 4  /* c_kv INT4 as MLA_FMT_INT4, k_pe symmetric INT4 per 8 channels
+                             (the report's 7.6 KB per token, section 3.2 / summary) */
 } mla_format;
 
 /*
  * The cache of all layers of one model, for a batch of sequences.
  *
  * Planes, each [num_layers][batch][capacity][row] with the row sizes:
- *   ckv     BF16: 512 x bf16 (1024 B)   INT8: 512 x int8 (512 B)
- *           INT4: 256 x uint8 (256 B), byte k = code[2k] | code[2k+1] << 4
- *   kpe     BF16: 64 x bf16 (128 B)     INT8 / INT4: 64 x int8 (64 B)
- *   scale   INT8 / INT4: 40 x fp16 (80 B): the 32 latent-group scales, then
- *           the 8 k_pe-group scales. NULL for BF16.
- *   zero    INT4 only: 32 x fp16 (64 B) latent-group zero-points. NULL otherwise.
+ *   ckv     BF16: 512 x bf16 (1024 B)   INT8, INT8_KBF16: 512 x int8 (512 B)
+ *           INT4, INT4_KINT4: 256 x uint8 (256 B), byte k = code[2k] | code[2k+1] << 4
+ *   kpe     BF16, INT8_KBF16: 64 x bf16 (128 B)     INT8, INT4: 64 x int8 (64 B)
+ *           INT4_KINT4: 32 x uint8 (32 B), byte k = (code[2k] + 8) | (code[2k+1] + 8) << 4
+ *   scale   INT8, INT4, INT4_KINT4: 40 x fp16 (80 B): the 32 latent-group
+ *           scales, then the 8 k_pe-group scales. INT8_KBF16: 32 x fp16 (64 B),
+ *           the latent-group scales. NULL for BF16.
+ *   zero    INT4, INT4_KINT4: 32 x fp16 (64 B) latent-group zero-points. NULL otherwise.
  *   seq_lens  int32 [num_layers][batch]: tokens stored per (layer, sequence).
  *
  * Quantization of one group x (the definition parity is checked against):
@@ -76,6 +82,8 @@ typedef enum {
  *   INT4:  z = fp16 rounded toward -inf of min x, s = fp16_rne((max x - z) / 15)
  *          (each stored as +0 when zero), q = clamp(rne((x - z) / s), 0, 15),
  *          x_hat = q * s + z; s == 0 gives q = 0.
+ *   INT4 k_pe (INT4_KINT4): s = fp16_rne(max|x| / 7), q = clamp(rne(x / s), -7, 7),
+ *          x_hat = q * s; s == 0 gives q = 0.
  *   Every step is one IEEE fp32 operation; fp16 results that would overflow
  *   saturate to +-65504. Inputs must be finite. The decode path dequantizes
  *   to fp16, so dequantized magnitudes must stay below 65504.

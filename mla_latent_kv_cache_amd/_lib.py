@@ -18,7 +18,7 @@ MLA_ERR_WORKSPACE = -3
 MLA_ERR_CAPACITY = -4
 MLA_ERR_HIP = -5
 
-FORMATS = {"bf16": 0, "int8": 1, "int4": 2}
+FORMATS = {"bf16": 0, "int8": 1, "int4": 2, "int8_kbf16": 3, "int4_kint4": 4}
 
 # Every symbol include/mla_kv.h declares.
 SYMBOLS = (

@@ -72,17 +72,23 @@ class LatentCache:
             self.device = torch.device("cuda", torch.cuda.current_device())
         shape = (self.num_layers, self.batch, self.capacity)
         kw = dict(device=self.device)
-        if fmt == "bf16":
+        lat = {"bf16": "bf16", "int8": "int8", "int4": "int4", "int8_kbf16": "int8", "int4_kint4": "int4"}[fmt]
+        kp = {"bf16": "bf16", "int8_kbf16": "bf16", "int4_kint4": "int4"}.get(fmt, "int8")
+        if lat == "bf16":
             self.ckv = torch.empty(shape + (LATENT,), dtype=torch.bfloat16, **kw)
-            self.kpe = torch.empty(shape + (ROPE,), dtype=torch.bfloat16, **kw)
-            self.scale = None
-            self.zero = None
+        elif lat == "int8":
+            self.ckv = torch.empty(shape + (LATENT,), dtype=torch.int8, **kw)
         else:
-            ck = LATENT if fmt == "int8" else LATENT // 2
-            self.ckv = torch.empty(shape + (ck,), dtype=torch.int8 if fmt == "int8" else torch.uint8, **kw)
+            self.ckv = torch.empty(shape + (LATENT // 2,), dtype=torch.uint8, **kw)
+        if kp == "bf16":
+            self.kpe = torch.empty(shape + (ROPE,), dtype=torch.bfloat16, **kw)
+        elif kp == "int8":
             self.kpe = torch.empty(shape + (ROPE,), dtype=torch.int8, **kw)
-            self.scale = torch.empty(shape + (N_SCALES,), dtype=torch.float16, **kw)
-            self.zero = torch.empty(shape + (N_ZEROS,), dtype=torch.float16, **kw) if fmt == "int4" else None
+        else:
+            self.kpe = torch.empty(shape + (ROPE // 2,), dtype=torch.uint8, **kw)
+        n_scales = {"bf16": 0, "int8_kbf16": N_ZEROS}.get(fmt, N_SCALES)  # 0, 32 or 40 per row
+        self.scale = torch.empty(shape + (n_scales,), dtype=torch.float16, **kw) if n_scales else None
+        self.zero = torch.empty(shape + (N_ZEROS,), dtype=torch.float16, **kw) if lat == "int4" else None
         self.seq_lens = torch.zeros((self.num_layers, self.batch), dtype=torch.int32, **kw)
         self._lens = np.zeros((self.num_layers, self.batch), dtype=np.int64)
         self.struct = MlaCacheStruct(

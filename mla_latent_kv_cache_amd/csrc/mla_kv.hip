@@ -30,6 +30,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "mla_kv.h"
 
 namespace {
@@ -45,7 +47,25 @@ constexpr int kGroupL = 16;                // latent channels per quantization g
 constexpr int kGroupR = 8;                 // k_pe channels per quantization group
 constexpr int kNGroupL = kLatent / kGroupL;  // 32
 constexpr int kNGroupR = kRope / kGroupR;    // 8
-constexpr int kNScale = kNGroupL + kNGroupR; // 40 fp16 scales per row
+constexpr int kNScale = kNGroupL + kNGroupR; // 40 quantization groups per row
+
+// What each format stores: the latent as one of BF16 / INT8 / INT4, the k_pe
+// as bf16, INT8 or INT4 (symmetric), the fp16 scales per row, the row bytes.
+enum { kKpeBf16 = 0, kKpeI8 = 1, kKpeI4 = 2 };
+constexpr int lat_fmt(int f) {
+  return f == MLA_FMT_INT8_KBF16 ? MLA_FMT_INT8 : f == MLA_FMT_INT4_KINT4 ? MLA_FMT_INT4 : f;
+}
+constexpr int kpe_fmt(int f) {
+  return (f == MLA_FMT_BF16 || f == MLA_FMT_INT8_KBF16) ? kKpeBf16 : f == MLA_FMT_INT4_KINT4 ? kKpeI4 : kKpeI8;
+}
+constexpr int n_scales(int f) { return f == MLA_FMT_BF16 ? 0 : f == MLA_FMT_INT8_KBF16 ? kNGroupL : kNScale; }
+constexpr int ckv_bytes(int f) {
+  return lat_fmt(f) == MLA_FMT_BF16 ? kLatent * 2 : lat_fmt(f) == MLA_FMT_INT8 ? kLatent : kLatent / 2;
+}
+constexpr int kpe_bytes(int f) {
+  return kpe_fmt(f) == kKpeBf16 ? kRope * 2 : kpe_fmt(f) == kKpeI8 ? kRope : kRope / 2;
+}
+constexpr bool has_zero(int f) { return lat_fmt(f) == MLA_FMT_INT4; }
 constexpr int kTile = 16;                  // tokens per MFMA tile
 constexpr int kLdsRow = kRow + 8;          // fp16 per LDS tile row (1168 B, breaks bank aliasing)
 constexpr int kWaves = 4;                  // waves per split workgroup
@@ -104,18 +124,19 @@ __device__ __forceinline__ uint16_t f16_rd_sat(float v) {
   return b;
 }
 
-// Symmetric INT8 of n values: returns the fp16 scale bits, writes codes.
-template <int N>
+// Symmetric quantization of n values to codes in [-QMAX, QMAX] (127: INT8,
+// 7: INT4): returns the fp16 scale bits, writes codes.
+template <int N, int QMAX = 127>
 __device__ __forceinline__ uint16_t quant_sym8(const float (&x)[N], int8_t (&q)[N]) {
   float a = 0.0f;
 #pragma unroll
   for (int i = 0; i < N; ++i) a = fmaxf(a, fabsf(x[i]));
-  uint16_t sb = f16_rne_sat(__fdiv_rn(a, 127.0f));
+  uint16_t sb = f16_rne_sat(__fdiv_rn(a, (float)QMAX));
   float s = f16_bits_to_f32(sb);
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     float c = 0.0f;
-    if (s != 0.0f) c = fminf(fmaxf(rintf(__fdiv_rn(x[i], s)), -127.0f), 127.0f);
+    if (s != 0.0f) c = fminf(fmaxf(rintf(__fdiv_rn(x[i], s)), -(float)QMAX), (float)QMAX);
     q[i] = (int8_t)(int)c;
   }
   return sb;
@@ -195,7 +216,7 @@ __device__ __forceinline__ void append_group(const AppendArgs &a, int b, int t, 
     const uint16_t *src = a.ckv_new + ((int64_t)b * a.T + t) * kLatent + grp * kGroupL;
     const u32x4 v0 = *(const u32x4 *)src;
     const u32x4 v1 = *(const u32x4 *)(src + 8);
-    if (FMT == MLA_FMT_BF16) {
+    if (lat_fmt(FMT) == MLA_FMT_BF16) {
       u32x4 *dst = (u32x4 *)((uint16_t *)a.ckv + row * kLatent + grp * kGroupL);
       dst[0] = v0;
       dst[1] = v1;
@@ -209,7 +230,7 @@ __device__ __forceinline__ void append_group(const AppendArgs &a, int b, int t, 
       x[8 + 2 * i] = bf16_bits_to_f32(v1[i] & 0xFFFFu);
       x[8 + 2 * i + 1] = bf16_bits_to_f32(v1[i] >> 16);
     }
-    if (FMT == MLA_FMT_INT8) {
+    if (lat_fmt(FMT) == MLA_FMT_INT8) {
       int8_t q[kGroupL];
       const uint16_t sb = quant_sym8<kGroupL>(x, q);
       u32x4 w;
@@ -218,7 +239,7 @@ __device__ __forceinline__ void append_group(const AppendArgs &a, int b, int t, 
         w[i] = (uint32_t)(uint8_t)q[4 * i] | ((uint32_t)(uint8_t)q[4 * i + 1] << 8) |
                ((uint32_t)(uint8_t)q[4 * i + 2] << 16) | ((uint32_t)(uint8_t)q[4 * i + 3] << 24);
       *(u32x4 *)((int8_t *)a.ckv + row * kLatent + grp * kGroupL) = w;
-      a.scale[row * kNScale + grp] = sb;
+      a.scale[row * n_scales(FMT) + grp] = sb;
     } else {
       uint8_t q[kGroupL];
       uint16_t sb, zb;
@@ -232,7 +253,7 @@ __device__ __forceinline__ void append_group(const AppendArgs &a, int b, int t, 
         w[i] = v;
       }
       *(u32x2 *)((uint8_t *)a.ckv + row * (kLatent / 2) + grp * (kGroupL / 2)) = w;
-      a.scale[row * kNScale + grp] = sb;
+      a.scale[row * n_scales(FMT) + grp] = sb;
       a.zero[row * kNGroupL + grp] = zb;
     }
   } else {
@@ -250,7 +271,7 @@ __device__ __forceinline__ void append_group(const AppendArgs &a, int b, int t, 
         v[j] = f32_to_bf16_rne(y0) | (f32_to_bf16_rne(y1) << 16);
       }
     }
-    if (FMT == MLA_FMT_BF16) {
+    if (kpe_fmt(FMT) == kKpeBf16) {
       *(u32x4 *)((uint16_t *)a.kpe + row * kRope + g * kGroupR) = v;
       return;
     }
@@ -261,14 +282,23 @@ __device__ __forceinline__ void append_group(const AppendArgs &a, int b, int t, 
       x[2 * i + 1] = bf16_bits_to_f32(v[i] >> 16);
     }
     int8_t q[kGroupR];
-    const uint16_t sb = quant_sym8<kGroupR>(x, q);
-    u32x2 w;
+    if (kpe_fmt(FMT) == kKpeI8) {
+      const uint16_t sb = quant_sym8<kGroupR>(x, q);
+      u32x2 w;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      w[i] = (uint32_t)(uint8_t)q[4 * i] | ((uint32_t)(uint8_t)q[4 * i + 1] << 8) |
-             ((uint32_t)(uint8_t)q[4 * i + 2] << 16) | ((uint32_t)(uint8_t)q[4 * i + 3] << 24);
-    *(u32x2 *)((int8_t *)a.kpe + row * kRope + g * kGroupR) = w;
-    a.scale[row * kNScale + grp] = sb;
+      for (int i = 0; i < 2; ++i)
+        w[i] = (uint32_t)(uint8_t)q[4 * i] | ((uint32_t)(uint8_t)q[4 * i + 1] << 8) |
+               ((uint32_t)(uint8_t)q[4 * i + 2] << 16) | ((uint32_t)(uint8_t)q[4 * i + 3] << 24);
+      *(u32x2 *)((int8_t *)a.kpe + row * kRope + g * kGroupR) = w;
+      a.scale[row * n_scales(FMT) + grp] = sb;
+    } else {  // symmetric INT4: nibble code + 8, the even channel low
+      const uint16_t sb = quant_sym8<kGroupR, 7>(x, q);
+      uint32_t w = 0;
+#pragma unroll
+      for (int j = 0; j < kGroupR; ++j) w |= (uint32_t)(q[j] + 8) << (4 * j);
+      *(uint32_t *)((uint8_t *)a.kpe + row * (kRope / 2) + g * (kGroupR / 2)) = w;
+      a.scale[row * n_scales(FMT) + grp] = sb;
+    }
   }
 }
 
@@ -530,25 +560,12 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs s) {
 // Raw 16-byte chunks a lane loads for one token tile, before dequantization.
 // Lane l, chunk k of a plane covers the 16 bytes at l + 64*k of the tile's
 // contiguous rows of that plane (perfectly coalesced: a wave reads 1 KB).
-template <int FMT> struct Fmt;
-
-template <> struct Fmt<MLA_FMT_INT8> {
-  static constexpr int kLat = 8;  // latent chunks per lane (16 rows x 512 B)
-  static constexpr int kKpe = 1;  // k_pe chunks per lane (16 rows x 64 B)
-  static constexpr int kLatRowBytes = kLatent;
-  static constexpr int kKpeRowBytes = kRope;
-};
-template <> struct Fmt<MLA_FMT_INT4> {
-  static constexpr int kLat = 4;  // 16 rows x 256 B
-  static constexpr int kKpe = 1;
-  static constexpr int kLatRowBytes = kLatent / 2;
-  static constexpr int kKpeRowBytes = kRope;
-};
-template <> struct Fmt<MLA_FMT_BF16> {
-  static constexpr int kLat = 16;  // 16 rows x 1024 B
-  static constexpr int kKpe = 2;   // 16 rows x 128 B
-  static constexpr int kLatRowBytes = kLatent * 2;
-  static constexpr int kKpeRowBytes = kRope * 2;
+template <int FMT> struct Fmt {
+  static constexpr int kLatRowBytes = ckv_bytes(FMT);
+  static constexpr int kKpeRowBytes = kpe_bytes(FMT);
+  static constexpr int kLat = kTile * kLatRowBytes / 16 / 64;  // latent chunks per lane (BF16 16, INT8 8, INT4 4)
+  static constexpr int kKpeChunks = kTile * kKpeRowBytes / 16;  // the tile's k_pe chunks (128, 64 or 32)
+  static constexpr int kKpe = (kKpeChunks + 63) / 64;           // per lane; INT4 k_pe: lanes 0..31 only
 };
 
 // Chunk k of lane l: which tile row it belongs to and where its channels start.
@@ -577,7 +594,7 @@ struct RawTile {
   u32x4 kpe[kKpe];
   uint32_t lsc[kLat];   // latent scale bits (INT8: one group; INT4: two groups packed)
   uint32_t lzp[kLat];   // INT4 zero-point bits (two groups packed)
-  uint32_t ksc[kKpe];   // k_pe scale bits (two groups packed)
+  u32x2 ksc[kKpe];      // k_pe scale bits (INT8 k_pe: two groups in .x; INT4 k_pe: four groups)
 };
 
 struct SplitArgs {
@@ -654,10 +671,10 @@ __device__ __forceinline__ SplitRsrc split_rsrc(const SplitArgs &a, int b, int t
   SplitRsrc r;
   r.ckv = make_rsrc((const uint8_t *)a.ckv + row0 * Fmt<FMT>::kLatRowBytes, n * Fmt<FMT>::kLatRowBytes);
   r.kpe = make_rsrc((const uint8_t *)a.kpe + row0 * Fmt<FMT>::kKpeRowBytes, n * Fmt<FMT>::kKpeRowBytes);
-  r.scale = make_rsrc(FMT == MLA_FMT_BF16 ? a.kpe : (const void *)(a.scale + row0 * kNScale),
-                      FMT == MLA_FMT_BF16 ? 0 : n * kNScale * 2);
-  r.zero = make_rsrc(FMT == MLA_FMT_INT4 ? (const void *)(a.zero + row0 * kNGroupL) : a.kpe,
-                     FMT == MLA_FMT_INT4 ? n * kNGroupL * 2 : 0);
+  constexpr int NS = n_scales(FMT);
+  r.scale = make_rsrc(NS == 0 ? a.kpe : (const void *)(a.scale + row0 * NS), n * NS * 2);
+  r.zero = make_rsrc(has_zero(FMT) ? (const void *)(a.zero + row0 * kNGroupL) : a.kpe,
+                     has_zero(FMT) ? n * kNGroupL * 2 : 0);
   return r;
 }
 
@@ -672,24 +689,28 @@ __device__ __forceinline__ void load_raw(RawTile<FMT, NW> &r, const SplitRsrc &r
     const int ch = lat_chunk<FMT>(lane);
     r.lat[j] = bitcast<u32x4>(
         __builtin_amdgcn_raw_buffer_load_b128(rs.ckv, row * Fmt<FMT>::kLatRowBytes + ch * 16, 0, 0));
-    if (FMT == MLA_FMT_INT8) {
-      r.lsc[j] = __builtin_amdgcn_raw_buffer_load_b16(rs.scale, row * kNScale * 2 + ch * 2, 0, 0);
-    } else if (FMT == MLA_FMT_INT4) {
-      r.lsc[j] = __builtin_amdgcn_raw_buffer_load_b32(rs.scale, row * kNScale * 2 + ch * 4, 0, 0);
+    constexpr int NS = n_scales(FMT);
+    if (lat_fmt(FMT) == MLA_FMT_INT8) {
+      r.lsc[j] = __builtin_amdgcn_raw_buffer_load_b16(rs.scale, row * NS * 2 + ch * 2, 0, 0);
+    } else if (lat_fmt(FMT) == MLA_FMT_INT4) {
+      r.lsc[j] = __builtin_amdgcn_raw_buffer_load_b32(rs.scale, row * NS * 2 + ch * 4, 0, 0);
       r.lzp[j] = __builtin_amdgcn_raw_buffer_load_b32(rs.zero, row * kNGroupL * 2 + ch * 4, 0, 0);
     }
   }
 #pragma unroll
   for (int j = 0; j < RawTile<FMT, NW>::kKpe; ++j) {
     const int k = j * NW + hw;
-    const bool have = k < Fmt<FMT>::kKpe;  // waves past the last chunk read nothing (zeros)
+    // lanes and waves past the last chunk read nothing (zeros)
+    const bool have = lane + 64 * k < Fmt<FMT>::kKpeChunks;
     const int row = r0 + kpe_row<FMT>(lane, have ? k : 0);
     const int ch = kpe_chunk<FMT>(lane);
     const int off = have ? row * Fmt<FMT>::kKpeRowBytes + ch * 16 : kOffNone;
     r.kpe[j] = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rs.kpe, off, 0, 0));
-    if (FMT != MLA_FMT_BF16)
-      r.ksc[j] = __builtin_amdgcn_raw_buffer_load_b32(
-          rs.scale, have ? row * kNScale * 2 + kNGroupL * 2 + ch * 4 : kOffNone, 0, 0);
+    const int soff = row * n_scales(FMT) * 2 + kNGroupL * 2;
+    if (kpe_fmt(FMT) == kKpeI8)
+      r.ksc[j].x = __builtin_amdgcn_raw_buffer_load_b32(rs.scale, have ? soff + ch * 4 : kOffNone, 0, 0);
+    else if (kpe_fmt(FMT) == kKpeI4)
+      r.ksc[j] = bitcast<u32x2>(__builtin_amdgcn_raw_buffer_load_b64(rs.scale, have ? soff + ch * 8 : kOffNone, 0, 0));
   }
 }
 
@@ -734,7 +755,7 @@ template <int FMT> struct TileLayout {
   static constexpr int kHi = 0;
   static constexpr int kLo = kTile * kLdsRow;
   static constexpr int kZ = kLo + (FMT == MLA_FMT_BF16 ? 0 : kTile * kLdsRow);
-  static constexpr int kHalves = kZ + (FMT == MLA_FMT_INT4 ? kTile * kZRow : 0);
+  static constexpr int kHalves = kZ + (has_zero(FMT) ? kTile * kZRow : 0);
   static constexpr int kBytes = kHalves * 2;
 };
 
@@ -749,7 +770,7 @@ __device__ __forceinline__ void dequant_store(const RawTile<FMT, NW> &r, _Float1
     const int tr = lat_row<FMT>(lane, k);
     const int ch = lat_chunk<FMT>(lane);
     const u32x4 v = r.lat[j];
-    if (FMT == MLA_FMT_INT8) {
+    if (lat_fmt(FMT) == MLA_FMT_INT8) {
       const f16x2 s2 = splat_f16_bits(r.lsc[j]);
       f16x2 hi[8], lo[8];
 #pragma unroll
@@ -765,7 +786,7 @@ __device__ __forceinline__ void dequant_store(const RawTile<FMT, NW> &r, _Float1
       st16(dh + 8, hi[4], hi[5], hi[6], hi[7]);
       st16(dl, lo[0], lo[1], lo[2], lo[3]);
       st16(dl + 8, lo[4], lo[5], lo[6], lo[7]);
-    } else if (FMT == MLA_FMT_INT4) {
+    } else if (lat_fmt(FMT) == MLA_FMT_INT4) {
       // 32 channels: bytes 0-7 in group 2ch (scale/zero low half), 8-15 in 2ch+1.
       // The tile holds q*s; the zero-points go to their own rows and enter
       // the scores and the value sums through separate exact products.
@@ -802,17 +823,40 @@ __device__ __forceinline__ void dequant_store(const RawTile<FMT, NW> &r, _Float1
 #pragma unroll
   for (int j = 0; j < RawTile<FMT, NW>::kKpe; ++j) {
     const int k = j * NW + hw;
-    if (k >= Fmt<FMT>::kKpe) continue;
+    if (lane + 64 * k >= Fmt<FMT>::kKpeChunks) continue;
     const int tr = kpe_row<FMT>(lane, k);
     const int ch = kpe_chunk<FMT>(lane);
     const u32x4 v = r.kpe[j];
-    if (FMT == MLA_FMT_BF16) {
+    if (kpe_fmt(FMT) == kKpeBf16) {
       _Float16 *dst = tile + TL::kHi + tr * kLdsRow + kLatent + ch * 8;
       st16(dst, bf16x2_to_f16x2(v[0]), bf16x2_to_f16x2(v[1]), bf16x2_to_f16x2(v[2]),
            bf16x2_to_f16x2(v[3]));
+      if (FMT != MLA_FMT_BF16) {  // a quantized latent has a lo tile: bf16 k_pe is exact in hi
+        const f16x2 z = {(_Float16)0.0f, (_Float16)0.0f};
+        st16(tile + TL::kLo + tr * kLdsRow + kLatent + ch * 8, z, z, z, z);
+      }
+    } else if (kpe_fmt(FMT) == kKpeI4) {
+      // 32 channels = k_pe groups 4ch .. 4ch+3, one dword (8 nibbles, code + 8,
+      // the even channel low) each
+      const f16x2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+      _Float16 *dh = tile + TL::kHi + tr * kLdsRow + kLatent + ch * 32;
+      _Float16 *dl = tile + TL::kLo + tr * kLdsRow + kLatent + ch * 32;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f16x2 s2 = splat_f16_bits((i < 2 ? r.ksc[j].x : r.ksc[j].y) >> (16 * (i & 1)));
+        f16x2 hi[4], lo[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t u = v[i] >> (8 * p);  // channels 2p, 2p+1 of the group
+          const f16x2 q = bitcast<f16x2>((u & 0xFu) | ((u & 0xF0u) << 12) | 0x64006400u) - bias;
+          scale_split(q, s2, hi[p], lo[p]);
+        }
+        st16(dh + 8 * i, hi[0], hi[1], hi[2], hi[3]);
+        st16(dl + 8 * i, lo[0], lo[1], lo[2], lo[3]);
+      }
     } else {
       // 16 channels = k_pe groups 2ch (bytes 0-7) and 2ch+1 (bytes 8-15)
-      const f16x2 s0 = splat_f16_bits(r.ksc[j] & 0xFFFFu), s1 = splat_f16_bits(r.ksc[j] >> 16);
+      const f16x2 s0 = splat_f16_bits(r.ksc[j].x & 0xFFFFu), s1 = splat_f16_bits(r.ksc[j].x >> 16);
       f16x2 hi[8], lo[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -877,7 +921,7 @@ void split_kernel(SplitArgs a) {
   constexpr int NBUF = LD::NBUF;                    // wave-private tile, or double-buffered shared
   constexpr int NPF = 1;                            // raw tiles in flight per wave
   constexpr bool kLo = FMT != MLA_FMT_BF16;
-  constexpr bool kZp = FMT == MLA_FMT_INT4;
+  constexpr bool kZp = has_zero(FMT);
   __shared__ __attribute__((aligned(16))) unsigned char lds[LD::kBytes];
   __shared__ float ml_m[kWaves][16], ml_l[kWaves][16];
   __shared__ int rank_lens[kRankMaxB], rank_sel;
@@ -1117,30 +1161,39 @@ constexpr int kPart16 = kWaves * 64 * 8;              // floats: 4 waves x 64 la
 constexpr int kAuxRow = 80;      // staged row stride (bytes) of the scale, k_pe and zero blocks
 constexpr int kAuxRowBf16 = 144; // staged k_pe row stride for bf16 (128-byte rows, padded)
 
+// Staging area of each format (byte offsets of its blocks):
+//   k_pe bf16 (BF16, INT8_KBF16): k_pe block of 32 rows x 144 B first;
+//   latent scales (all quantized formats): 32 rows x 80 B;
+//   k_pe codes (INT8, INT4, INT4_KINT4): 32 rows x 80 B (64 or 32 B used);
+//   zero-points (INT4, INT4_KINT4): 32 rows x 80 B.
 template <int FMT> struct Aux16 {
-  static constexpr int kScale = 0;                                         // block offsets (bytes)
-  static constexpr int kKpe = FMT == MLA_FMT_BF16 ? 0 : kT16 * kAuxRow;
+  static constexpr bool kKBf = kpe_fmt(FMT) == kKpeBf16;
+  static constexpr int kKpeBytes = kKBf ? kT16 * kAuxRowBf16 : kT16 * kAuxRow;
+  static constexpr int kScale = kKBf ? kKpeBytes : 0;
+  static constexpr int kKpe = kKBf ? 0 : kT16 * kAuxRow;
   static constexpr int kZero = 2 * kT16 * kAuxRow;
-  static constexpr int kBytes = FMT == MLA_FMT_BF16 ? kT16 * kAuxRowBf16
-                                : FMT == MLA_FMT_INT4 ? 3 * kT16 * kAuxRow : 2 * kT16 * kAuxRow;
+  static constexpr int kBytes = FMT == MLA_FMT_BF16 ? kKpeBytes
+                                : kKBf ? kKpeBytes + kT16 * kAuxRow
+                                : has_zero(FMT) ? 3 * kT16 * kAuxRow : 2 * kT16 * kAuxRow;
 };
 
-template <int FMT> struct Raw16;
-template <> struct Raw16<MLA_FMT_INT8> {
+template <int LF> struct RawLat16;
+template <> struct RawLat16<MLA_FMT_INT8> {
   static constexpr int kLat = 2;  // 16-byte loads per half-tile row: 32 codes
   u32x4 lat[2][2];
   u32x4 sa, sb;                   // this lane's chunks of the small planes
 };
-template <> struct Raw16<MLA_FMT_INT4> {
+template <> struct RawLat16<MLA_FMT_INT4> {
   static constexpr int kLat = 1;  // 32 nibbles
   u32x4 lat[2][1];
   u32x4 sa, sb;
 };
-template <> struct Raw16<MLA_FMT_BF16> {
+template <> struct RawLat16<MLA_FMT_BF16> {
   static constexpr int kLat = 4;  // 32 bf16
   u32x4 lat[2][4];
   u32x4 sa, sb;
 };
+template <int FMT> using Raw16 = RawLat16<lat_fmt(FMT)>;
 
 // What a lane reads back from the staged small planes for rows i and 16+i.
 struct Meta16 {
@@ -1150,21 +1203,25 @@ struct Meta16 {
 
 // Byte offsets of this lane's data within a tile (the same for every tile).
 //   latent: rows i and 16+i, channels 128w+32g..+31
-//   small planes: chunk plan of the staging loads. Wave w (uniform) loads
-//     slot A: scale chunks 64w+l (w < 3; 160 chunks = 32 rows x 80 B), or for
-//             bf16 k_pe chunks 64w+l (256 chunks = 32 rows x 128 B);
-//     slot B: k_pe chunks 64w+l (w < 2; 128 chunks = 32 rows x 64 B), and for
-//             INT4 zero-point chunks 64(w-2)+l (w >= 2; 128 chunks).
+//   small planes: chunk plan of the staging loads, 16-byte chunks of the
+//   tile's contiguous rows; wave w (uniform) loads
+//     slot A: bf16 k_pe chunks 64w+l (256 = 32 rows x 128 B) where k_pe is
+//             bf16, else scale chunks 64w+l (w < 3; 160 = 32 rows x 80 B);
+//     slot B: INT8_KBF16: scale chunks 64w+l (w < 2; 128 = 32 rows x 64 B);
+//             otherwise k_pe code chunks 64w+l (INT8 k_pe: w < 2, 128 =
+//             32 rows x 64 B; INT4 k_pe: w = 0, 64 = 32 rows x 32 B), and
+//             with zero-points, their chunks 64(w-2)+l (w >= 2; 128).
 //   A chunk past its plane's tile reads nothing (kOffNone) and is not staged.
 template <int FMT> struct Off16 {
   int lat[2][Raw16<FMT>::kLat];
   int ga, gb;    // byte offsets in the tile (or kOffNone)
   int la, lb;    // LDS byte offsets in the staging area (or -1: not staged)
-  bool b_zero;   // slot B reads the zero-point plane (INT4, waves 2 and 3)
+  bool b_zero;   // slot B reads the zero-point plane (waves 2 and 3)
 };
 
 template <int FMT>
 __device__ __forceinline__ Off16<FMT> offsets16(int w, int lane) {
+  using AX = Aux16<FMT>;
   const int g = lane >> 4, i = lane & 15;
   Off16<FMT> o;
 #pragma unroll
@@ -1172,32 +1229,37 @@ __device__ __forceinline__ Off16<FMT> offsets16(int w, int lane) {
     const int row = 16 * rb + i;
 #pragma unroll
     for (int j = 0; j < Raw16<FMT>::kLat; ++j) {
-      if (FMT == MLA_FMT_INT8) o.lat[rb][j] = row * kLatent + 128 * w + 32 * g + 16 * j;
-      else if (FMT == MLA_FMT_INT4) o.lat[rb][j] = row * (kLatent / 2) + 64 * w + 16 * g;
+      if (lat_fmt(FMT) == MLA_FMT_INT8) o.lat[rb][j] = row * kLatent + 128 * w + 32 * g + 16 * j;
+      else if (lat_fmt(FMT) == MLA_FMT_INT4) o.lat[rb][j] = row * (kLatent / 2) + 64 * w + 16 * g;
       else o.lat[rb][j] = row * (kLatent * 2) + 2 * (128 * w + 32 * g) + 16 * j;
     }
   }
   o.ga = o.gb = kOffNone;
   o.la = o.lb = -1;
   o.b_zero = false;
-  if (FMT == MLA_FMT_BF16) {
-    const int c = 64 * w + lane;  // < 256
-    o.ga = 16 * c;
-    o.la = (c >> 3) * kAuxRowBf16 + 16 * (c & 7);
-  } else {
-    const int ca = 64 * w + lane;
-    if (ca < kT16 * kAuxRow / 16) {
-      o.ga = 16 * ca;
-      o.la = Aux16<FMT>::kScale + 16 * ca;
+  const int c = 64 * w + lane;
+  if (AX::kKBf) {
+    o.ga = 16 * c;  // < 256 chunks: every lane of every wave
+    o.la = AX::kKpe + (c >> 3) * kAuxRowBf16 + 16 * (c & 7);
+    if (FMT != MLA_FMT_BF16 && w < 2) {  // the 64-byte scale rows
+      o.gb = 16 * c;
+      o.lb = AX::kScale + (c >> 2) * kAuxRow + 16 * (c & 3);
     }
+  } else {
+    if (c < kT16 * n_scales(FMT) * 2 / 16) {  // the 80-byte scale rows: staged as they lie
+      o.ga = 16 * c;
+      o.la = AX::kScale + 16 * c;
+    }
+    constexpr int per_row = kpe_bytes(FMT) / 16;  // k_pe chunks per row: 4 or 2
     if (w < 2) {
-      const int cb = 64 * w + lane;  // k_pe chunk, 4 per 64-byte row
-      o.gb = 16 * cb;
-      o.lb = Aux16<FMT>::kKpe + (cb >> 2) * kAuxRow + 16 * (cb & 3);
-    } else if (FMT == MLA_FMT_INT4) {
-      const int cb = 64 * (w - 2) + lane;  // zero-point chunk, 4 per 64-byte row
-      o.gb = 16 * cb;
-      o.lb = Aux16<FMT>::kZero + (cb >> 2) * kAuxRow + 16 * (cb & 3);
+      if (c < kT16 * per_row) {
+        o.gb = 16 * c;
+        o.lb = AX::kKpe + (c / per_row) * kAuxRow + 16 * (c % per_row);
+      }
+    } else if (has_zero(FMT)) {
+      const int cz = 64 * (w - 2) + lane;  // zero-point chunk, 4 per 64-byte row
+      o.gb = 16 * cz;
+      o.lb = AX::kZero + (cz >> 2) * kAuxRow + 16 * (cz & 3);
       o.b_zero = true;
     }
   }
@@ -1222,12 +1284,11 @@ __device__ __forceinline__ void load16(Raw16<FMT> &r, const SplitRsrc &rs, const
 #pragma unroll
     for (int j = 0; j < Raw16<FMT>::kLat; ++j)
       r.lat[rb][j] = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rs.ckv, o.lat[rb][j], 0, 0));
-  if (FMT == MLA_FMT_BF16) {
-    r.sa = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rs.kpe, o.ga, 0, 0));
-  } else {
-    r.sa = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rs.scale, o.ga, 0, 0));
-    r.sb = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(zero_b ? rs.zero : rs.kpe, o.gb, 0, 0));
-  }
+  constexpr bool kKBf = kpe_fmt(FMT) == kKpeBf16;
+  r.sa = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(kKBf ? rs.kpe : rs.scale, o.ga, 0, 0));
+  if (FMT != MLA_FMT_BF16)
+    r.sb = bitcast<u32x4>(
+        __builtin_amdgcn_raw_buffer_load_b128(zero_b ? rs.zero : kKBf ? rs.scale : rs.kpe, o.gb, 0, 0));
 }
 
 // This lane's chunks into the staging area.
@@ -1244,19 +1305,23 @@ __device__ __forceinline__ Meta16 meta16(const uint8_t *aux, int w, int g, int i
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const int row = 16 * rb + i;
-    if (FMT == MLA_FMT_BF16) {
-      m.kq[rb] = *(const u32x2 *)(aux + row * kAuxRowBf16 + 2 * (16 * w + 4 * g));
-      m.sc[rb] = m.ks[rb] = m.zp[rb] = 0;
-    } else {
-      const uint8_t *srow = aux + Aux16<FMT>::kScale + row * kAuxRow;
-      m.sc[rb] = *(const uint32_t *)(srow + 2 * (8 * w + 2 * g));
-      m.ks[rb] = *(const uint16_t *)(srow + 2 * (kNGroupL + 2 * w + (g >> 1)));
-      m.kq[rb].x = *(const uint32_t *)(aux + Aux16<FMT>::kKpe + row * kAuxRow + 16 * w + 4 * g);
-      m.kq[rb].y = 0;
-      m.zp[rb] = FMT == MLA_FMT_INT4
-                     ? *(const uint32_t *)(aux + Aux16<FMT>::kZero + row * kAuxRow + 2 * (8 * w + 2 * g))
-                     : 0u;
+    using AX = Aux16<FMT>;
+    // k_pe channels 16w+4g .. +3 of the row
+    if (kpe_fmt(FMT) == kKpeBf16) {
+      m.kq[rb] = *(const u32x2 *)(aux + AX::kKpe + row * kAuxRowBf16 + 2 * (16 * w + 4 * g));
+    } else if (kpe_fmt(FMT) == kKpeI8) {
+      m.kq[rb] = u32x2{*(const uint32_t *)(aux + AX::kKpe + row * kAuxRow + 16 * w + 4 * g), 0u};
+    } else {  // four nibbles
+      m.kq[rb] = u32x2{*(const uint16_t *)(aux + AX::kKpe + row * kAuxRow + 8 * w + 2 * g), 0u};
     }
+    m.sc[rb] = m.ks[rb] = m.zp[rb] = 0;
+    if (FMT != MLA_FMT_BF16) {
+      const uint8_t *srow = aux + AX::kScale + row * kAuxRow;
+      m.sc[rb] = *(const uint32_t *)(srow + 2 * (8 * w + 2 * g));
+      if (kpe_fmt(FMT) != kKpeBf16) m.ks[rb] = *(const uint16_t *)(srow + 2 * (kNGroupL + 2 * w + (g >> 1)));
+    }
+    if (has_zero(FMT))
+      m.zp[rb] = *(const uint32_t *)(aux + AX::kZero + row * kAuxRow + 2 * (8 * w + 2 * g));
   }
   return m;
 }
@@ -1301,7 +1366,7 @@ template <int FMT>
 __device__ __forceinline__ void dequant16(const Raw16<FMT> &r, const Meta16 &m, int rb, f16x8 (&hi)[4],
                                           f16x8 (&lo)[4], _Float16 *vrow, int swz, uint32_t magic,
                                           f16x4 &khi, f16x4 &klo) {
-  if (FMT == MLA_FMT_INT8) {
+  if (lat_fmt(FMT) == MLA_FMT_INT8) {
     const f16x2 s0 = splat_f16_bits(m.sc[rb] & 0xFFFFu), s1 = splat_f16_bits(m.sc[rb] >> 16);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -1318,7 +1383,7 @@ __device__ __forceinline__ void dequant16(const Raw16<FMT> &r, const Meta16 &m, 
       lo[kk] = cat8(l0, l1, l2, l3);
       *(f16x8 *)(vrow + 8 * (kk ^ swz)) = hi[kk];
     }
-  } else if (FMT == MLA_FMT_INT4) {
+  } else if (lat_fmt(FMT) == MLA_FMT_INT4) {
     const f16x2 s0 = splat_f16_bits(m.sc[rb] & 0xFFFFu), s1 = splat_f16_bits(m.sc[rb] >> 16);
     const f16x2 bias = {(_Float16)1024.0f, (_Float16)1024.0f};
     // (x & 0x000F000F) | magic as one bit-field insert: magic (the fp16
@@ -1352,10 +1417,17 @@ __device__ __forceinline__ void dequant16(const Raw16<FMT> &r, const Meta16 &m, 
       *(f16x8 *)(vrow + 8 * (kk ^ swz)) = hi[kk];
     }
   }
-  if (FMT != MLA_FMT_BF16) {
+  if (kpe_fmt(FMT) != kKpeBf16) {
     const f16x2 ks = splat_f16_bits(m.ks[rb]);
     f16x2 q0, q1, h0, h1, l0, l1;
-    codes_i8x4(m.kq[rb].x, q0, q1);
+    if (kpe_fmt(FMT) == kKpeI8) {
+      codes_i8x4(m.kq[rb].x, q0, q1);
+    } else {  // nibbles code + 8 of channels 0..3: spliced into 1024.0, minus 1032
+      const uint32_t x = m.kq[rb].x;
+      const f16x2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+      q0 = bitcast<f16x2>((x & 0xFu) | ((x & 0xF0u) << 12) | 0x64006400u) - bias;
+      q1 = bitcast<f16x2>(((x >> 8) & 0xFu) | ((x & 0xF000u) << 4) | 0x64006400u) - bias;
+    }
     scale_split(q0, ks, h0, l0);
     scale_split(q1, ks, h1, l1);
     khi = f16x4{h0.x, h0.y, h1.x, h1.y};
@@ -1382,7 +1454,7 @@ template <int FMT>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(3, 3)))
 void split16_kernel(SplitArgs a) {
   constexpr bool kLo = FMT != MLA_FMT_BF16;
-  constexpr bool kZp = FMT == MLA_FMT_INT4;
+  constexpr bool kZp = has_zero(FMT);  // INT4 latent: zero-points, and the nibble operand order
   // +16: the zero-point read of the last row runs 8 fp16 past its block (unused slots)
   __shared__ __attribute__((aligned(16))) _Float16 wblk[kWaves * kWBlk];
   __shared__ __attribute__((aligned(16))) float part[kPart16];
@@ -1420,7 +1492,7 @@ void split16_kernel(SplitArgs a) {
     for (int kk = 0; kk < 4; ++kk) {
       qh[kk] = *(const f16x8 *)(q + kQHi + 128 * w + 32 * g + 8 * kk);
       ql[kk] = *(const f16x8 *)(q + kQLo + 128 * w + 32 * g + 8 * kk);
-      if (FMT == MLA_FMT_INT4) {  // the INT4 operand order: channels 0,4,1,5,2,6,3,7
+      if (kZp) {  // the INT4 operand order: channels 0,4,1,5,2,6,3,7
         qh[kk] = f16x8{qh[kk][0], qh[kk][4], qh[kk][1], qh[kk][5], qh[kk][2], qh[kk][6], qh[kk][3], qh[kk][7]};
         ql[kk] = f16x8{ql[kk][0], ql[kk][4], ql[kk][1], ql[kk][5], ql[kk][2], ql[kk][6], ql[kk][3], ql[kk][7]};
       }
@@ -1428,7 +1500,7 @@ void split16_kernel(SplitArgs a) {
     const f16x4 kh = *(const f16x4 *)(q + kQHi + kLatent + 16 * w + 4 * g);
     const f16x4 kl = *(const f16x4 *)(q + kQLo + kLatent + 16 * w + 4 * g);
     const _Float16 z0 = (_Float16)0.0f;
-    if (FMT == MLA_FMT_INT4) {
+    if (kZp) {
       const f16x2 sh = *(const f16x2 *)(q + kQSumHi + 8 * w + 2 * g);
       const f16x2 sl = *(const f16x2 *)(q + kQSumLo + 8 * w + 2 * g);
       kzh = f16x8{kh.x, kh.y, kh.z, kh.w, sh.x, sh.y, z0, z0};
@@ -1441,7 +1513,7 @@ void split16_kernel(SplitArgs a) {
 
   _Float16 *vblk = wblk + w * kWBlk;  // [32][kVRow] C_hi of this wave's channels
   uint32_t magic = 0;  // INT4: 0x64006400 in a VGPR, opaque to the optimizer
-  if constexpr (FMT == MLA_FMT_INT4) asm("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+  if constexpr (kZp) asm("v_mov_b32 %0, 0x64006400" : "=v"(magic));
 
   f32x4 acc[8];
 #pragma unroll
@@ -1489,17 +1561,18 @@ void split16_kernel(SplitArgs a) {
       if (kZp) z = bitcast<f16x2>(mt.zp[rb]);
       const f16x8 akh = {khi.x, khi.y, khi.z, khi.w, z.x, z.y, z0, z0};
       const f16x8 akl = {klo.x, klo.y, klo.z, klo.w, z0, z0, z0, z0};
-      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      // one accumulator chain per half-tile (the two halves interleave)
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi[kk], qh[kk], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi[kk], ql[kk], s1, 0, 0, 0);
-        if (kLo) s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo[kk], qh[kk], s1, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi[kk], qh[kk], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi[kk], ql[kk], s, 0, 0, 0);
+        if (kLo) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo[kk], qh[kk], s, 0, 0, 0);
       }
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(akh, kzh, s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(akh, kzl, s1, 0, 0, 0);
-      if (kLo) s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(akl, kzh, s1, 0, 0, 0);
-      sc[rb] = s0 + s1;
+      s = __builtin_amdgcn_mfma_f32_16x16x32_f16(akh, kzh, s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_f16(akh, kzl, s, 0, 0, 0);
+      if (kLo) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(akl, kzh, s, 0, 0, 0);
+      sc[rb] = s;
     }
 
     // ---- 3. the next tile's loads. They go out only after the score sums
@@ -1781,25 +1854,30 @@ __global__ __launch_bounds__(256) void get_kernel(const void *ckv, const void *k
     const int b = (int)(row / cap), t = (int)(row % cap);
     float v = 0.0f;
     if (t < seq_lens[b]) {
+      constexpr int NS = n_scales(FMT);
       if (c < kLatent) {
-        if (FMT == MLA_FMT_BF16) {
+        if (lat_fmt(FMT) == MLA_FMT_BF16) {
           v = bf16_bits_to_f32(((const uint16_t *)ckv)[row * kLatent + c]);
-        } else if (FMT == MLA_FMT_INT8) {
-          v = (float)((const int8_t *)ckv)[row * kLatent + c] *
-              f16_bits_to_f32(scale[row * kNScale + c / kGroupL]);
+        } else if (lat_fmt(FMT) == MLA_FMT_INT8) {
+          v = (float)((const int8_t *)ckv)[row * kLatent + c] * f16_bits_to_f32(scale[row * NS + c / kGroupL]);
         } else {
           const uint8_t byte = ((const uint8_t *)ckv)[row * (kLatent / 2) + c / 2];
           const float q = (float)((c & 1) ? (byte >> 4) : (byte & 15));
-          v = fmaf(q, f16_bits_to_f32(scale[row * kNScale + c / kGroupL]),
+          v = fmaf(q, f16_bits_to_f32(scale[row * NS + c / kGroupL]),
                    f16_bits_to_f32(zero[row * kNGroupL + c / kGroupL]));
         }
       } else {
         const int d = c - kLatent;
-        if (FMT == MLA_FMT_BF16)
+        if (kpe_fmt(FMT) == kKpeBf16) {
           v = bf16_bits_to_f32(((const uint16_t *)kpe)[row * kRope + d]);
-        else
+        } else if (kpe_fmt(FMT) == kKpeI8) {
           v = (float)((const int8_t *)kpe)[row * kRope + d] *
-              f16_bits_to_f32(scale[row * kNScale + kNGroupL + d / kGroupR]);
+              f16_bits_to_f32(scale[row * NS + kNGroupL + d / kGroupR]);
+        } else {
+          const uint8_t byte = ((const uint8_t *)kpe)[row * (kRope / 2) + d / 2];
+          const float q = (float)((int)((d & 1) ? (byte >> 4) : (byte & 15)) - 8);
+          v = q * f16_bits_to_f32(scale[row * NS + kNGroupL + d / kGroupR]);
+        }
       }
     }
     if (c < kLatent) {
@@ -1816,7 +1894,7 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 int check_cache(const mla_cache *c) {
   if (!c) return MLA_ERR_INVALID_ARG;
-  if (c->format < MLA_FMT_BF16 || c->format > MLA_FMT_INT4) return MLA_ERR_INVALID_ARG;
+  if (c->format < MLA_FMT_BF16 || c->format > MLA_FMT_INT4_KINT4) return MLA_ERR_INVALID_ARG;
   if (c->num_layers < 1 || c->batch < 1 || c->capacity < 1) return MLA_ERR_INVALID_ARG;
   if (c->kv_lora_rank != kLatent || c->rope_dim != kRope || c->group_latent != kGroupL ||
       c->group_rope != kGroupR)
@@ -1825,16 +1903,14 @@ int check_cache(const mla_cache *c) {
   if (!aligned16(c->ckv) || !aligned16(c->kpe) || ((uintptr_t)c->seq_lens & 3u)) return MLA_ERR_INVALID_ARG;
   const bool quant = c->format != MLA_FMT_BF16;
   if (quant != (c->scale != nullptr)) return MLA_ERR_INVALID_ARG;
-  if ((c->format == MLA_FMT_INT4) != (c->zero != nullptr)) return MLA_ERR_INVALID_ARG;
+  if (has_zero(c->format) != (c->zero != nullptr)) return MLA_ERR_INVALID_ARG;
   if (c->scale && !aligned16(c->scale)) return MLA_ERR_INVALID_ARG;
   if (c->zero && !aligned16(c->zero)) return MLA_ERR_INVALID_ARG;
   return MLA_OK;
 }
 
-int64_t ckv_row_bytes(int fmt) {
-  return fmt == MLA_FMT_BF16 ? kLatent * 2 : fmt == MLA_FMT_INT8 ? kLatent : kLatent / 2;
-}
-int64_t kpe_row_bytes(int fmt) { return fmt == MLA_FMT_BF16 ? kRope * 2 : kRope; }
+int64_t ckv_row_bytes(int fmt) { return ckv_bytes(fmt); }
+int64_t kpe_row_bytes(int fmt) { return kpe_bytes(fmt); }
 
 struct LayerPlanes {
   void *ckv, *kpe;
@@ -1847,13 +1923,24 @@ LayerPlanes layer_planes(const mla_cache *c, int layer) {
   LayerPlanes p;
   p.ckv = (uint8_t *)c->ckv + rows * ckv_row_bytes(c->format);
   p.kpe = (uint8_t *)c->kpe + rows * kpe_row_bytes(c->format);
-  p.scale = c->scale ? c->scale + rows * kNScale : nullptr;
+  p.scale = c->scale ? c->scale + rows * n_scales(c->format) : nullptr;
   p.zero = c->zero ? c->zero + rows * kNGroupL : nullptr;
   p.seq_lens = c->seq_lens + (int64_t)layer * c->batch;
   return p;
 }
 
 bool heads_ok(int heads) { return heads == 16 || heads == 32 || heads == 64 || heads == 128; }
+
+// Calls f(std::integral_constant<int, FMT>) for the cache's (validated) format.
+template <typename F> void with_format(int fmt, F &&f) {
+  switch (fmt) {
+    case MLA_FMT_INT8: f(std::integral_constant<int, MLA_FMT_INT8>{}); break;
+    case MLA_FMT_INT4: f(std::integral_constant<int, MLA_FMT_INT4>{}); break;
+    case MLA_FMT_INT8_KBF16: f(std::integral_constant<int, MLA_FMT_INT8_KBF16>{}); break;
+    case MLA_FMT_INT4_KINT4: f(std::integral_constant<int, MLA_FMT_INT4_KINT4>{}); break;
+    default: f(std::integral_constant<int, MLA_FMT_BF16>{}); break;
+  }
+}
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -1948,23 +2035,17 @@ extern "C" int mla_cache_append(const mla_cache *cache, int32_t layer, const voi
   hipStream_t s = (hipStream_t)hip_stream;
   if (t_new <= kStepAppendMaxT) {  // a decode step: one launch, lengths advanced in-kernel
     const dim3 g((unsigned)a.B), bl(128);
-    if (cache->format == MLA_FMT_INT8)
-      hipLaunchKernelGGL(append_step_kernel<MLA_FMT_INT8>, g, bl, 0, s, a);
-    else if (cache->format == MLA_FMT_INT4)
-      hipLaunchKernelGGL(append_step_kernel<MLA_FMT_INT4>, g, bl, 0, s, a);
-    else
-      hipLaunchKernelGGL(append_step_kernel<MLA_FMT_BF16>, g, bl, 0, s, a);
+    with_format(cache->format, [&](auto f) {
+      hipLaunchKernelGGL(append_step_kernel<decltype(f)::value>, g, bl, 0, s, a);
+    });
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
   }
   const int64_t items = (int64_t)a.B * a.T * kNScale;
   int64_t blocks = (items + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  if (cache->format == MLA_FMT_INT8)
-    hipLaunchKernelGGL(append_kernel<MLA_FMT_INT8>, dim3((unsigned)blocks), dim3(256), 0, s, a);
-  else if (cache->format == MLA_FMT_INT4)
-    hipLaunchKernelGGL(append_kernel<MLA_FMT_INT4>, dim3((unsigned)blocks), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(append_kernel<MLA_FMT_BF16>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  with_format(cache->format, [&](auto f) {
+    hipLaunchKernelGGL(append_kernel<decltype(f)::value>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  });
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
   hipLaunchKernelGGL(seqlen_kernel, dim3((a.B + 255) / 256), dim3(256), 0, s, p.seq_lens, n_new, a.B,
                      a.T, a.cap);
@@ -2069,10 +2150,8 @@ int run_partial(const mla_cache *cache, const DecodePlan &pl, int layer, int hea
   a.min_chunk = pl.min_chunk;
   a.hh_count = heads <= 64 ? 1 : heads / 64;
   const dim3 grid((unsigned)(pl.ns * a.hh_count), (unsigned)cache->batch);
-  hipError_t e;
-  if (cache->format == MLA_FMT_INT8) e = launch_split_fmt<MLA_FMT_INT8>(a, heads, grid, s);
-  else if (cache->format == MLA_FMT_INT4) e = launch_split_fmt<MLA_FMT_INT4>(a, heads, grid, s);
-  else e = launch_split_fmt<MLA_FMT_BF16>(a, heads, grid, s);
+  hipError_t e = hipSuccess;
+  with_format(cache->format, [&](auto f) { e = launch_split_fmt<decltype(f)::value>(a, heads, grid, s); });
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -2152,9 +2231,7 @@ int step_begin(const mla_cache *cache, int32_t layer, const void *ckv_new, const
   sa.H = heads;
   sa.n_absorb = (int)n_absorb;
   const dim3 g((unsigned)(n_absorb + cache->batch)), bl(256);
-  if (cache->format == MLA_FMT_INT8) hipLaunchKernelGGL(step_kernel<MLA_FMT_INT8>, g, bl, 0, s, sa);
-  else if (cache->format == MLA_FMT_INT4) hipLaunchKernelGGL(step_kernel<MLA_FMT_INT4>, g, bl, 0, s, sa);
-  else hipLaunchKernelGGL(step_kernel<MLA_FMT_BF16>, g, bl, 0, s, sa);
+  with_format(cache->format, [&](auto f) { hipLaunchKernelGGL(step_kernel<decltype(f)::value>, g, bl, 0, s, sa); });
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -2237,15 +2314,10 @@ extern "C" int mla_cache_get(const mla_cache *cache, int32_t layer, float *ckv_o
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   const dim3 g((unsigned)blocks), bl(256);
-  if (cache->format == MLA_FMT_INT8)
-    hipLaunchKernelGGL(get_kernel<MLA_FMT_INT8>, g, bl, 0, s, p.ckv, p.kpe, p.scale, p.zero, p.seq_lens,
+  with_format(cache->format, [&](auto f) {
+    hipLaunchKernelGGL(get_kernel<decltype(f)::value>, g, bl, 0, s, p.ckv, p.kpe, p.scale, p.zero, p.seq_lens,
                        cache->batch, cache->capacity, ckv_out, kpe_out);
-  else if (cache->format == MLA_FMT_INT4)
-    hipLaunchKernelGGL(get_kernel<MLA_FMT_INT4>, g, bl, 0, s, p.ckv, p.kpe, p.scale, p.zero, p.seq_lens,
-                       cache->batch, cache->capacity, ckv_out, kpe_out);
-  else
-    hipLaunchKernelGGL(get_kernel<MLA_FMT_BF16>, g, bl, 0, s, p.ckv, p.kpe, p.scale, p.zero, p.seq_lens,
-                       cache->batch, cache->capacity, ckv_out, kpe_out);
+  });
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;
 }

@@ -56,16 +56,13 @@ def _same_bits(a, b, what):
 
 
 def assert_planes_equal(got, ref, fmt, what=""):
-    """Bit-exact comparison of GPU cache planes with the oracle's."""
-    if fmt == "bf16":
-        _same_bits(got["ckv"].float().numpy(), ref["ckv"], f"{what}: bf16 latent")
-        _same_bits(got["kpe"].float().numpy(), ref["kpe"], f"{what}: bf16 k_pe")
-        return
-    _same_bits(got["ckv"].numpy(), ref["ckv"], f"{what}: latent codes")
-    _same_bits(got["kpe"].numpy(), ref["kpe"], f"{what}: k_pe codes")
-    _same_bits(got["scale"].numpy(), ref["scale"], f"{what}: scales")
-    if fmt == "int4":
-        _same_bits(got["zero"].numpy(), ref["zero"], f"{what}: zero-points")
+    """Bit-exact comparison of GPU cache planes with the oracle's (every plane
+    the format has; bf16 planes compared as their fp32 widening)."""
+    assert set(got) == set(ref), (sorted(got), sorted(ref))
+    for key in ref:
+        g = got[key]
+        g = g.float().numpy() if g.dtype == torch.bfloat16 else g.numpy()
+        _same_bits(g, ref[key], f"{what}: {fmt} {key}")
 
 
 def oracle_decode(ckv, kpe, fmt, q_nope, q_pe, w_uk, w_uv, scale=W.SOFTMAX_SCALE):
@@ -96,7 +93,7 @@ def random_problem(fmt, B, H, lens, seed, cap=None, device="cuda"):
     kpe = torch.zeros((B, n, 64), dtype=torch.bfloat16, device=device)
     rows = []
     for b in range(B):
-        c, k = random_rows(n, seed * 101 + b, "skew" if fmt == "int4" else "outlier", device)
+        c, k = random_rows(n, seed * 101 + b, "skew" if fmt.startswith("int4") else "outlier", device)
         ckv[b], kpe[b] = c, k
         rows.append((c[:lens[b]], k[:lens[b]]))
     cache.append(0, ckv, kpe, n_new=lens)

@@ -27,7 +27,7 @@ def cache_struct(fmt="int8", L=2, B=3, cap=100, **over):
     f = _lib.FORMATS[fmt]
     s = _lib.MlaCacheStruct(f, L, B, cap, 512, 64, 16, 8, FAKE, FAKE + 0x100000,
                             FAKE + 0x200000 if fmt != "bf16" else 0,
-                            FAKE + 0x300000 if fmt == "int4" else 0, FAKE + 0x400000)
+                            FAKE + 0x300000 if fmt.startswith("int4") else 0, FAKE + 0x400000)
     for k, v in over.items():
         setattr(s, k, v)
     return s
@@ -92,6 +92,13 @@ def test_format_plane_rules():
     assert _ws(cache_struct("bf16", scale=FAKE))[0] == _lib.MLA_ERR_INVALID_ARG
     assert _ws(cache_struct("int4"))[0] == 0
     assert _ws(cache_struct("int4", zero=0))[0] == _lib.MLA_ERR_INVALID_ARG
+    # latent INT8 with bf16 k_pe: scales, no zero-points; INT4 with INT4 k_pe: both
+    assert _ws(cache_struct("int8_kbf16"))[0] == 0
+    assert _ws(cache_struct("int8_kbf16", scale=0))[0] == _lib.MLA_ERR_INVALID_ARG
+    assert _ws(cache_struct("int8_kbf16", zero=FAKE))[0] == _lib.MLA_ERR_INVALID_ARG
+    assert _ws(cache_struct("int4_kint4"))[0] == 0
+    assert _ws(cache_struct("int4_kint4", zero=0))[0] == _lib.MLA_ERR_INVALID_ARG
+    assert _ws(cache_struct("int8", format=5))[0] == _lib.MLA_ERR_INVALID_ARG
 
 
 def test_null_cache_and_outputs():

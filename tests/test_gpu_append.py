@@ -10,7 +10,7 @@ from mla_latent_kv_cache_amd import _lib
 from gpu_util import assert_planes_equal, f32, oracle_planes, random_rows
 
 pytestmark = pytest.mark.gpu
-FORMATS = ["bf16", "int8", "int4"]
+FORMATS = ["bf16", "int8", "int4", "int8_kbf16", "int4_kint4"]
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
@@ -22,7 +22,7 @@ def test_append_in_pieces_bit_exact(fmt):
         ckv = torch.empty((B, T, 512), dtype=torch.bfloat16, device="cuda")
         kpe = torch.empty((B, T, 64), dtype=torch.bfloat16, device="cuda")
         for b in range(B):
-            c, k = random_rows(T, 1000 * piece + b, "skew" if fmt == "int4" else "outlier")
+            c, k = random_rows(T, 1000 * piece + b, "skew" if fmt.startswith("int4") else "outlier")
             ckv[b], kpe[b] = c, k
             rows[b].append((c, k))
         cache.append(1, ckv, kpe)
@@ -77,7 +77,7 @@ def edge_rows():
     return to_bf(rows), to_bf(kp)
 
 
-@pytest.mark.parametrize("fmt", ["int8", "int4"])
+@pytest.mark.parametrize("fmt", ["int8", "int4", "int8_kbf16", "int4_kint4"])
 def test_append_edge_groups_bit_exact(fmt):
     c, k = edge_rows()
     cache = LatentCache(fmt, 1, 1, 8)

@@ -17,7 +17,7 @@ def check_all(cache, rows, q_nope, q_pe, w_uk, w_uv, out, fmt, what):
         assert_close(f32(out[b]), ref, f"{what} seq {b} (len {c.shape[0]})")
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "int8", "int4"])
+@pytest.mark.parametrize("fmt", ["bf16", "int8", "int4", "int8_kbf16", "int4_kint4"])
 @pytest.mark.parametrize("heads", [16, 32, 64, 128])
 def test_decode_formats_and_heads(fmt, heads):
     lens = [1, 17, 600, 0]
@@ -29,7 +29,7 @@ def test_decode_formats_and_heads(fmt, heads):
         assert not out[3].any()  # empty sequence -> zeros
 
 
-@pytest.mark.parametrize("fmt", ["int8", "int4"])
+@pytest.mark.parametrize("fmt", ["int8", "int4", "int8_kbf16", "int4_kint4"])
 def test_tile_and_split_boundaries(fmt):
     lens = [15, 16, 17, 31, 32, 33, 63, 64, 65, 255, 256, 257]
     cache, rows, qn, qp, wuk, wuv = random_problem(fmt, len(lens), 16, lens, seed=5, cap=272)

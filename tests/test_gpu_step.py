@@ -19,7 +19,7 @@ def new_tokens(B, H, seed, fmt):
     ckv = torch.empty((B, 512), dtype=torch.bfloat16, device="cuda")
     kpe = torch.empty((B, 64), dtype=torch.bfloat16, device="cuda")
     for b in range(B):
-        c, k = random_rows(1, seed * 31 + b, "skew" if fmt == "int4" else "outlier")
+        c, k = random_rows(1, seed * 31 + b, "skew" if fmt.startswith("int4") else "outlier")
         ckv[b], kpe[b] = c[0], k[0]
     g = torch.Generator(device="cuda")
     g.manual_seed(seed + 7)
@@ -44,7 +44,7 @@ def tables(rows_needed):
     return cos, sin, (torch.from_numpy(cos).cuda(), torch.from_numpy(sin).cuda())
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "int8", "int4"])
+@pytest.mark.parametrize("fmt", ["bf16", "int8", "int4", "int8_kbf16", "int4_kint4"])
 @pytest.mark.parametrize("heads", [16, 32])
 def test_step_with_rope_against_oracle(fmt, heads):
     cap = 320
