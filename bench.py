@@ -45,8 +45,8 @@ def kernel_sha():
 
 
 def row_bytes(fmt):
-    from oracle import accounting  # byte arithmetic only
-    return accounting.cache_row_bytes(fmt)
+    from mla_latent_kv_cache_amd.cache import row_bytes as rb
+    return rb(fmt)
 
 
 # ----------------------------------------------------------------- GPU side
@@ -54,14 +54,20 @@ def row_bytes(fmt):
 class Runner:
     """Holds one workload's cache, weights, queries and the ctypes calls of a step."""
 
-    def __init__(self, wid, extra_steps):
+    def __init__(self, wid, extra_steps, fmt=None, layers=None):
+        import dataclasses
         import torch
         from mla_latent_kv_cache_amd import LatentCache, _lib
         from mla_latent_kv_cache_amd import workloads as W
         self.torch = torch
         self.W = W
         self.wid = wid
-        self.w = w = W.WORKLOADS[wid]
+        w = W.WORKLOADS[wid]
+        if fmt is not None or layers is not None:  # the same inputs in another cache format / depth
+            fmt, layers = fmt or w.fmt, layers or w.layers
+            shape = w.name.split("_", 2)[2]  # e.g. b64_h16_ragged1024-16384
+            w = dataclasses.replace(w, fmt=fmt, layers=layers, name=f"{fmt}_l{layers}_{shape}")
+        self.w = w
         self.lens0 = W.lengths(wid)
         ragged = isinstance(w.seq, tuple)
         cap = int(self.lens0.max()) + w.append + extra_steps
@@ -155,9 +161,9 @@ class Runner:
         return cache + weights + queries + output + append
 
 
-def measure(wid, steps, warmup):
+def measure(wid, steps, warmup, fmt=None, layers=None):
     import torch
-    r = Runner(wid, steps + warmup)
+    r = Runner(wid, steps + warmup, fmt, layers)
     for _ in range(warmup):
         r.step()
     torch.cuda.synchronize()
@@ -369,6 +375,8 @@ def main():
     ap.add_argument("--workload", type=int, default=3, help="index into workloads.WORKLOADS")
     ap.add_argument("--int4-workload", type=int, default=2, help="-1 to skip")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="0 to skip the CPU baseline")
+    ap.add_argument("--no-formats", action="store_true",
+                    help="skip the one-layer runs of the INT8_KBF16 and INT4_KINT4 cache formats")
     ap.add_argument("--pmc-run", action="store_true",
                     help="only issue the launches that the HBM counter summary is taken from")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -401,6 +409,18 @@ def main():
                                    "kv_tokens_per_step", "num_splits")}
         int4["unit"] = "KV-tokens/s"
         int4["roofline"] = roofline(r4)
+    formats = None
+    if not args.no_formats:
+        # the other two cache formats, on one layer of the same inputs: INT8
+        # latent with bf16 k_pe on the ragged INT8 workload, INT4 with INT4
+        # k_pe on the INT4 workload
+        formats = {}
+        for fmt, wid in (("int8_kbf16", args.workload), ("int4_kint4", max(args.int4_workload, 0))):
+            rf = measure(wid, args.steps, args.warmup, fmt=fmt, layers=1)
+            formats[fmt] = {k: rf[k] for k in ("workload", "value", "ms_per_step", "gb_per_s", "hbm_frac",
+                                               "kv_tokens_per_step", "num_splits")}
+            formats[fmt]["unit"] = "KV-tokens/s"
+            formats[fmt]["roofline"] = roofline(rf)
     cpu = None
     if args.cpu_seconds > 0:
         log("timing the oracle on the host cores")
@@ -430,6 +450,7 @@ def main():
         "roofline": roofline(main_res),
         "cpu_baseline": cpu,
         "int4": int4,
+        "formats": formats,
     }
     print(json.dumps(line), flush=True)
 

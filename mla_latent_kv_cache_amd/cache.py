@@ -21,6 +21,16 @@ N_SCALES = 40
 N_ZEROS = 32
 
 
+def row_bytes(fmt):
+    """Bytes one token occupies in one layer of a cache of this format: the
+    planes' row sizes of include/mla_kv.h added up (1152, 656, 464, 704, 432)."""
+    lat = {"bf16": LATENT * 2, "int8": LATENT, "int4": LATENT // 2, "int8_kbf16": LATENT, "int4_kint4": LATENT // 2}
+    kpe = {"bf16": ROPE * 2, "int8": ROPE, "int4": ROPE, "int8_kbf16": ROPE * 2, "int4_kint4": ROPE // 2}
+    scales = {"bf16": 0, "int8_kbf16": N_ZEROS}.get(fmt, N_SCALES)
+    zeros = N_ZEROS if fmt in ("int4", "int4_kint4") else 0
+    return lat[fmt] + kpe[fmt] + 2 * (scales + zeros)
+
+
 def rope_tables(rows, base=10000.0, device="cuda"):
     """RoPE angle tables for decode_step: (cos, sin), fp32 [rows, 32], row p
     holding cos / sin of p * base^(-2i/64) for channel pair (2i, 2i+1),

@@ -71,3 +71,10 @@ def test_cache_row_bytes_with_metadata():
     # every cache row plane is a whole number of 16-byte vectors
     for nbytes in (512, 256, 64, 128, 80, 64):
         assert nbytes % 16 == 0
+
+
+def test_package_row_bytes_equal_the_oracle():
+    # the binding's own row arithmetic (used by the benchmark) against the oracle's
+    from mla_latent_kv_cache_amd.cache import row_bytes
+    for fmt in ("bf16", "int8", "int4", "int8_kbf16", "int4_kint4"):
+        assert row_bytes(fmt) == acc.cache_row_bytes(fmt), fmt
