@@ -329,6 +329,46 @@ def _pmc_means(csv_path, counter):
     return out
 
 
+def summarize_stats(wid, stats_csv, out_path):
+    """Write the profiles/ table of this library's kernels from a rocprofv3
+    --kernel-trace --stats run of this script (its run_kernel_stats.csv)."""
+    import csv
+    from mla_latent_kv_cache_amd import workloads as W
+    w = W.WORKLOADS[wid]
+    rows = []
+    with open(stats_csv) as f:
+        for r in csv.DictReader(f):
+            name = r["Name"]
+            if "at::" in name or "rocclr" in name:
+                continue  # torch kernels building the synthetic inputs, runtime copies
+            m = re.search(r"(\w+_kernel)(?:<(\d)>|I?L?i?(\d)E)?", name)
+            short = m.group(1) + (f"<{m.group(2) or m.group(3)}>" if m and (m.group(2) or m.group(3)) else "") \
+                if m else name[:40]
+            rows.append((short, int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                         float(r["MaxNs"]) / 1e3, float(r["TotalDurationNs"]) / 1e6))
+    rows.sort(key=lambda x: -x[5])
+    cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- python3 bench.py "
+           f"--steps 3 --warmup 1 --cpu-seconds 0 --int4-workload -1 --no-formats --workload {wid}")
+    lines = [
+        f"# rocprofv3 kernel statistics, {w.name}: 1 warmup + 3 timed decode steps (every layer)",
+        "# Commands (repository root, one MI355X):",
+        f"#   {cmd}",
+        f"#   python3 bench.py --summarize-stats <dir>/run_kernel_stats.csv --workload {wid}",
+        "# Rows: this library's kernels (the torch kernels that build the synthetic inputs are omitted).",
+        "# append_kernel<f> is the one-off prefill. A decode step runs, per layer, step_kernel<f>",
+        "# (mla_decode_step_begin: store the new token with its k_pe turned, absorb the turned query),",
+        "# split16_kernel<f> (mla_decode_partial, 16 heads) and reduce_kernel (mla_decode_combine).",
+        "# <f>: 0 bf16, 1 INT8, 2 INT4, 3 INT8 latent + bf16 k_pe, 4 INT4 latent + INT4 k_pe.",
+        f"{'kernel':28s}{'calls':>7s}{'avg_us':>11s}{'min_us':>11s}{'max_us':>11s}{'total_ms':>11s}",
+    ]
+    for r in rows:
+        lines.append(f"{r[0]:28s}{r[1]:7d}{r[2]:11.2f}{r[3]:11.2f}{r[4]:11.2f}{r[5]:11.3f}")
+    os.makedirs(os.path.dirname(out_path), exist_ok=True)
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log(f"wrote {out_path}")
+
+
 def summarize_pmc(wid, fetch_csv, write_csv, out_path):
     """Write the profiles/ summary that roofline() reads: HBM bytes per partial
     launch from FETCH_SIZE and WRITE_SIZE, each scaled by what the same counter
@@ -379,9 +419,17 @@ def main():
                     help="skip the one-layer runs of the INT8_KBF16 and INT4_KINT4 cache formats")
     ap.add_argument("--pmc-run", action="store_true",
                     help="only issue the launches that the HBM counter summary is taken from")
+    ap.add_argument("--summarize-stats", metavar="STATS_CSV",
+                    help="write profiles/kernel_stats_<workload>.txt from a rocprofv3 --stats run")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/pmc_partial_<workload>.txt from two rocprofv3 counter runs")
     args = ap.parse_args()
+    if args.summarize_stats:
+        from mla_latent_kv_cache_amd import workloads as W
+        name = W.WORKLOADS[args.workload].name
+        summarize_stats(args.workload, args.summarize_stats,
+                        os.path.join(ROOT, "profiles", f"kernel_stats_{name}.txt"))
+        return
     if args.summarize_pmc:
         from mla_latent_kv_cache_amd import workloads as W
         name = W.WORKLOADS[args.workload].name
