@@ -102,6 +102,17 @@ typedef struct mla_cache {
   uint16_t *scale;
   uint16_t *zero;
   int32_t *seq_lens;
+  /* Paged layout (page_size > 0; "DeepSeek的MLA技术", limits and future
+   * directions, item 3: MLA together with PagedAttention): each plane is a pool
+   * [num_layers][num_pages][page_size][row], and token p of sequence b lives at
+   * row p % page_size of page block_table[b][p / page_size] in every layer.
+   * page_size: a power of two >= 32 dividing capacity; num_pages >= 1;
+   * block_table: device int32 [batch][capacity / page_size]. A page index
+   * outside [0, num_pages) reads as an empty page and is never written.
+   * page_size = 0 (and block_table = NULL): the contiguous planes above. */
+  int32_t page_size;
+  int32_t num_pages;
+  const int32_t *block_table;
 } mla_cache;
 
 /*

@@ -52,6 +52,9 @@ class MlaCacheStruct(ctypes.Structure):
         ("scale", ctypes.c_void_p),
         ("zero", ctypes.c_void_p),
         ("seq_lens", ctypes.c_void_p),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("block_table", ctypes.c_void_p),
     ]
 
 

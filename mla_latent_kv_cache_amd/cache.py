@@ -72,7 +72,12 @@ class LatentCache:
     A host mirror of the lengths guards capacity before each append.
     """
 
-    def __init__(self, fmt, num_layers, batch, capacity, device="cuda"):
+    def __init__(self, fmt, num_layers, batch, capacity, device="cuda", page_size=0, num_pages=None,
+                 block_table=None):
+        """page_size > 0 makes the planes pools of num_pages pages of page_size
+        tokens per layer; block_table (int32 [batch, capacity // page_size],
+        host or device) maps each sequence's token blocks to pages (default:
+        sequence b's blocks are pages b * blocks .. in order)."""
         if fmt not in FORMATS:
             raise ValueError(f"format must be one of {list(FORMATS)}")
         self.fmt = fmt
@@ -80,7 +85,19 @@ class LatentCache:
         self.device = torch.device(device)
         if self.device.type == "cuda" and self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
-        shape = (self.num_layers, self.batch, self.capacity)
+        self.page_size = int(page_size)
+        self.block_table = None
+        if self.page_size:
+            blocks = self.capacity // self.page_size
+            self.num_pages = int(num_pages) if num_pages is not None else self.batch * blocks
+            if block_table is None:
+                block_table = torch.arange(self.batch * blocks, dtype=torch.int32).reshape(self.batch, blocks)
+            self.block_table = torch.as_tensor(block_table, dtype=torch.int32).to(self.device).contiguous()
+            _need(self.block_table, "block_table", torch.int32, (self.batch, blocks), self.device)
+            shape = (self.num_layers, self.num_pages, self.page_size)
+        else:
+            self.num_pages = 0
+            shape = (self.num_layers, self.batch, self.capacity)
         kw = dict(device=self.device)
         lat = {"bf16": "bf16", "int8": "int8", "int4": "int4", "int8_kbf16": "int8", "int4_kint4": "int4"}[fmt]
         kp = {"bf16": "bf16", "int8_kbf16": "bf16", "int4_kint4": "int4"}.get(fmt, "int8")
@@ -106,7 +123,8 @@ class LatentCache:
             self.ckv.data_ptr(), self.kpe.data_ptr(),
             self.scale.data_ptr() if self.scale is not None else 0,
             self.zero.data_ptr() if self.zero is not None else 0,
-            self.seq_lens.data_ptr())
+            self.seq_lens.data_ptr(), self.page_size, self.num_pages,
+            self.block_table.data_ptr() if self.block_table is not None else 0)
 
     # ------------------------------------------------------------ queries
     def lengths(self, layer=None):
@@ -275,11 +293,18 @@ class LatentCache:
         return ckv, kpe
 
     def planes(self, layer, b):
-        """The raw cache planes of one sequence (first seq_len rows), as host numpy arrays."""
+        """The raw cache planes of one sequence (first seq_len rows, gathered
+        through the block table when paged), as host tensors."""
         n = int(self._lens[layer, b])
-        out = {"ckv": self.ckv[layer, b, :n].cpu(), "kpe": self.kpe[layer, b, :n].cpu()}
-        if self.scale is not None:
-            out["scale"] = self.scale[layer, b, :n].cpu()
-        if self.zero is not None:
-            out["zero"] = self.zero[layer, b, :n].cpu()
+        planes = {"ckv": self.ckv, "kpe": self.kpe, "scale": self.scale, "zero": self.zero}
+        out = {}
+        for key, t in planes.items():
+            if t is None:
+                continue
+            if self.page_size:
+                pos = torch.arange(n, device=self.device)
+                pages = self.block_table[b].long()[pos // self.page_size]
+                out[key] = t[layer, pages, pos % self.page_size].cpu()
+            else:
+                out[key] = t[layer, b, :n].cpu()
         return out

@@ -177,6 +177,26 @@ __device__ __forceinline__ void lds_stores_done() {
 
 // ------------------------------------------------------------------ append
 
+// Paged planes: token p of sequence b is row p % size of page table[b][p / size]
+// of the layer's pool; size = 0 means contiguous rows b * cap + p.
+struct Paging {
+  const int32_t *table;  // [B][max_pages]
+  int size, shift, max_pages, num_pages;  // size = 1 << shift (a power of two >= 32)
+};
+
+// Page of token p of sequence b, or -1 when the table entry is outside the pool.
+__device__ __forceinline__ int page_of(const Paging &pg, int b, int p) {
+  const int page = pg.table[(int64_t)b * pg.max_pages + (p >> pg.shift)];
+  return (page >= 0 && page < pg.num_pages) ? page : -1;
+}
+
+// Row within the layer's plane of token p of sequence b, or -1 (no page).
+__device__ __forceinline__ int64_t plane_row(const Paging &pg, int b, int cap, int p) {
+  if (pg.size == 0) return (int64_t)b * cap + p;
+  const int page = page_of(pg, b, p);
+  return page < 0 ? -1 : ((int64_t)page << pg.shift) + (p & (pg.size - 1));
+}
+
 struct AppendArgs {
   void *ckv;            // layer base of the ckv plane
   void *kpe;
@@ -188,6 +208,7 @@ struct AppendArgs {
   const int32_t *n_new;     // optional [B]
   const float *rope_cos;    // optional fp32 [rows][32]: the k_pe of new tokens turns by its row
   const float *rope_sin;    // (fused decode step only; plain appends store k_pe as given)
+  Paging pg;
   int B, T, cap;
 };
 
@@ -211,7 +232,8 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float v) {
 // new token t of sequence b at row `pos` of the cache.
 template <int FMT>
 __device__ __forceinline__ void append_group(const AppendArgs &a, int b, int t, int grp, int pos) {
-  const int64_t row = (int64_t)b * a.cap + pos;
+  const int64_t row = plane_row(a.pg, b, a.cap, pos);
+  if (row < 0) return;  // no page for this position: nothing is stored
   if (grp < kNGroupL) {
     const uint16_t *src = a.ckv_new + ((int64_t)b * a.T + t) * kLatent + grp * kGroupL;
     const u32x4 v0 = *(const u32x4 *)src;
@@ -607,6 +629,7 @@ struct SplitArgs {
   float *ws_m;              // [B][nsplit][H]
   float *ws_l;              // [B][nsplit][H]
   float *ws_acc;            // [B][nsplit][H][512]
+  Paging pg;
   int B, H, cap, nsplit, min_chunk, hh_count;
 };
 
@@ -664,10 +687,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, (int)kRsrcWord3);
 }
 
+// Descriptors over n plane rows starting at row0 (n = 0: empty, every load reads zeros).
 template <int FMT>
-__device__ __forceinline__ SplitRsrc split_rsrc(const SplitArgs &a, int b, int t_begin, int t_end) {
-  const int64_t row0 = (int64_t)b * a.cap + t_begin;
-  const int64_t n = t_end - t_begin;
+__device__ __forceinline__ SplitRsrc rows_rsrc(const SplitArgs &a, int64_t row0, int64_t n) {
   SplitRsrc r;
   r.ckv = make_rsrc((const uint8_t *)a.ckv + row0 * Fmt<FMT>::kLatRowBytes, n * Fmt<FMT>::kLatRowBytes);
   r.kpe = make_rsrc((const uint8_t *)a.kpe + row0 * Fmt<FMT>::kKpeRowBytes, n * Fmt<FMT>::kKpeRowBytes);
@@ -676,6 +698,27 @@ __device__ __forceinline__ SplitRsrc split_rsrc(const SplitArgs &a, int b, int t
   r.zero = make_rsrc(has_zero(FMT) ? (const void *)(a.zero + row0 * kNGroupL) : a.kpe,
                      has_zero(FMT) ? n * kNGroupL * 2 : 0);
   return r;
+}
+
+// Rows [t_begin, t_end) of sequence b in the contiguous layout.
+template <int FMT>
+__device__ __forceinline__ SplitRsrc split_rsrc(const SplitArgs &a, int b, int t_begin, int t_end) {
+  return rows_rsrc<FMT>(a, (int64_t)b * a.cap + t_begin, t_end - t_begin);
+}
+
+// Paged layout: rows [r0, t_end) of a sequence, cut at the end of r0's page
+// (`page`, from page_of; -1 or r0 >= t_end: empty).
+template <int FMT>
+__device__ __forceinline__ SplitRsrc page_rsrc(const SplitArgs &a, int page, int r0, int t_end) {
+  if (page < 0 || r0 >= t_end) return rows_rsrc<FMT>(a, 0, 0);
+  const int off = r0 & (a.pg.size - 1);
+  const int end = min(t_end, r0 - off + a.pg.size);
+  return rows_rsrc<FMT>(a, ((int64_t)page << a.pg.shift) + off, end - r0);
+}
+
+// The page of token r of sequence b for page_rsrc (-1 past t_end).
+__device__ __forceinline__ int tile_page(const SplitArgs &a, int b, int r, int t_end) {
+  return r < t_end ? page_of(a.pg, b, r) : -1;
 }
 
 // Raw chunks of the tile whose first row is row `r0` of the split.
@@ -972,10 +1015,21 @@ void split_kernel(SplitArgs a) {
 
   _Float16 *tiles = (_Float16 *)lds + (int64_t)tg * NBUF * TL::kHalves;
 
-  const SplitRsrc rs = split_rsrc<FMT>(a, b, t_begin, t_end);
+  // contiguous: one descriptor over the split, tiles at row offsets; paged:
+  // a descriptor per 16-token tile (a tile never crosses a page)
+  const bool paged = a.pg.size != 0;
+  const SplitRsrc rs = paged ? rows_rsrc<FMT>(a, 0, 0) : split_rsrc<FMT>(a, b, t_begin, t_end);
+  auto load_tile = [&](RawTile<FMT, HGW> &r, int tile) {
+    if (paged) {
+      const int r0 = t_begin + tile * kTile;
+      load_raw<FMT, HGW>(r, page_rsrc<FMT>(a, tile_page(a, b, r0, t_end), r0, t_end), 0, lane, hw);
+    } else {
+      load_raw<FMT, HGW>(r, rs, tile * kTile, lane, hw);
+    }
+  };
   RawTile<FMT, HGW> raw[NPF];
 #pragma unroll
-  for (int p = 0; p < NPF; ++p) load_raw<FMT, HGW>(raw[p], rs, (tg + p * TG) * kTile, lane, hw);
+  for (int p = 0; p < NPF; ++p) load_tile(raw[p], tg + p * TG);
 
   for (int it0 = 0; it0 < niters; it0 += NPF) {
 #pragma unroll
@@ -987,7 +1041,7 @@ void split_kernel(SplitArgs a) {
       _Float16 *tb = tiles + (NBUF == 1 ? 0 : (it & 1)) * TL::kHalves;
       if (valid) dequant_store<FMT, HGW>(raw[p], tb, lane, hw);
       lds_stores_done();
-      load_raw<FMT, HGW>(raw[p], rs, (tile + NPF * TG) * kTile, lane, hw);
+      load_tile(raw[p], tile + NPF * TG);
       if (HGW > 1) {
         __syncthreads();
       } else {
@@ -1524,9 +1578,18 @@ void split16_kernel(SplitArgs a) {
   const Off16<FMT> off = offsets16<FMT>(w, lane);
   const bool zero_b = off.b_zero;  // uniform: depends on the wave only
   Raw16<FMT> raw[kNpf16];
+  // Paged layout: each tile's descriptors come from its page, whose index is
+  // read from the block table one tile ahead of the loads that use it.
+  const bool paged = a.pg.size != 0;
+  auto rsrc_of = [&](int r0, int page) {
+    return paged ? page_rsrc<FMT>(a, page, r0, t_end) : tile_rsrc<FMT>(a, b, r0, t_end);
+  };
 #pragma unroll
-  for (int p = 0; p < kNpf16; ++p)
-    load16<FMT>(raw[p], tile_rsrc<FMT>(a, b, t_begin + p * kT16, t_end), off, zero_b);
+  for (int p = 0; p < kNpf16; ++p) {
+    const int r0 = t_begin + p * kT16;
+    load16<FMT>(raw[p], rsrc_of(r0, paged ? tile_page(a, b, r0, t_end) : 0), off, zero_b);
+  }
+  int next_page = paged ? tile_page(a, b, t_begin + kNpf16 * kT16, t_end) : 0;
 
   for (int it0 = 0; it0 < ntiles; it0 += kNpf16) {
 #pragma unroll
@@ -1583,7 +1646,9 @@ void split16_kernel(SplitArgs a) {
     // Always issued, so the count of outstanding loads is the same on every
     // path.
     __builtin_amdgcn_sched_barrier(0);
-    load16<FMT>(raw[p], tile_rsrc<FMT>(a, b, t_begin + (it + kNpf16) * kT16, t_end), off, zero_b);
+    const int r_next = t_begin + (it + kNpf16) * kT16;
+    load16<FMT>(raw[p], rsrc_of(r_next, next_page), off, zero_b);
+    if (paged) next_page = tile_page(a, b, r_next + kT16, t_end);
 
     // ---- 4. partial scores of the four waves
     // [wave][half][lane][4]: consecutive lanes use consecutive 16 bytes
@@ -1844,16 +1909,17 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float *ws_m, const fl
 template <int FMT>
 __global__ __launch_bounds__(256) void get_kernel(const void *ckv, const void *kpe,
                                                   const uint16_t *scale, const uint16_t *zero,
-                                                  const int32_t *seq_lens, int B, int cap,
+                                                  const int32_t *seq_lens, Paging pg, int B, int cap,
                                                   float *ckv_out, float *kpe_out) {
   const int64_t total = (int64_t)B * cap * kRow;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * blockDim.x) {
     const int c = (int)(idx % kRow);
-    const int64_t row = idx / kRow;
-    const int b = (int)(row / cap), t = (int)(row % cap);
+    const int64_t orow = idx / kRow;  // output row [B][cap]
+    const int b = (int)(orow / cap), t = (int)(orow % cap);
     float v = 0.0f;
-    if (t < seq_lens[b]) {
+    const int64_t row = t < seq_lens[b] ? plane_row(pg, b, cap, t) : -1;  // plane row
+    if (row >= 0) {
       constexpr int NS = n_scales(FMT);
       if (c < kLatent) {
         if (lat_fmt(FMT) == MLA_FMT_BF16) {
@@ -1881,9 +1947,9 @@ __global__ __launch_bounds__(256) void get_kernel(const void *ckv, const void *k
       }
     }
     if (c < kLatent) {
-      if (ckv_out) ckv_out[row * kLatent + c] = v;
+      if (ckv_out) ckv_out[orow * kLatent + c] = v;
     } else if (kpe_out) {
-      kpe_out[row * kRope + (c - kLatent)] = v;
+      kpe_out[orow * kRope + (c - kLatent)] = v;
     }
   }
 }
@@ -1906,7 +1972,25 @@ int check_cache(const mla_cache *c) {
   if (has_zero(c->format) != (c->zero != nullptr)) return MLA_ERR_INVALID_ARG;
   if (c->scale && !aligned16(c->scale)) return MLA_ERR_INVALID_ARG;
   if (c->zero && !aligned16(c->zero)) return MLA_ERR_INVALID_ARG;
+  if (c->page_size < 0) return MLA_ERR_INVALID_ARG;
+  if (c->page_size == 0) return c->block_table ? MLA_ERR_INVALID_ARG : MLA_OK;
+  // paged: pages are a power of two of at least 32 tokens (whole 32-token
+  // tiles) and tile the capacity
+  if (c->page_size < 32 || (c->page_size & (c->page_size - 1)) || c->capacity % c->page_size)
+    return MLA_ERR_INVALID_ARG;
+  if (c->num_pages < 1 || !c->block_table || ((uintptr_t)c->block_table & 3u)) return MLA_ERR_INVALID_ARG;
   return MLA_OK;
+}
+
+Paging paging_of(const mla_cache *c) {
+  Paging p;
+  p.table = c->page_size ? c->block_table : nullptr;
+  p.size = c->page_size;
+  p.shift = 0;
+  while (c->page_size && (1 << p.shift) < c->page_size) ++p.shift;
+  p.max_pages = c->page_size ? c->capacity / c->page_size : 0;
+  p.num_pages = c->page_size ? c->num_pages : 0;
+  return p;
 }
 
 int64_t ckv_row_bytes(int fmt) { return ckv_bytes(fmt); }
@@ -1919,7 +2003,9 @@ struct LayerPlanes {
 };
 
 LayerPlanes layer_planes(const mla_cache *c, int layer) {
-  const int64_t rows = (int64_t)layer * c->batch * c->capacity;
+  // rows of one layer: batch * capacity contiguous, or its pool of pages
+  const int64_t rows = (int64_t)layer * (c->page_size ? (int64_t)c->num_pages * c->page_size
+                                                      : (int64_t)c->batch * c->capacity);
   LayerPlanes p;
   p.ckv = (uint8_t *)c->ckv + rows * ckv_row_bytes(c->format);
   p.kpe = (uint8_t *)c->kpe + rows * kpe_row_bytes(c->format);
@@ -2029,6 +2115,7 @@ extern "C" int mla_cache_append(const mla_cache *cache, int32_t layer, const voi
   a.kpe_new = (const uint16_t *)kpe_new;
   a.n_new = n_new;
   a.rope_cos = a.rope_sin = nullptr;
+  a.pg = paging_of(cache);
   a.B = cache->batch;
   a.T = t_new;
   a.cap = cache->capacity;
@@ -2148,6 +2235,7 @@ int run_partial(const mla_cache *cache, const DecodePlan &pl, int layer, int hea
   a.cap = cache->capacity;
   a.nsplit = pl.ns;
   a.min_chunk = pl.min_chunk;
+  a.pg = paging_of(cache);
   a.hh_count = heads <= 64 ? 1 : heads / 64;
   const dim3 grid((unsigned)(pl.ns * a.hh_count), (unsigned)cache->batch);
   hipError_t e = hipSuccess;
@@ -2220,6 +2308,7 @@ int step_begin(const mla_cache *cache, int32_t layer, const void *ckv_new, const
   sa.ap.n_new = nullptr;
   sa.ap.rope_cos = rope_cos;
   sa.ap.rope_sin = rope_sin;
+  sa.ap.pg = paging_of(cache);
   sa.ap.B = cache->batch;
   sa.ap.T = 1;
   sa.ap.cap = cache->capacity;
@@ -2316,7 +2405,7 @@ extern "C" int mla_cache_get(const mla_cache *cache, int32_t layer, float *ckv_o
   const dim3 g((unsigned)blocks), bl(256);
   with_format(cache->format, [&](auto f) {
     hipLaunchKernelGGL(get_kernel<decltype(f)::value>, g, bl, 0, s, p.ckv, p.kpe, p.scale, p.zero, p.seq_lens,
-                       cache->batch, cache->capacity, ckv_out, kpe_out);
+                       paging_of(cache), cache->batch, cache->capacity, ckv_out, kpe_out);
   });
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;

@@ -101,6 +101,19 @@ def test_format_plane_rules():
     assert _ws(cache_struct("int8", format=5))[0] == _lib.MLA_ERR_INVALID_ARG
 
 
+def test_paging_rules():
+    ok = dict(cap=256, page_size=64, num_pages=10, block_table=FAKE + 0x500000)
+    assert _ws(cache_struct("int8", **ok))[0] == 0
+    assert _ws(cache_struct("int8", **{**ok, "page_size": 48}))[0] == _lib.MLA_ERR_INVALID_ARG   # not a power of two
+    assert _ws(cache_struct("int8", **{**ok, "page_size": 16}))[0] == _lib.MLA_ERR_INVALID_ARG   # under one tile
+    assert _ws(cache_struct("int8", **{**ok, "cap": 200}))[0] == _lib.MLA_ERR_INVALID_ARG        # pages do not tile it
+    assert _ws(cache_struct("int8", **{**ok, "num_pages": 0}))[0] == _lib.MLA_ERR_INVALID_ARG
+    assert _ws(cache_struct("int8", **{**ok, "block_table": 0}))[0] == _lib.MLA_ERR_INVALID_ARG
+    assert _ws(cache_struct("int8", **{**ok, "block_table": FAKE + 2}))[0] == _lib.MLA_ERR_INVALID_ARG
+    assert _ws(cache_struct("int8", page_size=0, block_table=FAKE))[0] == _lib.MLA_ERR_INVALID_ARG
+    assert _ws(cache_struct("int8", page_size=-64))[0] == _lib.MLA_ERR_INVALID_ARG
+
+
 def test_null_cache_and_outputs():
     L = _lib.lib()
     n = ctypes.c_size_t(0)

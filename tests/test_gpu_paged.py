@@ -1,0 +1,123 @@
+"""The paged cache layout on the GPU: the same rows stored through a shuffled
+block table give bit-identical planes (gathered), gets, decodes and fused
+steps as the contiguous layout, for every format and 16/32 heads; block-table
+entries past a sequence's length may be anything."""
+
+import numpy as np
+import pytest
+import torch
+
+from mla_latent_kv_cache_amd import LatentCache
+from oracle import rope as R
+
+from gpu_util import oracle_decode, assert_close, f32, random_rows
+
+pytestmark = pytest.mark.gpu
+TAU = 1.0 / np.sqrt(192.0)
+FORMATS = ["bf16", "int8", "int4", "int8_kbf16", "int4_kint4"]
+
+
+def shuffled_table(B, blocks, num_pages, seed):
+    perm = np.random.default_rng(seed).permutation(num_pages)[: B * blocks]
+    return torch.tensor(perm.reshape(B, blocks), dtype=torch.int32)
+
+
+def fill(cache, lens, seed, fmt):
+    B = len(lens)
+    n = max(lens)
+    ckv = torch.zeros((B, n, 512), dtype=torch.bfloat16, device="cuda")
+    kpe = torch.zeros((B, n, 64), dtype=torch.bfloat16, device="cuda")
+    rows = []
+    for b in range(B):
+        c, k = random_rows(n, seed * 97 + b, "skew" if fmt.startswith("int4") else "outlier")
+        ckv[b], kpe[b] = c, k
+        rows.append((c[: lens[b]], k[: lens[b]]))
+    # two appends, so rows cross page boundaries in the middle of an append
+    first = [min(l, 45) for l in lens]
+    cache.append(0, ckv[:, :45].contiguous() if n >= 45 else ckv, kpe[:, :45].contiguous() if n >= 45 else kpe,
+                 n_new=first)
+    if n > 45:
+        rest = [l - f for l, f in zip(lens, first)]
+        cache.append(0, ckv[:, 45:].contiguous(), kpe[:, 45:].contiguous(), n_new=rest)
+    return rows
+
+
+def queries(B, H, seed):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    qn = torch.randn((B, H, 128), generator=g, device="cuda").to(torch.bfloat16)
+    qp = torch.randn((B, H, 64), generator=g, device="cuda").to(torch.bfloat16)
+    wuk = (torch.randn((H, 128, 512), generator=g, device="cuda") / 512 ** 0.5).to(torch.bfloat16)
+    wuv = (torch.randn((H, 512, 128), generator=g, device="cuda") / 512 ** 0.5).to(torch.bfloat16)
+    return qn, qp, wuk, wuv
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("heads", [16, 32])
+def test_paged_equals_contiguous(fmt, heads):
+    lens, cap, ps = [0, 1, 64, 65, 200, 255], 256, 64
+    B, blocks = len(lens), cap // ps
+    num_pages = B * blocks + 5  # spare pages that no sequence uses
+    table = shuffled_table(B, blocks, num_pages, seed=3)
+    flat = LatentCache(fmt, 1, B, cap)
+    paged = LatentCache(fmt, 1, B, cap, page_size=ps, num_pages=num_pages, block_table=table)
+    rows = fill(flat, lens, 11, fmt)
+    fill(paged, lens, 11, fmt)
+    qn, qp, wuk, wuv = queries(B, heads, 12)
+    for splits in (0, 3):
+        o_flat = flat.decode(0, qn, qp, wuk, wuv, TAU, num_splits=splits)
+        o_paged = paged.decode(0, qn, qp, wuk, wuv, TAU, num_splits=splits)
+        torch.cuda.synchronize()
+        assert torch.equal(o_flat, o_paged), (fmt, heads, splits)
+    for b in range(B):
+        pf, pp = flat.planes(0, b), paged.planes(0, b)
+        for k in pf:
+            assert torch.equal(pf[k], pp[k]), (b, k)
+        assert_close(f32(o_paged[b]), oracle_decode(rows[b][0], rows[b][1], fmt, qn[b], qp[b], wuk, wuv, TAU),
+                     f"{fmt} paged seq {b}")
+    gf, gp = flat.get(0), paged.get(0)
+    torch.cuda.synchronize()
+    assert torch.equal(gf[0], gp[0]) and torch.equal(gf[1], gp[1])
+
+
+@pytest.mark.parametrize("fmt", ["int8", "int4_kint4"])
+def test_paged_fused_step_equals_contiguous(fmt):
+    lens, cap, ps, H = [63, 64, 127, 0], 128, 32, 16
+    B, blocks = len(lens), cap // ps
+    table = shuffled_table(B, blocks, B * blocks, seed=5)
+    flat = LatentCache(fmt, 1, B, cap)
+    paged = LatentCache(fmt, 1, B, cap, page_size=ps, num_pages=B * blocks, block_table=table)
+    fill(flat, lens, 21, fmt)
+    fill(paged, lens, 21, fmt)
+    cos, sin = R.rope_tables(cap + 1)
+    rope = (torch.from_numpy(cos).cuda(), torch.from_numpy(sin).cuda())
+    for step in range(2):
+        c, k = random_rows(B, 300 + step)
+        qn, qp, wuk, wuv = queries(B, H, 40 + step)
+        o1 = flat.decode_step(0, c.contiguous(), k.contiguous(), qn, qp, wuk, wuv, TAU, rope=rope)
+        o2 = paged.decode_step(0, c.contiguous(), k.contiguous(), qn, qp, wuk, wuv, TAU, rope=rope)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2), step
+        assert torch.equal(flat.seq_lens, paged.seq_lens)
+    for b in range(B):
+        pf, pp = flat.planes(0, b), paged.planes(0, b)
+        for key in pf:
+            assert torch.equal(pf[key], pp[key]), (b, key)
+
+
+def test_table_entries_past_the_length_are_never_used():
+    fmt, lens, cap, ps, H = "int8", [40, 100], 256, 64, 16
+    B, blocks = 2, cap // ps
+    table = torch.tensor([[3, 7, 0, 0], [5, 1, 6, 2]], dtype=torch.int32)
+    bad = table.clone()
+    bad[0, 1:] = torch.tensor([-1, 10 ** 6, -5], dtype=torch.int32)  # sequence 0 uses block 0 only
+    bad[1, 2:] = torch.tensor([-3, 99999], dtype=torch.int32)        # sequence 1 uses blocks 0, 1
+    good = LatentCache(fmt, 1, B, cap, page_size=ps, num_pages=8, block_table=table)
+    odd = LatentCache(fmt, 1, B, cap, page_size=ps, num_pages=8, block_table=bad)
+    fill(good, lens, 31, fmt)
+    fill(odd, lens, 31, fmt)
+    qn, qp, wuk, wuv = queries(B, H, 32)
+    o1 = good.decode(0, qn, qp, wuk, wuv, TAU, num_splits=2)
+    o2 = odd.decode(0, qn, qp, wuk, wuv, TAU, num_splits=2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
