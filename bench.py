@@ -54,7 +54,7 @@ def row_bytes(fmt):
 class Runner:
     """Holds one workload's cache, weights, queries and the ctypes calls of a step."""
 
-    def __init__(self, wid, extra_steps, fmt=None, layers=None):
+    def __init__(self, wid, extra_steps, fmt=None, layers=None, page_size=0):
         import dataclasses
         import torch
         from mla_latent_kv_cache_amd import LatentCache, _lib
@@ -67,6 +67,8 @@ class Runner:
             fmt, layers = fmt or w.fmt, layers or w.layers
             shape = w.name.split("_", 2)[2]  # e.g. b64_h16_ragged1024-16384
             w = dataclasses.replace(w, fmt=fmt, layers=layers, name=f"{fmt}_l{layers}_{shape}")
+        if page_size:
+            w = dataclasses.replace(w, name=f"{w.name}_paged{page_size}")
         self.w = w
         self.lens0 = W.lengths(wid)
         ragged = isinstance(w.seq, tuple)
@@ -74,7 +76,16 @@ class Runner:
         cap = (cap + 15) // 16 * 16
         dev = torch.device("cuda:0")
         t0 = time.time()
-        self.cache = cache = LatentCache(w.fmt, w.layers, w.batch, cap, device=dev)
+        if page_size:
+            # pages of page_size tokens, handed to the sequences in a shuffled order
+            cap = (cap + page_size - 1) // page_size * page_size
+            blocks = cap // page_size
+            perm = np.random.default_rng(7).permutation(w.batch * blocks)
+            table = perm.reshape(w.batch, blocks).astype(np.int32)
+            self.cache = cache = LatentCache(w.fmt, w.layers, w.batch, cap, device=dev, page_size=page_size,
+                                             num_pages=w.batch * blocks, block_table=table)
+        else:
+            self.cache = cache = LatentCache(w.fmt, w.layers, w.batch, cap, device=dev)
         for layer in range(w.layers):
             ckv, kpe = W.latent_batch(wid, layer, int(self.lens0.max()), device=dev,
                                       counts=self.lens0 if ragged else None)
@@ -161,9 +172,9 @@ class Runner:
         return cache + weights + queries + output + append
 
 
-def measure(wid, steps, warmup, fmt=None, layers=None):
+def measure(wid, steps, warmup, fmt=None, layers=None, page_size=0):
     import torch
-    r = Runner(wid, steps + warmup, fmt, layers)
+    r = Runner(wid, steps + warmup, fmt, layers, page_size)
     for _ in range(warmup):
         r.step()
     torch.cuda.synchronize()
@@ -191,7 +202,7 @@ def measure(wid, steps, warmup, fmt=None, layers=None):
     avg_bytes = float(np.mean(part_bytes))
     res = {
         "workload": r.w.name, "fmt": r.w.fmt, "layers": r.w.layers, "batch": r.w.batch,
-        "heads": r.w.heads, "num_splits": r.ns, "ms_per_step": ms / steps,
+        "heads": r.w.heads, "num_splits": r.ns, "steps": steps, "warmup": warmup, "ms_per_step": ms / steps,
         "kv_tokens_per_step": kv / steps, "value": kv / (ms / 1e3),
         "gb_per_s": algo / (ms / 1e3) / 1e9,
         "partial_avg_us": avg_ms * 1e3, "partial_bytes_per_launch": avg_bytes,
@@ -329,7 +340,7 @@ def _pmc_means(csv_path, counter):
     return out
 
 
-def summarize_stats(wid, stats_csv, out_path):
+def summarize_stats(wid, stats_csv, out_path, steps, warmup):
     """Write the profiles/ table of this library's kernels from a rocprofv3
     --kernel-trace --stats run of this script (its run_kernel_stats.csv)."""
     import csv
@@ -348,12 +359,13 @@ def summarize_stats(wid, stats_csv, out_path):
                          float(r["MaxNs"]) / 1e3, float(r["TotalDurationNs"]) / 1e6))
     rows.sort(key=lambda x: -x[5])
     cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- python3 bench.py "
-           f"--steps 3 --warmup 1 --cpu-seconds 0 --int4-workload -1 --no-formats --workload {wid}")
+           f"--steps {steps} --warmup {warmup} --cpu-seconds 0 --int4-workload -1 --no-formats --workload {wid}")
     lines = [
-        f"# rocprofv3 kernel statistics, {w.name}: 1 warmup + 3 timed decode steps (every layer)",
+        f"# rocprofv3 kernel statistics, {w.name}: {warmup} warmup + {steps} timed decode steps (every layer)",
         "# Commands (repository root, one MI355X):",
         f"#   {cmd}",
-        f"#   python3 bench.py --summarize-stats <dir>/run_kernel_stats.csv --workload {wid}",
+        f"#   python3 bench.py --summarize-stats <dir>/run_kernel_stats.csv --workload {wid} "
+        f"--steps {steps} --warmup {warmup}",
         "# Rows: this library's kernels (the torch kernels that build the synthetic inputs are omitted).",
         "# append_kernel<f> is the one-off prefill. A decode step runs, per layer, step_kernel<f>",
         "# (mla_decode_step_begin: store the new token with its k_pe turned, absorb the turned query),",
@@ -416,7 +428,7 @@ def main():
     ap.add_argument("--int4-workload", type=int, default=2, help="-1 to skip")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="0 to skip the CPU baseline")
     ap.add_argument("--no-formats", action="store_true",
-                    help="skip the one-layer runs of the INT8_KBF16 and INT4_KINT4 cache formats")
+                    help="skip the one-layer runs of the INT8_KBF16 and INT4_KINT4 formats and the paged layout")
     ap.add_argument("--pmc-run", action="store_true",
                     help="only issue the launches that the HBM counter summary is taken from")
     ap.add_argument("--summarize-stats", metavar="STATS_CSV",
@@ -428,7 +440,7 @@ def main():
         from mla_latent_kv_cache_amd import workloads as W
         name = W.WORKLOADS[args.workload].name
         summarize_stats(args.workload, args.summarize_stats,
-                        os.path.join(ROOT, "profiles", f"kernel_stats_{name}.txt"))
+                        os.path.join(ROOT, "profiles", f"kernel_stats_{name}.txt"), args.steps, args.warmup)
         return
     if args.summarize_pmc:
         from mla_latent_kv_cache_amd import workloads as W
@@ -450,11 +462,19 @@ def main():
         return
 
     main_res = measure(args.workload, args.steps, args.warmup)
+    # The one-layer runs below issue one partial launch per step where the
+    # main run issues one per layer: they take that many times the steps and
+    # warmup steps, so that they warm up and time as many launches. (With
+    # the main run's step counts they time a few milliseconds just after a
+    # new cache is filled, some 15% below their steady rate.)
+    per_layer = W.WORKLOADS[args.workload].layers
+    sub_steps, sub_warmup = args.steps * per_layer, args.warmup * per_layer
+    keys = ("workload", "value", "ms_per_step", "gb_per_s", "hbm_frac", "kv_tokens_per_step", "num_splits",
+            "steps", "warmup")
     int4 = None
     if args.int4_workload >= 0:
-        r4 = measure(args.int4_workload, args.steps, args.warmup)
-        int4 = {k: r4[k] for k in ("workload", "value", "ms_per_step", "gb_per_s", "hbm_frac",
-                                   "kv_tokens_per_step", "num_splits")}
+        r4 = measure(args.int4_workload, sub_steps, sub_warmup)
+        int4 = {k: r4[k] for k in keys}
         int4["unit"] = "KV-tokens/s"
         int4["roofline"] = roofline(r4)
     formats = None
@@ -464,11 +484,15 @@ def main():
         # k_pe on the INT4 workload
         formats = {}
         for fmt, wid in (("int8_kbf16", args.workload), ("int4_kint4", max(args.int4_workload, 0))):
-            rf = measure(wid, args.steps, args.warmup, fmt=fmt, layers=1)
-            formats[fmt] = {k: rf[k] for k in ("workload", "value", "ms_per_step", "gb_per_s", "hbm_frac",
-                                               "kv_tokens_per_step", "num_splits")}
+            rf = measure(wid, sub_steps, sub_warmup, fmt=fmt, layers=1)
+            formats[fmt] = {k: rf[k] for k in keys}
             formats[fmt]["unit"] = "KV-tokens/s"
             formats[fmt]["roofline"] = roofline(rf)
+        # the paged layout: one layer of the ragged INT8 inputs in 64-token pages, shuffled
+        rp = measure(args.workload, sub_steps, sub_warmup, layers=1, page_size=64)
+        formats["int8_paged64"] = {k: rp[k] for k in keys}
+        formats["int8_paged64"]["unit"] = "KV-tokens/s"
+        formats["int8_paged64"]["roofline"] = roofline(rp)
     cpu = None
     if args.cpu_seconds > 0:
         log("timing the oracle on the host cores")

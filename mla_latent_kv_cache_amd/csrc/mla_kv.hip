@@ -1578,18 +1578,30 @@ void split16_kernel(SplitArgs a) {
   const Off16<FMT> off = offsets16<FMT>(w, lane);
   const bool zero_b = off.b_zero;  // uniform: depends on the wave only
   Raw16<FMT> raw[kNpf16];
-  // Paged layout: each tile's descriptors come from its page, whose index is
-  // read from the block table one tile ahead of the loads that use it.
+  // Paged layout: each tile's descriptors come from its page. The page index
+  // is read from the sequence's block-table row one tile ahead, with a buffer
+  // (vector) load: a scalar load would share its wait counter with LDS
+  // traffic, and every LDS wait of the tile would then wait for it too.
   const bool paged = a.pg.size != 0;
+  const __amdgpu_buffer_rsrc_t trow =
+      make_rsrc(paged ? (const void *)(a.pg.table + (int64_t)b * a.pg.max_pages) : a.kpe,
+                paged ? a.pg.max_pages * 4 : 0);
+  auto page_entry = [&](int r) {  // raw table entry of token r (any lane; reads 0 past the row)
+    return __builtin_amdgcn_raw_buffer_load_b32(trow, (r >> a.pg.shift) * 4, 0, 0);
+  };
+  auto checked = [&](uint32_t entry, int r) {  // the page of token r, or -1
+    const int pg = (int)__builtin_amdgcn_readfirstlane(entry);
+    return (r < t_end && pg >= 0 && pg < a.pg.num_pages) ? pg : -1;
+  };
   auto rsrc_of = [&](int r0, int page) {
     return paged ? page_rsrc<FMT>(a, page, r0, t_end) : tile_rsrc<FMT>(a, b, r0, t_end);
   };
 #pragma unroll
   for (int p = 0; p < kNpf16; ++p) {
     const int r0 = t_begin + p * kT16;
-    load16<FMT>(raw[p], rsrc_of(r0, paged ? tile_page(a, b, r0, t_end) : 0), off, zero_b);
+    load16<FMT>(raw[p], rsrc_of(r0, paged ? checked(page_entry(r0), r0) : 0), off, zero_b);
   }
-  int next_page = paged ? tile_page(a, b, t_begin + kNpf16 * kT16, t_end) : 0;
+  uint32_t next_entry = paged ? page_entry(t_begin + kNpf16 * kT16) : 0u;
 
   for (int it0 = 0; it0 < ntiles; it0 += kNpf16) {
 #pragma unroll
@@ -1647,8 +1659,8 @@ void split16_kernel(SplitArgs a) {
     // path.
     __builtin_amdgcn_sched_barrier(0);
     const int r_next = t_begin + (it + kNpf16) * kT16;
-    load16<FMT>(raw[p], rsrc_of(r_next, next_page), off, zero_b);
-    if (paged) next_page = tile_page(a, b, r_next + kT16, t_end);
+    load16<FMT>(raw[p], rsrc_of(r_next, paged ? checked(next_entry, r_next) : 0), off, zero_b);
+    if (paged) next_entry = page_entry(r_next + kT16);
 
     // ---- 4. partial scores of the four waves
     // [wave][half][lane][4]: consecutive lanes use consecutive 16 bytes
