@@ -247,10 +247,12 @@ def roofline(res):
 
 def cpu_baseline(wid, seconds):
     """The oracle as it stands, on the host cores, over a bounded sample of the
-    workload: whole sequences of layer 0, one fused decode step each (dequantize
+    workload: the sequences of layer 0, one fused decode step each (dequantize
     the cache rows; turn, quantize and append the new token; absorbed decode
-    with the turned query in float64)."""
-    import torch
+    with the turned query in float64), in passes over the layer until about
+    `seconds` of oracle time. Building the synthetic rows and quantizing the
+    cached prefix is done once and not timed: on the GPU that cache is
+    resident before the timed region."""
     from mla_latent_kv_cache_amd import workloads as W
     from oracle import quant as Q
     from oracle import rope as R
@@ -259,21 +261,25 @@ def cpu_baseline(wid, seconds):
     cos, sin = R.rope_tables(int(lens.max()) + 1)
     wuk, wuv = (t.float().numpy() for t in W.weights(wid, 0, "cpu"))
     qn, qp = (t.float().numpy() for t in W.queries(wid, 0, "cpu"))
-    tokens, elapsed, seqs = 0, 0.0, 0
-    b = 0
-    while elapsed < seconds and b < w.batch:
+    prepared = []
+    for b in range(w.batch):
         c, k = W.latent_rows(wid, 0, b, int(lens[b]), "cpu")
-        planes = Q.quantize_rows(c.float().numpy(), k.float().numpy(), w.fmt)
         nc, nk = W.latent_rows(wid, 0, b, 1, "cpu", kind="step")
-        nc, nk = nc.float().numpy(), nk.float().numpy()
-        t0 = time.perf_counter()
-        ch, kh = Q.dequantize_rows(planes, w.fmt)
-        R.decode_step(ch, kh, int(lens[b]), int(lens[b]) + 1, nc[0], nk[0], qn[b], qp[b], wuk, wuv,
-                      W.SOFTMAX_SCALE, w.fmt, cos, sin)
-        elapsed += time.perf_counter() - t0
-        tokens += int(lens[b]) + 1
-        seqs += 1
-        b += 1
+        prepared.append((Q.quantize_rows(c.float().numpy(), k.float().numpy(), w.fmt),
+                         nc.float().numpy()[0], nk.float().numpy()[0]))
+    tokens, elapsed, seqs, passes = 0, 0.0, 0, 0
+    while elapsed < seconds:
+        passes += 1
+        for b, (planes, nc, nk) in enumerate(prepared):
+            if elapsed >= seconds:
+                break
+            t0 = time.perf_counter()
+            ch, kh = Q.dequantize_rows(planes, w.fmt)
+            R.decode_step(ch, kh, int(lens[b]), int(lens[b]) + 1, nc, nk, qn[b], qp[b], wuk, wuv,
+                          W.SOFTMAX_SCALE, w.fmt, cos, sin)
+            elapsed += time.perf_counter() - t0
+            tokens += int(lens[b]) + 1
+            seqs += 1
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
@@ -283,10 +289,10 @@ def cpu_baseline(wid, seconds):
     return {
         "value": tokens / elapsed, "unit": "KV-tokens/s",
         "cores": threads if threads else cores, "kind": "oracle",
-        "sample": f"{seqs} sequences of layer 0 of {w.name} ({tokens} KV tokens), one fused decode "
-                  f"step each: oracle RoPE, quantize and append of the new token, fp64 dequantize "
-                  f"and absorbed decode; "
-                  f"{elapsed:.1f}s on {cores} host cores visible, BLAS threads {threads}",
+        "sample": f"{seqs} sequence-steps in {passes} pass(es) over the {w.batch} sequences of layer 0 of "
+                  f"{w.name} ({tokens} KV tokens), one fused decode step each: oracle RoPE, quantize and "
+                  f"append of the new token, fp64 dequantize and absorbed decode; {elapsed:.1f}s of oracle "
+                  f"time on {cores} host cores visible, BLAS threads {threads}",
     }
 
 
@@ -426,7 +432,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=3, help="index into workloads.WORKLOADS")
     ap.add_argument("--int4-workload", type=int, default=2, help="-1 to skip")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="0 to skip the CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="0 to skip the CPU baseline")
     ap.add_argument("--no-formats", action="store_true",
                     help="skip the one-layer runs of the INT8_KBF16 and INT4_KINT4 formats and the paged layout")
     ap.add_argument("--pmc-run", action="store_true",

@@ -10,7 +10,7 @@ import torch
 from mla_latent_kv_cache_amd import LatentCache
 from oracle import rope as R
 
-from gpu_util import oracle_decode, assert_close, f32, random_rows
+from gpu_util import assert_close, assert_planes_equal, f32, oracle_decode, oracle_planes, random_rows
 
 pytestmark = pytest.mark.gpu
 TAU = 1.0 / np.sqrt(192.0)
@@ -73,6 +73,8 @@ def test_paged_equals_contiguous(fmt, heads):
         pf, pp = flat.planes(0, b), paged.planes(0, b)
         for k in pf:
             assert torch.equal(pf[k], pp[k]), (b, k)
+        if lens[b]:
+            assert_planes_equal(pp, oracle_planes(rows[b][0], rows[b][1], fmt), fmt, f"paged seq {b}")
         assert_close(f32(o_paged[b]), oracle_decode(rows[b][0], rows[b][1], fmt, qn[b], qp[b], wuk, wuv, TAU),
                      f"{fmt} paged seq {b}")
     gf, gp = flat.get(0), paged.get(0)

@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+from mla_latent_kv_cache_amd import LatentCache
 from mla_latent_kv_cache_amd import workloads as W
 
 from gpu_util import (assert_close, assert_planes_equal, build_workload, f32, oracle_decode,
@@ -127,3 +128,28 @@ def test_workload4_int4_wide_heads_64_splits_sampled():
     torch.cuda.synchronize()
     assert torch.isfinite(out).all()
     check_sequences(wid, cache, 0, (0, 11), out, qn, qp, wuk, wuv)
+
+
+def test_workload3_int8_one_layer_paged64_sampled():
+    """One layer of the ragged INT8 inputs in 64-token pages handed out in a
+    shuffled order (the benchmark's paged run): sampled codes bit-exact through
+    the block table, sampled outputs against the oracle."""
+    wid, ps = 3, 64
+    w = W.WORKLOADS[wid]
+    lens = W.lengths(wid)
+    cap = (W.capacity(wid) + ps - 1) // ps * ps
+    blocks = cap // ps
+    table = np.random.default_rng(7).permutation(w.batch * blocks).reshape(w.batch, blocks).astype(np.int32)
+    cache = LatentCache(w.fmt, 1, w.batch, cap, device="cuda", page_size=ps, num_pages=w.batch * blocks,
+                        block_table=table)
+    ckv, kpe = W.latent_batch(wid, 0, int(lens.max()), device="cuda", counts=lens)
+    cache.append(0, ckv, kpe, n_new=lens)
+    del ckv, kpe
+    qn, qp = W.queries(wid, 0, "cuda")
+    wuk, wuv = W.weights(wid, 0, "cuda")
+    out = cache.decode(0, qn, qp, wuk, wuv, W.SOFTMAX_SCALE, num_splits=w.num_splits)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    longest, shortest = int(np.argmax(lens)), int(np.argmin(lens))
+    check_codes(wid, cache, 0, longest, nrows=700)
+    check_sequences(wid, cache, 0, (0, longest, shortest), out, qn, qp, wuk, wuv)
