@@ -65,9 +65,15 @@ typedef enum {
 /*
  * The cache of all layers of one model, for a batch of sequences.
  *
- * Planes, each [num_layers][batch][capacity][row] with the row sizes:
+ * Planes, each [num_layers][batch][capacity][row] (ckv: see below) with the
+ * row sizes:
  *   ckv     BF16: 512 x bf16 (1024 B)   INT8, INT8_KBF16: 512 x int8 (512 B)
  *           INT4, INT4_KINT4: 256 x uint8 (256 B), byte k = code[2k] | code[2k+1] << 4
+ *           The ckv plane is [num_layers][batch][cap16][row], cap16 = capacity
+ *           rounded up to a multiple of 16, and stores each sequence's rows in
+ *           blocks of 16: in the block of rows 16m..16m+15, the 16-byte chunk c
+ *           of row 16m+i (its bytes 16c..16c+15) lies at byte (16c + i) * 16
+ *           of the block. The rows never stored may hold anything.
  *   kpe     BF16, INT8_KBF16: 64 x bf16 (128 B)     INT8, INT4: 64 x int8 (64 B)
  *           INT4_KINT4: 32 x uint8 (32 B), byte k = (code[2k] + 8) | (code[2k+1] + 8) << 4
  *   scale   INT8, INT4, INT4_KINT4: 40 x fp16 (80 B): the 32 latent-group
@@ -104,8 +110,9 @@ typedef struct mla_cache {
   int32_t *seq_lens;
   /* Paged layout (page_size > 0; "DeepSeek的MLA技术", limits and future
    * directions, item 3: MLA together with PagedAttention): each plane is a pool
-   * [num_layers][num_pages][page_size][row], and token p of sequence b lives at
-   * row p % page_size of page block_table[b][p / page_size] in every layer.
+   * [num_layers][num_pages][page_size][row] (the ckv pages in 16-row blocks as
+   * above), and token p of sequence b lives at row p % page_size of page
+   * block_table[b][p / page_size] in every layer.
    * page_size: a power of two >= 32 dividing capacity; num_pages >= 1;
    * block_table: device int32 [batch][capacity / page_size]. A page index
    * outside [0, num_pages) reads as an empty page and is never written.

@@ -41,6 +41,17 @@ def rope_tables(rows, base=10000.0, device="cuda"):
             torch.sin(ang).to(torch.float32).to(device).contiguous())
 
 
+def _unblock(t):
+    """Latent rows in logical order from the block layout: t [..., R, row]
+    (R a multiple of 16) holds, in each 16 rows, chunk c of row i at byte
+    (16 c + i) * 16 of the block."""
+    shape = t.shape
+    row_bytes = shape[-1] * t.element_size()
+    u = t.contiguous().view(torch.uint8).reshape(tuple(shape[:-2]) + (shape[-2] // 16, row_bytes // 16, 16, 16))
+    u = u.transpose(-3, -2).contiguous()  # [.., blocks, row i, chunk c, 16 B]
+    return u.reshape(tuple(shape[:-2]) + (shape[-2], row_bytes)).view(t.dtype).reshape(shape)
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
@@ -67,8 +78,11 @@ def _need(t, name, dtype, shape, device):
 class LatentCache:
     """Per-layer latent cache planes for `batch` sequences of up to `capacity` tokens.
 
-    Layout (see include/mla_kv.h): ckv, kpe, scale, zero are
-    [num_layers, batch, capacity, row] tensors; seq_lens is int32 [num_layers, batch].
+    Layout (see include/mla_kv.h): kpe, scale, zero are [num_layers, batch,
+    capacity, row] tensors; ckv is [num_layers, batch, capacity rounded up to
+    16, row] with each 16 rows stored as blocks of 16-byte chunks (chunk c of
+    row i at byte (16 c + i) * 16 of the block; `planes` undoes this);
+    seq_lens is int32 [num_layers, batch].
     A host mirror of the lengths guards capacity before each append.
     """
 
@@ -98,15 +112,17 @@ class LatentCache:
         else:
             self.num_pages = 0
             shape = (self.num_layers, self.batch, self.capacity)
+        # latent rows in whole 16-row blocks per sequence (pages hold whole blocks)
+        lshape = shape if self.page_size else (self.num_layers, self.batch, (self.capacity + 15) // 16 * 16)
         kw = dict(device=self.device)
         lat = {"bf16": "bf16", "int8": "int8", "int4": "int4", "int8_kbf16": "int8", "int4_kint4": "int4"}[fmt]
         kp = {"bf16": "bf16", "int8_kbf16": "bf16", "int4_kint4": "int4"}.get(fmt, "int8")
         if lat == "bf16":
-            self.ckv = torch.empty(shape + (LATENT,), dtype=torch.bfloat16, **kw)
+            self.ckv = torch.empty(lshape + (LATENT,), dtype=torch.bfloat16, **kw)
         elif lat == "int8":
-            self.ckv = torch.empty(shape + (LATENT,), dtype=torch.int8, **kw)
+            self.ckv = torch.empty(lshape + (LATENT,), dtype=torch.int8, **kw)
         else:
-            self.ckv = torch.empty(shape + (LATENT // 2,), dtype=torch.uint8, **kw)
+            self.ckv = torch.empty(lshape + (LATENT // 2,), dtype=torch.uint8, **kw)
         if kp == "bf16":
             self.kpe = torch.empty(shape + (ROPE,), dtype=torch.bfloat16, **kw)
         elif kp == "int8":
@@ -302,9 +318,12 @@ class LatentCache:
             if t is None:
                 continue
             if self.page_size:
-                pos = torch.arange(n, device=self.device)
-                pages = self.block_table[b].long()[pos // self.page_size]
-                out[key] = t[layer, pages, pos % self.page_size].cpu()
+                used = self.block_table[b].long()[: (n + self.page_size - 1) // self.page_size]
+                rows = t[layer, used]  # [pages, page_size, row]
+                if key == "ckv":
+                    rows = _unblock(rows)
+                out[key] = rows.reshape((-1,) + tuple(t.shape[3:]))[:n].cpu()
             else:
-                out[key] = t[layer, b, :n].cpu()
+                rows = t[layer, b]
+                out[key] = (_unblock(rows[None])[0] if key == "ckv" else rows)[:n].cpu()
         return out

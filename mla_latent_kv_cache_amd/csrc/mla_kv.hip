@@ -197,6 +197,26 @@ __device__ __forceinline__ int64_t plane_row(const Paging &pg, int b, int cap, i
   return page < 0 ? -1 : ((int64_t)page << pg.shift) + (p & (pg.size - 1));
 }
 
+// The latent plane keeps its rows in blocks of 16: within a block, the
+// 16-byte chunk c of row i lies at byte (16 c + i) * 16, so chunk c of the
+// block's 16 rows is 256 contiguous bytes, and a 64-lane load of chunks
+// c..c+3 of a block (lane 16 g + i: chunk c + g of row i, the operand layout
+// of the matrix instructions) reads 1 KB in one piece. Each sequence's rows
+// start on a block: in the contiguous layout its latent rows are
+// lat_stride(capacity) apart (capacity rounded up to 16); a page holds whole
+// blocks. The other planes keep plain rows.
+__host__ __device__ constexpr int lat_stride(int cap) { return (cap + 15) & ~15; }
+
+// Byte offset of chunk c of row `row` (rows counted from a block start).
+__device__ __forceinline__ int64_t lat_off(int64_t row, int c, int row_bytes) {
+  return (row >> 4) * (int64_t)(16 * row_bytes) + (int64_t)(c * 16 + (int)(row & 15)) * 16;
+}
+
+// Latent row of a token whose row in the other planes is `row` (from plane_row).
+__device__ __forceinline__ int64_t lat_row_of(const Paging &pg, int64_t row, int b, int cap, int p) {
+  return pg.size ? row : (int64_t)b * lat_stride(cap) + p;
+}
+
 struct AppendArgs {
   void *ckv;            // layer base of the ckv plane
   void *kpe;
@@ -235,13 +255,13 @@ __device__ __forceinline__ void append_group(const AppendArgs &a, int b, int t, 
   const int64_t row = plane_row(a.pg, b, a.cap, pos);
   if (row < 0) return;  // no page for this position: nothing is stored
   if (grp < kNGroupL) {
+    const int64_t lrow = lat_row_of(a.pg, row, b, a.cap, pos);
     const uint16_t *src = a.ckv_new + ((int64_t)b * a.T + t) * kLatent + grp * kGroupL;
     const u32x4 v0 = *(const u32x4 *)src;
     const u32x4 v1 = *(const u32x4 *)(src + 8);
-    if (lat_fmt(FMT) == MLA_FMT_BF16) {
-      u32x4 *dst = (u32x4 *)((uint16_t *)a.ckv + row * kLatent + grp * kGroupL);
-      dst[0] = v0;
-      dst[1] = v1;
+    if (lat_fmt(FMT) == MLA_FMT_BF16) {  // 16 channels: chunks 2 grp and 2 grp + 1
+      *(u32x4 *)((uint8_t *)a.ckv + lat_off(lrow, 2 * grp, kLatent * 2)) = v0;
+      *(u32x4 *)((uint8_t *)a.ckv + lat_off(lrow, 2 * grp + 1, kLatent * 2)) = v1;
       return;
     }
     float x[kGroupL];
@@ -260,7 +280,7 @@ __device__ __forceinline__ void append_group(const AppendArgs &a, int b, int t, 
       for (int i = 0; i < 4; ++i)
         w[i] = (uint32_t)(uint8_t)q[4 * i] | ((uint32_t)(uint8_t)q[4 * i + 1] << 8) |
                ((uint32_t)(uint8_t)q[4 * i + 2] << 16) | ((uint32_t)(uint8_t)q[4 * i + 3] << 24);
-      *(u32x4 *)((int8_t *)a.ckv + row * kLatent + grp * kGroupL) = w;
+      *(u32x4 *)((uint8_t *)a.ckv + lat_off(lrow, grp, kLatent)) = w;  // chunk grp
       a.scale[row * n_scales(FMT) + grp] = sb;
     } else {
       uint8_t q[kGroupL];
@@ -274,7 +294,8 @@ __device__ __forceinline__ void append_group(const AppendArgs &a, int b, int t, 
         for (int j = 0; j < 8; ++j) v |= (uint32_t)q[8 * i + j] << (4 * j);
         w[i] = v;
       }
-      *(u32x2 *)((uint8_t *)a.ckv + row * (kLatent / 2) + grp * (kGroupL / 2)) = w;
+      // the first or second half of chunk grp / 2
+      *(u32x2 *)((uint8_t *)a.ckv + lat_off(lrow, grp >> 1, kLatent / 2) + (grp & 1) * 8) = w;
       a.scale[row * n_scales(FMT) + grp] = sb;
       a.zero[row * kNGroupL + grp] = zb;
     }
@@ -590,15 +611,11 @@ template <int FMT> struct Fmt {
   static constexpr int kKpe = (kKpeChunks + 63) / 64;           // per lane; INT4 k_pe: lanes 0..31 only
 };
 
-// Chunk k of lane l: which tile row it belongs to and where its channels start.
-template <int FMT> __device__ __forceinline__ int lat_row(int lane, int k) {
-  constexpr int per_row = Fmt<FMT>::kLatRowBytes / 16;  // chunks per row
-  return (lane + 64 * k) / per_row;
-}
-template <int FMT> __device__ __forceinline__ int lat_chunk(int lane) {
-  constexpr int per_row = Fmt<FMT>::kLatRowBytes / 16;
-  return lane % per_row;  // (lane + 64k) % per_row == lane % per_row, per_row | 64
-}
+// Latent chunk k of lane l in a 16-row tile (one block of the latent plane):
+// the tile's bytes in order, 16 per lane, so chunk k of lane l is row l % 16,
+// chunk l / 16 + 4 k (the block stores chunk c of row i at (16 c + i) * 16).
+template <int FMT> __device__ __forceinline__ int lat_row(int lane, int k) { return lane & 15; }
+template <int FMT> __device__ __forceinline__ int lat_chunk(int lane, int k) { return (lane >> 4) + 4 * k; }
 template <int FMT> __device__ __forceinline__ int kpe_row(int lane, int k) {
   constexpr int per_row = Fmt<FMT>::kKpeRowBytes / 16;
   return (lane + 64 * k) / per_row;
@@ -644,10 +661,15 @@ constexpr int kRankMaxB = 256;
 static_assert(kThreads >= kRankMaxB, "one thread per ranked sequence");
 
 // Call with every thread of a 256-thread workgroup (it holds barriers).
-// Returns the sequence of this workgroup's grid row, uniform across it.
-__device__ __forceinline__ int seq_of_row(const int *seq_lens, int B, int cap, int *lens_sh, int *sel) {
+// Returns the sequence of this workgroup's grid row, uniform across it, and in
+// L its length clamped to [0, cap] (from the copy in LDS: a second read from
+// global memory would add one more round trip before the first tile's loads).
+__device__ __forceinline__ int seq_of_row(const int *seq_lens, int B, int cap, int *lens_sh, int *sel, int &L) {
   const int row = blockIdx.y;
-  if (B > kRankMaxB) return row;
+  if (B > kRankMaxB) {
+    L = min(max(seq_lens[row], 0), cap);
+    return row;
+  }
   const int tid = threadIdx.x;
   if (tid < B) lens_sh[tid] = min(max(seq_lens[tid], 0), cap);
   __syncthreads();
@@ -661,7 +683,9 @@ __device__ __forceinline__ int seq_of_row(const int *seq_lens, int B, int cap, i
     if (r == row) *sel = tid;  // ranks are a permutation: exactly one thread writes
   }
   __syncthreads();
-  return __builtin_amdgcn_readfirstlane(*sel);
+  const int b = __builtin_amdgcn_readfirstlane(*sel);
+  L = __builtin_amdgcn_readfirstlane(lens_sh[b]);
+  return b;
 }
 
 // Tokens per split of a sequence of length L: ceil(L / nsplit) rounded up to a
@@ -678,6 +702,7 @@ __device__ __forceinline__ int split_chunk(int L, int nsplit, int min_chunk) {
 // exactly instead of draining the queue before each use).
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9 buffer resource dword 3
 constexpr int kOffNone = 0x7FFFFFF0;        // an offset past any descriptor
+constexpr int kLatLoadPolicy = 2;           // buffer-load cache policy operand: nt (non-temporal)
 
 struct SplitRsrc {
   __amdgpu_buffer_rsrc_t ckv, kpe, scale, zero;
@@ -687,11 +712,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, (int)kRsrcWord3);
 }
 
-// Descriptors over n plane rows starting at row0 (n = 0: empty, every load reads zeros).
+// Descriptors over n plane rows starting at row0, latent row lrow0 (a block
+// start; n = 0: empty, every load reads zeros). The latent descriptor covers
+// whole 16-row blocks: rows past n in the last block are read too, and the
+// kernels neutralize them (zero scales, or zeroed registers for bf16).
 template <int FMT>
-__device__ __forceinline__ SplitRsrc rows_rsrc(const SplitArgs &a, int64_t row0, int64_t n) {
+__device__ __forceinline__ SplitRsrc rows_rsrc(const SplitArgs &a, int64_t row0, int64_t lrow0, int64_t n) {
   SplitRsrc r;
-  r.ckv = make_rsrc((const uint8_t *)a.ckv + row0 * Fmt<FMT>::kLatRowBytes, n * Fmt<FMT>::kLatRowBytes);
+  r.ckv = make_rsrc((const uint8_t *)a.ckv + lrow0 * Fmt<FMT>::kLatRowBytes,
+                    ((n + 15) & ~(int64_t)15) * Fmt<FMT>::kLatRowBytes);
   r.kpe = make_rsrc((const uint8_t *)a.kpe + row0 * Fmt<FMT>::kKpeRowBytes, n * Fmt<FMT>::kKpeRowBytes);
   constexpr int NS = n_scales(FMT);
   r.scale = make_rsrc(NS == 0 ? a.kpe : (const void *)(a.scale + row0 * NS), n * NS * 2);
@@ -703,17 +732,19 @@ __device__ __forceinline__ SplitRsrc rows_rsrc(const SplitArgs &a, int64_t row0,
 // Rows [t_begin, t_end) of sequence b in the contiguous layout.
 template <int FMT>
 __device__ __forceinline__ SplitRsrc split_rsrc(const SplitArgs &a, int b, int t_begin, int t_end) {
-  return rows_rsrc<FMT>(a, (int64_t)b * a.cap + t_begin, t_end - t_begin);
+  return rows_rsrc<FMT>(a, (int64_t)b * a.cap + t_begin, (int64_t)b * lat_stride(a.cap) + t_begin,
+                        t_end - t_begin);
 }
 
 // Paged layout: rows [r0, t_end) of a sequence, cut at the end of r0's page
 // (`page`, from page_of; -1 or r0 >= t_end: empty).
 template <int FMT>
 __device__ __forceinline__ SplitRsrc page_rsrc(const SplitArgs &a, int page, int r0, int t_end) {
-  if (page < 0 || r0 >= t_end) return rows_rsrc<FMT>(a, 0, 0);
+  if (page < 0 || r0 >= t_end) return rows_rsrc<FMT>(a, 0, 0, 0);
   const int off = r0 & (a.pg.size - 1);
   const int end = min(t_end, r0 - off + a.pg.size);
-  return rows_rsrc<FMT>(a, ((int64_t)page << a.pg.shift) + off, end - r0);
+  const int64_t row0 = ((int64_t)page << a.pg.shift) + off;
+  return rows_rsrc<FMT>(a, row0, row0, end - r0);
 }
 
 // The page of token r of sequence b for page_rsrc (-1 past t_end).
@@ -722,16 +753,23 @@ __device__ __forceinline__ int tile_page(const SplitArgs &a, int b, int r, int t
 }
 
 // Raw chunks of the tile whose first row is row `r0` of the split.
+// r0: the tile's first row in the descriptors (a block start). The latent
+// descriptor covers whole blocks, so rows from `left` on (past the split) are
+// read too: quantized rows there dequantize to zero (their scales and
+// zero-points read as zeros), bf16 rows are pointed past the descriptor.
 template <int FMT, int NW>
-__device__ __forceinline__ void load_raw(RawTile<FMT, NW> &r, const SplitRsrc &rs, int r0, int lane,
+__device__ __forceinline__ void load_raw(RawTile<FMT, NW> &r, const SplitRsrc &rs, int r0, int left, int lane,
                                          int hw) {
 #pragma unroll
   for (int j = 0; j < RawTile<FMT, NW>::kLat; ++j) {
     const int k = j * NW + hw;
-    const int row = r0 + lat_row<FMT>(lane, k);
-    const int ch = lat_chunk<FMT>(lane);
-    r.lat[j] = bitcast<u32x4>(
-        __builtin_amdgcn_raw_buffer_load_b128(rs.ckv, row * Fmt<FMT>::kLatRowBytes + ch * 16, 0, 0));
+    const int tr = lat_row<FMT>(lane, k);
+    const int row = r0 + tr;
+    const int ch = lat_chunk<FMT>(lane, k);
+    // lat_off(row, ch) with r0 a block start: the tile's bytes in lane order
+    const int loff = lat_fmt(FMT) != MLA_FMT_BF16 || tr < left ? r0 * Fmt<FMT>::kLatRowBytes + (lane + 64 * k) * 16
+                                                                 : kOffNone;
+    r.lat[j] = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rs.ckv, loff, 0, kLatLoadPolicy));
     constexpr int NS = n_scales(FMT);
     if (lat_fmt(FMT) == MLA_FMT_INT8) {
       r.lsc[j] = __builtin_amdgcn_raw_buffer_load_b16(rs.scale, row * NS * 2 + ch * 2, 0, 0);
@@ -811,7 +849,7 @@ __device__ __forceinline__ void dequant_store(const RawTile<FMT, NW> &r, _Float1
   for (int j = 0; j < RawTile<FMT, NW>::kLat; ++j) {
     const int k = j * NW + hw;
     const int tr = lat_row<FMT>(lane, k);
-    const int ch = lat_chunk<FMT>(lane);
+    const int ch = lat_chunk<FMT>(lane, k);
     const u32x4 v = r.lat[j];
     if (lat_fmt(FMT) == MLA_FMT_INT8) {
       const f16x2 s2 = splat_f16_bits(r.lsc[j]);
@@ -971,7 +1009,8 @@ void split_kernel(SplitArgs a) {
 
   const int split = blockIdx.x / a.hh_count;
   const int hh = blockIdx.x % a.hh_count;
-  const int b = seq_of_row(a.seq_lens, a.B, a.cap, rank_lens, &rank_sel);
+  int L;
+  const int b = seq_of_row(a.seq_lens, a.B, a.cap, rank_lens, &rank_sel, L);
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, li = lane & 15;
@@ -979,7 +1018,6 @@ void split_kernel(SplitArgs a) {
   const int head0 = (hh * HGW) * 16;              // first head of this workgroup
   const int head = head0 + hw * 16 + li;          // the head this lane's columns belong to
 
-  const int L = min(max(a.seq_lens[b], 0), a.cap);
   const int chunk = split_chunk(L, a.nsplit, a.min_chunk);
   const int t_begin = min(split * chunk, L);
   const int t_end = min(t_begin + chunk, L);
@@ -1018,13 +1056,13 @@ void split_kernel(SplitArgs a) {
   // contiguous: one descriptor over the split, tiles at row offsets; paged:
   // a descriptor per 16-token tile (a tile never crosses a page)
   const bool paged = a.pg.size != 0;
-  const SplitRsrc rs = paged ? rows_rsrc<FMT>(a, 0, 0) : split_rsrc<FMT>(a, b, t_begin, t_end);
+  const SplitRsrc rs = paged ? rows_rsrc<FMT>(a, 0, 0, 0) : split_rsrc<FMT>(a, b, t_begin, t_end);
   auto load_tile = [&](RawTile<FMT, HGW> &r, int tile) {
+    const int r0 = t_begin + tile * kTile;
     if (paged) {
-      const int r0 = t_begin + tile * kTile;
-      load_raw<FMT, HGW>(r, page_rsrc<FMT>(a, tile_page(a, b, r0, t_end), r0, t_end), 0, lane, hw);
+      load_raw<FMT, HGW>(r, page_rsrc<FMT>(a, tile_page(a, b, r0, t_end), r0, t_end), 0, t_end - r0, lane, hw);
     } else {
-      load_raw<FMT, HGW>(r, rs, tile * kTile, lane, hw);
+      load_raw<FMT, HGW>(r, rs, tile * kTile, t_end - r0, lane, hw);
     }
   };
   RawTile<FMT, HGW> raw[NPF];
@@ -1255,8 +1293,20 @@ struct Meta16 {
   u32x2 kq[2];
 };
 
+// The latent channels that lane group g of wave w holds in k-step kk (8
+// channels from the returned one on): each 16-byte load of a lane is one
+// latent chunk, and the 64 lanes of a load read 4 consecutive chunks of the
+// 16 rows of a block (1 KB in one piece). INT8: 16-channel chunks
+// 8w + 4j + g (j = kk / 2); INT4: the 32-channel chunk 4w + g (nibble order
+// within it); BF16: 8-channel chunks 16w + 4kk + g.
+template <int FMT> __device__ __forceinline__ constexpr int lane_chan(int w, int g, int kk) {
+  return lat_fmt(FMT) == MLA_FMT_INT8   ? 128 * w + 64 * (kk >> 1) + 16 * g + 8 * (kk & 1)
+         : lat_fmt(FMT) == MLA_FMT_INT4 ? 128 * w + 32 * g + 8 * kk
+                                        : 128 * w + 32 * kk + 8 * g;
+}
+
 // Byte offsets of this lane's data within a tile (the same for every tile).
-//   latent: rows i and 16+i, channels 128w+32g..+31
+//   latent: rows i and 16+i (blocks rb = 0, 1), the chunks of lane_chan
 //   small planes: chunk plan of the staging loads, 16-byte chunks of the
 //   tile's contiguous rows; wave w (uniform) loads
 //     slot A: bf16 k_pe chunks 64w+l (256 = 32 rows x 128 B) where k_pe is
@@ -1280,12 +1330,12 @@ __device__ __forceinline__ Off16<FMT> offsets16(int w, int lane) {
   Off16<FMT> o;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    const int row = 16 * rb + i;
 #pragma unroll
     for (int j = 0; j < Raw16<FMT>::kLat; ++j) {
-      if (lat_fmt(FMT) == MLA_FMT_INT8) o.lat[rb][j] = row * kLatent + 128 * w + 32 * g + 16 * j;
-      else if (lat_fmt(FMT) == MLA_FMT_INT4) o.lat[rb][j] = row * (kLatent / 2) + 64 * w + 16 * g;
-      else o.lat[rb][j] = row * (kLatent * 2) + 2 * (128 * w + 32 * g) + 16 * j;
+      // chunk c of row i of block rb: rb * 16 * row_bytes + (16 c + i) * 16
+      if (lat_fmt(FMT) == MLA_FMT_INT8) o.lat[rb][j] = rb * 16 * kLatent + (8 * w + 4 * j) * 256 + lane * 16;
+      else if (lat_fmt(FMT) == MLA_FMT_INT4) o.lat[rb][j] = rb * 16 * (kLatent / 2) + 4 * w * 256 + lane * 16;
+      else o.lat[rb][j] = rb * 16 * (kLatent * 2) + (16 * w + 4 * j) * 256 + lane * 16;
     }
   }
   o.ga = o.gb = kOffNone;
@@ -1331,13 +1381,27 @@ __device__ __forceinline__ SplitRsrc tile_rsrc(const SplitArgs &a, int b, int r0
 
 // Issue every load of one tile. `zero_b` is wave-uniform: it selects the
 // descriptor of slot B. Rows past the descriptor read as zeros.
+//
+// Every latent byte is read once, by one load that takes whole 64-byte pieces
+// of its lines, so the latent loads carry the non-temporal hint (the cache
+// policy operand's nt bit): streamed lines are not kept in the caches, which
+// measured some 7% faster than the default policy on the ragged INT8 decode.
+//
+// The latent descriptor covers whole 16-row blocks, so the rows of the last
+// block past the split are read too. Quantized rows there dequantize to zero
+// (their scales and zero-points, read through plain row descriptors, are
+// zero); bf16 rows could hold anything, so from row `left` of the tile on
+// (bf16 latents only) their loads are pointed past the descriptor.
 template <int FMT>
-__device__ __forceinline__ void load16(Raw16<FMT> &r, const SplitRsrc &rs, const Off16<FMT> &o, bool zero_b) {
+__device__ __forceinline__ void load16(Raw16<FMT> &r, const SplitRsrc &rs, const Off16<FMT> &o, bool zero_b,
+                                       int left, int i) {
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int j = 0; j < Raw16<FMT>::kLat; ++j)
-      r.lat[rb][j] = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rs.ckv, o.lat[rb][j], 0, 0));
+    for (int j = 0; j < Raw16<FMT>::kLat; ++j) {
+      const int off = lat_fmt(FMT) == MLA_FMT_BF16 && 16 * rb + i >= left ? kOffNone : o.lat[rb][j];
+      r.lat[rb][j] = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rs.ckv, off, 0, kLatLoadPolicy));
+    }
   constexpr bool kKBf = kpe_fmt(FMT) == kKpeBf16;
   r.sa = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(kKBf ? rs.kpe : rs.scale, o.ga, 0, 0));
   if (FMT != MLA_FMT_BF16)
@@ -1371,7 +1435,11 @@ __device__ __forceinline__ Meta16 meta16(const uint8_t *aux, int w, int g, int i
     m.sc[rb] = m.ks[rb] = m.zp[rb] = 0;
     if (FMT != MLA_FMT_BF16) {
       const uint8_t *srow = aux + AX::kScale + row * kAuxRow;
-      m.sc[rb] = *(const uint32_t *)(srow + 2 * (8 * w + 2 * g));
+      if (lat_fmt(FMT) == MLA_FMT_INT8)  // the groups of chunks 8w + g and 8w + 4 + g
+        m.sc[rb] = (uint32_t)*(const uint16_t *)(srow + 2 * (8 * w + g)) |
+                   ((uint32_t)*(const uint16_t *)(srow + 2 * (8 * w + 4 + g)) << 16);
+      else  // INT4: groups 8w + 2g and 8w + 2g + 1 (the chunk's 32 channels)
+        m.sc[rb] = *(const uint32_t *)(srow + 2 * (8 * w + 2 * g));
       if (kpe_fmt(FMT) != kKpeBf16) m.ks[rb] = *(const uint16_t *)(srow + 2 * (kNGroupL + 2 * w + (g >> 1)));
     }
     if (has_zero(FMT))
@@ -1435,7 +1503,8 @@ __device__ __forceinline__ void dequant16(const Raw16<FMT> &r, const Meta16 &m, 
       scale_split(q3, s2, h3, l3);
       hi[kk] = cat8(h0, h1, h2, h3);
       lo[kk] = cat8(l0, l1, l2, l3);
-      *(f16x8 *)(vrow + 8 * (kk ^ swz)) = hi[kk];
+      // columns lane_chan - 128 w = 16 g + 64 j + 8 h: vrow is at 16 g
+      *(f16x8 *)(vrow + 64 * (kk >> 1) + 8 * ((kk & 1) ^ swz)) = hi[kk];
     }
   } else if (lat_fmt(FMT) == MLA_FMT_INT4) {
     const f16x2 s0 = splat_f16_bits(m.sc[rb] & 0xFFFFu), s1 = splat_f16_bits(m.sc[rb] >> 16);
@@ -1459,7 +1528,8 @@ __device__ __forceinline__ void dequant16(const Raw16<FMT> &r, const Meta16 &m, 
       scale_split(q37, s2, h37, l37);
       hi[kk] = cat8(h04, h15, h26, h37);  // channels 0,4,1,5,2,6,3,7
       lo[kk] = cat8(l04, l15, l26, l37);
-      *(f16x8 *)(vrow + 8 * (kk ^ swz)) = hi[kk];  // same order; re-paired at the final store
+      // columns 32 g + 8 kk (vrow is at 32 g), same order; re-paired at the final store
+      *(f16x8 *)(vrow + 8 * (kk ^ swz)) = hi[kk];
     }
   } else {
 #pragma unroll
@@ -1468,7 +1538,8 @@ __device__ __forceinline__ void dequant16(const Raw16<FMT> &r, const Meta16 &m, 
       hi[kk] = cat8(bf16x2_to_f16x2(v[0]), bf16x2_to_f16x2(v[1]), bf16x2_to_f16x2(v[2]),
                     bf16x2_to_f16x2(v[3]));
       lo[kk] = f16x8{};
-      *(f16x8 *)(vrow + 8 * (kk ^ swz)) = hi[kk];
+      // columns 32 kk + 8 g (vrow is at 8 (g ^ swz): the swap of chunk pairs)
+      *(f16x8 *)(vrow + 32 * kk) = hi[kk];
     }
   }
   if (kpe_fmt(FMT) != kKpeBf16) {
@@ -1518,12 +1589,12 @@ void split16_kernel(SplitArgs a) {
   __shared__ int rank_lens[kRankMaxB], rank_sel;
 
   const int split = blockIdx.x;
-  const int b = seq_of_row(a.seq_lens, a.B, a.cap, rank_lens, &rank_sel);
+  int L;
+  const int b = seq_of_row(a.seq_lens, a.B, a.cap, rank_lens, &rank_sel, L);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 4, i = lane & 15;
 
-  const int L = min(max(a.seq_lens[b], 0), a.cap);
   const int chunk = split_chunk(L, a.nsplit, a.min_chunk);
   const int t_begin = min(split * chunk, L);
   const int t_end = min(t_begin + chunk, L);
@@ -1544,8 +1615,8 @@ void split16_kernel(SplitArgs a) {
     const _Float16 *q = a.qa + ((int64_t)b * a.H + i) * kQRec;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      qh[kk] = *(const f16x8 *)(q + kQHi + 128 * w + 32 * g + 8 * kk);
-      ql[kk] = *(const f16x8 *)(q + kQLo + 128 * w + 32 * g + 8 * kk);
+      qh[kk] = *(const f16x8 *)(q + kQHi + lane_chan<FMT>(w, g, kk));
+      ql[kk] = *(const f16x8 *)(q + kQLo + lane_chan<FMT>(w, g, kk));
       if (kZp) {  // the INT4 operand order: channels 0,4,1,5,2,6,3,7
         qh[kk] = f16x8{qh[kk][0], qh[kk][4], qh[kk][1], qh[kk][5], qh[kk][2], qh[kk][6], qh[kk][3], qh[kk][7]};
         ql[kk] = f16x8{ql[kk][0], ql[kk][4], ql[kk][1], ql[kk][5], ql[kk][2], ql[kk][6], ql[kk][3], ql[kk][7]};
@@ -1599,7 +1670,7 @@ void split16_kernel(SplitArgs a) {
 #pragma unroll
   for (int p = 0; p < kNpf16; ++p) {
     const int r0 = t_begin + p * kT16;
-    load16<FMT>(raw[p], rsrc_of(r0, paged ? checked(page_entry(r0), r0) : 0), off, zero_b);
+    load16<FMT>(raw[p], rsrc_of(r0, paged ? checked(page_entry(r0), r0) : 0), off, zero_b, t_end - r0, i);
   }
   uint32_t next_entry = paged ? page_entry(t_begin + kNpf16 * kT16) : 0u;
 
@@ -1619,7 +1690,11 @@ void split16_kernel(SplitArgs a) {
     for (int rb = 0; rb < 2; ++rb) {
       f16x8 hi[4], lo[4];
       f16x4 khi, klo;
-      dequant16<FMT>(raw[p], mt, rb, hi, lo, vblk + (16 * rb + i) * kVRow + 32 * g, vswz(i), magic, khi, klo);
+      // this lane's first value-block column (the stores add per-k-step offsets)
+      const int vcol = lat_fmt(FMT) == MLA_FMT_INT8   ? 16 * g
+                       : lat_fmt(FMT) == MLA_FMT_INT4 ? 32 * g
+                                                      : 8 * (g ^ vswz(i));
+      dequant16<FMT>(raw[p], mt, rb, hi, lo, vblk + (16 * rb + i) * kVRow + vcol, vswz(i), magic, khi, klo);
       // INT4: the zero-points of the wave's 8 groups go to columns 128..135 of
       // its value block (chunk 16, swapped with 17 like the others), for the
       // value-side zero-point product
@@ -1659,7 +1734,7 @@ void split16_kernel(SplitArgs a) {
     // path.
     __builtin_amdgcn_sched_barrier(0);
     const int r_next = t_begin + (it + kNpf16) * kT16;
-    load16<FMT>(raw[p], rsrc_of(r_next, paged ? checked(next_entry, r_next) : 0), off, zero_b);
+    load16<FMT>(raw[p], rsrc_of(r_next, paged ? checked(next_entry, r_next) : 0), off, zero_b, t_end - r_next, i);
     if (paged) next_entry = page_entry(r_next + kT16);
 
     // ---- 4. partial scores of the four waves
@@ -1934,12 +2009,15 @@ __global__ __launch_bounds__(256) void get_kernel(const void *ckv, const void *k
     if (row >= 0) {
       constexpr int NS = n_scales(FMT);
       if (c < kLatent) {
+        const int64_t lrow = lat_row_of(pg, row, b, cap, t);
+        const uint8_t *lat = (const uint8_t *)ckv;
         if (lat_fmt(FMT) == MLA_FMT_BF16) {
-          v = bf16_bits_to_f32(((const uint16_t *)ckv)[row * kLatent + c]);
+          v = bf16_bits_to_f32(*(const uint16_t *)(lat + lat_off(lrow, c / 8, kLatent * 2) + (c % 8) * 2));
         } else if (lat_fmt(FMT) == MLA_FMT_INT8) {
-          v = (float)((const int8_t *)ckv)[row * kLatent + c] * f16_bits_to_f32(scale[row * NS + c / kGroupL]);
+          v = (float)*(const int8_t *)(lat + lat_off(lrow, c / 16, kLatent) + c % 16) *
+              f16_bits_to_f32(scale[row * NS + c / kGroupL]);
         } else {
-          const uint8_t byte = ((const uint8_t *)ckv)[row * (kLatent / 2) + c / 2];
+          const uint8_t byte = lat[lat_off(lrow, c / 32, kLatent / 2) + (c % 32) / 2];
           const float q = (float)((c & 1) ? (byte >> 4) : (byte & 15));
           v = fmaf(q, f16_bits_to_f32(scale[row * NS + c / kGroupL]),
                    f16_bits_to_f32(zero[row * kNGroupL + c / kGroupL]));
@@ -2015,11 +2093,14 @@ struct LayerPlanes {
 };
 
 LayerPlanes layer_planes(const mla_cache *c, int layer) {
-  // rows of one layer: batch * capacity contiguous, or its pool of pages
+  // rows of one layer: batch * capacity contiguous, or its pool of pages; the
+  // latent plane's sequences are lat_stride(capacity) rows apart
   const int64_t rows = (int64_t)layer * (c->page_size ? (int64_t)c->num_pages * c->page_size
                                                       : (int64_t)c->batch * c->capacity);
+  const int64_t lrows = (int64_t)layer * (c->page_size ? (int64_t)c->num_pages * c->page_size
+                                                       : (int64_t)c->batch * lat_stride(c->capacity));
   LayerPlanes p;
-  p.ckv = (uint8_t *)c->ckv + rows * ckv_row_bytes(c->format);
+  p.ckv = (uint8_t *)c->ckv + lrows * ckv_row_bytes(c->format);
   p.kpe = (uint8_t *)c->kpe + rows * kpe_row_bytes(c->format);
   p.scale = c->scale ? c->scale + rows * n_scales(c->format) : nullptr;
   p.zero = c->zero ? c->zero + rows * kNGroupL : nullptr;
