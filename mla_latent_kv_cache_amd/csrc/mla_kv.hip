@@ -1870,29 +1870,35 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 constexpr int kMergeChunk = 16;  // splits merged per round of loads
 
-// Per (head h, 4 batch rows), one wave per row: merge the splits with
-// log-sum-exp weights and normalize, then all four waves form
-// out[b,h,:] = o_lat W_UV[h]. The merge takes the splits 16 at a time: lane s
-// loads m and l of split s while every lane loads its 8 latent channels of all
-// 16 splits, in one round of loads. The chunk's maximum updates a running
-// maximum (what was merged before is rescaled by 2^(M_old - M_new)), and each
-// split's weight 2^(m_s - M) is taken from its lane as a scalar. A split with
-// l = 0 holds no tokens and its sums were never written: it gets weight zero
-// and its sums are skipped, not multiplied. Grid (H, ceil(B/4)).
-__global__ __launch_bounds__(256) void reduce_kernel(const float *ws_m, const float *ws_l,
-                                                     const float *ws_acc, const uint16_t *w_uv,
-                                                     int B, int H, int nsplit, float *out) {
+// Per (head h, 4 batch rows), two waves per row (each half of the 512 latent
+// channels): merge the splits with log-sum-exp weights and normalize, then all
+// eight waves form out[b,h,:] = o_lat W_UV[h]. The merge takes the splits 16 at
+// a time: lane s loads m and l of split s while every lane loads its 4 latent
+// channels of all 16 splits, in one round of loads. The chunk's maximum updates
+// a running maximum (what was merged before is rescaled by 2^(M_old - M_new)),
+// and each split's weight 2^(m_s - M) is taken from its lane as a scalar. A
+// split with l = 0 holds no tokens and its sums were never written: it gets
+// weight zero and its sums are skipped, not multiplied. Grid (H, ceil(B/4)),
+// 512 threads.
+constexpr int kReduceThreads = 512;
+constexpr int kReduceCS = kReduceThreads / 16;  // latent row chunks of the projection (16 rows each)
+static_assert(kReduceBT * kVDim == kReduceThreads && kReduceCS * 16 == kLatent && 2 * kReduceBT * 64 == kReduceThreads,
+              "two waves per row, one output per thread");
+__global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const float *ws_m, const float *ws_l,
+                                                                const float *ws_acc, const uint16_t *w_uv,
+                                                                int B, int H, int nsplit, float *out) {
   __shared__ float olat[kReduceBT][kLatent];
-  __shared__ float red[16][kReduceBT][kVDim];
+  __shared__ float red[kReduceCS][kReduceBT][kVDim];
   const int h = blockIdx.x;
   const int b0 = blockIdx.y * kReduceBT;
   const int tid = threadIdx.x;
-  const int bt = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int bt = wv >> 1, half = wv & 1;
   const int b = b0 + bt;  // uniform across the wave
-  f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 o0 = {0.f, 0.f, 0.f, 0.f};
   if (b < B) {
     const int64_t base = (int64_t)b * nsplit * H + h;
-    const float *acc = ws_acc + base * kLatent + 8 * lane;
+    const float *acc = ws_acc + base * kLatent + (kLatent / 2) * half + 4 * lane;
     float M = -INFINITY, Ls = 0.0f;
     for (int c0 = 0; c0 < nsplit; c0 += kMergeChunk) {
       const int cn = min(kMergeChunk, nsplit - c0);  // uniform
@@ -1901,21 +1907,15 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float *ws_m, const fl
         ll = ws_l[base + (int64_t)(c0 + lane) * H];
         ml = ws_m[base + (int64_t)(c0 + lane) * H];
       }
-      f32x4 a0[kMergeChunk], a1[kMergeChunk];
+      f32x4 a0[kMergeChunk];
 #pragma unroll
-      for (int j = 0; j < kMergeChunk; ++j) {
-        if (j < cn) {
-          const float *src = acc + (int64_t)(c0 + j) * H * kLatent;
-          a0[j] = *(const f32x4 *)src;
-          a1[j] = *(const f32x4 *)(src + 4);
-        }
-      }
+      for (int j = 0; j < kMergeChunk; ++j)
+        if (j < cn) a0[j] = *(const f32x4 *)(acc + (int64_t)(c0 + j) * H * kLatent);
       const float mc = wave_max(ll > 0.0f ? ml : -INFINITY);
       if (mc == -INFINITY) continue;  // no split of the chunk holds tokens
       const float mn = fmaxf(M, mc);
       const float alpha = __builtin_amdgcn_exp2f(M - mn);  // 0 while nothing is merged
       o0 *= alpha;
-      o1 *= alpha;
       Ls *= alpha;
       M = mn;
       const float wl = ll > 0.0f ? __builtin_amdgcn_exp2f(ml - M) : 0.0f;
@@ -1926,27 +1926,22 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float *ws_m, const fl
           const float wgt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j));
           if (wgt != 0.0f) {  // uniform
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              o0[k] = fmaf(wgt, a0[j][k], o0[k]);
-              o1[k] = fmaf(wgt, a1[j][k], o1[k]);
-            }
+            for (int k = 0; k < 4; ++k) o0[k] = fmaf(wgt, a0[j][k], o0[k]);
           }
         }
       }
     }
     const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
     o0 *= inv;
-    o1 *= inv;
   }
-  // this thread's W_UV rows for the projection (8 output columns of 32 latent
+  // this thread's W_UV rows for the projection (8 output columns of 16 latent
   // rows), in flight while the merged rows go through LDS
   const int eg = tid & 15, cs = tid >> 4;
-  const uint16_t *w = w_uv + ((int64_t)h * kLatent + cs * 32) * kVDim + 8 * eg;
-  u32x4 wv[32];
+  const uint16_t *w = w_uv + ((int64_t)h * kLatent + cs * 16) * kVDim + 8 * eg;
+  u32x4 wr[16];
 #pragma unroll
-  for (int cc = 0; cc < 32; ++cc) wv[cc] = *(const u32x4 *)(w + cc * kVDim);
-  *(f32x4 *)&olat[bt][8 * lane] = o0;
-  *(f32x4 *)&olat[bt][8 * lane + 4] = o1;
+  for (int cc = 0; cc < 16; ++cc) wr[cc] = *(const u32x4 *)(w + cc * kVDim);
+  *(f32x4 *)&olat[bt][(kLatent / 2) * half + 4 * lane] = o0;
   __syncthreads();
   float acc[kReduceBT][8];
 #pragma unroll
@@ -1954,13 +1949,13 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float *ws_m, const fl
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[r][k] = 0.0f;
 #pragma unroll
-  for (int c4 = 0; c4 < 8; ++c4) {
+  for (int c4 = 0; c4 < 4; ++c4) {
     f32x4 ov[kReduceBT];
 #pragma unroll
-    for (int r = 0; r < kReduceBT; ++r) ov[r] = *(const f32x4 *)&olat[r][cs * 32 + 4 * c4];
+    for (int r = 0; r < kReduceBT; ++r) ov[r] = *(const f32x4 *)&olat[r][cs * 16 + 4 * c4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const u32x4 wq = wv[4 * c4 + q];
+      const u32x4 wq = wr[4 * c4 + q];
       float wf[8];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -1979,16 +1974,13 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float *ws_m, const fl
     for (int k = 0; k < 8; ++k) red[cs][r][8 * eg + k] = acc[r][k];
   lds_stores_done();
   __syncthreads();
+  // one output per thread: kReduceBT * kVDim = 512
+  const int r = tid / kVDim, e = tid % kVDim;
+  const int bo = b0 + r;
+  float v = 0.0f;
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int o = tid + 256 * k;
-    const int r = o / kVDim, e = o % kVDim;
-    const int bo = b0 + r;
-    float v = 0.0f;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) v += red[q][r][e];
-    if (bo < B) out[((int64_t)bo * H + h) * kVDim + e] = v;
-  }
+  for (int q = 0; q < kReduceCS; ++q) v += red[q][r][e];
+  if (bo < B) out[((int64_t)bo * H + h) * kVDim + e] = v;
 }
 
 // --------------------------------------------------------------------- get
@@ -2340,7 +2332,7 @@ int run_combine(const mla_cache *cache, const DecodePlan &pl, const void *w_uv, 
                 void *workspace, float *out, hipStream_t s) {
   const int B = cache->batch;
   uint8_t *ws = (uint8_t *)workspace;
-  hipLaunchKernelGGL(reduce_kernel, dim3(heads, (B + kReduceBT - 1) / kReduceBT), dim3(256), 0, s,
+  hipLaunchKernelGGL(reduce_kernel, dim3(heads, (B + kReduceBT - 1) / kReduceBT), dim3(kReduceThreads), 0, s,
                      (const float *)(ws + pl.wl.m), (const float *)(ws + pl.wl.l),
                      (const float *)(ws + pl.wl.acc), (const uint16_t *)w_uv, B, heads, pl.ns, out);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
