@@ -173,30 +173,40 @@ class Runner:
 
 
 def measure(wid, steps, warmup, fmt=None, layers=None, page_size=0):
+    """W untimed steps, then the K timed steps (value, ms_per_step), then K more
+    steps with a pair of HIP events around every partial-attention launch (its
+    average duration, for the roofline). The timed steps carry no per-launch
+    events: an event recorded between two launches holds the next launch back
+    by some 4-5 us, which is measurement overhead, not decode work."""
     import torch
-    r = Runner(wid, steps + warmup, fmt, layers, page_size)
+    r = Runner(wid, 2 * steps + warmup, fmt, layers, page_size)
     for _ in range(warmup):
         r.step()
     torch.cuda.synchronize()
     log(f"{r.w.name}: warmup done ({warmup} steps); timing {steps} steps")
-    events = []
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(r.stream)
     for _ in range(steps):
-        r.step(events)
+        r.step()
     t_end.record(r.stream)
     torch.cuda.synchronize()
     ms = t_start.elapsed_time(t_end)
     first = warmup + 1
     kv = sum(r.kv_tokens(first + i) for i in range(steps))
     algo = sum(r.algorithmic_bytes(first + i) for i in range(steps))
+    # the partial kernel's launches, timed one by one on the stream they run on
+    events = []
+    for _ in range(steps):
+        r.step(events)
+    torch.cuda.synchronize()
     part_ms = [e0.elapsed_time(e1) for e0, e1, _ in events]
     # algorithmic bytes of each partial launch: the cache rows it attends
+    first_ev = warmup + steps + 1
     part_bytes = []
     for i in range(steps):
-        per_launch = r.layer_tokens(first + i) * row_bytes(r.w.fmt)
+        per_launch = r.layer_tokens(first_ev + i) * row_bytes(r.w.fmt)
         part_bytes += [per_launch] * r.w.layers
     avg_ms = float(np.mean(part_ms))
     avg_bytes = float(np.mean(part_bytes))
@@ -240,6 +250,7 @@ def roofline(res):
         "kernel": ("split16_kernel" if res["heads"] == 16 else "split_kernel") + " (mla_decode_partial)",
         "per_launch_bytes": res["partial_bytes_per_launch"],
         "avg_launch_us": round(res["partial_avg_us"], 2),
+        "launches_timed": res["partial_launches"],
     }
 
 
