@@ -84,6 +84,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 template <typename To, typename From>
 __device__ __forceinline__ To bitcast(From v) {
@@ -671,14 +672,20 @@ __device__ __forceinline__ int seq_of_row(const int *seq_lens, int B, int cap, i
     return row;
   }
   const int tid = threadIdx.x;
-  if (tid < B) lens_sh[tid] = min(max(seq_lens[tid], 0), cap);
+  const int B4 = (B + 3) & ~3;  // lengths padded with -1 to whole groups of 4 (they never count)
+  if (tid < B4) lens_sh[tid] = tid < B ? min(max(seq_lens[tid], 0), cap) : -1;
   __syncthreads();
   if (tid < B) {
     const int lt = lens_sh[tid];
     int r = 0;
-    for (int j = 0; j < B; ++j) {
-      const int lj = lens_sh[j];
-      r += (lj > lt) | ((lj == lt) & (j < tid));
+    // four lengths per LDS read, the reads unrolled so that their latencies
+    // overlap (one dependent read per sequence made this loop the longest
+    // part of a short workgroup)
+#pragma unroll 8
+    for (int j = 0; j < B4; j += 4) {
+      const i32x4 l4 = *(const i32x4 *)(lens_sh + j);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) r += (l4[k] > lt) | ((l4[k] == lt) & (j + k < tid));
     }
     if (r == row) *sel = tid;  // ranks are a permutation: exactly one thread writes
   }
@@ -1005,7 +1012,8 @@ void split_kernel(SplitArgs a) {
   constexpr bool kZp = has_zero(FMT);
   __shared__ __attribute__((aligned(16))) unsigned char lds[LD::kBytes];
   __shared__ float ml_m[kWaves][16], ml_l[kWaves][16];
-  __shared__ int rank_lens[kRankMaxB], rank_sel;
+  __shared__ __attribute__((aligned(16))) int rank_lens[kRankMaxB];
+  __shared__ int rank_sel;
 
   const int split = blockIdx.x / a.hh_count;
   const int hh = blockIdx.x % a.hh_count;
@@ -1586,7 +1594,8 @@ void split16_kernel(SplitArgs a) {
   // read only between the two barriers of a tile (the next tile's staging
   // writes come after the second)
   __shared__ __attribute__((aligned(16))) uint8_t aux[Aux16<FMT>::kBytes];
-  __shared__ int rank_lens[kRankMaxB], rank_sel;
+  __shared__ __attribute__((aligned(16))) int rank_lens[kRankMaxB];
+  __shared__ int rank_sel;
 
   const int split = blockIdx.x;
   int L;
