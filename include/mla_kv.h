@@ -167,11 +167,20 @@ int mla_decode_auto_splits(const mla_cache *cache, int32_t heads, int32_t *num_s
  *   w_uv     bf16 [heads][512][128]    value up-projection: V[h] = c W_UV[h]
  *   heads    16, 32, 64 or 128
  *   softmax_scale   multiplies q.k before the softmax (e.g. 1/sqrt(192))
- *   num_splits      KV splits per sequence, 0 = auto, else 1..4096. Split s
- *                   of sequence b covers tokens [s*chunk, (s+1)*chunk) with
+ *   num_splits      0 = auto, else 1..4096.
+ *                   32, 64, 128 heads: KV splits per sequence. Split s of
+ *                   sequence b covers tokens [s*chunk, (s+1)*chunk) with
  *                   chunk = ceil(seq_len / num_splits) rounded up to 32, and
  *                   for num_splits = 0 at least 256 (short sequences use
  *                   fewer splits).
+ *                   16 heads: splits per sequence on average. The partial
+ *                   phase runs W = num_splits * batch workgroups; the
+ *                   batch's 32-token tiles, sequence after sequence, are
+ *                   cut into W equal runs (a run may end one sequence and
+ *                   start the next), so every workgroup gets the same work
+ *                   whatever the mix of lengths. Auto: about three
+ *                   workgroups per CU, at least 4 tiles each for full
+ *                   sequences.
  *   workspace       device scratch of at least mla_decode_workspace_bytes;
  *                   its contents on entry do not matter
  *   out      fp32 [batch][heads][128]

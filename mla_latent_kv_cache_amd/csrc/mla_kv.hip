@@ -73,6 +73,8 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kMrgRow = kLatent + 4;       // fp32 per head row in the merge area
 constexpr int kMaxSplits = 4096;
 constexpr int kAutoMinChunk = 256;         // fewest tokens per split in the automatic plan
+constexpr int kAutoMinTiles = 4;           // 16 heads: fewest 32-token tiles per workgroup (full sequences)
+constexpr int kWgPerCu = 3;                // resident 16-head partial workgroups per CU
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -644,9 +646,10 @@ struct SplitArgs {
   const uint16_t *zero;
   const int32_t *seq_lens;  // layer row
   const _Float16 *qa;       // [B][H][kQRec]
-  float *ws_m;              // [B][nsplit][H]
-  float *ws_l;              // [B][nsplit][H]
-  float *ws_acc;            // [B][nsplit][H][512]
+  float *ws_m;              // [records][H]: [B][nsplit] for 32+ heads, W + B for 16
+  float *ws_l;              // [records][H]
+  float *ws_acc;            // [records][H][512]
+  int32_t *rec_tab;         // 16 heads: [B][2] first record and record count
   Paging pg;
   int B, H, cap, nsplit, min_chunk, hh_count;
 };
@@ -1583,6 +1586,111 @@ __device__ __forceinline__ void dequant16(const Raw16<FMT> &r, const Meta16 &m, 
 //   4. stores its partial scores, barrier, and adds the four waves' partials
 //      in a fixed order;
 //   5. online softmax and the value MFMAs of its channels.
+// ---- balanced plan of the 16-head partial kernel
+//
+// The batch's tiles (ceil(L_b / 32) per sequence, sequences in batch order)
+// form one list of T tiles, and workgroup w of the W in the grid takes tiles
+// [w q, min((w + 1) q, T)) with q = ceil(T / W): every workgroup gets the same
+// number of tiles (within one), whatever the mix of lengths, and a range may
+// cover the end of one sequence and the start of the next. Each (workgroup,
+// sequence) pair it covers is one partial record, at index w + b: along the
+// list, w and b never decrease and one of them grows at every new pair, so
+// w + b is unique, below W + B. Workgroup 0 writes, for every sequence, its
+// first record and record count, which the combine reads.
+__device__ __forceinline__ int tiles_of(int L) { return (L + kT16 - 1) / kT16; }
+__device__ __forceinline__ int clamp_len(int v, int cap) { return min(max(v, 0), cap); }
+
+// Inclusive prefix sum of v over the workgroup's threads, and in `total` the
+// sum over all of them. Every thread calls it; sh holds kWaves ints.
+__device__ __forceinline__ int wg_scan(int v, int *sh, int &total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(v, off);
+    if (lane >= off) v += u;
+  }
+  if (lane == 63) sh[w] = v;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) {
+    const int t = sh[k];
+    before += k < w ? t : 0;
+    total += t;
+  }
+  __syncthreads();  // sh may be written again by the next call
+  return v + before;
+}
+
+struct PlanStart {
+  int b, S, L;  // first sequence of the range (B: none), its first global tile, its length
+  int g0, g1;   // the workgroup's global tiles [g0, g1)
+};
+
+// Every thread calls it (barriers inside); sh holds at least kWaves + 3 ints.
+__device__ __forceinline__ PlanStart plan_start(const SplitArgs &a, int *sh) {
+  const int tid = threadIdx.x;
+  const int W = gridDim.x, wg = blockIdx.x;
+  int T = 0, n0 = 0, incl0 = 0, L0 = 0, tot0 = 0;
+  for (int c0 = 0; c0 < a.B; c0 += kThreads) {  // total tiles
+    const int b = c0 + tid;
+    const int L = b < a.B ? clamp_len(a.seq_lens[b], a.cap) : 0;
+    const int n = tiles_of(L);
+    int tot;
+    const int incl = wg_scan(n, sh, tot);
+    if (c0 == 0) {
+      n0 = n;
+      incl0 = incl;
+      L0 = L;
+      tot0 = tot;
+    }
+    T += tot;
+  }
+  const int q = T > 0 ? (int)(((int64_t)T + W - 1) / W) : 1;
+  const int g0 = (int)min((int64_t)wg * q, (int64_t)T);
+  const int g1 = min(g0 + q, T);
+  if (tid == 0) {
+    sh[kWaves] = a.B;
+    sh[kWaves + 1] = 0;
+    sh[kWaves + 2] = 0;
+  }
+  __syncthreads();
+  int carry = 0;
+  for (int c0 = 0; c0 < a.B; c0 += kThreads) {  // locate g0; the record table
+    const int b = c0 + tid;
+    int n = n0, incl = incl0, L = L0, tot = tot0;
+    if (c0 > 0) {
+      L = b < a.B ? clamp_len(a.seq_lens[b], a.cap) : 0;
+      n = tiles_of(L);
+      incl = wg_scan(n, sh, tot);
+    }
+    const int S = carry + incl - n;
+    if (b < a.B) {
+      if (n > 0 && S <= g0 && g0 < S + n) {  // at most one thread of the grid's batch
+        sh[kWaves] = b;
+        sh[kWaves + 1] = S;
+        sh[kWaves + 2] = L;
+      }
+      if (wg == 0) {
+        const int first = n > 0 ? S / q : 0;
+        a.rec_tab[2 * b] = first + b;
+        a.rec_tab[2 * b + 1] = n > 0 ? (S + n - 1) / q - first + 1 : 0;
+      }
+    }
+    carry += tot;
+  }
+  __syncthreads();
+  PlanStart p;
+  p.b = __builtin_amdgcn_readfirstlane(sh[kWaves]);
+  p.S = __builtin_amdgcn_readfirstlane(sh[kWaves + 1]);
+  p.L = __builtin_amdgcn_readfirstlane(sh[kWaves + 2]);
+  p.g0 = __builtin_amdgcn_readfirstlane(g0);
+  p.g1 = __builtin_amdgcn_readfirstlane(g1);
+  __syncthreads();  // sh is reused by the first tile
+  return p;
+}
+
 template <int FMT>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(3, 3)))
 void split16_kernel(SplitArgs a) {
@@ -1590,31 +1698,29 @@ void split16_kernel(SplitArgs a) {
   constexpr bool kZp = has_zero(FMT);  // INT4 latent: zero-points, and the nibble operand order
   // +16: the zero-point read of the last row runs 8 fp16 past its block (unused slots)
   __shared__ __attribute__((aligned(16))) _Float16 wblk[kWaves * kWBlk];
+  // partial scores of a tile; before the first tile, the plan's scratch
   __shared__ __attribute__((aligned(16))) float part[kPart16];
   // read only between the two barriers of a tile (the next tile's staging
   // writes come after the second)
   __shared__ __attribute__((aligned(16))) uint8_t aux[Aux16<FMT>::kBytes];
-  __shared__ __attribute__((aligned(16))) int rank_lens[kRankMaxB];
-  __shared__ int rank_sel;
 
-  const int split = blockIdx.x;
-  int L;
-  const int b = seq_of_row(a.seq_lens, a.B, a.cap, rank_lens, &rank_sel, L);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 4, i = lane & 15;
 
-  const int chunk = split_chunk(L, a.nsplit, a.min_chunk);
-  const int t_begin = min(split * chunk, L);
-  const int t_end = min(t_begin + chunk, L);
-  const int64_t ws_row = ((int64_t)b * a.nsplit + split) * a.H;
-  if (t_begin >= t_end) {  // empty unit: identity of the merge
-    if (tid < 16) {
-      a.ws_m[ws_row + tid] = -INFINITY;
-      a.ws_l[ws_row + tid] = 0.0f;
-    }
-    return;
-  }
+  const PlanStart plan = plan_start(a, (int *)part);
+  int b = plan.b, S = plan.S, L = plan.L;
+  // one pass per sequence the range covers (all uniform across the workgroup)
+  while (b < a.B) {
+  // all wave-uniform; said so, so that the descriptors built from them stay
+  // in scalar registers
+  b = __builtin_amdgcn_readfirstlane(b);
+  S = __builtin_amdgcn_readfirstlane(S);
+  L = __builtin_amdgcn_readfirstlane(L);
+  const int n = tiles_of(L);
+  const int t_begin = __builtin_amdgcn_readfirstlane((max(plan.g0, S) - S) * kT16);
+  const int t_end = __builtin_amdgcn_readfirstlane(min(L, (min(plan.g1, S + n) - S) * kT16));
+  const int64_t ws_row = ((int64_t)blockIdx.x + b) * a.H;
   const int ntiles = (t_end - t_begin + kT16 - 1) / kT16;
 
   // queries of head i for this wave's channels, in the MFMA B layout
@@ -1859,6 +1965,13 @@ void split16_kernel(SplitArgs a) {
     a.ws_m[ws_row + i] = m_run;
     a.ws_l[ws_row + i] = l_run;
   }
+  S += n;
+  if (S >= plan.g1) break;
+  do {  // the next sequence that holds tokens (one exists: the range is not done)
+    ++b;
+    L = b < a.B ? clamp_len(a.seq_lens[b], a.cap) : 0;
+  } while (b < a.B && L == 0);
+  }
 }
 
 // ------------------------------------------------------------------ reduce
@@ -1894,8 +2007,9 @@ constexpr int kReduceCS = kReduceThreads / 16;  // latent row chunks of the proj
 static_assert(kReduceBT * kVDim == kReduceThreads && kReduceCS * 16 == kLatent && 2 * kReduceBT * 64 == kReduceThreads,
               "two waves per row, one output per thread");
 __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const float *ws_m, const float *ws_l,
-                                                                const float *ws_acc, const uint16_t *w_uv,
-                                                                int B, int H, int nsplit, float *out) {
+                                                                const float *ws_acc, const int32_t *rec_tab,
+                                                                const uint16_t *w_uv, int B, int H, int nsplit,
+                                                                float *out) {
   __shared__ float olat[kReduceBT][kLatent];
   __shared__ float red[kReduceCS][kReduceBT][kVDim];
   const int h = blockIdx.x;
@@ -1906,11 +2020,18 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const float *ws_
   const int b = b0 + bt;  // uniform across the wave
   f32x4 o0 = {0.f, 0.f, 0.f, 0.f};
   if (b < B) {
-    const int64_t base = (int64_t)b * nsplit * H + h;
+    // the sequence's records: nsplit from b * nsplit, or (16 heads) as the
+    // partial kernel's table lists them
+    int first = b * nsplit, count = nsplit;
+    if (rec_tab) {
+      first = __builtin_amdgcn_readfirstlane(rec_tab[2 * b]);
+      count = __builtin_amdgcn_readfirstlane(rec_tab[2 * b + 1]);
+    }
+    const int64_t base = (int64_t)first * H + h;
     const float *acc = ws_acc + base * kLatent + (kLatent / 2) * half + 4 * lane;
     float M = -INFINITY, Ls = 0.0f;
-    for (int c0 = 0; c0 < nsplit; c0 += kMergeChunk) {
-      const int cn = min(kMergeChunk, nsplit - c0);  // uniform
+    for (int c0 = 0; c0 < count; c0 += kMergeChunk) {
+      const int cn = min(kMergeChunk, count - c0);  // uniform
       float ml = -INFINITY, ll = 0.0f;
       if (lane < cn) {
         ll = ws_l[base + (int64_t)(c0 + lane) * H];
@@ -2125,20 +2246,26 @@ template <typename F> void with_format(int fmt, F &&f) {
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t qa, m, l, acc, total;
+  size_t qa, m, l, acc, tab, total;
 };
 
+// Partial records: nsplit per sequence for 32+ heads; for 16 heads one per
+// (workgroup, sequence) pair of the balanced plan, W + B with W = nsplit * B
+// workgroups, plus the per-sequence record table.
 WsLayout ws_layout(int B, int H, int nsplit) {
+  const size_t recs = (size_t)B * nsplit + (H == 16 ? (size_t)B : 0);
   WsLayout w;
   size_t off = 0;
   w.qa = off;
   off = align256(off + (size_t)B * H * kQRec * 2);
   w.m = off;
-  off = align256(off + (size_t)B * nsplit * H * 4);
+  off = align256(off + recs * H * 4);
   w.l = off;
-  off = align256(off + (size_t)B * nsplit * H * 4);
+  off = align256(off + recs * H * 4);
   w.acc = off;
-  off = align256(off + (size_t)B * nsplit * H * kLatent * 4);
+  off = align256(off + recs * H * kLatent * 4);
+  w.tab = off;
+  off = align256(off + (H == 16 ? (size_t)B * 2 * 4 : 0));
   w.total = off;
   return w;
 }
@@ -2149,6 +2276,18 @@ int auto_splits(const mla_cache *c, int heads, int *out) {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return MLA_ERR_HIP;
   if (cus < 1) cus = 1;
+  if (heads == 16) {
+    // Balanced plan: nsplit * B workgroups of equal work, as many as are
+    // resident at once (three per CU), and at least kAutoMinTiles tiles each
+    // when every sequence is full.
+    int64_t ns = (int64_t)kWgPerCu * cus / c->batch;
+    const int64_t by_len = ((int64_t)c->capacity + kT16 * kAutoMinTiles - 1) / (kT16 * kAutoMinTiles);
+    if (ns > by_len) ns = by_len;
+    if (ns < 1) ns = 1;
+    if (ns > kMaxSplits) ns = kMaxSplits;
+    *out = (int)ns;
+    return MLA_OK;
+  }
   const int hh = heads <= 64 ? 1 : heads / 64;
   const int64_t units = (int64_t)c->batch * hh;
   // About four workgroups per CU when every sequence is full (the partial
@@ -2331,7 +2470,10 @@ int run_partial(const mla_cache *cache, const DecodePlan &pl, int layer, int hea
   a.min_chunk = pl.min_chunk;
   a.pg = paging_of(cache);
   a.hh_count = heads <= 64 ? 1 : heads / 64;
-  const dim3 grid((unsigned)(pl.ns * a.hh_count), (unsigned)cache->batch);
+  a.rec_tab = (int32_t *)(ws + pl.wl.tab);
+  // 16 heads: the balanced plan's nsplit * B workgroups in one row
+  const dim3 grid = heads == 16 ? dim3((unsigned)(pl.ns * cache->batch))
+                                : dim3((unsigned)(pl.ns * a.hh_count), (unsigned)cache->batch);
   hipError_t e = hipSuccess;
   with_format(cache->format, [&](auto f) { e = launch_split_fmt<decltype(f)::value>(a, heads, grid, s); });
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
@@ -2343,7 +2485,8 @@ int run_combine(const mla_cache *cache, const DecodePlan &pl, const void *w_uv, 
   uint8_t *ws = (uint8_t *)workspace;
   hipLaunchKernelGGL(reduce_kernel, dim3(heads, (B + kReduceBT - 1) / kReduceBT), dim3(kReduceThreads), 0, s,
                      (const float *)(ws + pl.wl.m), (const float *)(ws + pl.wl.l),
-                     (const float *)(ws + pl.wl.acc), (const uint16_t *)w_uv, B, heads, pl.ns, out);
+                     (const float *)(ws + pl.wl.acc), heads == 16 ? (const int32_t *)(ws + pl.wl.tab) : nullptr,
+                     (const uint16_t *)w_uv, B, heads, pl.ns, out);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
