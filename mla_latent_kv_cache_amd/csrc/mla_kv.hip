@@ -1404,8 +1404,8 @@ __device__ __forceinline__ SplitRsrc tile_rsrc(const SplitArgs &a, int b, int r0
 // zero); bf16 rows could hold anything, so from row `left` of the tile on
 // (bf16 latents only) their loads are pointed past the descriptor.
 template <int FMT>
-__device__ __forceinline__ void load16(Raw16<FMT> &r, const SplitRsrc &rs, const Off16<FMT> &o, bool zero_b,
-                                       int left, int i) {
+__device__ __forceinline__ void load16_lat(Raw16<FMT> &r, const SplitRsrc &rs, const Off16<FMT> &o, int left,
+                                           int i) {
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -1413,6 +1413,14 @@ __device__ __forceinline__ void load16(Raw16<FMT> &r, const SplitRsrc &rs, const
       const int off = lat_fmt(FMT) == MLA_FMT_BF16 && 16 * rb + i >= left ? kOffNone : o.lat[rb][j];
       r.lat[rb][j] = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rs.ckv, off, 0, kLatLoadPolicy));
     }
+}
+
+// The small planes' loads of a tile. They are issued a tile ahead of their
+// use and before the same tile's latent loads: loads return in order, so the
+// staging of the small planes never waits for latent bytes.
+template <int FMT>
+__device__ __forceinline__ void load16_small(Raw16<FMT> &r, const SplitRsrc &rs, const Off16<FMT> &o,
+                                             bool zero_b) {
   constexpr bool kKBf = kpe_fmt(FMT) == kKpeBf16;
   r.sa = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(kKBf ? rs.kpe : rs.scale, o.ga, 0, 0));
   if (FMT != MLA_FMT_BF16)
@@ -1785,7 +1793,9 @@ void split16_kernel(SplitArgs a) {
 #pragma unroll
   for (int p = 0; p < kNpf16; ++p) {
     const int r0 = t_begin + p * kT16;
-    load16<FMT>(raw[p], rsrc_of(r0, paged ? checked(page_entry(r0), r0) : 0), off, zero_b, t_end - r0, i);
+    const SplitRsrc rs0 = rsrc_of(r0, paged ? checked(page_entry(r0), r0) : 0);
+    load16_small<FMT>(raw[p], rs0, off, zero_b);
+    load16_lat<FMT>(raw[p], rs0, off, t_end - r0, i);
   }
   uint32_t next_entry = paged ? page_entry(t_begin + kNpf16 * kT16) : 0u;
 
@@ -1798,6 +1808,13 @@ void split16_kernel(SplitArgs a) {
     stage16<FMT>(raw[p], off, aux);
     __syncthreads();
     const Meta16 mt = meta16<FMT>(aux, w, g, i);
+    // the small planes of the tile kNpf16 ahead (their registers were read by
+    // the staging stores, which the barrier has waited for)
+    const int r_next = t_begin + (it + kNpf16) * kT16;
+    const SplitRsrc rs_next = rsrc_of(r_next, paged ? checked(next_entry, r_next) : 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load16_small<FMT>(raw[p], rs_next, off, zero_b);
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- 2. dequantize in registers; partial scores; C_hi to the value block
     f32x4 sc[2];
@@ -1848,8 +1865,7 @@ void split16_kernel(SplitArgs a) {
     // Always issued, so the count of outstanding loads is the same on every
     // path.
     __builtin_amdgcn_sched_barrier(0);
-    const int r_next = t_begin + (it + kNpf16) * kT16;
-    load16<FMT>(raw[p], rsrc_of(r_next, paged ? checked(next_entry, r_next) : 0), off, zero_b, t_end - r_next, i);
+    load16_lat<FMT>(raw[p], rs_next, off, t_end - r_next, i);
     if (paged) next_entry = page_entry(r_next + kT16);
 
     // ---- 4. partial scores of the four waves
