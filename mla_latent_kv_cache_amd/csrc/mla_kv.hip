@@ -1699,7 +1699,9 @@ __device__ __forceinline__ PlanStart plan_start(const SplitArgs &a, int *sh) {
   return p;
 }
 
-template <int FMT>
+// PAGED: the cache is paged (a compile-time choice: the per-tile descriptor code
+// of the other layout is then absent from the tile loop)
+template <int FMT, bool PAGED>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(3, 3)))
 void split16_kernel(SplitArgs a) {
   constexpr bool kLo = FMT != MLA_FMT_BF16;
@@ -1776,7 +1778,7 @@ void split16_kernel(SplitArgs a) {
   // is read from the sequence's block-table row one tile ahead, with a buffer
   // (vector) load: a scalar load would share its wait counter with LDS
   // traffic, and every LDS wait of the tile would then wait for it too.
-  const bool paged = a.pg.size != 0;
+  constexpr bool paged = PAGED;
   const __amdgpu_buffer_rsrc_t trow =
       make_rsrc(paged ? (const void *)(a.pg.table + (int64_t)b * a.pg.max_pages) : a.kpe,
                 paged ? a.pg.max_pages * 4 : 0);
@@ -1788,7 +1790,8 @@ void split16_kernel(SplitArgs a) {
     return (r < t_end && pg >= 0 && pg < a.pg.num_pages) ? pg : -1;
   };
   auto rsrc_of = [&](int r0, int page) {
-    return paged ? page_rsrc<FMT>(a, page, r0, t_end) : tile_rsrc<FMT>(a, b, r0, t_end);
+    if constexpr (PAGED) return page_rsrc<FMT>(a, page, r0, t_end);
+    else return tile_rsrc<FMT>(a, b, r0, t_end);
   };
 #pragma unroll
   for (int p = 0; p < kNpf16; ++p) {
@@ -2322,7 +2325,10 @@ int auto_splits(const mla_cache *c, int heads, int *out) {
 
 template <int FMT>
 hipError_t launch_split_fmt(const SplitArgs &a, int heads, dim3 grid, hipStream_t st) {
-  if (heads == 16) hipLaunchKernelGGL((split16_kernel<FMT>), grid, dim3(kThreads), 0, st, a);
+  if (heads == 16) {
+    if (a.pg.size != 0) hipLaunchKernelGGL((split16_kernel<FMT, true>), grid, dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((split16_kernel<FMT, false>), grid, dim3(kThreads), 0, st, a);
+  }
   else if (heads == 32) hipLaunchKernelGGL((split_kernel<FMT, 2>), grid, dim3(kThreads), 0, st, a);
   else hipLaunchKernelGGL((split_kernel<FMT, 4>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();

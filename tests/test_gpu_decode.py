@@ -6,6 +6,7 @@ import pytest
 import torch
 
 from gpu_util import assert_close, f32, oracle_decode, random_problem
+from mla_latent_kv_cache_amd import LatentCache
 
 pytestmark = pytest.mark.gpu
 TAU = 1.0 / np.sqrt(192.0)
@@ -41,9 +42,10 @@ def test_tile_and_split_boundaries(fmt):
 
 @pytest.mark.parametrize("fmt,heads", [("int8", 16), ("int4", 16), ("int8", 32)])
 def test_dispatch_order_ties_and_large_batch(fmt, heads):
-    # The partial kernels serve sequences in order of decreasing length (ties
-    # by index) for batches of up to 256 and in batch order above that: many
-    # tied lengths, and a batch past that bound, both against the oracle.
+    # 32+ heads: the partial kernel serves sequences in order of decreasing
+    # length (ties by index) for batches of up to 256 and in batch order above
+    # that. 16 heads: the balanced plan scans the lengths 256 at a time. Many
+    # tied lengths, and a batch past 256, both against the oracle.
     rng = np.random.default_rng(7)
     tied = rng.choice([0, 5, 33, 96, 129], size=40).tolist()
     large = rng.integers(0, 70, size=260).tolist()
@@ -115,3 +117,39 @@ def test_three_phases_equal_one_call():
     out = cache.decode_combine(wuv, ws2, num_splits=6)
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("fmt", ["int8", "int4"])
+def test_balanced_plan_runs(fmt):
+    # 16 heads: W = splits * B workgroups each take an equal run of the batch's
+    # 32-token tiles, and a run may cover the end of one sequence and the start
+    # of the next. Runs over many short and empty sequences; more workgroups
+    # than tiles (idle workgroups); every workgroup on one long sequence among
+    # empty ones (one record per workgroup for it); and a batch of 300, whose
+    # lengths are scanned in two passes of 256.
+    rng = np.random.default_rng(11)
+    cases = [
+        ([0, 1, 0, 0, 31, 33, 0, 2, 64, 0, 5, 700, 0, 0, 17], (1, 2, 5, 40, 0)),
+        ([0] * 10 + [2000] + [0] * 5, (1, 3, 0)),
+        ((rng.integers(0, 41, size=300) * (rng.random(300) > 0.2)).tolist(), (1, 2, 0)),
+    ]
+    for n, (lens, split_list) in enumerate(cases):
+        cache, rows, qn, qp, wuk, wuv = random_problem(fmt, len(lens), 16, lens, seed=60 + n)
+        for splits in split_list:
+            out = cache.decode(0, qn, qp, wuk, wuv, TAU, num_splits=splits)
+            torch.cuda.synchronize()
+            check_all(cache, rows, qn, qp, wuk, wuv, out, fmt, f"case {n} B{len(lens)} splits {splits}")
+            for b, L in enumerate(lens):
+                if L == 0:
+                    assert not out[b].any(), f"case {n} splits {splits}: empty sequence {b} not zero"
+
+
+def test_auto_split_rule_16_heads():
+    # 16 heads, num_splits = 0: floor(3 * CUs / batch) workgroups per sequence
+    # on average (three resident per CU), at most ceil(capacity / 128) (4 tiles
+    # each for full sequences), at least 1
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for B, cap in ((1, 256), (8, 4160), (32, 2048), (64, 4096), (300, 64), (1000, 64)):
+        cache = LatentCache("int8", 1, B, cap, device=torch.device("cuda"))
+        want = max(1, min(3 * cus // B, -(-cap // 128)))
+        assert cache.auto_splits(16) == want, (B, cap)
