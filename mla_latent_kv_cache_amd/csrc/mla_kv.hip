@@ -1547,8 +1547,11 @@ __device__ __forceinline__ void dequant16(const Raw16<FMT> &r, const Meta16 &m, 
       scale_split(q37, s2, h37, l37);
       hi[kk] = cat8(h04, h15, h26, h37);  // channels 0,4,1,5,2,6,3,7
       lo[kk] = cat8(l04, l15, l26, l37);
-      // columns 32 g + 8 kk (vrow is at 32 g), same order; re-paired at the final store
-      *(f16x8 *)(vrow + 8 * (kk ^ swz)) = hi[kk];
+      // the codes themselves (exact in fp16) go to the value block: the
+      // values take the scale on the softmax side, as an exact hi/lo pair.
+      // Columns 32 g + 8 kk (vrow is at 32 g), same order; re-paired at the
+      // final store.
+      *(f16x8 *)(vrow + 8 * (kk ^ swz)) = cat8(q04, q15, q26, q37);
     }
   } else {
 #pragma unroll
@@ -1706,6 +1709,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgp
 void split16_kernel(SplitArgs a) {
   constexpr bool kLo = FMT != MLA_FMT_BF16;
   constexpr bool kZp = has_zero(FMT);  // INT4 latent: zero-points, and the nibble operand order
+  // INT4 latents: weights below 2^4, as they multiply the scales in fp16
+  constexpr float kLazyOf = kZp ? 4.0f : kLazy;
   // +16: the zero-point read of the last row runs 8 fp16 past its block (unused slots)
   __shared__ __attribute__((aligned(16))) _Float16 wblk[kWaves * kWBlk];
   // partial scores of a tile; before the first tile, the plan's scratch
@@ -1833,7 +1838,20 @@ void split16_kernel(SplitArgs a) {
       // INT4: the zero-points of the wave's 8 groups go to columns 128..135 of
       // its value block (chunk 16, swapped with 17 like the others), for the
       // value-side zero-point product
-      if (kZp) *(uint32_t *)(vblk + (16 * rb + i) * kVRow + 128 + 8 * vswz(i) + 2 * g) = mt.zp[rb];
+      if (kZp) {
+        *(uint32_t *)(vblk + (16 * rb + i) * kVRow + 128 + 8 * vswz(i) + 2 * g) = mt.zp[rb];
+        // The scales of the wave's groups 2g and 2g+1 for token 16 rb + i,
+        // transposed into the other 16-byte chunk of columns 128..143 (which
+        // the zero-points leave free on every row): group n's 32 scales take
+        // rows 4n..4n+3, token order as the value product's B operand holds
+        // them (lane group g': tokens 4g'..4g'+3, then 16+4g'..16+4g'+3).
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int trow = 4 * (2 * g + h2) + (i >> 2);
+          *(uint16_t *)(vblk + trow * kVRow + 136 - 8 * vswz(trow) + 4 * rb + (i & 3)) =
+              (uint16_t)(mt.sc[rb] >> (16 * h2));
+        }
+      }
       // Every score product is a 16x16x32 MFMA, so each accumulator is fed
       // by one MFMA shape only: on this GPU a 16x16x16 MFMA that takes as its
       // accumulator the result of a 16x16x32 MFMA issued just before it reads
@@ -1902,7 +1920,7 @@ void split16_kernel(SplitArgs a) {
     // maximum exceeds it by more than 2^kLazy, so weights stay below 2^kLazy
     // (exact in fp16 relative terms) and most tiles skip the rescale.
     // Every wave holds the same scores and takes the same decision.
-    if (__builtin_amdgcn_ballot_w64(tmax > m_run + kLazy)) {
+    if (__builtin_amdgcn_ballot_w64(tmax > m_run + kLazyOf)) {
       const float m_new = fmaxf(m_run, tmax);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
@@ -1931,16 +1949,38 @@ void split16_kernel(SplitArgs a) {
     const int col = 8 * (((i >> 1) & 1) ^ sg) + 4 * (i & 1);  // this lane's 4 fp16 of 16
     const _Float16 *v0 = vblk + (4 * g + (i >> 2)) * kVRow + col;
     const _Float16 *v1 = v0 + 16 * kVRow;
+    if (kZp) {
+      // INT4: block n holds group n's codes; its scales s_t (transposed, rows
+      // 4n..4n+3) go into the weights: p_t s_t = ph + pl exactly (fp16 hi/lo;
+      // p <= 2^4 here, so the product stays in the fp16 range for any scale up
+      // to 4094, as q s did before), and acc gets sum_t p_t s_t q_t with no
+      // rounding of s q. The fp16 weights stay normal down to p = 2^-14.
+      const f16x8 pbs = pb;
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const f16x4 a0 = lds_read_tr16(v0 + 16 * n);
-      const f16x4 a1 = lds_read_tr16(v1 + 16 * n);
-      const f16x8 av = f16x8{a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb, acc[n], 0, 0, 0);
+      for (int n = 0; n < 8; ++n) {
+        const f16x4 a0 = lds_read_tr16(v0 + 16 * n);
+        const f16x4 a1 = lds_read_tr16(v1 + 16 * n);
+        const f16x8 av = f16x8{a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        const int trow = 4 * n + g;
+        const f16x8 st = *(const f16x8 *)(vblk + trow * kVRow + 136 - 8 * vswz(trow));
+        const f16x8 ph = pbs * st;
+        const f16x8 pl = __builtin_elementwise_fma(pbs, st, -ph);
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, ph, acc[n], 0, 0, 0);
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pl, acc[n], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const f16x4 a0 = lds_read_tr16(v0 + 16 * n);
+        const f16x4 a1 = lds_read_tr16(v1 + 16 * n);
+        const f16x8 av = f16x8{a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb, acc[n], 0, 0, 0);
+      }
     }
     if (kZp) {
-      // columns 128..135 of the block are the 8 groups; the lanes that read
-      // columns 136..143 fill the unused slots 8..15 of this product
+      // columns 128..135 of the block are the 8 groups' zero-points; the
+      // lanes that read the other chunk (the transposed scales) fill the
+      // unused slots 8..15 of this product
       const _Float16 *z0 = vblk + (4 * g + (i >> 2)) * kVRow + 128 + col;
       const f16x4 a0 = lds_read_tr16(z0);
       const f16x4 a1 = lds_read_tr16(z0 + 16 * kVRow);
