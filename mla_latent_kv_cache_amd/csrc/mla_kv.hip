@@ -1150,11 +1150,18 @@ void split_kernel(SplitArgs a) {
       const f16x4 pb = {(_Float16)p4[0], (_Float16)p4[1], (_Float16)p4[2], (_Float16)p4[3]};
 
       // ---- values
+      // C_hi and (quantized formats) C_lo: the value product takes the
+      // dequantized latent exactly, as the scores do; fp16 C_hi alone rounds
+      // values near 100 (outlier channels) by up to 2^-5
       const _Float16 *vb = tb + TL::kHi + (4 * g + (li >> 2)) * kLdsRow + 4 * (li & 3);
 #pragma unroll
       for (int n = 0; n < kLatent / 16; ++n) {
         const f16x4 av = lds_read_tr16(vb + 16 * n);
         acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pb, acc[n], 0, 0, 0);
+        if (kLo) {
+          const f16x4 al = lds_read_tr16(vb + (TL::kLo - TL::kHi) + 16 * n);
+          acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(al, pb, acc[n], 0, 0, 0);
+        }
       }
       if (kZp) {
         const _Float16 *zb = tb + TL::kZ + (4 * g + (li >> 2)) * kZRow + 4 * (li & 3);

@@ -153,3 +153,18 @@ def test_auto_split_rule_16_heads():
         cache = LatentCache("int8", 1, B, cap, device=torch.device("cuda"))
         want = max(1, min(3 * cus // B, -(-cap // 128)))
         assert cache.auto_splits(16) == want, (B, cap)
+
+
+@pytest.mark.parametrize("heads", [16, 32, 128])
+@pytest.mark.parametrize("fmt", ["int8", "int4", "int8_kbf16", "int4_kint4"])
+def test_short_sequences_with_outlier_channels(fmt, heads):
+    # Short sequences concentrate the softmax on a few tokens, and the x20
+    # outlier channels put latent values near 100: the value product must take
+    # the dequantized latent without fp16 rounding (2^-11 of 100 per element
+    # would show in outputs that cancel after W_UV)
+    lens = [5, 29, 60, 100, 200, 3]
+    for seed in (71, 72, 73):
+        cache, rows, qn, qp, wuk, wuv = random_problem(fmt, len(lens), heads, lens, seed=seed + heads)
+        out = cache.decode(0, qn, qp, wuk, wuv, TAU)
+        torch.cuda.synchronize()
+        check_all(cache, rows, qn, qp, wuk, wuv, out, fmt, f"{fmt} H{heads} seed {seed}")
