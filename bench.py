@@ -86,10 +86,27 @@ class Runner:
                                              num_pages=w.batch * blocks, block_table=table)
         else:
             self.cache = cache = LatentCache(w.fmt, w.layers, w.batch, cap, device=dev)
+        # The prefill goes through mla_cache_append, one call per layer, each timed
+        # with a pair of HIP events (the synthetic inputs are made outside them).
+        lens_dev = torch.tensor(self.lens0, dtype=torch.int32, device=dev) if ragged else None
+        stream = torch.cuda.current_stream()
+        self.prefill_ms, self.prefill_tokens = 0.0, 0
         for layer in range(w.layers):
             ckv, kpe = W.latent_batch(wid, layer, int(self.lens0.max()), device=dev,
                                       counts=self.lens0 if ragged else None)
-            cache.append(layer, ckv, kpe, n_new=self.lens0 if ragged else None)
+            T = ckv.shape[1]
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            _lib.check(_lib.lib().mla_cache_append(ctypes.byref(cache.struct), layer, ctypes.c_void_p(ckv.data_ptr()),
+                                                   ctypes.c_void_p(kpe.data_ptr()), T,
+                                                   ctypes.c_void_p(lens_dev.data_ptr()) if ragged else None,
+                                                   ctypes.c_void_p(stream.cuda_stream)), "prefill append")
+            e1.record(stream)
+            cache._lens[layer] += self.lens0 if ragged else T
+            e1.synchronize()
+            self.prefill_ms += e0.elapsed_time(e1)
+            self.prefill_tokens += int(self.lens0.sum()) if ragged else w.batch * T
             del ckv, kpe
         torch.cuda.synchronize()
         log(f"{w.name}: prefilled {int(self.lens0.sum()) * w.layers} tokens "
@@ -172,6 +189,48 @@ class Runner:
         return cache + weights + queries + output + append
 
 
+def append_result(what, tokens, ms, fmt):
+    """Appended tokens/s and GB/s: each token reads its bf16 row (1024 + 128 B)
+    and writes its cache row."""
+    per_token = 1152 + row_bytes(fmt)
+    return {"workload": what, "tokens": tokens, "value": tokens / (ms / 1e3), "unit": "appended tokens/s",
+            "gb_per_s": tokens * per_token / (ms / 1e3) / 1e9, "bytes_per_token": per_token, "ms": ms}
+
+
+def measure_append64(reps=50):
+    """The decode-time append of the INT8 workload of 8 sequences: 64 new tokens
+    per sequence in one mla_cache_append call, repeated into fresh rows; each
+    call timed with HIP events."""
+    import torch
+    from mla_latent_kv_cache_amd import LatentCache, _lib
+    from mla_latent_kv_cache_amd import workloads as W
+    wid = 1
+    w = W.WORKLOADS[wid]
+    dev = torch.device("cuda:0")
+    T = w.append
+    cache = LatentCache(w.fmt, 1, w.batch, T * (reps + 5), device=dev)
+    ckv, kpe = W.latent_batch(wid, 0, T, device=dev, kind="append")
+    stream = torch.cuda.current_stream()
+    L = _lib.lib()
+    ms = []
+    for i in range(reps + 5):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        _lib.check(L.mla_cache_append(ctypes.byref(cache.struct), 0, ctypes.c_void_p(ckv.data_ptr()),
+                                      ctypes.c_void_p(kpe.data_ptr()), T, None,
+                                      ctypes.c_void_p(stream.cuda_stream)), "append")
+        e1.record(stream)
+        cache._lens[0] += T
+        if i >= 5:
+            ms.append((e0, e1))
+    torch.cuda.synchronize()
+    total = sum(a.elapsed_time(b) for a, b in ms)
+    res = append_result(f"{w.fmt} B{w.batch} T{T} per call", reps * w.batch * T, total, w.fmt)
+    res["us_per_call"] = total / reps * 1e3
+    return res
+
+
 def measure(wid, steps, warmup, fmt=None, layers=None, page_size=0):
     """W untimed steps, then the K timed steps (value, ms_per_step), then K more
     steps with a pair of HIP events around every partial-attention launch (its
@@ -220,6 +279,7 @@ def measure(wid, steps, warmup, fmt=None, layers=None, page_size=0):
         "partial_launches": len(part_ms),
     }
     res["hbm_frac"] = res["gb_per_s"] / HBM_PEAK_GBS
+    res["prefill"] = append_result(r.w.name + " prefill", r.prefill_tokens, r.prefill_ms, r.w.fmt)
     log(f"{r.w.name}: {res['ms_per_step']:.3f} ms/step, {res['value'] / 1e9:.2f} G KV-tokens/s, "
         f"{res['gb_per_s']:.0f} GB/s step ({100 * res['hbm_frac']:.1f}% of 8 TB/s); partial kernel "
         f"{res['partial_avg_us']:.1f} us/launch, {res['partial_gb_per_s']:.0f} GB/s")
@@ -510,6 +570,9 @@ def main():
         formats["int8_paged64"] = {k: rp[k] for k in keys}
         formats["int8_paged64"]["unit"] = "KV-tokens/s"
         formats["int8_paged64"]["roofline"] = roofline(rp)
+    append = {"prefill_" + main_res["fmt"]: main_res["prefill"], "decode_append_int8": measure_append64()}
+    if args.int4_workload >= 0:
+        append["prefill_int4"] = r4["prefill"]
     cpu = None
     if args.cpu_seconds > 0:
         log("timing the oracle on the host cores")
@@ -540,6 +603,7 @@ def main():
         "cpu_baseline": cpu,
         "int4": int4,
         "formats": formats,
+        "append": append,
     }
     print(json.dumps(line), flush=True)
 

@@ -998,9 +998,10 @@ template <int FMT, int HGW> struct SplitLds {
 //           A = tile row t = i, B = this lane's head i held in registers;
 //           lane (g, i) gets tokens 4g..4g+3 of head i. INT4 adds
 //           sum_g z[t][g] Qsum[h][g] for the zero-points.
-//   values  O^T[c][h] += sum_t C_hi[t][c] P[t][h]: 32 MFMA 16x16x16 f16 per
-//           tile; B = P exactly as the score MFMA left it in registers,
-//           A = channel 16n+i of tokens 4g..4g+3 by an LDS transpose read;
+//   values  O^T[c][h] += sum_t (C_hi + C_lo)[t][c] P[t][h]: 64 MFMA 16x16x16
+//           f16 per tile (32 for bf16 latents, which have no C_lo); B = P
+//           exactly as the score MFMA left it in registers, A = channel
+//           16n+i of tokens 4g..4g+3 by an LDS transpose read;
 //           lane (g, i) accumulates channels 16n+4g..16n+4g+3 of head i.
 //           INT4 accumulates sum_t P[t][h] z[t][g] beside it.
 template <int FMT, int HGW>
@@ -1237,10 +1238,12 @@ void split_kernel(SplitArgs a) {
 //           accumulation); the four partial score tiles meet in LDS and every
 //           wave adds them in the same order, so all waves hold the same
 //           scores and the same softmax state;
-//   values  accumulates O^T[c][h] = sum_t C_hi[t][c] P[t][h] for its own 128
-//           channels: its C_hi goes to a wave-private LDS block and comes back
-//           transposed (ds_read_b64_tr_b16) as the A operand, P is the B
-//           operand exactly as the score MFMA left it in registers.
+//   values  accumulates O^T[c][h] = sum_t C[t][c] P[t][h] for its own 128
+//           channels: its C_hi (INT4: the exact codes) goes to a wave-private
+//           LDS block and comes back transposed (ds_read_b64_tr_b16) as the A
+//           operand; P is the B operand as the score MFMA left it in
+//           registers (INT4: P times each group's scales, as an exact fp16
+//           hi/lo pair).
 // Lane l = 16g + i: in the score, row i of each 16-token half of the tile and
 // channels 32g..32g+31 of the wave's block (two quantization groups); in the
 // accumulators, head i.
