@@ -75,6 +75,7 @@ constexpr int kMaxSplits = 4096;
 constexpr int kAutoMinChunk = 256;         // fewest tokens per split in the automatic plan
 constexpr int kAutoMinTiles = 4;           // 16 heads: fewest 32-token tiles per workgroup (full sequences)
 constexpr int kWgPerCu = 3;                // resident 16-head partial workgroups per CU
+constexpr float kLazy = 8.0f;              // log2 of the largest softmax weight before a rescale
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -1132,22 +1133,30 @@ void split_kernel(SplitArgs a) {
       }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m_run, tmax);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      // Lazy running max, as in the 16-head kernel: the reference point moves
+      // only when some head's tile maximum exceeds it by more than 2^kLazy
+      // (weights stay below 2^kLazy, exact in fp16 relative terms), so most
+      // tiles skip rescaling the wave's 512 channels of sums. The wave's own
+      // heads decide (one wave holds 16 heads and their softmax state).
+      if (__builtin_amdgcn_ballot_w64(tmax > m_run + kLazy)) {
+        const float m_new = fmaxf(m_run, tmax);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+        m_run = m_new;
+#pragma unroll
+        for (int n = 0; n < kLatent / 16; ++n) acc[n] *= alpha;
+        if (kZp) {
+          accz[0] *= alpha;
+          accz[1] *= alpha;
+        }
+      }
       float psum = 0.0f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p4[r] = __builtin_amdgcn_exp2f(p4[r] - m_new);
+        p4[r] = __builtin_amdgcn_exp2f(p4[r] - m_run);
         psum += p4[r];
       }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int n = 0; n < kLatent / 16; ++n) acc[n] *= alpha;
-      if (kZp) {
-        accz[0] *= alpha;
-        accz[1] *= alpha;
-      }
+      l_run += psum;
       const f16x4 pb = {(_Float16)p4[0], (_Float16)p4[1], (_Float16)p4[2], (_Float16)p4[3]};
 
       // ---- values
@@ -1252,7 +1261,6 @@ constexpr int kT16 = 32;             // tokens per tile
 #define MLA_NPF16 1
 #endif
 constexpr int kNpf16 = MLA_NPF16;    // tiles of loads in flight per wave
-constexpr float kLazy = 8.0f;         // log2 of the largest softmax weight before a rescale
 // A wave's value block: 32 rows (tokens) of 128 channels, then (INT4) the 8
 // zero-points of the wave's groups, padded to 144 fp16 (72 dwords, 8 banks
 // apart), so the four rows a transposed read spans start 8 banks apart and
