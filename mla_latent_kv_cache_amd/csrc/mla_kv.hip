@@ -1844,6 +1844,11 @@ void split16_kernel(SplitArgs a) {
 
     // ---- 2. dequantize in registers; partial scores; C_hi to the value block
     f32x4 sc[2];
+    // Wave priority: a wave issuing its dequantization and score MFMAs (and,
+    // below, its value MFMAs) goes before the other waves of the SIMD, which
+    // are then mostly waiting on loads or a barrier; the matrix and vector
+    // pipes stay fed. About 3% on the INT8 and INT4 partial launches.
+    __builtin_amdgcn_s_setprio(2);
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       f16x8 hi[4], lo[4];
@@ -1896,6 +1901,7 @@ void split16_kernel(SplitArgs a) {
       sc[rb] = s;
     }
 
+    __builtin_amdgcn_s_setprio(0);
     // ---- 3. the next tile's loads. They go out only after the score sums
     // above have been read back from the MFMA results, so no matrix
     // instruction is still pending when they are issued: a load that falls
@@ -1958,6 +1964,7 @@ void split16_kernel(SplitArgs a) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) pb[r] = (_Float16)p8[r];
 
+    __builtin_amdgcn_s_setprio(2);
     // values of this wave's 128 channels (its own block, no barrier needed)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -2005,6 +2012,7 @@ void split16_kernel(SplitArgs a) {
       const f16x8 az = f16x8{a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
       accz = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, pb, accz, 0, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 
   }
