@@ -167,20 +167,15 @@ int mla_decode_auto_splits(const mla_cache *cache, int32_t heads, int32_t *num_s
  *   w_uv     bf16 [heads][512][128]    value up-projection: V[h] = c W_UV[h]
  *   heads    16, 32, 64 or 128
  *   softmax_scale   multiplies q.k before the softmax (e.g. 1/sqrt(192))
- *   num_splits      0 = auto, else 1..4096.
- *                   32, 64, 128 heads: KV splits per sequence. Split s of
- *                   sequence b covers tokens [s*chunk, (s+1)*chunk) with
- *                   chunk = ceil(seq_len / num_splits) rounded up to 32, and
- *                   for num_splits = 0 at least 256 (short sequences use
- *                   fewer splits).
- *                   16 heads: splits per sequence on average. The partial
- *                   phase runs W = num_splits * batch workgroups; the
- *                   batch's 32-token tiles, sequence after sequence, are
- *                   cut into W equal runs (a run may end one sequence and
- *                   start the next), so every workgroup gets the same work
- *                   whatever the mix of lengths. Auto: about three
- *                   workgroups per CU, at least 4 tiles each for full
- *                   sequences.
+ *   num_splits      0 = auto, else 1..4096: KV splits per sequence on
+ *                   average. The batch's 32-token tiles, sequence after
+ *                   sequence, are cut into W = num_splits * batch equal runs
+ *                   (a run may end one sequence and start the next), so the
+ *                   work is the same for every run whatever the mix of
+ *                   lengths; the partial phase runs each run once per slice
+ *                   of 16 heads (W * heads / 16 workgroups). Auto: about
+ *                   three workgroups per CU, at least 4 tiles per run for
+ *                   full sequences.
  *   workspace       device scratch of at least mla_decode_workspace_bytes;
  *                   its contents on entry do not matter
  *   out      fp32 [batch][heads][128]
@@ -252,8 +247,9 @@ int mla_decode_step_begin(const mla_cache *cache, int32_t layer, const void *ckv
  *
  *   absorb    q_abs = softmax_scale * log2(e) * q_nope W_UK[h], and q_pe scaled
  *             the same way, into the workspace (fp16)
- *   partial   split-KV attention of each (sequence, split) over the cache of
- *             `layer`: per-split running max, sum and unnormalized latent sum
+ *   partial   split-KV attention of each run of tiles (see num_splits) over
+ *             the cache of `layer`: per (run, sequence) running max, sum and
+ *             unnormalized latent sum
  *             into the workspace (the hot loop)
  *   combine   log-sum-exp merge of the splits, normalization, and projection
  *             through W_UV into out

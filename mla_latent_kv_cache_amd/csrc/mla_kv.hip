@@ -17,10 +17,13 @@
 //   append_kernel       quantize new bf16 rows into the cache planes
 //   seqlen_kernel       advance seq_lens after an append
 //   absorb_kernel       q_abs = scale*log2(e) * q_nope W_UK[h]  -> fp16 workspace
-//   split_kernel        split-KV partial attention over one token range per
-//                       workgroup: 16-byte loads of codes, in-register dequant
-//                       to fp16, LDS tile, MFMA scores and MFMA value sums,
-//                       online softmax in base 2
+//   append_step_kernel  one new token per sequence (the decode step's append)
+//   step_kernel         the fused step's first launch: absorb, turn and store
+//   split16_kernel      split-KV partial attention: each workgroup takes an
+//                       equal run of the batch's 32-token tiles for 16 heads
+//                       (a head slice of the query); 16-byte loads of codes,
+//                       in-register dequant to fp16, MFMA scores and value
+//                       sums, online softmax in base 2
 //   reduce_kernel       log-sum-exp merge of the splits, then o_lat W_UV[h]
 //   get_kernel          dequantize a layer to fp32 (inspection aid)
 
@@ -66,15 +69,11 @@ constexpr int kpe_bytes(int f) {
   return kpe_fmt(f) == kKpeBf16 ? kRope * 2 : kpe_fmt(f) == kKpeI8 ? kRope : kRope / 2;
 }
 constexpr bool has_zero(int f) { return lat_fmt(f) == MLA_FMT_INT4; }
-constexpr int kTile = 16;                  // tokens per MFMA tile
-constexpr int kLdsRow = kRow + 8;          // fp16 per LDS tile row (1168 B, breaks bank aliasing)
 constexpr int kWaves = 4;                  // waves per split workgroup
 constexpr int kThreads = kWaves * 64;
-constexpr int kMrgRow = kLatent + 4;       // fp32 per head row in the merge area
 constexpr int kMaxSplits = 4096;
-constexpr int kAutoMinChunk = 256;         // fewest tokens per split in the automatic plan
-constexpr int kAutoMinTiles = 4;           // 16 heads: fewest 32-token tiles per workgroup (full sequences)
-constexpr int kWgPerCu = 3;                // resident 16-head partial workgroups per CU
+constexpr int kAutoMinTiles = 4;           // fewest 32-token tiles per range of the automatic plan (full sequences)
+constexpr int kWgPerCu = 3;                // resident partial workgroups per CU
 constexpr float kLazy = 8.0f;              // log2 of the largest softmax weight before a rescale
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -604,40 +603,10 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs s) {
 
 // ------------------------------------------------------------- split-KV core
 
-// Raw 16-byte chunks a lane loads for one token tile, before dequantization.
-// Lane l, chunk k of a plane covers the 16 bytes at l + 64*k of the tile's
-// contiguous rows of that plane (perfectly coalesced: a wave reads 1 KB).
+// Row bytes of a format's latent and k_pe planes.
 template <int FMT> struct Fmt {
   static constexpr int kLatRowBytes = ckv_bytes(FMT);
   static constexpr int kKpeRowBytes = kpe_bytes(FMT);
-  static constexpr int kLat = kTile * kLatRowBytes / 16 / 64;  // latent chunks per lane (BF16 16, INT8 8, INT4 4)
-  static constexpr int kKpeChunks = kTile * kKpeRowBytes / 16;  // the tile's k_pe chunks (128, 64 or 32)
-  static constexpr int kKpe = (kKpeChunks + 63) / 64;           // per lane; INT4 k_pe: lanes 0..31 only
-};
-
-// Latent chunk k of lane l in a 16-row tile (one block of the latent plane):
-// the tile's bytes in order, 16 per lane, so chunk k of lane l is row l % 16,
-// chunk l / 16 + 4 k (the block stores chunk c of row i at (16 c + i) * 16).
-template <int FMT> __device__ __forceinline__ int lat_row(int lane, int k) { return lane & 15; }
-template <int FMT> __device__ __forceinline__ int lat_chunk(int lane, int k) { return (lane >> 4) + 4 * k; }
-template <int FMT> __device__ __forceinline__ int kpe_row(int lane, int k) {
-  constexpr int per_row = Fmt<FMT>::kKpeRowBytes / 16;
-  return (lane + 64 * k) / per_row;
-}
-template <int FMT> __device__ __forceinline__ int kpe_chunk(int lane) {
-  constexpr int per_row = Fmt<FMT>::kKpeRowBytes / 16;
-  return lane % per_row;
-}
-
-template <int FMT, int NW>  // NW: waves sharing (and splitting) the dequant of one tile
-struct RawTile {
-  static constexpr int kLat = Fmt<FMT>::kLat / NW;
-  static constexpr int kKpe = (Fmt<FMT>::kKpe + NW - 1) / NW;
-  u32x4 lat[kLat];
-  u32x4 kpe[kKpe];
-  uint32_t lsc[kLat];   // latent scale bits (INT8: one group; INT4: two groups packed)
-  uint32_t lzp[kLat];   // INT4 zero-point bits (two groups packed)
-  u32x2 ksc[kKpe];      // k_pe scale bits (INT8 k_pe: two groups in .x; INT4 k_pe: four groups)
 };
 
 struct SplitArgs {
@@ -647,64 +616,13 @@ struct SplitArgs {
   const uint16_t *zero;
   const int32_t *seq_lens;  // layer row
   const _Float16 *qa;       // [B][H][kQRec]
-  float *ws_m;              // [records][H]: [B][nsplit] for 32+ heads, W + B for 16
+  float *ws_m;              // [records][H], records <= W + B (the balanced plan)
   float *ws_l;              // [records][H]
   float *ws_acc;            // [records][H][512]
-  int32_t *rec_tab;         // 16 heads: [B][2] first record and record count
+  int32_t *rec_tab;         // [B][2] first record and record count
   Paging pg;
-  int B, H, cap, nsplit, min_chunk, hh_count;
+  int B, H, cap, nsplit;
 };
-
-// Dispatch order of the partial kernels: grid row r (blockIdx.y) serves the
-// sequence of rank r when sequences are ranked by decreasing length (ties by
-// index). Workgroups are dispatched in grid order, so the longest splits start
-// first and the short ones fill the compute units behind them, instead of a
-// long split starting last and running alone at the end. The rank is found by
-// the workgroup itself from the lengths (one compare per pair of sequences) for
-// batches of up to kRankMaxB; larger batches keep the identity order.
-constexpr int kRankMaxB = 256;
-static_assert(kThreads >= kRankMaxB, "one thread per ranked sequence");
-
-// Call with every thread of a 256-thread workgroup (it holds barriers).
-// Returns the sequence of this workgroup's grid row, uniform across it, and in
-// L its length clamped to [0, cap] (from the copy in LDS: a second read from
-// global memory would add one more round trip before the first tile's loads).
-__device__ __forceinline__ int seq_of_row(const int *seq_lens, int B, int cap, int *lens_sh, int *sel, int &L) {
-  const int row = blockIdx.y;
-  if (B > kRankMaxB) {
-    L = min(max(seq_lens[row], 0), cap);
-    return row;
-  }
-  const int tid = threadIdx.x;
-  const int B4 = (B + 3) & ~3;  // lengths padded with -1 to whole groups of 4 (they never count)
-  if (tid < B4) lens_sh[tid] = tid < B ? min(max(seq_lens[tid], 0), cap) : -1;
-  __syncthreads();
-  if (tid < B) {
-    const int lt = lens_sh[tid];
-    int r = 0;
-    // four lengths per LDS read, the reads unrolled so that their latencies
-    // overlap (one dependent read per sequence made this loop the longest
-    // part of a short workgroup)
-#pragma unroll 8
-    for (int j = 0; j < B4; j += 4) {
-      const i32x4 l4 = *(const i32x4 *)(lens_sh + j);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) r += (l4[k] > lt) | ((l4[k] == lt) & (j + k < tid));
-    }
-    if (r == row) *sel = tid;  // ranks are a permutation: exactly one thread writes
-  }
-  __syncthreads();
-  const int b = __builtin_amdgcn_readfirstlane(*sel);
-  L = __builtin_amdgcn_readfirstlane(lens_sh[b]);
-  return b;
-}
-
-// Tokens per split of a sequence of length L: ceil(L / nsplit) rounded up to a
-// whole 32-token tile, and at least min_chunk. Splits past the sequence are empty.
-__device__ __forceinline__ int split_chunk(int L, int nsplit, int min_chunk) {
-  const int c = ((L + nsplit - 1) / nsplit + 31) / 32 * 32;
-  return max(c, min_chunk);
-}
 
 // Buffer descriptors over one split's rows of each plane. A buffer load past
 // the descriptor's byte count returns zero without touching memory, so rows
@@ -758,54 +676,6 @@ __device__ __forceinline__ SplitRsrc page_rsrc(const SplitArgs &a, int page, int
   return rows_rsrc<FMT>(a, row0, row0, end - r0);
 }
 
-// The page of token r of sequence b for page_rsrc (-1 past t_end).
-__device__ __forceinline__ int tile_page(const SplitArgs &a, int b, int r, int t_end) {
-  return r < t_end ? page_of(a.pg, b, r) : -1;
-}
-
-// Raw chunks of the tile whose first row is row `r0` of the split.
-// r0: the tile's first row in the descriptors (a block start). The latent
-// descriptor covers whole blocks, so rows from `left` on (past the split) are
-// read too: quantized rows there dequantize to zero (their scales and
-// zero-points read as zeros), bf16 rows are pointed past the descriptor.
-template <int FMT, int NW>
-__device__ __forceinline__ void load_raw(RawTile<FMT, NW> &r, const SplitRsrc &rs, int r0, int left, int lane,
-                                         int hw) {
-#pragma unroll
-  for (int j = 0; j < RawTile<FMT, NW>::kLat; ++j) {
-    const int k = j * NW + hw;
-    const int tr = lat_row<FMT>(lane, k);
-    const int row = r0 + tr;
-    const int ch = lat_chunk<FMT>(lane, k);
-    // lat_off(row, ch) with r0 a block start: the tile's bytes in lane order
-    const int loff = lat_fmt(FMT) != MLA_FMT_BF16 || tr < left ? r0 * Fmt<FMT>::kLatRowBytes + (lane + 64 * k) * 16
-                                                                 : kOffNone;
-    r.lat[j] = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rs.ckv, loff, 0, kLatLoadPolicy));
-    constexpr int NS = n_scales(FMT);
-    if (lat_fmt(FMT) == MLA_FMT_INT8) {
-      r.lsc[j] = __builtin_amdgcn_raw_buffer_load_b16(rs.scale, row * NS * 2 + ch * 2, 0, 0);
-    } else if (lat_fmt(FMT) == MLA_FMT_INT4) {
-      r.lsc[j] = __builtin_amdgcn_raw_buffer_load_b32(rs.scale, row * NS * 2 + ch * 4, 0, 0);
-      r.lzp[j] = __builtin_amdgcn_raw_buffer_load_b32(rs.zero, row * kNGroupL * 2 + ch * 4, 0, 0);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < RawTile<FMT, NW>::kKpe; ++j) {
-    const int k = j * NW + hw;
-    // lanes and waves past the last chunk read nothing (zeros)
-    const bool have = lane + 64 * k < Fmt<FMT>::kKpeChunks;
-    const int row = r0 + kpe_row<FMT>(lane, have ? k : 0);
-    const int ch = kpe_chunk<FMT>(lane);
-    const int off = have ? row * Fmt<FMT>::kKpeRowBytes + ch * 16 : kOffNone;
-    r.kpe[j] = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rs.kpe, off, 0, 0));
-    const int soff = row * n_scales(FMT) * 2 + kNGroupL * 2;
-    if (kpe_fmt(FMT) == kKpeI8)
-      r.ksc[j].x = __builtin_amdgcn_raw_buffer_load_b32(rs.scale, have ? soff + ch * 4 : kOffNone, 0, 0);
-    else if (kpe_fmt(FMT) == kKpeI4)
-      r.ksc[j] = bitcast<u32x2>(__builtin_amdgcn_raw_buffer_load_b64(rs.scale, have ? soff + ch * 8 : kOffNone, 0, 0));
-  }
-}
-
 // 4 signed bytes -> the 4 codes as exact fp16: bias to unsigned, splice into
 // the mantissa of 1024.0, subtract 1152 (both exact).
 __device__ __forceinline__ void codes_i8x4(uint32_t w, f16x2 &lo, f16x2 &hi) {
@@ -834,139 +704,6 @@ __device__ __forceinline__ f16x2 splat_f16_bits(uint32_t bits16) {
   return f16x2{h, h};
 }
 
-__device__ __forceinline__ void st16(_Float16 *p, f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
-  u32x4 v = {bitcast<uint32_t>(a), bitcast<uint32_t>(b), bitcast<uint32_t>(c), bitcast<uint32_t>(d)};
-  *(u32x4 *)p = v;
-}
-
-// LDS tile of one token group: dequantized latent+k_pe rows as fp16 hi
-// ([16][kLdsRow]), their exact fp16 residuals lo (quantized formats), and the
-// per-group zero-points ([16][kZRow], INT4).
-constexpr int kZRow = 40;  // fp16 per zero-point row (80 B: 16-byte aligned rows)
-template <int FMT> struct TileLayout {
-  static constexpr int kHi = 0;
-  static constexpr int kLo = kTile * kLdsRow;
-  static constexpr int kZ = kLo + (FMT == MLA_FMT_BF16 ? 0 : kTile * kLdsRow);
-  static constexpr int kHalves = kZ + (has_zero(FMT) ? kTile * kZRow : 0);
-  static constexpr int kBytes = kHalves * 2;
-};
-
-// Dequantize this lane's raw chunks into the LDS tile.
-template <int FMT, int NW>
-__device__ __forceinline__ void dequant_store(const RawTile<FMT, NW> &r, _Float16 *tile, int lane,
-                                              int hw) {
-  using TL = TileLayout<FMT>;
-#pragma unroll
-  for (int j = 0; j < RawTile<FMT, NW>::kLat; ++j) {
-    const int k = j * NW + hw;
-    const int tr = lat_row<FMT>(lane, k);
-    const int ch = lat_chunk<FMT>(lane, k);
-    const u32x4 v = r.lat[j];
-    if (lat_fmt(FMT) == MLA_FMT_INT8) {
-      const f16x2 s2 = splat_f16_bits(r.lsc[j]);
-      f16x2 hi[8], lo[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f16x2 q0, q1;
-        codes_i8x4(v[i], q0, q1);
-        scale_split(q0, s2, hi[2 * i], lo[2 * i]);
-        scale_split(q1, s2, hi[2 * i + 1], lo[2 * i + 1]);
-      }
-      _Float16 *dh = tile + TL::kHi + tr * kLdsRow + ch * 16;
-      _Float16 *dl = tile + TL::kLo + tr * kLdsRow + ch * 16;
-      st16(dh, hi[0], hi[1], hi[2], hi[3]);
-      st16(dh + 8, hi[4], hi[5], hi[6], hi[7]);
-      st16(dl, lo[0], lo[1], lo[2], lo[3]);
-      st16(dl + 8, lo[4], lo[5], lo[6], lo[7]);
-    } else if (lat_fmt(FMT) == MLA_FMT_INT4) {
-      // 32 channels: bytes 0-7 in group 2ch (scale/zero low half), 8-15 in 2ch+1.
-      // The tile holds q*s; the zero-points go to their own rows and enter
-      // the scores and the value sums through separate exact products.
-      const f16x2 s0 = splat_f16_bits(r.lsc[j] & 0xFFFFu), s1 = splat_f16_bits(r.lsc[j] >> 16);
-      _Float16 *dh = tile + TL::kHi + tr * kLdsRow + ch * 32;
-      _Float16 *dl = tile + TL::kLo + tr * kLdsRow + ch * 32;
-      const f16x2 bias = {(_Float16)1024.0f, (_Float16)1024.0f};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t w = v[i];
-        const f16x2 s2 = i < 2 ? s0 : s1;
-        // nibble j of w is channel 8i + j; pairs (0,4), (1,5), (2,6), (3,7)
-        const f16x2 q04 = bitcast<f16x2>((w & 0x000F000Fu) | 0x64006400u) - bias;
-        const f16x2 q15 = bitcast<f16x2>(((w >> 4) & 0x000F000Fu) | 0x64006400u) - bias;
-        const f16x2 q26 = bitcast<f16x2>(((w >> 8) & 0x000F000Fu) | 0x64006400u) - bias;
-        const f16x2 q37 = bitcast<f16x2>(((w >> 12) & 0x000F000Fu) | 0x64006400u) - bias;
-        f16x2 h04, l04, h15, l15, h26, l26, h37, l37;
-        scale_split(q04, s2, h04, l04);
-        scale_split(q15, s2, h15, l15);
-        scale_split(q26, s2, h26, l26);
-        scale_split(q37, s2, h37, l37);
-        st16(dh + 8 * i, f16x2{h04.x, h15.x}, f16x2{h26.x, h37.x}, f16x2{h04.y, h15.y},
-             f16x2{h26.y, h37.y});
-        st16(dl + 8 * i, f16x2{l04.x, l15.x}, f16x2{l26.x, l37.x}, f16x2{l04.y, l15.y},
-             f16x2{l26.y, l37.y});
-      }
-      *(uint32_t *)(tile + TL::kZ + tr * kZRow + 2 * ch) = r.lzp[j];
-    } else {
-      _Float16 *dst = tile + TL::kHi + tr * kLdsRow + ch * 8;
-      st16(dst, bf16x2_to_f16x2(v[0]), bf16x2_to_f16x2(v[1]), bf16x2_to_f16x2(v[2]),
-           bf16x2_to_f16x2(v[3]));
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < RawTile<FMT, NW>::kKpe; ++j) {
-    const int k = j * NW + hw;
-    if (lane + 64 * k >= Fmt<FMT>::kKpeChunks) continue;
-    const int tr = kpe_row<FMT>(lane, k);
-    const int ch = kpe_chunk<FMT>(lane);
-    const u32x4 v = r.kpe[j];
-    if (kpe_fmt(FMT) == kKpeBf16) {
-      _Float16 *dst = tile + TL::kHi + tr * kLdsRow + kLatent + ch * 8;
-      st16(dst, bf16x2_to_f16x2(v[0]), bf16x2_to_f16x2(v[1]), bf16x2_to_f16x2(v[2]),
-           bf16x2_to_f16x2(v[3]));
-      if (FMT != MLA_FMT_BF16) {  // a quantized latent has a lo tile: bf16 k_pe is exact in hi
-        const f16x2 z = {(_Float16)0.0f, (_Float16)0.0f};
-        st16(tile + TL::kLo + tr * kLdsRow + kLatent + ch * 8, z, z, z, z);
-      }
-    } else if (kpe_fmt(FMT) == kKpeI4) {
-      // 32 channels = k_pe groups 4ch .. 4ch+3, one dword (8 nibbles, code + 8,
-      // the even channel low) each
-      const f16x2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
-      _Float16 *dh = tile + TL::kHi + tr * kLdsRow + kLatent + ch * 32;
-      _Float16 *dl = tile + TL::kLo + tr * kLdsRow + kLatent + ch * 32;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f16x2 s2 = splat_f16_bits((i < 2 ? r.ksc[j].x : r.ksc[j].y) >> (16 * (i & 1)));
-        f16x2 hi[4], lo[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint32_t u = v[i] >> (8 * p);  // channels 2p, 2p+1 of the group
-          const f16x2 q = bitcast<f16x2>((u & 0xFu) | ((u & 0xF0u) << 12) | 0x64006400u) - bias;
-          scale_split(q, s2, hi[p], lo[p]);
-        }
-        st16(dh + 8 * i, hi[0], hi[1], hi[2], hi[3]);
-        st16(dl + 8 * i, lo[0], lo[1], lo[2], lo[3]);
-      }
-    } else {
-      // 16 channels = k_pe groups 2ch (bytes 0-7) and 2ch+1 (bytes 8-15)
-      const f16x2 s0 = splat_f16_bits(r.ksc[j].x & 0xFFFFu), s1 = splat_f16_bits(r.ksc[j].x >> 16);
-      f16x2 hi[8], lo[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f16x2 q0, q1;
-        codes_i8x4(v[i], q0, q1);
-        scale_split(q0, i < 2 ? s0 : s1, hi[2 * i], lo[2 * i]);
-        scale_split(q1, i < 2 ? s0 : s1, hi[2 * i + 1], lo[2 * i + 1]);
-      }
-      _Float16 *dh = tile + TL::kHi + tr * kLdsRow + kLatent + ch * 16;
-      _Float16 *dl = tile + TL::kLo + tr * kLdsRow + kLatent + ch * 16;
-      st16(dh, hi[0], hi[1], hi[2], hi[3]);
-      st16(dh + 8, hi[4], hi[5], hi[6], hi[7]);
-      st16(dl, lo[0], lo[1], lo[2], lo[3]);
-      st16(dl + 8, lo[4], lo[5], lo[6], lo[7]);
-    }
-  }
-}
-
 typedef __fp16 fp16x4_lds __attribute__((__vector_size__(4 * sizeof(__fp16))));
 
 // LDS transpose read (gfx950 ds_read_b64_tr_b16): in each 16-lane group g,
@@ -978,266 +715,10 @@ __device__ __forceinline__ f16x4 lds_read_tr16(const _Float16 *p) {
   return bitcast<f16x4>(v);
 }
 
-constexpr int kMergeBytes = kWaves * 16 * kMrgRow * 4;             // 132,096
-constexpr int kOzBytes = kWaves * 16 * kNGroupL * 4;               // 8,192
-template <int FMT, int HGW> struct SplitLds {
-  static constexpr int TG = kWaves / HGW;
-  static constexpr int NBUF = HGW == 1 ? 1 : 2;
-  static constexpr int kTiles = TG * NBUF * TileLayout<FMT>::kBytes;
-  static constexpr int kEnd = kMergeBytes + kOzBytes;
-  static constexpr int kBytes = kTiles > kEnd ? kTiles : kEnd;
-};
+// ------------------------------------------------------- split-KV core
 
-// One workgroup = 4 waves = one (sequence b, split s, head block hh) unit.
-// HGW waves (one per 16 heads) share each token tile; the 4/HGW token groups
-// take interleaved tiles of the split and are merged at the end through LDS.
-//
-// Per wave, with lane = 16*g + i (g = 0..3, i = 0..15):
-//   scores  S^T[t][h] = sum_c C[t][c] Q[h][c], as C_hi Q_hi + C_hi Q_lo +
-//           C_lo Q_hi with 16x16x32 f16 MFMAs (fp32 accumulation), which keeps
-//           the scores to about fp32 accuracy although every operand is fp16;
-//           A = tile row t = i, B = this lane's head i held in registers;
-//           lane (g, i) gets tokens 4g..4g+3 of head i. INT4 adds
-//           sum_g z[t][g] Qsum[h][g] for the zero-points.
-//   values  O^T[c][h] += sum_t (C_hi + C_lo)[t][c] P[t][h]: 64 MFMA 16x16x16
-//           f16 per tile (32 for bf16 latents, which have no C_lo); B = P
-//           exactly as the score MFMA left it in registers, A = channel
-//           16n+i of tokens 4g..4g+3 by an LDS transpose read;
-//           lane (g, i) accumulates channels 16n+4g..16n+4g+3 of head i.
-//           INT4 accumulates sum_t P[t][h] z[t][g] beside it.
-template <int FMT, int HGW>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
-void split_kernel(SplitArgs a) {
-  using TL = TileLayout<FMT>;
-  using LD = SplitLds<FMT, HGW>;
-  constexpr int TG = LD::TG;                        // token groups
-  constexpr int NBUF = LD::NBUF;                    // wave-private tile, or double-buffered shared
-  constexpr int NPF = 1;                            // raw tiles in flight per wave
-  constexpr bool kLo = FMT != MLA_FMT_BF16;
-  constexpr bool kZp = has_zero(FMT);
-  __shared__ __attribute__((aligned(16))) unsigned char lds[LD::kBytes];
-  __shared__ float ml_m[kWaves][16], ml_l[kWaves][16];
-  __shared__ __attribute__((aligned(16))) int rank_lens[kRankMaxB];
-  __shared__ int rank_sel;
-
-  const int split = blockIdx.x / a.hh_count;
-  const int hh = blockIdx.x % a.hh_count;
-  int L;
-  const int b = seq_of_row(a.seq_lens, a.B, a.cap, rank_lens, &rank_sel, L);
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int g = lane >> 4, li = lane & 15;
-  const int tg = wave / HGW, hw = wave % HGW;
-  const int head0 = (hh * HGW) * 16;              // first head of this workgroup
-  const int head = head0 + hw * 16 + li;          // the head this lane's columns belong to
-
-  const int chunk = split_chunk(L, a.nsplit, a.min_chunk);
-  const int t_begin = min(split * chunk, L);
-  const int t_end = min(t_begin + chunk, L);
-  const int64_t ws_row = ((int64_t)b * a.nsplit + split) * a.H;
-  if (t_begin >= t_end) {  // empty unit: identity of the merge
-    if (tid < HGW * 16) {
-      a.ws_m[ws_row + head0 + tid] = -INFINITY;
-      a.ws_l[ws_row + head0 + tid] = 0.0f;
-    }
-    return;
-  }
-  const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
-  const int niters = (ntiles + TG - 1) / TG;
-
-  // Queries of head `head` in the MFMA B layout: k-step s holds channels 32s+8g..+7.
-  f16x8 qh[kRow / 32], ql[kRow / 32], qsh, qsl;
-  {
-    const _Float16 *q = a.qa + ((int64_t)b * a.H + head) * kQRec + 8 * g;
-#pragma unroll
-    for (int s = 0; s < kRow / 32; ++s) {
-      qh[s] = *(const f16x8 *)(q + kQHi + 32 * s);
-      ql[s] = *(const f16x8 *)(q + kQLo + 32 * s);
-    }
-    qsh = *(const f16x8 *)(q + kQSumHi);
-    qsl = *(const f16x8 *)(q + kQSumLo);
-  }
-
-  f32x4 acc[kLatent / 16];
-#pragma unroll
-  for (int n = 0; n < kLatent / 16; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 accz[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-  float m_run = -INFINITY, l_run = 0.0f;
-
-  _Float16 *tiles = (_Float16 *)lds + (int64_t)tg * NBUF * TL::kHalves;
-
-  // contiguous: one descriptor over the split, tiles at row offsets; paged:
-  // a descriptor per 16-token tile (a tile never crosses a page)
-  const bool paged = a.pg.size != 0;
-  const SplitRsrc rs = paged ? rows_rsrc<FMT>(a, 0, 0, 0) : split_rsrc<FMT>(a, b, t_begin, t_end);
-  auto load_tile = [&](RawTile<FMT, HGW> &r, int tile) {
-    const int r0 = t_begin + tile * kTile;
-    if (paged) {
-      load_raw<FMT, HGW>(r, page_rsrc<FMT>(a, tile_page(a, b, r0, t_end), r0, t_end), 0, t_end - r0, lane, hw);
-    } else {
-      load_raw<FMT, HGW>(r, rs, tile * kTile, t_end - r0, lane, hw);
-    }
-  };
-  RawTile<FMT, HGW> raw[NPF];
-#pragma unroll
-  for (int p = 0; p < NPF; ++p) load_tile(raw[p], tg + p * TG);
-
-  for (int it0 = 0; it0 < niters; it0 += NPF) {
-#pragma unroll
-    for (int p = 0; p < NPF; ++p) {
-      const int it = it0 + p;
-      if (it >= niters) break;  // uniform across the workgroup
-      const int tile = tg + it * TG;
-      const bool valid = tile < ntiles;
-      _Float16 *tb = tiles + (NBUF == 1 ? 0 : (it & 1)) * TL::kHalves;
-      if (valid) dequant_store<FMT, HGW>(raw[p], tb, lane, hw);
-      lds_stores_done();
-      load_tile(raw[p], tile + NPF * TG);
-      if (HGW > 1) {
-        __syncthreads();
-      } else {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      }
-      if (!valid) continue;
-      const int t0 = t_begin + tile * kTile;
-
-      // ---- scores (three fp16 products keep about fp32 accuracy)
-      f32x4 sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
-      const _Float16 *rh = tb + TL::kHi + li * kLdsRow + 8 * g;
-      const _Float16 *rl = tb + TL::kLo + li * kLdsRow + 8 * g;
-#pragma unroll
-      for (int s = 0; s < kRow / 32; ++s) {
-        const f16x8 ah = *(const f16x8 *)(rh + 32 * s);
-        sc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, qh[s], sc0, 0, 0, 0);
-        sc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, ql[s], sc1, 0, 0, 0);
-        if (kLo) {
-          const f16x8 al = *(const f16x8 *)(rl + 32 * s);
-          sc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, qh[s], sc1, 0, 0, 0);
-        }
-      }
-      if (kZp) {
-        const f16x8 az = *(const f16x8 *)(tb + TL::kZ + li * kZRow + 8 * g);
-        sc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, qsh, sc1, 0, 0, 0);
-        sc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, qsl, sc1, 0, 0, 0);
-      }
-      const f32x4 sc = sc0 + sc1;
-      // ---- online softmax (base 2); lane (g, i) holds tokens t0+4g+r of head i
-      float p4[4];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p4[r] = (t0 + 4 * g + r < t_end) ? sc[r] : -INFINITY;
-        tmax = fmaxf(tmax, p4[r]);
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      // Lazy running max, as in the 16-head kernel: the reference point moves
-      // only when some head's tile maximum exceeds it by more than 2^kLazy
-      // (weights stay below 2^kLazy, exact in fp16 relative terms), so most
-      // tiles skip rescaling the wave's 512 channels of sums. The wave's own
-      // heads decide (one wave holds 16 heads and their softmax state).
-      if (__builtin_amdgcn_ballot_w64(tmax > m_run + kLazy)) {
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-        m_run = m_new;
-#pragma unroll
-        for (int n = 0; n < kLatent / 16; ++n) acc[n] *= alpha;
-        if (kZp) {
-          accz[0] *= alpha;
-          accz[1] *= alpha;
-        }
-      }
-      float psum = 0.0f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p4[r] = __builtin_amdgcn_exp2f(p4[r] - m_run);
-        psum += p4[r];
-      }
-      l_run += psum;
-      const f16x4 pb = {(_Float16)p4[0], (_Float16)p4[1], (_Float16)p4[2], (_Float16)p4[3]};
-
-      // ---- values
-      // C_hi and (quantized formats) C_lo: the value product takes the
-      // dequantized latent exactly, as the scores do; fp16 C_hi alone rounds
-      // values near 100 (outlier channels) by up to 2^-5
-      const _Float16 *vb = tb + TL::kHi + (4 * g + (li >> 2)) * kLdsRow + 4 * (li & 3);
-#pragma unroll
-      for (int n = 0; n < kLatent / 16; ++n) {
-        const f16x4 av = lds_read_tr16(vb + 16 * n);
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pb, acc[n], 0, 0, 0);
-        if (kLo) {
-          const f16x4 al = lds_read_tr16(vb + (TL::kLo - TL::kHi) + 16 * n);
-          acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(al, pb, acc[n], 0, 0, 0);
-        }
-      }
-      if (kZp) {
-        const _Float16 *zb = tb + TL::kZ + (4 * g + (li >> 2)) * kZRow + 4 * (li & 3);
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-          const f16x4 az = lds_read_tr16(zb + 16 * n);
-          accz[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(az, pb, accz[n], 0, 0, 0);
-        }
-      }
-    }
-  }
-
-  // ---- merge the token groups of this workgroup through LDS, write the partial
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  __syncthreads();  // every wave is done with the tiles; the area becomes the merge area
-  float *mrg = (float *)lds;
-  if (kZp) {
-    // add sum_t p_t z[t][g(c)] to every channel c of group g(c) = n
-    float *oz = (float *)(lds + kMergeBytes) + (int64_t)wave * 16 * kNGroupL;
-#pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) oz[li * kNGroupL + 16 * n + 4 * g + r] = accz[n][r];
-    lds_stores_done();
-#pragma unroll
-    for (int n = 0; n < kLatent / 16; ++n) acc[n] += oz[li * kNGroupL + n];
-  }
-  if (g == 0) {
-    ml_m[wave][li] = m_run;
-    ml_l[wave][li] = l_run;
-  }
-  {
-    float *dst = mrg + ((int64_t)wave * 16 + li) * kMrgRow + 4 * g;
-#pragma unroll
-    for (int n = 0; n < kLatent / 16; ++n) *(f32x4 *)(dst + 16 * n) = acc[n];
-  }
-  lds_stores_done();
-  __syncthreads();
-  // HGW*16 heads x 512 channels, 256 threads: thread -> (head-in-block, channel)
-  for (int e = tid; e < HGW * 16 * kLatent; e += kThreads) {
-    const int c = e % kLatent;
-    const int hb = e / kLatent;  // 0 .. HGW*16-1
-    const int w_hw = hb / 16, w_li = hb % 16;
-    float M = -INFINITY;
-#pragma unroll
-    for (int q = 0; q < TG; ++q) M = fmaxf(M, ml_m[q * HGW + w_hw][w_li]);
-    float o = 0.0f, l = 0.0f;
-#pragma unroll
-    for (int q = 0; q < TG; ++q) {
-      const float mq = ml_m[q * HGW + w_hw][w_li];
-      const float w = mq == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mq - M);
-      o += w * mrg[((int64_t)(q * HGW + w_hw) * 16 + w_li) * kMrgRow + c];
-      l += w * ml_l[q * HGW + w_hw][w_li];
-    }
-    a.ws_acc[(ws_row + head0 + hb) * kLatent + c] = o;
-    if (c == 0) {
-      a.ws_m[ws_row + head0 + hb] = M;
-      a.ws_l[ws_row + head0 + hb] = l;
-    }
-  }
-}
-
-// ------------------------------------------------- split-KV core, 16 heads
-
-// For 16 heads the four waves of a workgroup share each 32-token tile and
+// For one slice of 16 heads the four waves of a workgroup share each 32-token
+// tile and
 // divide the channels: wave w owns latent channels [128w, 128w+128) and k_pe
 // channels [16w, 16w+16). Each wave loads its channels of the tile straight
 // into the MFMA operand layout, dequantizes them in registers (as fp16 hi and
@@ -1657,10 +1138,10 @@ struct PlanStart {
   int g0, g1;   // the workgroup's global tiles [g0, g1)
 };
 
-// Every thread calls it (barriers inside); sh holds at least kWaves + 3 ints.
-__device__ __forceinline__ PlanStart plan_start(const SplitArgs &a, int *sh) {
+// Range wg of the W ranges. Every thread calls it (barriers inside); sh holds
+// at least kWaves + 3 ints.
+__device__ __forceinline__ PlanStart plan_start(const SplitArgs &a, int W, int wg, int *sh) {
   const int tid = threadIdx.x;
-  const int W = gridDim.x, wg = blockIdx.x;
   int T = 0, n0 = 0, incl0 = 0, L0 = 0, tot0 = 0;
   for (int c0 = 0; c0 < a.B; c0 += kThreads) {  // total tiles
     const int b = c0 + tid;
@@ -1701,7 +1182,7 @@ __device__ __forceinline__ PlanStart plan_start(const SplitArgs &a, int *sh) {
         sh[kWaves + 1] = S;
         sh[kWaves + 2] = L;
       }
-      if (wg == 0) {
+      if (blockIdx.x == 0) {  // the first workgroup of the grid
         const int first = n > 0 ? S / q : 0;
         a.rec_tab[2 * b] = first + b;
         a.rec_tab[2 * b + 1] = n > 0 ? (S + n - 1) / q - first + 1 : 0;
@@ -1741,7 +1222,13 @@ void split16_kernel(SplitArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 4, i = lane & 15;
 
-  const PlanStart plan = plan_start(a, (int *)part);
+  // More than 16 heads: the grid holds W ranges x (H / 16) head slices, the
+  // slices of a range adjacent, so that they run together and read the
+  // range's tiles while they are still in the caches; slice hs serves heads
+  // 16 hs .. 16 hs + 15 (its queries and its rows of every record).
+  const int nslice = a.H / 16;
+  const int rng = blockIdx.x / nslice, hs = blockIdx.x % nslice;
+  const PlanStart plan = plan_start(a, gridDim.x / nslice, rng, (int *)part);
   int b = plan.b, S = plan.S, L = plan.L;
   // one pass per sequence the range covers (all uniform across the workgroup)
   while (b < a.B) {
@@ -1753,14 +1240,14 @@ void split16_kernel(SplitArgs a) {
   const int n = tiles_of(L);
   const int t_begin = __builtin_amdgcn_readfirstlane((max(plan.g0, S) - S) * kT16);
   const int t_end = __builtin_amdgcn_readfirstlane(min(L, (min(plan.g1, S + n) - S) * kT16));
-  const int64_t ws_row = ((int64_t)blockIdx.x + b) * a.H;
+  const int64_t ws_row = ((int64_t)rng + b) * a.H + 16 * hs;
   const int ntiles = (t_end - t_begin + kT16 - 1) / kT16;
 
   // queries of head i for this wave's channels, in the MFMA B layout
   f16x8 qh[4], ql[4];
   f16x8 kzh, kzl;  // k_pe channels 16w+4g..+3, then (INT4) the sums of groups 8w+2g, +1, then 0
   {
-    const _Float16 *q = a.qa + ((int64_t)b * a.H + i) * kQRec;
+    const _Float16 *q = a.qa + ((int64_t)b * a.H + 16 * hs + i) * kQRec;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       qh[kk] = *(const f16x8 *)(q + kQHi + lane_chan<FMT>(w, g, kk));
@@ -2078,7 +1565,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 constexpr int kMergeChunk = 16;  // splits merged per round of loads
 
 // Per (head h, 4 batch rows), two waves per row (each half of the 512 latent
-// channels): merge the splits with log-sum-exp weights and normalize, then all
+// channels): merge the sequence's partial records (the splits: first record
+// and count from the partial kernel's table) with log-sum-exp weights and
+// normalize, then all
 // eight waves form out[b,h,:] = o_lat W_UV[h]. The merge takes the splits 16 at
 // a time: lane s loads m and l of split s while every lane loads its 4 latent
 // channels of all 16 splits, in one round of loads. The chunk's maximum updates
@@ -2093,8 +1582,7 @@ static_assert(kReduceBT * kVDim == kReduceThreads && kReduceCS * 16 == kLatent &
               "two waves per row, one output per thread");
 __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const float *ws_m, const float *ws_l,
                                                                 const float *ws_acc, const int32_t *rec_tab,
-                                                                const uint16_t *w_uv, int B, int H, int nsplit,
-                                                                float *out) {
+                                                                const uint16_t *w_uv, int B, int H, float *out) {
   __shared__ float olat[kReduceBT][kLatent];
   __shared__ float red[kReduceCS][kReduceBT][kVDim];
   const int h = blockIdx.x;
@@ -2105,13 +1593,9 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const float *ws_
   const int b = b0 + bt;  // uniform across the wave
   f32x4 o0 = {0.f, 0.f, 0.f, 0.f};
   if (b < B) {
-    // the sequence's records: nsplit from b * nsplit, or (16 heads) as the
-    // partial kernel's table lists them
-    int first = b * nsplit, count = nsplit;
-    if (rec_tab) {
-      first = __builtin_amdgcn_readfirstlane(rec_tab[2 * b]);
-      count = __builtin_amdgcn_readfirstlane(rec_tab[2 * b + 1]);
-    }
+    // the sequence's records, as the partial kernel's table lists them
+    const int first = __builtin_amdgcn_readfirstlane(rec_tab[2 * b]);
+    const int count = __builtin_amdgcn_readfirstlane(rec_tab[2 * b + 1]);
     const int64_t base = (int64_t)first * H + h;
     const float *acc = ws_acc + base * kLatent + (kLatent / 2) * half + 4 * lane;
     float M = -INFINITY, Ls = 0.0f;
@@ -2334,11 +1818,11 @@ struct WsLayout {
   size_t qa, m, l, acc, tab, total;
 };
 
-// Partial records: nsplit per sequence for 32+ heads; for 16 heads one per
-// (workgroup, sequence) pair of the balanced plan, W + B with W = nsplit * B
-// workgroups, plus the per-sequence record table.
+// Partial records: one per (range, sequence) pair of the balanced plan, at
+// most W + B with W = nsplit * B ranges, each with rows for all H heads; then
+// the per-sequence record table.
 WsLayout ws_layout(int B, int H, int nsplit) {
-  const size_t recs = (size_t)B * nsplit + (H == 16 ? (size_t)B : 0);
+  const size_t recs = (size_t)B * nsplit + (size_t)B;
   WsLayout w;
   size_t off = 0;
   w.qa = off;
@@ -2350,7 +1834,7 @@ WsLayout ws_layout(int B, int H, int nsplit) {
   w.acc = off;
   off = align256(off + recs * H * kLatent * 4);
   w.tab = off;
-  off = align256(off + (H == 16 ? (size_t)B * 2 * 4 : 0));
+  off = align256(off + (size_t)B * 2 * 4);
   w.total = off;
   return w;
 }
@@ -2361,27 +1845,12 @@ int auto_splits(const mla_cache *c, int heads, int *out) {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return MLA_ERR_HIP;
   if (cus < 1) cus = 1;
-  if (heads == 16) {
-    // Balanced plan: nsplit * B workgroups of equal work, as many as are
-    // resident at once (three per CU), and at least kAutoMinTiles tiles each
-    // when every sequence is full.
-    int64_t ns = (int64_t)kWgPerCu * cus / c->batch;
-    const int64_t by_len = ((int64_t)c->capacity + kT16 * kAutoMinTiles - 1) / (kT16 * kAutoMinTiles);
-    if (ns > by_len) ns = by_len;
-    if (ns < 1) ns = 1;
-    if (ns > kMaxSplits) ns = kMaxSplits;
-    *out = (int)ns;
-    return MLA_OK;
-  }
-  const int hh = heads <= 64 ? 1 : heads / 64;
-  const int64_t units = (int64_t)c->batch * hh;
-  // About four workgroups per CU when every sequence is full (the partial
-  // kernels dispatch the longest sequences first, so ragged batches still
-  // balance); splits of the automatic plan hold at least kAutoMinChunk tokens,
-  // so short sequences use fewer of them.
-  int64_t want = (4 * (int64_t)cus + units - 1) / units;
-  const int64_t by_len = (c->capacity + kAutoMinChunk - 1) / kAutoMinChunk;
-  int64_t ns = want < by_len ? want : by_len;
+  // Balanced plan: nsplit * B ranges of equal work, times heads / 16 head
+  // slices, as many workgroups as are resident at once (three per CU), and at
+  // least kAutoMinTiles tiles per range when every sequence is full.
+  int64_t ns = (int64_t)kWgPerCu * cus / ((int64_t)c->batch * (heads / 16));
+  const int64_t by_len = ((int64_t)c->capacity + kT16 * kAutoMinTiles - 1) / (kT16 * kAutoMinTiles);
+  if (ns > by_len) ns = by_len;
   if (ns < 1) ns = 1;
   if (ns > kMaxSplits) ns = kMaxSplits;
   *out = (int)ns;
@@ -2390,13 +1859,9 @@ int auto_splits(const mla_cache *c, int heads, int *out) {
 
 
 template <int FMT>
-hipError_t launch_split_fmt(const SplitArgs &a, int heads, dim3 grid, hipStream_t st) {
-  if (heads == 16) {
-    if (a.pg.size != 0) hipLaunchKernelGGL((split16_kernel<FMT, true>), grid, dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL((split16_kernel<FMT, false>), grid, dim3(kThreads), 0, st, a);
-  }
-  else if (heads == 32) hipLaunchKernelGGL((split_kernel<FMT, 2>), grid, dim3(kThreads), 0, st, a);
-  else hipLaunchKernelGGL((split_kernel<FMT, 4>), grid, dim3(kThreads), 0, st, a);
+hipError_t launch_split_fmt(const SplitArgs &a, dim3 grid, hipStream_t st) {
+  if (a.pg.size != 0) hipLaunchKernelGGL((split16_kernel<FMT, true>), grid, dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL((split16_kernel<FMT, false>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -2489,7 +1954,6 @@ namespace {
 
 struct DecodePlan {
   int ns;
-  int min_chunk;  // kAutoMinChunk for the automatic split count, else one tile
   WsLayout wl;
 };
 
@@ -2507,7 +1971,6 @@ int plan_decode(const mla_cache *cache, int heads, int num_splits, const void *w
     if (st != MLA_OK) return st;
   }
   plan->ns = ns;
-  plan->min_chunk = num_splits == 0 ? kAutoMinChunk : kT16;
   plan->wl = ws_layout(cache->batch, heads, ns);
   if (!workspace || workspace_bytes < plan->wl.total || ((uintptr_t)workspace & 255u))
     return MLA_ERR_WORKSPACE;
@@ -2555,15 +2018,12 @@ int run_partial(const mla_cache *cache, const DecodePlan &pl, int layer, int hea
   a.H = heads;
   a.cap = cache->capacity;
   a.nsplit = pl.ns;
-  a.min_chunk = pl.min_chunk;
   a.pg = paging_of(cache);
-  a.hh_count = heads <= 64 ? 1 : heads / 64;
   a.rec_tab = (int32_t *)(ws + pl.wl.tab);
-  // 16 heads: the balanced plan's nsplit * B workgroups in one row
-  const dim3 grid = heads == 16 ? dim3((unsigned)(pl.ns * cache->batch))
-                                : dim3((unsigned)(pl.ns * a.hh_count), (unsigned)cache->batch);
+  // the balanced plan's nsplit * B ranges, each as heads / 16 adjacent head slices
+  const dim3 grid((unsigned)((int64_t)pl.ns * cache->batch * (heads / 16)));
   hipError_t e = hipSuccess;
-  with_format(cache->format, [&](auto f) { e = launch_split_fmt<decltype(f)::value>(a, heads, grid, s); });
+  with_format(cache->format, [&](auto f) { e = launch_split_fmt<decltype(f)::value>(a, grid, s); });
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -2573,8 +2033,8 @@ int run_combine(const mla_cache *cache, const DecodePlan &pl, const void *w_uv, 
   uint8_t *ws = (uint8_t *)workspace;
   hipLaunchKernelGGL(reduce_kernel, dim3(heads, (B + kReduceBT - 1) / kReduceBT), dim3(kReduceThreads), 0, s,
                      (const float *)(ws + pl.wl.m), (const float *)(ws + pl.wl.l),
-                     (const float *)(ws + pl.wl.acc), heads == 16 ? (const int32_t *)(ws + pl.wl.tab) : nullptr,
-                     (const uint16_t *)w_uv, B, heads, pl.ns, out);
+                     (const float *)(ws + pl.wl.acc), (const int32_t *)(ws + pl.wl.tab),
+                     (const uint16_t *)w_uv, B, heads, out);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

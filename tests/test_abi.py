@@ -64,18 +64,18 @@ def test_workspace_size_formula():
     # absorbed queries: per (sequence, head) 576 channels as fp16 hi and lo, plus
     # 32 group sums as hi and lo
     qa = a256(B * H * (2 * 576 + 2 * 32) * 2)
-    # 16 heads: ns * B workgroups of the balanced plan, one record per
-    # (workgroup, sequence) pair it covers, at most ns * B + B; then the
-    # per-sequence table (first record, count) as int32 pairs
+    # the balanced plan's ns * B ranges, one record per (range, sequence) pair
+    # a range covers, at most ns * B + B; then the per-sequence table (first
+    # record, count) as int32 pairs
     recs = ns * B + B
     expect = qa + 2 * a256(recs * H * 4) + a256(recs * H * 512 * 4) + a256(B * 2 * 4)
     assert n == expect
-    # 32+ heads: ns records per sequence, no table
+    # any head count: the same records and table, rows for every head
     st, n = _ws(s, 32, 4)
     assert st == 0
     H = 32
     qa = a256(B * H * (2 * 576 + 2 * 32) * 2)
-    assert n == qa + 2 * a256(B * ns * H * 4) + a256(B * ns * H * 512 * 4)
+    assert n == qa + 2 * a256(recs * H * 4) + a256(recs * H * 512 * 4) + a256(B * 2 * 4)
 
 
 @pytest.mark.parametrize("field,value,status", [
