@@ -621,7 +621,7 @@ struct SplitArgs {
   float *ws_acc;            // [records][H][512]
   int32_t *rec_tab;         // [B][2] first record and record count
   Paging pg;
-  int B, H, cap, nsplit;
+  int B, H, cap;
 };
 
 // Buffer descriptors over one split's rows of each plane. A buffer load past
@@ -718,9 +718,8 @@ __device__ __forceinline__ f16x4 lds_read_tr16(const _Float16 *p) {
 // ------------------------------------------------------- split-KV core
 
 // For one slice of 16 heads the four waves of a workgroup share each 32-token
-// tile and
-// divide the channels: wave w owns latent channels [128w, 128w+128) and k_pe
-// channels [16w, 16w+16). Each wave loads its channels of the tile straight
+// tile and divide the channels: wave w owns latent channels [128w, 128w+128)
+// and k_pe channels [16w, 16w+16). Each wave loads its channels of the tile straight
 // into the MFMA operand layout, dequantizes them in registers (as fp16 hi and
 // exact residual lo), and
 //   scores  adds its share of S^T[t][h] = sum_c C[t][c] Q[h][c] as
@@ -743,7 +742,8 @@ constexpr int kT16 = 32;             // tokens per tile
 #endif
 constexpr int kNpf16 = MLA_NPF16;    // tiles of loads in flight per wave
 // A wave's value block: 32 rows (tokens) of 128 channels, then (INT4) the 8
-// zero-points of the wave's groups, padded to 144 fp16 (72 dwords, 8 banks
+// zero-points of the wave's groups in one 16-byte chunk and the wave's group
+// scales, transposed, in the other; rows of 144 fp16 (72 dwords, 8 banks
 // apart), so the four rows a transposed read spans start 8 banks apart and
 // never share a bank. Writes go row per lane, 16 bytes at a time; there the
 // 16-byte chunks of rows with bit 2 xor bit 3 of the row set are swapped in
@@ -2017,7 +2017,6 @@ int run_partial(const mla_cache *cache, const DecodePlan &pl, int layer, int hea
   a.B = cache->batch;
   a.H = heads;
   a.cap = cache->capacity;
-  a.nsplit = pl.ns;
   a.pg = paging_of(cache);
   a.rec_tab = (int32_t *)(ws + pl.wl.tab);
   // the balanced plan's nsplit * B ranges, each as heads / 16 adjacent head slices
