@@ -307,7 +307,7 @@ def roofline(res):
         "bound": "hbm", "achieved": round(res["partial_gb_per_s"], 1), "peak": HBM_PEAK_GBS,
         "unit": "GB/s", "frac": round(res["partial_gb_per_s"] / HBM_PEAK_GBS, 4),
         "traffic": stored_traffic(res["workload"]),
-        "kernel": ("split16_kernel" if res["heads"] == 16 else "split_kernel") + " (mla_decode_partial)",
+        "kernel": "split16_kernel (mla_decode_partial)",
         "per_launch_bytes": res["partial_bytes_per_launch"],
         "avg_launch_us": round(res["partial_avg_us"], 2),
         "launches_timed": res["partial_launches"],
@@ -402,7 +402,7 @@ def _pmc_means(csv_path, counter):
             if row["Counter_Name"] != counter:
                 continue
             name = row["Kernel_Name"]
-            kind = "partial" if "split16_kernel" in name or "split_kernel" in name else \
+            kind = "partial" if "split16_kernel" in name else \
                 "copy" if "copyBuffer" in name or "copy" in name.lower() else None
             if kind is None:
                 continue

@@ -42,10 +42,10 @@ def test_tile_and_split_boundaries(fmt):
 
 @pytest.mark.parametrize("fmt,heads", [("int8", 16), ("int4", 16), ("int8", 32)])
 def test_dispatch_order_ties_and_large_batch(fmt, heads):
-    # 32+ heads: the partial kernel serves sequences in order of decreasing
-    # length (ties by index) for batches of up to 256 and in batch order above
-    # that. 16 heads: the balanced plan scans the lengths 256 at a time. Many
-    # tied lengths, and a batch past 256, both against the oracle.
+    # The balanced plan scans the lengths 256 at a time and cuts the batch's
+    # tiles into equal runs: many tied lengths, and a batch past 256 (two
+    # passes of the scan), at 16 heads and at 32 (two head slices), both
+    # against the oracle.
     rng = np.random.default_rng(7)
     tied = rng.choice([0, 5, 33, 96, 129], size=40).tolist()
     large = rng.integers(0, 70, size=260).tolist()
