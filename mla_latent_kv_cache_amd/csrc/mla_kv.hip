@@ -348,19 +348,19 @@ __device__ __forceinline__ void append_group(const AppendArgs &a, int b, int t, 
   }
 }
 
-// Bulk append: one thread per quantization group, grid-stride over B*T*40.
-// seq_lens advances in seqlen_kernel, launched after it on the same stream,
-// so every block reads the old length.
+// Bulk append: one thread per quantization group of one new row; grid row y
+// serves sequences y, y + gridDim.y, ..., whose n_new[b] rows take the first
+// n_new[b] * 40 threads of the row (blocks past them skip the sequence at once,
+// so the padding of a ragged batch costs nothing, and no index needs a
+// division by a runtime count). seq_lens advances in seqlen_kernel, launched
+// after it on the same stream, so every block reads the old length.
 template <int FMT>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
-  const int64_t total = (int64_t)a.B * a.T * kNScale;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * blockDim.x) {
-    const int grp = (int)(idx % kNScale);
-    const int64_t bt = idx / kNScale;
-    const int t = (int)(bt % a.T);
-    const int b = (int)(bt / a.T);
-    const int n = a.n_new ? a.n_new[b] : a.T;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int t = (int)(idx / kNScale);
+  const int grp = (int)(idx % kNScale);
+  for (int b = blockIdx.y; b < a.B; b += gridDim.y) {
+    const int n = a.n_new ? min(max(a.n_new[b], 0), a.T) : a.T;
     if (t >= n) continue;
     const int pos = a.seq_lens[b] + t;
     if (pos < 0 || pos >= a.cap) continue;
@@ -1913,11 +1913,10 @@ extern "C" int mla_cache_append(const mla_cache *cache, int32_t layer, const voi
     });
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
   }
-  const int64_t items = (int64_t)a.B * a.T * kNScale;
-  int64_t blocks = (items + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
+  const int64_t blocks = ((int64_t)a.T * kNScale + 255) / 256;
+  const unsigned rows = (unsigned)(a.B < 65535 ? a.B : 65535);  // grid rows (sequences strided over them)
   with_format(cache->format, [&](auto f) {
-    hipLaunchKernelGGL(append_kernel<decltype(f)::value>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(append_kernel<decltype(f)::value>, dim3((unsigned)blocks, rows), dim3(256), 0, s, a);
   });
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
   hipLaunchKernelGGL(seqlen_kernel, dim3((a.B + 255) / 256), dim3(256), 0, s, p.seq_lens, n_new, a.B,
