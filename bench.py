@@ -444,7 +444,8 @@ def summarize_stats(wid, stats_csv, out_path, steps, warmup):
         f"#   python3 bench.py --summarize-stats <dir>/run_kernel_stats.csv --workload {wid} "
         f"--steps {steps} --warmup {warmup}",
         "# Rows: this library's kernels (the torch kernels that build the synthetic inputs are omitted).",
-        "# append_kernel<f> is the one-off prefill. A decode step runs, per layer, step_kernel<f>",
+        "# append_kernel<f> is the prefill (one call per layer) and the benchmark's decode-time append of",
+        "# 8 x 64 tokens (55 short calls). A decode step runs, per layer, step_kernel<f>",
         "# (mla_decode_step_begin: store the new token with its k_pe turned, absorb the turned query),",
         "# split16_kernel<f> (mla_decode_partial, 16 heads) and reduce_kernel (mla_decode_combine).",
         "# <f>: 0 bf16, 1 INT8, 2 INT4, 3 INT8 latent + bf16 k_pe, 4 INT4 latent + INT4 k_pe.",
