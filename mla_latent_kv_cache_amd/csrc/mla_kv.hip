@@ -622,6 +622,7 @@ struct SplitArgs {
   int32_t *rec_tab;         // [B][2] first record and record count
   Paging pg;
   int B, H, cap;
+  int W;  // ranges of the balanced plan
 };
 
 // Buffer descriptors over one split's rows of each plane. A buffer load past
@@ -632,6 +633,12 @@ struct SplitArgs {
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9 buffer resource dword 3
 constexpr int kOffNone = 0x7FFFFFF0;        // an offset past any descriptor
 constexpr int kLatLoadPolicy = 2;           // buffer-load cache policy operand: nt (non-temporal)
+#ifndef MLA_SLICE_POLICY
+#define MLA_SLICE_POLICY 0
+#endif
+// more than 16 heads: every head slice reads the latent, so the lines are
+// worth keeping in the caches (the default policy)
+constexpr int kSliceLoadPolicy = MLA_SLICE_POLICY;
 
 struct SplitRsrc {
   __amdgpu_buffer_rsrc_t ckv, kpe, scale, zero;
@@ -902,7 +909,7 @@ __device__ __forceinline__ SplitRsrc tile_rsrc(const SplitArgs &a, int b, int r0
 // (their scales and zero-points, read through plain row descriptors, are
 // zero); bf16 rows could hold anything, so from row `left` of the tile on
 // (bf16 latents only) their loads are pointed past the descriptor.
-template <int FMT>
+template <int FMT, int POL>
 __device__ __forceinline__ void load16_lat(Raw16<FMT> &r, const SplitRsrc &rs, const Off16<FMT> &o, int left,
                                            int i) {
 #pragma unroll
@@ -910,7 +917,7 @@ __device__ __forceinline__ void load16_lat(Raw16<FMT> &r, const SplitRsrc &rs, c
 #pragma unroll
     for (int j = 0; j < Raw16<FMT>::kLat; ++j) {
       const int off = lat_fmt(FMT) == MLA_FMT_BF16 && 16 * rb + i >= left ? kOffNone : o.lat[rb][j];
-      r.lat[rb][j] = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rs.ckv, off, 0, kLatLoadPolicy));
+      r.lat[rb][j] = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rs.ckv, off, 0, POL));
     }
 }
 
@@ -1202,8 +1209,9 @@ __device__ __forceinline__ PlanStart plan_start(const SplitArgs &a, int W, int w
 }
 
 // PAGED: the cache is paged (a compile-time choice: the per-tile descriptor code
-// of the other layout is then absent from the tile loop)
-template <int FMT, bool PAGED>
+// of the other layout is then absent from the tile loop). SLICED: more than 16
+// heads, run as head slices that each read the latent.
+template <int FMT, bool PAGED, bool SLICED>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(3, 3)))
 void split16_kernel(SplitArgs a) {
   constexpr bool kLo = FMT != MLA_FMT_BF16;
@@ -1226,9 +1234,14 @@ void split16_kernel(SplitArgs a) {
   // slices of a range adjacent, so that they run together and read the
   // range's tiles while they are still in the caches; slice hs serves heads
   // 16 hs .. 16 hs + 15 (its queries and its rows of every record).
+  // Workgroups are handed to the 8 XCDs (each with its own L2) round-robin
+  // by index, so the slices of a range sit 8 indices apart: all on one XCD,
+  // in one window of 8 * nslice indices. Indices past the W ranges (the grid
+  // is rounded up to whole windows) get empty ranges.
   const int nslice = a.H / 16;
-  const int rng = blockIdx.x / nslice, hs = blockIdx.x % nslice;
-  const PlanStart plan = plan_start(a, gridDim.x / nslice, rng, (int *)part);
+  const int win = blockIdx.x / (8 * nslice), in_win = blockIdx.x % (8 * nslice);
+  const int hs = in_win / 8, rng = 8 * win + in_win % 8;
+  const PlanStart plan = plan_start(a, a.W, rng, (int *)part);
   int b = plan.b, S = plan.S, L = plan.L;
   // one pass per sequence the range covers (all uniform across the workgroup)
   while (b < a.B) {
@@ -1289,6 +1302,7 @@ void split16_kernel(SplitArgs a) {
   // (vector) load: a scalar load would share its wait counter with LDS
   // traffic, and every LDS wait of the tile would then wait for it too.
   constexpr bool paged = PAGED;
+  constexpr int kPol = SLICED ? kSliceLoadPolicy : kLatLoadPolicy;  // latent loads' cache policy
   const __amdgpu_buffer_rsrc_t trow =
       make_rsrc(paged ? (const void *)(a.pg.table + (int64_t)b * a.pg.max_pages) : a.kpe,
                 paged ? a.pg.max_pages * 4 : 0);
@@ -1308,7 +1322,7 @@ void split16_kernel(SplitArgs a) {
     const int r0 = t_begin + p * kT16;
     const SplitRsrc rs0 = rsrc_of(r0, paged ? checked(page_entry(r0), r0) : 0);
     load16_small<FMT>(raw[p], rs0, off, zero_b);
-    load16_lat<FMT>(raw[p], rs0, off, t_end - r0, i);
+    load16_lat<FMT, kPol>(raw[p], rs0, off, t_end - r0, i);
   }
   uint32_t next_entry = paged ? page_entry(t_begin + kNpf16 * kT16) : 0u;
 
@@ -1397,7 +1411,7 @@ void split16_kernel(SplitArgs a) {
     // Always issued, so the count of outstanding loads is the same on every
     // path.
     __builtin_amdgcn_sched_barrier(0);
-    load16_lat<FMT>(raw[p], rs_next, off, t_end - r_next, i);
+    load16_lat<FMT, kPol>(raw[p], rs_next, off, t_end - r_next, i);
     if (paged) next_entry = page_entry(r_next + kT16);
 
     // ---- 4. partial scores of the four waves
@@ -1860,8 +1874,14 @@ int auto_splits(const mla_cache *c, int heads, int *out) {
 
 template <int FMT>
 hipError_t launch_split_fmt(const SplitArgs &a, dim3 grid, hipStream_t st) {
-  if (a.pg.size != 0) hipLaunchKernelGGL((split16_kernel<FMT, true>), grid, dim3(kThreads), 0, st, a);
-  else hipLaunchKernelGGL((split16_kernel<FMT, false>), grid, dim3(kThreads), 0, st, a);
+  const bool sliced = a.H > 16;
+  if (a.pg.size != 0) {
+    if (sliced) hipLaunchKernelGGL((split16_kernel<FMT, true, true>), grid, dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((split16_kernel<FMT, true, false>), grid, dim3(kThreads), 0, st, a);
+  } else {
+    if (sliced) hipLaunchKernelGGL((split16_kernel<FMT, false, true>), grid, dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((split16_kernel<FMT, false, false>), grid, dim3(kThreads), 0, st, a);
+  }
   return hipGetLastError();
 }
 
@@ -2018,8 +2038,10 @@ int run_partial(const mla_cache *cache, const DecodePlan &pl, int layer, int hea
   a.cap = cache->capacity;
   a.pg = paging_of(cache);
   a.rec_tab = (int32_t *)(ws + pl.wl.tab);
-  // the balanced plan's nsplit * B ranges, each as heads / 16 adjacent head slices
-  const dim3 grid((unsigned)((int64_t)pl.ns * cache->batch * (heads / 16)));
+  // the balanced plan's nsplit * B ranges, each as heads / 16 head slices,
+  // rounded up to whole windows of 8 ranges (see split16_kernel)
+  a.W = pl.ns * cache->batch;
+  const dim3 grid((unsigned)(((int64_t)a.W + 7) / 8 * 8 * (heads / 16)));
   hipError_t e = hipSuccess;
   with_format(cache->format, [&](auto f) { e = launch_split_fmt<decltype(f)::value>(a, grid, s); });
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
