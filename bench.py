@@ -430,9 +430,11 @@ def summarize_stats(wid, stats_csv, out_path, steps, warmup):
             name = r["Name"]
             if "at::" in name or "rocclr" in name:
                 continue  # torch kernels building the synthetic inputs, runtime copies
-            m = re.search(r"(\w+_kernel)(?:<(\d)(?:, ?(true|false))?>|I?L?i?(\d)E)?", name)
+            m = re.search(r"(\w+_kernel)(?:<(\d)((?:, ?(?:true|false))*)>|I?L?i?(\d)E)?", name)
+            flags = re.findall(r"true|false", m.group(3) or "") if m else []
             short = (m.group(1) + (f"<{m.group(2) or m.group(4)}>" if (m.group(2) or m.group(4)) else "")
-                     + (" paged" if m.group(3) == "true" else "")) if m else name[:40]
+                     + "".join(f" {tag}" for tag, f in zip(("paged", "sliced"), flags) if f == "true")) \
+                if m else name[:40]
             rows.append((short, int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
                          float(r["MaxNs"]) / 1e3, float(r["TotalDurationNs"]) / 1e6))
     rows.sort(key=lambda x: -x[5])
