@@ -91,8 +91,18 @@ typedef enum {
  *   INT4 k_pe (INT4_KINT4): s = fp16_rne(max|x| / 7), q = clamp(rne(x / s), -7, 7),
  *          x_hat = q * s; s == 0 gives q = 0.
  *   Every step is one IEEE fp32 operation; fp16 results that would overflow
- *   saturate to +-65504. Inputs must be finite. The decode path dequantizes
- *   to fp16, so dequantized magnitudes must stay below 65504.
+ *   saturate to +-65504. Inputs must be finite.
+ *
+ * Domain of the decode path. It multiplies codes by scales in fp16, so every
+ * product q * s of a stored row must be finite in fp16:
+ *   - every format: inputs within +-65280 (bf16 planes are read as fp16;
+ *     INT8 groups then have 127 * s <= 65280, INT4 k_pe groups 7 * s <= 65296);
+ *   - INT4 latents (INT4, INT4_KINT4) in addition: each 16-channel group's
+ *     range max - min below 65490, so that 15 * s <= 65460 (the zero-point
+ *     is applied separately and never added in fp16). Inputs within +-32744
+ *     satisfy both.
+ * Outside this domain mla_cache_append still stores the exact codes, but the
+ * decode outputs are undefined. mla_cache_get has no such limit.
  */
 typedef struct mla_cache {
   int32_t format;       /* mla_format */
@@ -238,6 +248,62 @@ int mla_decode_step_begin(const mla_cache *cache, int32_t layer, const void *ckv
                           void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /*
+ * Several layers in one call. The configuration with independent layers
+ * (one decode step of each of a model's layers over the same batch) runs as
+ * one set of launches instead of one per layer: the balanced plan then cuts
+ * the tiles of every (layer, sequence) pair, layer after layer, into equal
+ * runs, so no launch ends on the tail of one layer's work.
+ *
+ *   layer0, layer_count   layers [layer0, layer0 + layer_count) of the cache,
+ *                         layer_count >= 1
+ *   every per-layer argument is stacked over those layers, layer-major:
+ *     q_nope bf16 [layer_count][batch][heads][128], q_pe [layer_count][batch][heads][64],
+ *     w_uk [layer_count][heads][128][512], w_uv [layer_count][heads][512][128],
+ *     out fp32 [layer_count][batch][heads][128];
+ *     for the step, ckv_new bf16 [layer_count][batch][512], kpe_new [layer_count][batch][64]
+ *   num_splits      as for one layer: W = num_splits * batch runs in all,
+ *                   now over every layer's tiles (0 = auto: about three
+ *                   workgroups per CU)
+ *   workspace       mla_decode_workspace_bytes_layers for the same
+ *                   layer_count, heads and num_splits
+ *
+ * mla_decode_attn_layers over one layer is mla_decode_attn; mla_decode_step_layers
+ * over one layer is mla_decode_step. Over several layers each layer's result
+ * is what the one-layer call gives for that layer, up to the rounding that
+ * depends on where the runs are cut. Errors as for the one-layer calls;
+ * MLA_ERR_INVALID_ARG for a layer range outside the cache.
+ */
+int mla_decode_workspace_bytes_layers(const mla_cache *cache, int32_t layer_count, int32_t heads,
+                                      int32_t num_splits, size_t *bytes);
+int mla_decode_auto_splits_layers(const mla_cache *cache, int32_t layer_count, int32_t heads,
+                                  int32_t *num_splits);
+int mla_decode_attn_layers(const mla_cache *cache, int32_t layer0, int32_t layer_count, const void *q_nope,
+                           const void *q_pe, const void *w_uk, const void *w_uv, int32_t heads,
+                           float softmax_scale, int32_t num_splits, void *workspace, size_t workspace_bytes,
+                           float *out, void *hip_stream);
+int mla_decode_step_layers(const mla_cache *cache, int32_t layer0, int32_t layer_count, const void *ckv_new,
+                           const void *kpe_new, const void *q_nope, const void *q_pe, const float *rope_cos,
+                           const float *rope_sin, int32_t rope_rows, const void *w_uk, const void *w_uv,
+                           int32_t heads, float softmax_scale, int32_t num_splits, void *workspace,
+                           size_t workspace_bytes, float *out, void *hip_stream);
+
+/* The phases of the layer-range calls, as for one layer below (layer0 only
+ * where the cache is read or written). */
+int mla_decode_step_begin_layers(const mla_cache *cache, int32_t layer0, int32_t layer_count,
+                                 const void *ckv_new, const void *kpe_new, const void *q_nope, const void *q_pe,
+                                 const float *rope_cos, const float *rope_sin, int32_t rope_rows,
+                                 const void *w_uk, int32_t heads, float softmax_scale, int32_t num_splits,
+                                 void *workspace, size_t workspace_bytes, void *hip_stream);
+int mla_decode_absorb_layers(const mla_cache *cache, int32_t layer_count, const void *q_nope, const void *q_pe,
+                             const void *w_uk, int32_t heads, float softmax_scale, int32_t num_splits,
+                             void *workspace, size_t workspace_bytes, void *hip_stream);
+int mla_decode_partial_layers(const mla_cache *cache, int32_t layer0, int32_t layer_count, int32_t heads,
+                              int32_t num_splits, void *workspace, size_t workspace_bytes, void *hip_stream);
+int mla_decode_combine_layers(const mla_cache *cache, int32_t layer_count, const void *w_uv, int32_t heads,
+                              int32_t num_splits, void *workspace, size_t workspace_bytes, float *out,
+                              void *hip_stream);
+
+/*
  * The three phases of mla_decode_attn, for callers that schedule them
  * separately (for example to time or overlap them). Calling, on one stream and
  * with one workspace, mla_decode_absorb, then mla_decode_partial, then
@@ -270,6 +336,31 @@ int mla_decode_combine(const mla_cache *cache, const void *w_uv, int32_t heads, 
  */
 int mla_cache_get(const mla_cache *cache, int32_t layer, float *ckv_out, float *kpe_out,
                   void *hip_stream);
+
+/*
+ * RoPE angle tables for mla_decode_step ("DeepSeek的MLA技术", optimization 2,
+ * reads the rotary embedding as first defined: channel pair (2i, 2i+1) of
+ * the 64 turns by the angle p * theta_i, theta_i = base^(-2i/64)):
+ *   cos_out, sin_out  fp32 [rows][32] (device, 4-byte aligned), row p holding
+ *                     cos and sin of p * theta_i, each evaluated in fp64 and
+ *                     rounded to fp32 (nearest even); theta_i is computed on
+ *                     the host in fp64.
+ *   rows >= 0 (0 is a no-op); base > 0 and finite (10000 in the rotary
+ *   embedding's definition).
+ * One launch on hip_stream. MLA_ERR_INVALID_ARG for a null or misaligned
+ * pointer, rows < 0 or a bad base.
+ */
+int mla_rope_tables(float *cos_out, float *sin_out, int32_t rows, double base, void *hip_stream);
+
+/*
+ * A measurement aid, not part of the decode path: reads `bytes` (a multiple of
+ * 16) of device memory at `buf` (16-byte aligned) with a plain streaming
+ * access pattern, as one launch of sink_words workgroups of 256 threads, and
+ * writes one word per workgroup to sink (device uint32 [sink_words]), the XOR
+ * of the words it read. Timing it gives the achievable HBM read rate beside
+ * the published peak.
+ */
+int mla_stream_read(const void *buf, size_t bytes, uint32_t *sink, int32_t sink_words, void *hip_stream);
 
 /* Static description of a status code. */
 const char *mla_status_str(int status);

@@ -27,11 +27,21 @@ SYMBOLS = (
     "mla_decode_auto_splits",
     "mla_decode_attn",
     "mla_decode_step",
+    "mla_decode_workspace_bytes_layers",
+    "mla_decode_auto_splits_layers",
+    "mla_decode_attn_layers",
+    "mla_decode_step_layers",
+    "mla_decode_step_begin_layers",
+    "mla_decode_absorb_layers",
+    "mla_decode_partial_layers",
+    "mla_decode_combine_layers",
+    "mla_stream_read",
     "mla_decode_step_begin",
     "mla_decode_absorb",
     "mla_decode_partial",
     "mla_decode_combine",
     "mla_cache_get",
+    "mla_rope_tables",
     "mla_status_str",
 )
 
@@ -88,6 +98,27 @@ def lib():
         L.mla_decode_step.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, ctypes.c_float, i32,
                                       vp, sz, vp, vp]
         L.mla_decode_step.restype = ctypes.c_int
+        L.mla_decode_workspace_bytes_layers.argtypes = [P, i32, i32, i32, ctypes.POINTER(sz)]
+        L.mla_decode_workspace_bytes_layers.restype = ctypes.c_int
+        L.mla_decode_auto_splits_layers.argtypes = [P, i32, i32, ctypes.POINTER(i32)]
+        L.mla_decode_auto_splits_layers.restype = ctypes.c_int
+        L.mla_decode_attn_layers.argtypes = [P, i32, i32, vp, vp, vp, vp, i32, ctypes.c_float, i32, vp, sz, vp,
+                                             vp]
+        L.mla_decode_attn_layers.restype = ctypes.c_int
+        L.mla_decode_step_layers.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32,
+                                             ctypes.c_float, i32, vp, sz, vp, vp]
+        L.mla_decode_step_layers.restype = ctypes.c_int
+        L.mla_decode_step_begin_layers.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, i32,
+                                                   ctypes.c_float, i32, vp, sz, vp]
+        L.mla_decode_step_begin_layers.restype = ctypes.c_int
+        L.mla_decode_absorb_layers.argtypes = [P, i32, vp, vp, vp, i32, ctypes.c_float, i32, vp, sz, vp]
+        L.mla_decode_absorb_layers.restype = ctypes.c_int
+        L.mla_decode_partial_layers.argtypes = [P, i32, i32, i32, i32, vp, sz, vp]
+        L.mla_decode_partial_layers.restype = ctypes.c_int
+        L.mla_decode_combine_layers.argtypes = [P, i32, vp, i32, i32, vp, sz, vp, vp]
+        L.mla_decode_combine_layers.restype = ctypes.c_int
+        L.mla_stream_read.argtypes = [vp, sz, vp, i32, vp]
+        L.mla_stream_read.restype = ctypes.c_int
         L.mla_decode_step_begin.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, i32, vp, i32, ctypes.c_float, i32,
                                             vp, sz, vp]
         L.mla_decode_step_begin.restype = ctypes.c_int
@@ -99,6 +130,8 @@ def lib():
         L.mla_decode_combine.restype = ctypes.c_int
         L.mla_cache_get.argtypes = [P, i32, vp, vp, vp]
         L.mla_cache_get.restype = ctypes.c_int
+        L.mla_rope_tables.argtypes = [vp, vp, i32, ctypes.c_double, vp]
+        L.mla_rope_tables.restype = ctypes.c_int
         L.mla_status_str.argtypes = [ctypes.c_int]
         L.mla_status_str.restype = ctypes.c_char_p
         _lib = L

@@ -31,14 +31,16 @@ def row_bytes(fmt):
     return lat[fmt] + kpe[fmt] + 2 * (scales + zeros)
 
 
-def rope_tables(rows, base=10000.0, device="cuda"):
-    """RoPE angle tables for decode_step: (cos, sin), fp32 [rows, 32], row p
-    holding cos / sin of p * base^(-2i/64) for channel pair (2i, 2i+1),
-    each evaluated in fp64 and rounded to fp32 (host-side set-up, once)."""
-    i = torch.arange(ROPE // 2, dtype=torch.float64)
-    ang = torch.arange(rows, dtype=torch.float64)[:, None] * (float(base) ** (-2.0 * i / ROPE))[None, :]
-    return (torch.cos(ang).to(torch.float32).to(device).contiguous(),
-            torch.sin(ang).to(torch.float32).to(device).contiguous())
+def rope_tables(rows, base=10000.0, device="cuda", stream=None):
+    """RoPE angle tables for decode_step, made by the library's
+    mla_rope_tables: (cos, sin), fp32 [rows, 32] on the device, row p holding
+    cos / sin of p * base^(-2i/64) for channel pair (2i, 2i+1)."""
+    device = torch.device(device)
+    cos = torch.empty((int(rows), ROPE // 2), dtype=torch.float32, device=device)
+    sin = torch.empty_like(cos)
+    check(_lib.lib().mla_rope_tables(_ptr(cos), _ptr(sin), int(rows), float(base), _stream(stream)),
+          "mla_rope_tables")
+    return cos, sin
 
 
 def _unblock(t):
@@ -266,6 +268,82 @@ class LatentCache:
                                          _ptr(w_uv), H, float(softmax_scale), num_splits, _ptr(workspace),
                                          workspace.numel(), _ptr(out), _stream(stream)), "mla_decode_step")
         self._lens[layer] = np.minimum(self._lens[layer] + 1, self.capacity)
+        return out
+
+    # ------------------------------------------------- several layers at once
+    def auto_splits_layers(self, layer_count, heads):
+        n = ctypes.c_int32(0)
+        check(_lib.lib().mla_decode_auto_splits_layers(ctypes.byref(self.struct), layer_count, heads,
+                                                       ctypes.byref(n)), "mla_decode_auto_splits_layers")
+        return n.value
+
+    def workspace_bytes_layers(self, layer_count, heads, num_splits=0):
+        n = ctypes.c_size_t(0)
+        check(_lib.lib().mla_decode_workspace_bytes_layers(ctypes.byref(self.struct), layer_count, heads,
+                                                           num_splits, ctypes.byref(n)),
+              "mla_decode_workspace_bytes_layers")
+        return n.value
+
+    def workspace_layers(self, layer_count, heads, num_splits=0):
+        return torch.empty(self.workspace_bytes_layers(layer_count, heads, num_splits), dtype=torch.uint8,
+                           device=self.device)
+
+    def _layers_args(self, layer0, q_nope, q_pe, w_uk, w_uv):
+        n = q_nope.shape[0] if q_nope.dim() == 4 else -1
+        if not (0 <= layer0 and n >= 1 and layer0 + n <= self.num_layers):
+            raise IndexError(f"layers [{layer0}, {layer0 + n}) out of range [0, {self.num_layers})")
+        H = q_nope.shape[2]
+        _need(q_nope, "q_nope", torch.bfloat16, (n, self.batch, H, NOPE), self.device)
+        _need(q_pe, "q_pe", torch.bfloat16, (n, self.batch, H, ROPE), self.device)
+        _need(w_uk, "w_uk", torch.bfloat16, (n, H, NOPE, LATENT), self.device)
+        _need(w_uv, "w_uv", torch.bfloat16, (n, H, LATENT, VDIM), self.device)
+        return n, H
+
+    def decode_layers(self, layer0, q_nope, q_pe, w_uk, w_uv, softmax_scale, num_splits=0, out=None,
+                      workspace=None, stream=None):
+        """Absorbed decode of layers layer0 .. layer0 + n - 1 in one set of
+        launches; every argument is stacked over the n layers (q_nope
+        [n,B,H,128], q_pe [n,B,H,64], w_uk [n,H,128,512], w_uv [n,H,512,128]).
+        Returns out fp32 [n, B, H, 128]."""
+        n, H = self._layers_args(layer0, q_nope, q_pe, w_uk, w_uv)
+        if out is None:
+            out = torch.empty((n, self.batch, H, VDIM), dtype=torch.float32, device=self.device)
+        _need(out, "out", torch.float32, (n, self.batch, H, VDIM), self.device)
+        if workspace is None:
+            workspace = self.workspace_layers(n, H, num_splits)
+        check(_lib.lib().mla_decode_attn_layers(ctypes.byref(self.struct), layer0, n, _ptr(q_nope), _ptr(q_pe),
+                                                _ptr(w_uk), _ptr(w_uv), H, float(softmax_scale), num_splits,
+                                                _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream)),
+              "mla_decode_attn_layers")
+        return out
+
+    def decode_step_layers(self, layer0, ckv_new, kpe_new, q_nope, q_pe, w_uk, w_uv, softmax_scale, rope=None,
+                           num_splits=0, out=None, workspace=None, stream=None):
+        """The fused decode step of layers layer0 .. layer0 + n - 1 in one set
+        of launches: ckv_new bf16 [n,B,512], kpe_new bf16 [n,B,64] (not
+        turned), the other arguments stacked as for decode_layers. Returns out
+        fp32 [n, B, H, 128]."""
+        n, H = self._layers_args(layer0, q_nope, q_pe, w_uk, w_uv)
+        _need(ckv_new, "ckv_new", torch.bfloat16, (n, self.batch, LATENT), self.device)
+        _need(kpe_new, "kpe_new", torch.bfloat16, (n, self.batch, ROPE), self.device)
+        cos = sin = None
+        rows = 0
+        if rope is not None:
+            cos, sin = rope
+            rows = cos.shape[0] if cos.dim() == 2 else -1
+            _need(cos, "rope cos", torch.float32, (rows, ROPE // 2), self.device)
+            _need(sin, "rope sin", torch.float32, (rows, ROPE // 2), self.device)
+        if out is None:
+            out = torch.empty((n, self.batch, H, VDIM), dtype=torch.float32, device=self.device)
+        _need(out, "out", torch.float32, (n, self.batch, H, VDIM), self.device)
+        if workspace is None:
+            workspace = self.workspace_layers(n, H, num_splits)
+        check(_lib.lib().mla_decode_step_layers(ctypes.byref(self.struct), layer0, n, _ptr(ckv_new), _ptr(kpe_new),
+                                                _ptr(q_nope), _ptr(q_pe), _ptr(cos), _ptr(sin), rows, _ptr(w_uk),
+                                                _ptr(w_uv), H, float(softmax_scale), num_splits, _ptr(workspace),
+                                                workspace.numel(), _ptr(out), _stream(stream)),
+              "mla_decode_step_layers")
+        self._lens[layer0:layer0 + n] = np.minimum(self._lens[layer0:layer0 + n] + 1, self.capacity)
         return out
 
     # ------------------------------------------------ decode, phase by phase

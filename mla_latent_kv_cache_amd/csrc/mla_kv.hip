@@ -69,6 +69,8 @@ constexpr int kpe_bytes(int f) {
   return kpe_fmt(f) == kKpeBf16 ? kRope * 2 : kpe_fmt(f) == kKpeI8 ? kRope : kRope / 2;
 }
 constexpr bool has_zero(int f) { return lat_fmt(f) == MLA_FMT_INT4; }
+constexpr int64_t kMaxSeqPlaneBytes = (int64_t)1 << 30;  // bytes of one sequence's rows in any plane
+constexpr int64_t kMaxGrid = INT32_MAX;    // workgroups in one launch
 constexpr int kWaves = 4;                  // waves per split workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kMaxSplits = 4096;
@@ -180,24 +182,32 @@ __device__ __forceinline__ void lds_stores_done() {
 
 // ------------------------------------------------------------------ append
 
-// Paged planes: token p of sequence b is row p % size of page table[b][p / size]
-// of the layer's pool; size = 0 means contiguous rows b * cap + p.
+// Sequences are numbered across the layers a call covers: sequence j is
+// batch entry j % batch of layer j / batch (counted from the call's first
+// layer, whose planes the kernels receive). Contiguous planes keep the rows of
+// sequence j at j * cap (the planes are [layer][batch][cap] rows).
+// Paged planes: token p of sequence j is row p % size of page
+// table[j % batch][p / size] of layer j / batch's pool (layer_rows rows
+// apart); size = 0 means contiguous rows.
 struct Paging {
-  const int32_t *table;  // [B][max_pages]
+  const int32_t *table;  // [batch][max_pages]
   int size, shift, max_pages, num_pages;  // size = 1 << shift (a power of two >= 32)
+  int batch;             // sequences per layer
+  int64_t layer_rows;    // rows of one layer's pool (num_pages * size)
 };
 
-// Page of token p of sequence b, or -1 when the table entry is outside the pool.
-__device__ __forceinline__ int page_of(const Paging &pg, int b, int p) {
-  const int page = pg.table[(int64_t)b * pg.max_pages + (p >> pg.shift)];
+// Page of token p of sequence j, or -1 when the table entry is outside the pool.
+__device__ __forceinline__ int page_of(const Paging &pg, int j, int p) {
+  const int page = pg.table[(int64_t)(j % pg.batch) * pg.max_pages + (p >> pg.shift)];
   return (page >= 0 && page < pg.num_pages) ? page : -1;
 }
 
-// Row within the layer's plane of token p of sequence b, or -1 (no page).
-__device__ __forceinline__ int64_t plane_row(const Paging &pg, int b, int cap, int p) {
-  if (pg.size == 0) return (int64_t)b * cap + p;
-  const int page = page_of(pg, b, p);
-  return page < 0 ? -1 : ((int64_t)page << pg.shift) + (p & (pg.size - 1));
+// Row within the planes of token p of sequence j, or -1 (no page).
+__device__ __forceinline__ int64_t plane_row(const Paging &pg, int j, int cap, int p) {
+  if (pg.size == 0) return (int64_t)j * cap + p;
+  const int page = page_of(pg, j, p);
+  return page < 0 ? -1
+                  : (int64_t)(j / pg.batch) * pg.layer_rows + ((int64_t)page << pg.shift) + (p & (pg.size - 1));
 }
 
 // The latent plane keeps its rows in blocks of 16: within a block, the
@@ -368,10 +378,12 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   }
 }
 
+// Counts are clamped to [0, T] here as in append_kernel, so a length never
+// moves past the rows that were stored.
 __global__ void seqlen_kernel(int32_t *seq_lens, const int32_t *n_new, int B, int T, int cap) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= B) return;
-  const int n = n_new ? n_new[b] : T;
+  const int n = n_new ? min(max(n_new[b], 0), T) : T;
   const int64_t v = (int64_t)seq_lens[b] + n;
   seq_lens[b] = (int32_t)(v > cap ? cap : v);
 }
@@ -383,7 +395,7 @@ constexpr int kStepAppendMaxT = 8;
 template <int FMT>
 __global__ __launch_bounds__(128) void append_step_kernel(AppendArgs a) {
   const int b = blockIdx.x;
-  const int n = a.n_new ? a.n_new[b] : a.T;
+  const int n = a.n_new ? min(max(a.n_new[b], 0), a.T) : a.T;
   const int base = a.seq_lens[b];
   for (int i = threadIdx.x; i < a.T * kNScale; i += blockDim.x) {
     const int t = i / kNScale, grp = i % kNScale;
@@ -544,17 +556,23 @@ __device__ __forceinline__ void absorb_block(const uint16_t *q_nope, const uint1
   }
 }
 
+// Grid (H, 512/64, layers x nbz): blockIdx.z = l * nbz + bz. Every argument is
+// layer-stacked: layer l's queries, weights and records follow layer l-1's.
 __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t *q_nope, const uint16_t *q_pe,
                                                      const uint16_t *w_uk, int B, int H, float qs,
-                                                     _Float16 *qa) {
-  absorb_block(q_nope, q_pe, w_uk, B, H, qs, qa, blockIdx.x, blockIdx.y, blockIdx.z, true);
+                                                     _Float16 *qa, int nbz) {
+  const int l = blockIdx.z / nbz, bz = blockIdx.z % nbz;
+  const int64_t rows = (int64_t)l * B * H;
+  absorb_block(q_nope + rows * kNope, q_pe + rows * kRope, w_uk + (int64_t)l * H * kNope * kLatent, B, H, qs,
+               qa + rows * kQRec, blockIdx.x, blockIdx.y, bz, true);
 }
 
 // ------------------------------------------------------------ fused step
 
-// First launch of the fused decode step (append one token, then attend). The
-// grid holds n_absorb absorption blocks (head-major over (h, cb, bz)) and then
-// one block per sequence b, which
+// First launch of the fused decode step (append one token, then attend) of
+// one or more layers. The grid holds, for each layer, n_absorb absorption
+// blocks (head-major over (h, cb, bz)), and then one block per sequence j
+// (layer-major over the layers' batches, see Paging), which
 //   * reads its length pos (the new token's position), quantizes and stores
 //     the new token at row pos with its k_pe turned by table row pos
 //     (unless the sequence is full), and advances the length after a barrier;
@@ -562,22 +580,26 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t *q_nope, con
 //     RoPE part of the query records, which the absorption blocks leave alone.
 // No block reads a length another block writes.
 struct StepArgs {
-  AppendArgs ap;            // T = 1; rope tables optional
-  const uint16_t *q_nope, *q_pe, *w_uk;
+  AppendArgs ap;            // T = 1; B = sequences of every layer; rope tables optional
+  const uint16_t *q_nope, *q_pe, *w_uk;  // layer-stacked
   _Float16 *qa;
   float qs;
-  int H, n_absorb;
+  int H, n_absorb;          // absorption blocks per layer
+  int batch, layers;        // sequences per layer, layers of the call
 };
 
 template <int FMT>
 __global__ __launch_bounds__(256) void step_kernel(StepArgs s) {
   const int blk = blockIdx.x;
-  if (blk < s.n_absorb) {  // uniform
-    const int h = blk % s.H, cb = (blk / s.H) % (kLatent / kAbsorbCB), bz = blk / (s.H * (kLatent / kAbsorbCB));
-    absorb_block(s.q_nope, s.q_pe, s.w_uk, s.ap.B, s.H, s.qs, s.qa, h, cb, bz, false);
+  if (blk < s.n_absorb * s.layers) {  // uniform
+    const int l = blk / s.n_absorb, r = blk % s.n_absorb;
+    const int h = r % s.H, cb = (r / s.H) % (kLatent / kAbsorbCB), bz = r / (s.H * (kLatent / kAbsorbCB));
+    const int64_t rows = (int64_t)l * s.batch * s.H;
+    absorb_block(s.q_nope + rows * kNope, s.q_pe, s.w_uk + (int64_t)l * s.H * kNope * kLatent, s.batch, s.H,
+                 s.qs, s.qa + rows * kQRec, h, cb, bz, false);
     return;
   }
-  const int b = blk - s.n_absorb;
+  const int b = blk - s.n_absorb * s.layers;
   const int tid = threadIdx.x;
   const int pos = s.ap.seq_lens[b];
   if (tid < kNScale && pos >= 0 && pos < s.ap.cap) append_group<FMT>(s.ap, b, 0, tid, pos);
@@ -614,14 +636,14 @@ struct SplitArgs {
   const void *kpe;
   const uint16_t *scale;
   const uint16_t *zero;
-  const int32_t *seq_lens;  // layer row
+  const int32_t *seq_lens;  // [B]: the call's layers' rows (layer-major)
   const _Float16 *qa;       // [B][H][kQRec]
   float *ws_m;              // [records][H], records <= W + B (the balanced plan)
   float *ws_l;              // [records][H]
   float *ws_acc;            // [records][H][512]
   int32_t *rec_tab;         // [B][2] first record and record count
   Paging pg;
-  int B, H, cap;
+  int B, H, cap;            // B: sequences of every layer of the call
   int W;  // ranges of the balanced plan
 };
 
@@ -672,14 +694,15 @@ __device__ __forceinline__ SplitRsrc split_rsrc(const SplitArgs &a, int b, int t
                         t_end - t_begin);
 }
 
-// Paged layout: rows [r0, t_end) of a sequence, cut at the end of r0's page
-// (`page`, from page_of; -1 or r0 >= t_end: empty).
+// Paged layout: rows [r0, t_end) of a sequence whose layer's pool starts at
+// row `base`, cut at the end of r0's page (`page`, from page_of; -1 or
+// r0 >= t_end: empty).
 template <int FMT>
-__device__ __forceinline__ SplitRsrc page_rsrc(const SplitArgs &a, int page, int r0, int t_end) {
+__device__ __forceinline__ SplitRsrc page_rsrc(const SplitArgs &a, int64_t base, int page, int r0, int t_end) {
   if (page < 0 || r0 >= t_end) return rows_rsrc<FMT>(a, 0, 0, 0);
   const int off = r0 & (a.pg.size - 1);
   const int end = min(t_end, r0 - off + a.pg.size);
-  const int64_t row0 = ((int64_t)page << a.pg.shift) + off;
+  const int64_t row0 = base + ((int64_t)page << a.pg.shift) + off;
   return rows_rsrc<FMT>(a, row0, row0, end - r0);
 }
 
@@ -1216,9 +1239,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgp
 void split16_kernel(SplitArgs a) {
   constexpr bool kLo = FMT != MLA_FMT_BF16;
   constexpr bool kZp = has_zero(FMT);  // INT4 latent: zero-points, and the nibble operand order
-  // INT4 latents: weights below 2^4, as they multiply the scales in fp16
-  constexpr float kLazyOf = kZp ? 4.0f : kLazy;
-  // +16: the zero-point read of the last row runs 8 fp16 past its block (unused slots)
+  // The softmax weights are p = 2^(s - m_run) for a reference m_run that
+  // moves lazily (below). kSlack: log2 of the largest weight allowed before
+  // the reference moves; kHead: how far above the tile maximum it is placed.
+  // INT8 / BF16: weights up to 2^8 (exact in fp16 relative terms). INT4: the
+  // weights multiply the group scales in fp16 (p s as an fp16 hi/lo pair), so
+  // they stay at or below 1 and p s is finite for every fp16 scale; the
+  // reference sits 2^4 above the maximum, so it still moves only when a
+  // head's maximum rises by more than 4.
+  constexpr float kSlack = kZp ? 0.0f : kLazy;
+  constexpr float kHead = kZp ? 4.0f : 0.0f;
   __shared__ __attribute__((aligned(16))) _Float16 wblk[kWaves * kWBlk];
   // partial scores of a tile; before the first tile, the plan's scratch
   __shared__ __attribute__((aligned(16))) float part[kPart16];
@@ -1303,8 +1333,11 @@ void split16_kernel(SplitArgs a) {
   // traffic, and every LDS wait of the tile would then wait for it too.
   constexpr bool paged = PAGED;
   constexpr int kPol = SLICED ? kSliceLoadPolicy : kLatLoadPolicy;  // latent loads' cache policy
+  // the sequence's block-table row and its layer's pool (paged layout)
+  const int pb = paged ? b % a.pg.batch : 0;
+  const int64_t pool = paged ? (int64_t)(b / a.pg.batch) * a.pg.layer_rows : 0;
   const __amdgpu_buffer_rsrc_t trow =
-      make_rsrc(paged ? (const void *)(a.pg.table + (int64_t)b * a.pg.max_pages) : a.kpe,
+      make_rsrc(paged ? (const void *)(a.pg.table + (int64_t)pb * a.pg.max_pages) : a.kpe,
                 paged ? a.pg.max_pages * 4 : 0);
   auto page_entry = [&](int r) {  // raw table entry of token r (any lane; reads 0 past the row)
     return __builtin_amdgcn_raw_buffer_load_b32(trow, (r >> a.pg.shift) * 4, 0, 0);
@@ -1314,7 +1347,7 @@ void split16_kernel(SplitArgs a) {
     return (r < t_end && pg >= 0 && pg < a.pg.num_pages) ? pg : -1;
   };
   auto rsrc_of = [&](int r0, int page) {
-    if constexpr (PAGED) return page_rsrc<FMT>(a, page, r0, t_end);
+    if constexpr (PAGED) return page_rsrc<FMT>(a, pool, page, r0, t_end);
     else return tile_rsrc<FMT>(a, b, r0, t_end);
   };
 #pragma unroll
@@ -1442,11 +1475,11 @@ void split16_kernel(SplitArgs a) {
                        fmaxf(fmaxf(p8[4], p8[5]), fmaxf(p8[6], p8[7])));
     tmax = max_across_groups(tmax);
     // Lazy running max: the reference point moves only when some head's tile
-    // maximum exceeds it by more than 2^kLazy, so weights stay below 2^kLazy
-    // (exact in fp16 relative terms) and most tiles skip the rescale.
+    // maximum exceeds it by more than kSlack, so weights stay at or below
+    // 2^kSlack and most tiles skip the rescale.
     // Every wave holds the same scores and takes the same decision.
-    if (__builtin_amdgcn_ballot_w64(tmax > m_run + kLazyOf)) {
-      const float m_new = fmaxf(m_run, tmax);
+    if (__builtin_amdgcn_ballot_w64(tmax > m_run + kSlack)) {
+      const float m_new = fmaxf(m_run, tmax + kHead);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
       m_run = m_new;
@@ -1478,9 +1511,9 @@ void split16_kernel(SplitArgs a) {
     if (kZp) {
       // INT4: block n holds group n's codes; its scales s_t (transposed, rows
       // 4n..4n+3) go into the weights: p_t s_t = ph + pl exactly (fp16 hi/lo;
-      // p <= 2^4 here, so the product stays in the fp16 range for any scale up
-      // to 4094, as q s did before), and acc gets sum_t p_t s_t q_t with no
-      // rounding of s q. The fp16 weights stay normal down to p = 2^-14.
+      // p <= 1 here, so the product is finite for every fp16 scale), and acc
+      // gets sum_t p_t s_t q_t with no rounding of s q. The fp16 weights stay
+      // normal down to p = 2^-14.
       const f16x8 pbs = pb;
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
@@ -1588,8 +1621,9 @@ constexpr int kMergeChunk = 16;  // splits merged per round of loads
 // a running maximum (what was merged before is rescaled by 2^(M_old - M_new)),
 // and each split's weight 2^(m_s - M) is taken from its lane as a scalar. A
 // split with l = 0 holds no tokens and its sums were never written: it gets
-// weight zero and its sums are skipped, not multiplied. Grid (H, ceil(B/4)),
-// 512 threads.
+// weight zero and its sums are skipped, not multiplied. Grid (H, ceil(B/4),
+// layers), 512 threads: layer l's sequences are l * B .. l * B + B - 1 of the
+// record table and of out, and its W_UV follows layer l-1's.
 constexpr int kReduceThreads = 512;
 constexpr int kReduceCS = kReduceThreads / 16;  // latent row chunks of the projection (16 rows each)
 static_assert(kReduceBT * kVDim == kReduceThreads && kReduceCS * 16 == kLatent && 2 * kReduceBT * 64 == kReduceThreads,
@@ -1601,6 +1635,10 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const float *ws_
   __shared__ float red[kReduceCS][kReduceBT][kVDim];
   const int h = blockIdx.x;
   const int b0 = blockIdx.y * kReduceBT;
+  const int64_t layer_seq = (int64_t)blockIdx.z * B;  // the layer's first sequence
+  rec_tab += 2 * layer_seq;
+  out += layer_seq * H * kVDim;
+  w_uv += (int64_t)blockIdx.z * H * kLatent * kVDim;
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int bt = wv >> 1, half = wv & 1;
@@ -1696,6 +1734,51 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const float *ws_
   if (bo < B) out[((int64_t)bo * H + h) * kVDim + e] = v;
 }
 
+// -------------------------------------------------------- stream-read probe
+
+// Reads n16 16-byte words with the access pattern of a plain streaming read
+// (grid-stride, consecutive lanes on consecutive words, four loads in flight
+// per thread) and folds them into one word per workgroup, so that no load is
+// dead. A measurement aid for the achievable HBM read rate.
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4 *buf, int64_t n16, uint32_t *sink) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  uint32_t x = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 a = __builtin_nontemporal_load(buf + i), b = __builtin_nontemporal_load(buf + i + stride);
+    const u32x4 c = __builtin_nontemporal_load(buf + i + 2 * stride);
+    const u32x4 d = __builtin_nontemporal_load(buf + i + 3 * stride);
+    x ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 a = buf[i];
+    x ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  __shared__ uint32_t red[4];
+  for (int off = 32; off >= 1; off >>= 1) x ^= __shfl_xor(x, off);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
+// ---------------------------------------------------------------- rope tables
+
+// theta_i = base^(-2i/64) of the 32 channel pairs, computed on the host.
+struct RopeTheta {
+  double t[kRope / 2];
+};
+
+// cos / sin of p * theta_i in fp64, rounded to fp32 (nearest even), for
+// table row p and pair i: one thread per entry.
+__global__ __launch_bounds__(256) void rope_table_kernel(float *cos_out, float *sin_out, int rows, RopeTheta th) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)rows * (kRope / 2)) return;
+  const int i = (int)(idx % (kRope / 2));
+  const double a = (double)(idx / (kRope / 2)) * th.t[i];
+  cos_out[idx] = (float)cos(a);
+  sin_out[idx] = (float)sin(a);
+}
+
 // --------------------------------------------------------------------- get
 
 template <int FMT>
@@ -1760,6 +1843,13 @@ int check_cache(const mla_cache *c) {
   if (c->kv_lora_rank != kLatent || c->rope_dim != kRope || c->group_latent != kGroupL ||
       c->group_rope != kGroupR)
     return MLA_ERR_UNSUPPORTED;
+  // The kernels address one sequence's rows of a plane through a buffer
+  // descriptor whose byte count is a 32-bit number, with kOffNone as an offset
+  // past every descriptor: a sequence's plane must stay below 2^30 bytes.
+  if ((int64_t)lat_stride(c->capacity) * ckv_bytes(c->format) > kMaxSeqPlaneBytes ||
+      (int64_t)c->capacity * (kpe_bytes(c->format) > 2 * kNScale ? kpe_bytes(c->format) : 2 * kNScale) >
+          kMaxSeqPlaneBytes)
+    return MLA_ERR_UNSUPPORTED;
   if (!c->ckv || !c->kpe || !c->seq_lens) return MLA_ERR_INVALID_ARG;
   if (!aligned16(c->ckv) || !aligned16(c->kpe) || ((uintptr_t)c->seq_lens & 3u)) return MLA_ERR_INVALID_ARG;
   const bool quant = c->format != MLA_FMT_BF16;
@@ -1785,6 +1875,8 @@ Paging paging_of(const mla_cache *c) {
   while (c->page_size && (1 << p.shift) < c->page_size) ++p.shift;
   p.max_pages = c->page_size ? c->capacity / c->page_size : 0;
   p.num_pages = c->page_size ? c->num_pages : 0;
+  p.batch = c->batch;
+  p.layer_rows = (int64_t)p.num_pages * c->page_size;
   return p;
 }
 
@@ -1832,15 +1924,18 @@ struct WsLayout {
   size_t qa, m, l, acc, tab, total;
 };
 
-// Partial records: one per (range, sequence) pair of the balanced plan, at
-// most W + B with W = nsplit * B ranges, each with rows for all H heads; then
-// the per-sequence record table.
-WsLayout ws_layout(int B, int H, int nsplit) {
-  const size_t recs = (size_t)B * nsplit + (size_t)B;
+// The workspace of a decode over `layers` layers of a batch (S = batch x
+// layers sequences): the absorbed queries of every sequence; the partial
+// records, one per (range, sequence) pair of the balanced plan, at most W + S
+// with W = nsplit * batch ranges, each with rows for all H heads; then the
+// per-sequence record table.
+WsLayout ws_layout(int batch, int layers, int H, int nsplit) {
+  const size_t S = (size_t)batch * layers;
+  const size_t recs = (size_t)batch * nsplit + S;
   WsLayout w;
   size_t off = 0;
   w.qa = off;
-  off = align256(off + (size_t)B * H * kQRec * 2);
+  off = align256(off + S * H * kQRec * 2);
   w.m = off;
   off = align256(off + recs * H * 4);
   w.l = off;
@@ -1848,22 +1943,22 @@ WsLayout ws_layout(int B, int H, int nsplit) {
   w.acc = off;
   off = align256(off + recs * H * kLatent * 4);
   w.tab = off;
-  off = align256(off + (size_t)B * 2 * 4);
+  off = align256(off + S * 2 * 4);
   w.total = off;
   return w;
 }
 
-int auto_splits(const mla_cache *c, int heads, int *out) {
+int auto_splits(const mla_cache *c, int heads, int layers, int *out) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return MLA_ERR_HIP;
   if (cus < 1) cus = 1;
-  // Balanced plan: nsplit * B ranges of equal work, times heads / 16 head
+  // Balanced plan: nsplit * batch ranges of equal work, times heads / 16 head
   // slices, as many workgroups as are resident at once (three per CU), and at
   // least kAutoMinTiles tiles per range when every sequence is full.
   int64_t ns = (int64_t)kWgPerCu * cus / ((int64_t)c->batch * (heads / 16));
-  const int64_t by_len = ((int64_t)c->capacity + kT16 * kAutoMinTiles - 1) / (kT16 * kAutoMinTiles);
+  const int64_t by_len = ((int64_t)c->capacity * layers + kT16 * kAutoMinTiles - 1) / (kT16 * kAutoMinTiles);
   if (ns > by_len) ns = by_len;
   if (ns < 1) ns = 1;
   if (ns > kMaxSplits) ns = kMaxSplits;
@@ -1883,6 +1978,187 @@ hipError_t launch_split_fmt(const SplitArgs &a, dim3 grid, hipStream_t st) {
     else hipLaunchKernelGGL((split16_kernel<FMT, false, false>), grid, dim3(kThreads), 0, st, a);
   }
   return hipGetLastError();
+}
+
+struct DecodePlan {
+  int ns;      // ranges per batch entry (W = ns * batch)
+  int layers;  // layers of the call
+  WsLayout wl;
+};
+
+bool layers_ok(const mla_cache *c, int layer0, int layers) {
+  return layer0 >= 0 && layers >= 1 && (int64_t)layer0 + layers <= c->num_layers;
+}
+
+// Validation shared by the decode entry points: cache, layers, heads, split
+// count and workspace. Fills the plan (split count, workspace layout) on success.
+int plan_decode(const mla_cache *cache, int layers, int heads, int num_splits, const void *workspace,
+                size_t workspace_bytes, DecodePlan *plan) {
+  int st = check_cache(cache);
+  if (st != MLA_OK) return st;
+  if (layers < 1 || layers > cache->num_layers) return MLA_ERR_INVALID_ARG;
+  if (!heads_ok(heads)) return MLA_ERR_UNSUPPORTED;
+  if (num_splits < 0 || num_splits > kMaxSplits) return MLA_ERR_INVALID_ARG;
+  int ns = num_splits;
+  if (ns == 0) {
+    st = auto_splits(cache, heads, layers, &ns);
+    if (st != MLA_OK) return st;
+  }
+  // ranges x head slices, rounded up to whole windows of 8 ranges; the plan
+  // counts the tiles of all the call's sequences in 32-bit integers
+  const int64_t seqs = (int64_t)cache->batch * layers;
+  if (((int64_t)ns * cache->batch + 7) / 8 * 8 * (heads / 16) > kMaxGrid) return MLA_ERR_UNSUPPORTED;
+  if (seqs * ((cache->capacity + kT16 - 1) / kT16) > kMaxGrid) return MLA_ERR_UNSUPPORTED;
+  plan->ns = ns;
+  plan->layers = layers;
+  plan->wl = ws_layout(cache->batch, layers, heads, ns);
+  if (!workspace || workspace_bytes < plan->wl.total || ((uintptr_t)workspace & 255u))
+    return MLA_ERR_WORKSPACE;
+  return MLA_OK;
+}
+
+int check_absorb_args(const void *q_nope, const void *q_pe, const void *w_uk, float softmax_scale) {
+  if (!q_nope || !q_pe || !w_uk) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(w_uk)) return MLA_ERR_INVALID_ARG;
+  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return MLA_ERR_INVALID_ARG;
+  return MLA_OK;
+}
+
+int check_combine_args(const void *w_uv, const float *out) {
+  if (!w_uv || !out || !aligned16(w_uv) || !aligned16(out)) return MLA_ERR_INVALID_ARG;
+  return MLA_OK;
+}
+
+int run_absorb(const mla_cache *cache, const DecodePlan &pl, const void *q_nope, const void *q_pe,
+               const void *w_uk, int heads, float softmax_scale, void *workspace, hipStream_t s) {
+  const int B = cache->batch;
+  const int nbz = (B + kAbsorbBT - 1) / kAbsorbBT;
+  _Float16 *qa = (_Float16 *)((uint8_t *)workspace + pl.wl.qa);
+  hipLaunchKernelGGL(absorb_kernel, dim3(heads, kLatent / kAbsorbCB, nbz * pl.layers), dim3(256), 0, s,
+                     (const uint16_t *)q_nope, (const uint16_t *)q_pe, (const uint16_t *)w_uk, B, heads,
+                     softmax_scale * kLog2e, qa, nbz);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int run_partial(const mla_cache *cache, const DecodePlan &pl, int layer0, int heads, void *workspace,
+                hipStream_t s) {
+  const LayerPlanes p = layer_planes(cache, layer0);
+  uint8_t *ws = (uint8_t *)workspace;
+  SplitArgs a;
+  a.ckv = p.ckv;
+  a.kpe = p.kpe;
+  a.scale = p.scale;
+  a.zero = p.zero;
+  a.seq_lens = p.seq_lens;
+  a.qa = (const _Float16 *)(ws + pl.wl.qa);
+  a.ws_m = (float *)(ws + pl.wl.m);
+  a.ws_l = (float *)(ws + pl.wl.l);
+  a.ws_acc = (float *)(ws + pl.wl.acc);
+  a.B = cache->batch * pl.layers;  // the sequences of every layer, layer after layer
+  a.H = heads;
+  a.cap = cache->capacity;
+  a.pg = paging_of(cache);
+  a.rec_tab = (int32_t *)(ws + pl.wl.tab);
+  // the balanced plan's nsplit * batch ranges, each as heads / 16 head slices,
+  // rounded up to whole windows of 8 ranges (see split16_kernel)
+  a.W = pl.ns * cache->batch;
+  const dim3 grid((unsigned)(((int64_t)a.W + 7) / 8 * 8 * (heads / 16)));
+  hipError_t e = hipSuccess;
+  with_format(cache->format, [&](auto f) { e = launch_split_fmt<decltype(f)::value>(a, grid, s); });
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int run_combine(const mla_cache *cache, const DecodePlan &pl, const void *w_uv, int heads,
+                void *workspace, float *out, hipStream_t s) {
+  const int B = cache->batch;
+  uint8_t *ws = (uint8_t *)workspace;
+  hipLaunchKernelGGL(reduce_kernel, dim3(heads, (B + kReduceBT - 1) / kReduceBT, pl.layers), dim3(kReduceThreads),
+                     0, s, (const float *)(ws + pl.wl.m), (const float *)(ws + pl.wl.l),
+                     (const float *)(ws + pl.wl.acc), (const int32_t *)(ws + pl.wl.tab),
+                     (const uint16_t *)w_uv, B, heads, out);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+// Decode of layers [layer0, layer0 + layers): three launches.
+int decode_layers(const mla_cache *cache, int32_t layer0, int32_t layers, const void *q_nope, const void *q_pe,
+                  const void *w_uk, const void *w_uv, int32_t heads, float softmax_scale, int32_t num_splits,
+                  void *workspace, size_t workspace_bytes, float *out, hipStream_t s) {
+  int st = check_cache(cache);
+  if (st != MLA_OK) return st;
+  if (!layers_ok(cache, layer0, layers)) return MLA_ERR_INVALID_ARG;
+  if (!heads_ok(heads)) return MLA_ERR_UNSUPPORTED;
+  if ((st = check_absorb_args(q_nope, q_pe, w_uk, softmax_scale)) != MLA_OK) return st;
+  if ((st = check_combine_args(w_uv, out)) != MLA_OK) return st;
+  DecodePlan pl;
+  if ((st = plan_decode(cache, layers, heads, num_splits, workspace, workspace_bytes, &pl)) != MLA_OK) return st;
+  if ((st = run_absorb(cache, pl, q_nope, q_pe, w_uk, heads, softmax_scale, workspace, s)) != MLA_OK) return st;
+  if ((st = run_partial(cache, pl, layer0, heads, workspace, s)) != MLA_OK) return st;
+  return run_combine(cache, pl, w_uv, heads, workspace, out, s);
+}
+
+// Validation and first launch of the fused decode step of layers
+// [layer0, layer0 + layers) (store the new tokens, turn and absorb the
+// queries). Fills the plan on success.
+int step_begin(const mla_cache *cache, int32_t layer0, int32_t layers, const void *ckv_new, const void *kpe_new,
+               const void *q_nope, const void *q_pe, const float *rope_cos, const float *rope_sin,
+               int32_t rope_rows, const void *w_uk, int32_t heads, float softmax_scale, int32_t num_splits,
+               void *workspace, size_t workspace_bytes, hipStream_t s, DecodePlan *pl) {
+  int st = check_cache(cache);
+  if (st != MLA_OK) return st;
+  if (!layers_ok(cache, layer0, layers)) return MLA_ERR_INVALID_ARG;
+  if (!ckv_new || !kpe_new || !aligned16(ckv_new) || !aligned16(kpe_new)) return MLA_ERR_INVALID_ARG;
+  if ((rope_cos == nullptr) != (rope_sin == nullptr)) return MLA_ERR_INVALID_ARG;
+  if (rope_cos && (((uintptr_t)rope_cos & 3u) || ((uintptr_t)rope_sin & 3u) ||
+                   (int64_t)rope_rows < (int64_t)cache->capacity + 1))
+    return MLA_ERR_INVALID_ARG;
+  if (!heads_ok(heads)) return MLA_ERR_UNSUPPORTED;
+  if ((st = check_absorb_args(q_nope, q_pe, w_uk, softmax_scale)) != MLA_OK) return st;
+  if ((st = plan_decode(cache, layers, heads, num_splits, workspace, workspace_bytes, pl)) != MLA_OK) return st;
+  const int64_t n_absorb =
+      (int64_t)heads * (kLatent / kAbsorbCB) * ((cache->batch + kAbsorbBT - 1) / kAbsorbBT);
+  if ((n_absorb + cache->batch) * layers > kMaxGrid) return MLA_ERR_UNSUPPORTED;
+  const LayerPlanes p = layer_planes(cache, layer0);
+  StepArgs sa;
+  sa.ap.ckv = p.ckv;
+  sa.ap.kpe = p.kpe;
+  sa.ap.scale = p.scale;
+  sa.ap.zero = p.zero;
+  sa.ap.seq_lens = p.seq_lens;
+  sa.ap.ckv_new = (const uint16_t *)ckv_new;
+  sa.ap.kpe_new = (const uint16_t *)kpe_new;
+  sa.ap.n_new = nullptr;
+  sa.ap.rope_cos = rope_cos;
+  sa.ap.rope_sin = rope_sin;
+  sa.ap.pg = paging_of(cache);
+  sa.ap.B = cache->batch * layers;
+  sa.ap.T = 1;
+  sa.ap.cap = cache->capacity;
+  sa.q_nope = (const uint16_t *)q_nope;
+  sa.q_pe = (const uint16_t *)q_pe;
+  sa.w_uk = (const uint16_t *)w_uk;
+  sa.qa = (_Float16 *)((uint8_t *)workspace + pl->wl.qa);
+  sa.qs = softmax_scale * kLog2e;
+  sa.H = heads;
+  sa.n_absorb = (int)n_absorb;
+  sa.batch = cache->batch;
+  sa.layers = layers;
+  const dim3 g((unsigned)((n_absorb + cache->batch) * layers)), bl(256);
+  with_format(cache->format, [&](auto f) { hipLaunchKernelGGL(step_kernel<decltype(f)::value>, g, bl, 0, s, sa); });
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int step_layers(const mla_cache *cache, int32_t layer0, int32_t layers, const void *ckv_new, const void *kpe_new,
+                const void *q_nope, const void *q_pe, const float *rope_cos, const float *rope_sin,
+                int32_t rope_rows, const void *w_uk, const void *w_uv, int32_t heads, float softmax_scale,
+                int32_t num_splits, void *workspace, size_t workspace_bytes, float *out, hipStream_t s) {
+  // everything the later launches need is validated before the first one
+  if (check_combine_args(w_uv, out) != MLA_OK) return MLA_ERR_INVALID_ARG;
+  DecodePlan pl;
+  int st = step_begin(cache, layer0, layers, ckv_new, kpe_new, q_nope, q_pe, rope_cos, rope_sin, rope_rows, w_uk,
+                      heads, softmax_scale, num_splits, workspace, workspace_bytes, s, &pl);
+  if (st != MLA_OK) return st;
+  if ((st = run_partial(cache, pl, layer0, heads, workspace, s)) != MLA_OK) return st;
+  return run_combine(cache, pl, w_uv, heads, workspace, out, s);
 }
 
 }  // namespace
@@ -1946,190 +2222,54 @@ extern "C" int mla_cache_append(const mla_cache *cache, int32_t layer, const voi
 }
 
 extern "C" int mla_decode_auto_splits(const mla_cache *cache, int32_t heads, int32_t *num_splits) {
+  return mla_decode_auto_splits_layers(cache, 1, heads, num_splits);
+}
+
+extern "C" int mla_decode_auto_splits_layers(const mla_cache *cache, int32_t layer_count, int32_t heads,
+                                             int32_t *num_splits) {
   int st = check_cache(cache);
   if (st != MLA_OK) return st;
-  if (!num_splits) return MLA_ERR_INVALID_ARG;
+  if (!num_splits || layer_count < 1 || layer_count > cache->num_layers) return MLA_ERR_INVALID_ARG;
   if (!heads_ok(heads)) return MLA_ERR_UNSUPPORTED;
-  return auto_splits(cache, heads, num_splits);
+  return auto_splits(cache, heads, layer_count, num_splits);
 }
 
 extern "C" int mla_decode_workspace_bytes(const mla_cache *cache, int32_t heads, int32_t num_splits,
                                           size_t *bytes) {
+  return mla_decode_workspace_bytes_layers(cache, 1, heads, num_splits, bytes);
+}
+
+extern "C" int mla_decode_workspace_bytes_layers(const mla_cache *cache, int32_t layer_count, int32_t heads,
+                                                 int32_t num_splits, size_t *bytes) {
   int st = check_cache(cache);
   if (st != MLA_OK) return st;
-  if (!bytes) return MLA_ERR_INVALID_ARG;
+  if (!bytes || layer_count < 1 || layer_count > cache->num_layers) return MLA_ERR_INVALID_ARG;
   if (!heads_ok(heads)) return MLA_ERR_UNSUPPORTED;
   if (num_splits < 0 || num_splits > kMaxSplits) return MLA_ERR_INVALID_ARG;
   int ns = num_splits;
   if (ns == 0) {
-    st = auto_splits(cache, heads, &ns);
+    st = auto_splits(cache, heads, layer_count, &ns);
     if (st != MLA_OK) return st;
   }
-  *bytes = ws_layout(cache->batch, heads, ns).total;
+  *bytes = ws_layout(cache->batch, layer_count, heads, ns).total;
   return MLA_OK;
 }
-
-namespace {
-
-struct DecodePlan {
-  int ns;
-  WsLayout wl;
-};
-
-// Validation shared by the decode entry points: cache, heads, split count and
-// workspace. Fills the plan (split count, workspace layout) on success.
-int plan_decode(const mla_cache *cache, int heads, int num_splits, const void *workspace,
-                size_t workspace_bytes, DecodePlan *plan) {
-  int st = check_cache(cache);
-  if (st != MLA_OK) return st;
-  if (!heads_ok(heads)) return MLA_ERR_UNSUPPORTED;
-  if (num_splits < 0 || num_splits > kMaxSplits) return MLA_ERR_INVALID_ARG;
-  int ns = num_splits;
-  if (ns == 0) {
-    st = auto_splits(cache, heads, &ns);
-    if (st != MLA_OK) return st;
-  }
-  plan->ns = ns;
-  plan->wl = ws_layout(cache->batch, heads, ns);
-  if (!workspace || workspace_bytes < plan->wl.total || ((uintptr_t)workspace & 255u))
-    return MLA_ERR_WORKSPACE;
-  return MLA_OK;
-}
-
-int check_absorb_args(const void *q_nope, const void *q_pe, const void *w_uk, float softmax_scale) {
-  if (!q_nope || !q_pe || !w_uk) return MLA_ERR_INVALID_ARG;
-  if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(w_uk)) return MLA_ERR_INVALID_ARG;
-  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return MLA_ERR_INVALID_ARG;
-  return MLA_OK;
-}
-
-int check_combine_args(const void *w_uv, const float *out) {
-  if (!w_uv || !out || !aligned16(w_uv) || !aligned16(out)) return MLA_ERR_INVALID_ARG;
-  return MLA_OK;
-}
-
-int run_absorb(const mla_cache *cache, const DecodePlan &pl, const void *q_nope, const void *q_pe,
-               const void *w_uk, int heads, float softmax_scale, void *workspace, hipStream_t s) {
-  const int B = cache->batch;
-  _Float16 *qa = (_Float16 *)((uint8_t *)workspace + pl.wl.qa);
-  hipLaunchKernelGGL(absorb_kernel, dim3(heads, kLatent / kAbsorbCB, (B + kAbsorbBT - 1) / kAbsorbBT),
-                     dim3(256), 0, s,
-                     (const uint16_t *)q_nope, (const uint16_t *)q_pe, (const uint16_t *)w_uk, B, heads,
-                     softmax_scale * kLog2e, qa);
-  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
-}
-
-int run_partial(const mla_cache *cache, const DecodePlan &pl, int layer, int heads, void *workspace,
-                hipStream_t s) {
-  const LayerPlanes p = layer_planes(cache, layer);
-  uint8_t *ws = (uint8_t *)workspace;
-  SplitArgs a;
-  a.ckv = p.ckv;
-  a.kpe = p.kpe;
-  a.scale = p.scale;
-  a.zero = p.zero;
-  a.seq_lens = p.seq_lens;
-  a.qa = (const _Float16 *)(ws + pl.wl.qa);
-  a.ws_m = (float *)(ws + pl.wl.m);
-  a.ws_l = (float *)(ws + pl.wl.l);
-  a.ws_acc = (float *)(ws + pl.wl.acc);
-  a.B = cache->batch;
-  a.H = heads;
-  a.cap = cache->capacity;
-  a.pg = paging_of(cache);
-  a.rec_tab = (int32_t *)(ws + pl.wl.tab);
-  // the balanced plan's nsplit * B ranges, each as heads / 16 head slices,
-  // rounded up to whole windows of 8 ranges (see split16_kernel)
-  a.W = pl.ns * cache->batch;
-  const dim3 grid((unsigned)(((int64_t)a.W + 7) / 8 * 8 * (heads / 16)));
-  hipError_t e = hipSuccess;
-  with_format(cache->format, [&](auto f) { e = launch_split_fmt<decltype(f)::value>(a, grid, s); });
-  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
-}
-
-int run_combine(const mla_cache *cache, const DecodePlan &pl, const void *w_uv, int heads,
-                void *workspace, float *out, hipStream_t s) {
-  const int B = cache->batch;
-  uint8_t *ws = (uint8_t *)workspace;
-  hipLaunchKernelGGL(reduce_kernel, dim3(heads, (B + kReduceBT - 1) / kReduceBT), dim3(kReduceThreads), 0, s,
-                     (const float *)(ws + pl.wl.m), (const float *)(ws + pl.wl.l),
-                     (const float *)(ws + pl.wl.acc), (const int32_t *)(ws + pl.wl.tab),
-                     (const uint16_t *)w_uv, B, heads, out);
-  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
-}
-
-}  // namespace
 
 extern "C" int mla_decode_attn(const mla_cache *cache, int32_t layer, const void *q_nope,
                                const void *q_pe, const void *w_uk, const void *w_uv, int32_t heads,
                                float softmax_scale, int32_t num_splits, void *workspace,
                                size_t workspace_bytes, float *out, void *hip_stream) {
-  int st = check_cache(cache);
-  if (st != MLA_OK) return st;
-  if (layer < 0 || layer >= cache->num_layers) return MLA_ERR_INVALID_ARG;
-  if (!heads_ok(heads)) return MLA_ERR_UNSUPPORTED;
-  if ((st = check_absorb_args(q_nope, q_pe, w_uk, softmax_scale)) != MLA_OK) return st;
-  if ((st = check_combine_args(w_uv, out)) != MLA_OK) return st;
-  DecodePlan pl;
-  if ((st = plan_decode(cache, heads, num_splits, workspace, workspace_bytes, &pl)) != MLA_OK) return st;
-  hipStream_t s = (hipStream_t)hip_stream;
-  if ((st = run_absorb(cache, pl, q_nope, q_pe, w_uk, heads, softmax_scale, workspace, s)) != MLA_OK)
-    return st;
-  if ((st = run_partial(cache, pl, layer, heads, workspace, s)) != MLA_OK) return st;
-  return run_combine(cache, pl, w_uv, heads, workspace, out, s);
+  return decode_layers(cache, layer, 1, q_nope, q_pe, w_uk, w_uv, heads, softmax_scale, num_splits, workspace,
+                       workspace_bytes, out, (hipStream_t)hip_stream);
 }
 
-namespace {
-
-// Validation and first launch of the fused decode step (store the new
-// token, turn and absorb the query). Fills the plan on success.
-int step_begin(const mla_cache *cache, int32_t layer, const void *ckv_new, const void *kpe_new,
-               const void *q_nope, const void *q_pe, const float *rope_cos, const float *rope_sin,
-               int32_t rope_rows, const void *w_uk, int32_t heads, float softmax_scale, int32_t num_splits,
-               void *workspace, size_t workspace_bytes, hipStream_t s, DecodePlan *pl) {
-  int st = check_cache(cache);
-  if (st != MLA_OK) return st;
-  if (layer < 0 || layer >= cache->num_layers) return MLA_ERR_INVALID_ARG;
-  if (!ckv_new || !kpe_new || !aligned16(ckv_new) || !aligned16(kpe_new)) return MLA_ERR_INVALID_ARG;
-  if ((rope_cos == nullptr) != (rope_sin == nullptr)) return MLA_ERR_INVALID_ARG;
-  if (rope_cos && (((uintptr_t)rope_cos & 3u) || ((uintptr_t)rope_sin & 3u) ||
-                   (int64_t)rope_rows < (int64_t)cache->capacity + 1))
-    return MLA_ERR_INVALID_ARG;
-  if (!heads_ok(heads)) return MLA_ERR_UNSUPPORTED;
-  if ((st = check_absorb_args(q_nope, q_pe, w_uk, softmax_scale)) != MLA_OK) return st;
-  if ((st = plan_decode(cache, heads, num_splits, workspace, workspace_bytes, pl)) != MLA_OK) return st;
-  const int64_t n_absorb =
-      (int64_t)heads * (kLatent / kAbsorbCB) * ((cache->batch + kAbsorbBT - 1) / kAbsorbBT);
-  if (n_absorb + cache->batch > INT32_MAX) return MLA_ERR_UNSUPPORTED;
-  const LayerPlanes p = layer_planes(cache, layer);
-  StepArgs sa;
-  sa.ap.ckv = p.ckv;
-  sa.ap.kpe = p.kpe;
-  sa.ap.scale = p.scale;
-  sa.ap.zero = p.zero;
-  sa.ap.seq_lens = p.seq_lens;
-  sa.ap.ckv_new = (const uint16_t *)ckv_new;
-  sa.ap.kpe_new = (const uint16_t *)kpe_new;
-  sa.ap.n_new = nullptr;
-  sa.ap.rope_cos = rope_cos;
-  sa.ap.rope_sin = rope_sin;
-  sa.ap.pg = paging_of(cache);
-  sa.ap.B = cache->batch;
-  sa.ap.T = 1;
-  sa.ap.cap = cache->capacity;
-  sa.q_nope = (const uint16_t *)q_nope;
-  sa.q_pe = (const uint16_t *)q_pe;
-  sa.w_uk = (const uint16_t *)w_uk;
-  sa.qa = (_Float16 *)((uint8_t *)workspace + pl->wl.qa);
-  sa.qs = softmax_scale * kLog2e;
-  sa.H = heads;
-  sa.n_absorb = (int)n_absorb;
-  const dim3 g((unsigned)(n_absorb + cache->batch)), bl(256);
-  with_format(cache->format, [&](auto f) { hipLaunchKernelGGL(step_kernel<decltype(f)::value>, g, bl, 0, s, sa); });
-  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+extern "C" int mla_decode_attn_layers(const mla_cache *cache, int32_t layer0, int32_t layer_count,
+                                      const void *q_nope, const void *q_pe, const void *w_uk, const void *w_uv,
+                                      int32_t heads, float softmax_scale, int32_t num_splits, void *workspace,
+                                      size_t workspace_bytes, float *out, void *hip_stream) {
+  return decode_layers(cache, layer0, layer_count, q_nope, q_pe, w_uk, w_uv, heads, softmax_scale, num_splits,
+                       workspace, workspace_bytes, out, (hipStream_t)hip_stream);
 }
-
-}  // namespace
 
 extern "C" int mla_decode_step(const mla_cache *cache, int32_t layer, const void *ckv_new,
                                const void *kpe_new, const void *q_nope, const void *q_pe,
@@ -2137,15 +2277,70 @@ extern "C" int mla_decode_step(const mla_cache *cache, int32_t layer, const void
                                const void *w_uk, const void *w_uv, int32_t heads, float softmax_scale,
                                int32_t num_splits, void *workspace, size_t workspace_bytes, float *out,
                                void *hip_stream) {
-  // everything the later launches need is validated before the first one
-  if (check_combine_args(w_uv, out) != MLA_OK) return MLA_ERR_INVALID_ARG;
-  hipStream_t s = (hipStream_t)hip_stream;
+  return step_layers(cache, layer, 1, ckv_new, kpe_new, q_nope, q_pe, rope_cos, rope_sin, rope_rows, w_uk, w_uv,
+                     heads, softmax_scale, num_splits, workspace, workspace_bytes, out, (hipStream_t)hip_stream);
+}
+
+extern "C" int mla_decode_step_layers(const mla_cache *cache, int32_t layer0, int32_t layer_count,
+                                      const void *ckv_new, const void *kpe_new, const void *q_nope,
+                                      const void *q_pe, const float *rope_cos, const float *rope_sin,
+                                      int32_t rope_rows, const void *w_uk, const void *w_uv, int32_t heads,
+                                      float softmax_scale, int32_t num_splits, void *workspace,
+                                      size_t workspace_bytes, float *out, void *hip_stream) {
+  return step_layers(cache, layer0, layer_count, ckv_new, kpe_new, q_nope, q_pe, rope_cos, rope_sin, rope_rows,
+                     w_uk, w_uv, heads, softmax_scale, num_splits, workspace, workspace_bytes, out,
+                     (hipStream_t)hip_stream);
+}
+
+extern "C" int mla_decode_step_begin_layers(const mla_cache *cache, int32_t layer0, int32_t layer_count,
+                                            const void *ckv_new, const void *kpe_new, const void *q_nope,
+                                            const void *q_pe, const float *rope_cos, const float *rope_sin,
+                                            int32_t rope_rows, const void *w_uk, int32_t heads,
+                                            float softmax_scale, int32_t num_splits, void *workspace,
+                                            size_t workspace_bytes, void *hip_stream) {
   DecodePlan pl;
-  int st = step_begin(cache, layer, ckv_new, kpe_new, q_nope, q_pe, rope_cos, rope_sin, rope_rows, w_uk,
-                      heads, softmax_scale, num_splits, workspace, workspace_bytes, s, &pl);
+  return step_begin(cache, layer0, layer_count, ckv_new, kpe_new, q_nope, q_pe, rope_cos, rope_sin, rope_rows,
+                    w_uk, heads, softmax_scale, num_splits, workspace, workspace_bytes, (hipStream_t)hip_stream,
+                    &pl);
+}
+
+extern "C" int mla_decode_absorb_layers(const mla_cache *cache, int32_t layer_count, const void *q_nope,
+                                        const void *q_pe, const void *w_uk, int32_t heads, float softmax_scale,
+                                        int32_t num_splits, void *workspace, size_t workspace_bytes,
+                                        void *hip_stream) {
+  int st = check_cache(cache);
   if (st != MLA_OK) return st;
-  if ((st = run_partial(cache, pl, layer, heads, workspace, s)) != MLA_OK) return st;
-  return run_combine(cache, pl, w_uv, heads, workspace, out, s);
+  if (!heads_ok(heads)) return MLA_ERR_UNSUPPORTED;
+  if ((st = check_absorb_args(q_nope, q_pe, w_uk, softmax_scale)) != MLA_OK) return st;
+  DecodePlan pl;
+  if ((st = plan_decode(cache, layer_count, heads, num_splits, workspace, workspace_bytes, &pl)) != MLA_OK)
+    return st;
+  return run_absorb(cache, pl, q_nope, q_pe, w_uk, heads, softmax_scale, workspace, (hipStream_t)hip_stream);
+}
+
+extern "C" int mla_decode_partial_layers(const mla_cache *cache, int32_t layer0, int32_t layer_count,
+                                         int32_t heads, int32_t num_splits, void *workspace,
+                                         size_t workspace_bytes, void *hip_stream) {
+  int st = check_cache(cache);
+  if (st != MLA_OK) return st;
+  if (!layers_ok(cache, layer0, layer_count)) return MLA_ERR_INVALID_ARG;
+  DecodePlan pl;
+  if ((st = plan_decode(cache, layer_count, heads, num_splits, workspace, workspace_bytes, &pl)) != MLA_OK)
+    return st;
+  return run_partial(cache, pl, layer0, heads, workspace, (hipStream_t)hip_stream);
+}
+
+extern "C" int mla_decode_combine_layers(const mla_cache *cache, int32_t layer_count, const void *w_uv,
+                                         int32_t heads, int32_t num_splits, void *workspace,
+                                         size_t workspace_bytes, float *out, void *hip_stream) {
+  int st = check_cache(cache);
+  if (st != MLA_OK) return st;
+  if (!heads_ok(heads)) return MLA_ERR_UNSUPPORTED;
+  if ((st = check_combine_args(w_uv, out)) != MLA_OK) return st;
+  DecodePlan pl;
+  if ((st = plan_decode(cache, layer_count, heads, num_splits, workspace, workspace_bytes, &pl)) != MLA_OK)
+    return st;
+  return run_combine(cache, pl, w_uv, heads, workspace, out, (hipStream_t)hip_stream);
 }
 
 extern "C" int mla_decode_step_begin(const mla_cache *cache, int32_t layer, const void *ckv_new,
@@ -2155,7 +2350,7 @@ extern "C" int mla_decode_step_begin(const mla_cache *cache, int32_t layer, cons
                                      int32_t num_splits, void *workspace, size_t workspace_bytes,
                                      void *hip_stream) {
   DecodePlan pl;
-  return step_begin(cache, layer, ckv_new, kpe_new, q_nope, q_pe, rope_cos, rope_sin, rope_rows, w_uk, heads,
+  return step_begin(cache, layer, 1, ckv_new, kpe_new, q_nope, q_pe, rope_cos, rope_sin, rope_rows, w_uk, heads,
                     softmax_scale, num_splits, workspace, workspace_bytes, (hipStream_t)hip_stream, &pl);
 }
 
@@ -2168,9 +2363,8 @@ extern "C" int mla_decode_absorb(const mla_cache *cache, const void *q_nope, con
   if (!heads_ok(heads)) return MLA_ERR_UNSUPPORTED;
   if ((st = check_absorb_args(q_nope, q_pe, w_uk, softmax_scale)) != MLA_OK) return st;
   DecodePlan pl;
-  if ((st = plan_decode(cache, heads, num_splits, workspace, workspace_bytes, &pl)) != MLA_OK) return st;
-  return run_absorb(cache, pl, q_nope, q_pe, w_uk, heads, softmax_scale, workspace,
-                    (hipStream_t)hip_stream);
+  if ((st = plan_decode(cache, 1, heads, num_splits, workspace, workspace_bytes, &pl)) != MLA_OK) return st;
+  return run_absorb(cache, pl, q_nope, q_pe, w_uk, heads, softmax_scale, workspace, (hipStream_t)hip_stream);
 }
 
 extern "C" int mla_decode_partial(const mla_cache *cache, int32_t layer, int32_t heads,
@@ -2180,7 +2374,7 @@ extern "C" int mla_decode_partial(const mla_cache *cache, int32_t layer, int32_t
   if (st != MLA_OK) return st;
   if (layer < 0 || layer >= cache->num_layers) return MLA_ERR_INVALID_ARG;
   DecodePlan pl;
-  if ((st = plan_decode(cache, heads, num_splits, workspace, workspace_bytes, &pl)) != MLA_OK) return st;
+  if ((st = plan_decode(cache, 1, heads, num_splits, workspace, workspace_bytes, &pl)) != MLA_OK) return st;
   return run_partial(cache, pl, layer, heads, workspace, (hipStream_t)hip_stream);
 }
 
@@ -2192,8 +2386,30 @@ extern "C" int mla_decode_combine(const mla_cache *cache, const void *w_uv, int3
   if (!heads_ok(heads)) return MLA_ERR_UNSUPPORTED;
   if ((st = check_combine_args(w_uv, out)) != MLA_OK) return st;
   DecodePlan pl;
-  if ((st = plan_decode(cache, heads, num_splits, workspace, workspace_bytes, &pl)) != MLA_OK) return st;
+  if ((st = plan_decode(cache, 1, heads, num_splits, workspace, workspace_bytes, &pl)) != MLA_OK) return st;
   return run_combine(cache, pl, w_uv, heads, workspace, out, (hipStream_t)hip_stream);
+}
+
+extern "C" int mla_stream_read(const void *buf, size_t bytes, uint32_t *sink, int32_t sink_words,
+                               void *hip_stream) {
+  if (!buf || !sink || !aligned16(buf) || (bytes & 15u) || ((uintptr_t)sink & 3u) || sink_words < 1)
+    return MLA_ERR_INVALID_ARG;
+  if (bytes == 0) return MLA_OK;
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)sink_words), dim3(256), 0, (hipStream_t)hip_stream,
+                     (const u32x4 *)buf, (int64_t)(bytes / 16), sink);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+extern "C" int mla_rope_tables(float *cos_out, float *sin_out, int32_t rows, double base, void *hip_stream) {
+  if (!cos_out || !sin_out || ((uintptr_t)cos_out & 3u) || ((uintptr_t)sin_out & 3u)) return MLA_ERR_INVALID_ARG;
+  if (rows < 0 || !(base > 0.0) || isinf(base)) return MLA_ERR_INVALID_ARG;
+  if (rows == 0) return MLA_OK;
+  RopeTheta th;
+  for (int i = 0; i < kRope / 2; ++i) th.t[i] = pow(base, (-2.0 * i) / kRope);
+  const int64_t blocks = ((int64_t)rows * (kRope / 2) + 255) / 256;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)hip_stream, cos_out,
+                     sin_out, rows, th);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 extern "C" int mla_cache_get(const mla_cache *cache, int32_t layer, float *ckv_out, float *kpe_out,

@@ -1,5 +1,8 @@
 """Shared helpers for the GPU parity tests (HIP path vs the CPU oracle)."""
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -119,3 +122,33 @@ def build_workload(wid, device="cuda"):
         del ckv, kpe
     torch.cuda.synchronize()
     return cache, lens
+
+
+def oracle_threads():
+    """Host threads for oracle work that runs beside a GPU test (numpy releases
+    the interpreter lock in its array loops and in BLAS)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def run_oracle_jobs(jobs, threads=None, window=None):
+    """Run oracle jobs on a thread pool and yield (key, result) in submission
+    order. `jobs` yields (key, fn, args); the producer side (which may make GPU
+    tensors and copy them to the host) runs on the calling thread, at most
+    `window` jobs ahead of the results consumed."""
+    threads = threads or oracle_threads()
+    window = window or 2 * threads
+    pending = []
+    with ThreadPoolExecutor(max_workers=threads) as pool:
+        for key, fn, args in jobs:
+            pending.append((key, pool.submit(fn, *args)))
+            while len(pending) >= window:
+                k, fut = pending.pop(0)
+                yield k, fut.result()
+        for k, fut in pending:
+            yield k, fut.result()
+
+
+def oracle_decode_np(ckv, kpe, fmt, q_nope, q_pe, w_uk, w_uv, scale=W.SOFTMAX_SCALE):
+    """oracle_decode on host float32 arrays (thread-pool friendly: no torch)."""
+    ch, kh = Q.dequantize_rows(Q.quantize_rows(ckv, kpe, fmt), fmt)
+    return A.decode_absorbed(q_nope, q_pe, w_uk, w_uv, ch, kh, scale)

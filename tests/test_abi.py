@@ -211,6 +211,37 @@ def test_get_argument_validation_before_launch():
     assert L.mla_cache_get(ctypes.byref(s), 0, None, None, None) == _lib.MLA_OK
 
 
+def test_size_limits_before_launch():
+    # one sequence's rows of any plane must stay below 2^30 bytes (the kernels
+    # address them through 32-bit buffer descriptors)
+    L = _lib.lib()
+    ok = cache_struct("bf16", cap=(1 << 20))            # 1 Mi tokens x 1024 B
+    assert _ws(ok, 16, 4)[0] == _lib.MLA_OK
+    big = cache_struct("bf16", cap=(1 << 20) + 1)
+    assert _ws(big, 16, 4)[0] == _lib.MLA_ERR_UNSUPPORTED
+    assert L.mla_cache_append(ctypes.byref(big), 0, FAKE, FAKE, 1, None, None) == _lib.MLA_ERR_UNSUPPORTED
+    assert _ws(cache_struct("int4", cap=(1 << 22)), 16, 4)[0] == _lib.MLA_OK   # 256-byte latent rows
+    assert _ws(cache_struct("int4", cap=(1 << 23) + 1), 16, 4)[0] == _lib.MLA_ERR_UNSUPPORTED
+    # the partial grid (ranges x head slices) and the plan's tile count are
+    # 32-bit: a batch whose tiles or workgroups pass 2^31 - 1 is refused
+    huge = cache_struct("int8", B=1 << 20, cap=(1 << 20))
+    assert _decode(huge) == _lib.MLA_ERR_UNSUPPORTED
+    wide = cache_struct("int8", B=1 << 19, cap=64)
+    assert _ws(wide, 128, 4096)[0] == _lib.MLA_OK  # the size alone is fine
+    ws = _ws(wide, 128, 4096)[1]
+    assert _decode(wide, heads=128, splits=4096, ws_bytes=ws) == _lib.MLA_ERR_UNSUPPORTED
+
+
+def test_rope_tables_argument_validation_before_launch():
+    L = _lib.lib()
+    assert L.mla_rope_tables(0, FAKE, 10, 10000.0, None) == _lib.MLA_ERR_INVALID_ARG
+    assert L.mla_rope_tables(FAKE, FAKE + 2, 10, 10000.0, None) == _lib.MLA_ERR_INVALID_ARG
+    assert L.mla_rope_tables(FAKE, FAKE, -1, 10000.0, None) == _lib.MLA_ERR_INVALID_ARG
+    assert L.mla_rope_tables(FAKE, FAKE, 10, 0.0, None) == _lib.MLA_ERR_INVALID_ARG
+    assert L.mla_rope_tables(FAKE, FAKE, 10, math.inf, None) == _lib.MLA_ERR_INVALID_ARG
+    assert L.mla_rope_tables(FAKE, FAKE, 0, 10000.0, None) == _lib.MLA_OK  # nothing to launch
+
+
 def test_python_binding_has_no_fallback(monkeypatch, tmp_path):
     # With the library missing the binding raises instead of computing anything.
     monkeypatch.setattr(_lib, "_lib", None)

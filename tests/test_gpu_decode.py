@@ -168,3 +168,50 @@ def test_short_sequences_with_outlier_channels(fmt, heads):
         out = cache.decode(0, qn, qp, wuk, wuv, TAU)
         torch.cuda.synchronize()
         check_all(cache, rows, qn, qp, wuk, wuv, out, fmt, f"{fmt} H{heads} seed {seed}")
+
+
+@pytest.mark.parametrize("fmt", ["int4", "int4_kint4", "int8", "int8_kbf16"])
+def test_groups_at_the_edge_of_the_fp16_domain(fmt):
+    # The decode path multiplies codes by scales in fp16 (include/mla_kv.h,
+    # domain of the decode path). Groups at the edge of that domain: INT4
+    # latents with a 16-channel range of 65280 (scale 4352, 15 s = 65280) and
+    # INT8 latents at +-65024 (scale 512, 127 s = 65024). Such tokens give
+    # scores in the thousands, so the softmax concentrates on one of them and
+    # the INT4 weights multiply the largest scales (p s with p <= 1).
+    lens = [3, 40, 97, 130]
+    B, H = len(lens), 16
+    cache = LatentCache(fmt, 1, B, max(lens), device=torch.device("cuda"))
+    from gpu_util import random_rows
+    rows = []
+    ckv = torch.zeros((B, max(lens), 512), dtype=torch.bfloat16, device="cuda")
+    kpe = torch.zeros((B, max(lens), 64), dtype=torch.bfloat16, device="cuda")
+    rng = np.random.default_rng(5)
+    for b, n in enumerate(lens):
+        c, k = random_rows(n, 500 + b, "skew" if fmt.startswith("int4") else "outlier")
+        c = c.float()
+        # a few tokens with one group at the edge, spread over the tiles
+        for t in rng.choice(n, size=min(n, 4), replace=False):
+            g = int(rng.integers(0, 32))
+            if fmt.startswith("int4"):
+                vals = torch.linspace(-32640.0, 32640.0, 16)[torch.from_numpy(rng.permutation(16))]
+            else:
+                vals = torch.from_numpy(rng.choice([-65024.0, 65024.0], size=16)).float()
+            c[t, 16 * g:16 * g + 16] = vals.to(c.device)
+        c = c.to(torch.bfloat16)
+        ckv[b, :n], kpe[b, :n] = c, k
+        rows.append((c, k))
+    cache.append(0, ckv, kpe, n_new=lens)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(6)
+    qn = torch.randn((B, H, 128), generator=g, device="cuda").to(torch.bfloat16)
+    qp = torch.randn((B, H, 64), generator=g, device="cuda").to(torch.bfloat16)
+    wuk = (torch.randn((H, 128, 512), generator=g, device="cuda") / 512 ** 0.5).to(torch.bfloat16)
+    wuv = (torch.randn((H, 512, 128), generator=g, device="cuda") / 512 ** 0.5).to(torch.bfloat16)
+    # the scales really are at the edge
+    from gpu_util import oracle_planes
+    sc = np.concatenate([oracle_planes(c, k, fmt)["scale"][:, :32].astype(np.float64).ravel() for c, k in rows])
+    assert sc.max() == (4352.0 if fmt.startswith("int4") else 512.0)
+    for splits in (1, 0):
+        out = cache.decode(0, qn, qp, wuk, wuv, TAU, num_splits=splits)
+        torch.cuda.synchronize()
+        check_all(cache, rows, qn, qp, wuk, wuv, out, fmt, f"{fmt} edge groups splits {splits}")

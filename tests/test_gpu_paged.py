@@ -83,8 +83,9 @@ def test_paged_equals_contiguous(fmt, heads):
 
 
 @pytest.mark.parametrize("fmt", ["int8", "int4_kint4"])
-def test_paged_fused_step_equals_contiguous(fmt):
-    lens, cap, ps, H = [63, 64, 127, 0], 128, 32, 16
+@pytest.mark.parametrize("H", [16, 32, 128])
+def test_paged_fused_step_equals_contiguous(fmt, H):
+    lens, cap, ps = [63, 64, 127, 0], 128, 32
     B, blocks = len(lens), cap // ps
     table = shuffled_table(B, blocks, B * blocks, seed=5)
     flat = LatentCache(fmt, 1, B, cap)
@@ -105,6 +106,34 @@ def test_paged_fused_step_equals_contiguous(fmt):
         pf, pp = flat.planes(0, b), paged.planes(0, b)
         for key in pf:
             assert torch.equal(pf[key], pp[key]), (b, key)
+
+
+def test_paged_fused_step_against_oracle_32_heads():
+    # the paged step on its own against the oracle: stored rows bit-exact
+    # through the block table, outputs within tolerance
+    fmt, lens, cap, ps, H = "int4", [0, 31, 32, 95, 127], 128, 32, 32
+    B, blocks = len(lens), cap // ps
+    table = shuffled_table(B, blocks, B * blocks + 3, seed=9)
+    paged = LatentCache(fmt, 1, B, cap, page_size=ps, num_pages=B * blocks + 3, block_table=table)
+    rows = fill(paged, lens, 41, fmt)
+    cos, sin = R.rope_tables(cap + 1)
+    rope = (torch.from_numpy(cos).cuda(), torch.from_numpy(sin).cuda())
+    c, k = random_rows(B, 400, "skew")
+    qn, qp, wuk, wuv = queries(B, H, 42)
+    out = paged.decode_step(0, c.contiguous(), k.contiguous(), qn, qp, wuk, wuv, TAU, rope=rope)
+    torch.cuda.synchronize()
+    assert paged.seq_lens[0].tolist() == [n + 1 for n in lens]
+    from oracle import quant as Q
+    for b in range(B):
+        if lens[b]:
+            ch, kh = Q.dequantize_rows(oracle_planes(rows[b][0], rows[b][1], fmt), fmt)
+        else:
+            ch, kh = np.zeros((0, 512)), np.zeros((0, 64))
+        planes, n, ref = R.decode_step(ch, kh, lens[b], cap, f32(c[b]), f32(k[b]), f32(qn[b]), f32(qp[b]),
+                                       f32(wuk), f32(wuv), TAU, fmt, cos, sin)
+        assert_close(f32(out[b]), ref, f"paged step seq {b}")
+        got = {key: v[-1:] for key, v in paged.planes(0, b).items()}
+        assert_planes_equal(got, {key: v[None] for key, v in planes.items()}, fmt, f"paged step seq {b} row")
 
 
 def test_table_entries_past_the_length_are_never_used():

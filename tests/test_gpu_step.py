@@ -45,7 +45,7 @@ def tables(rows_needed):
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "int8", "int4", "int8_kbf16", "int4_kint4"])
-@pytest.mark.parametrize("heads", [16, 32])
+@pytest.mark.parametrize("heads", [16, 32, 64, 128])
 def test_step_with_rope_against_oracle(fmt, heads):
     cap = 320
     lens = [0, 1, 37, 319, 320]  # the last sequence is full: nothing is stored
@@ -129,3 +129,52 @@ def test_step_phases_equal_one_call():
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
     assert torch.equal(a.seq_lens, b_.seq_lens)
+
+
+@pytest.mark.parametrize("fmt,heads", [("int8", 16), ("int4", 16), ("int8", 128), ("int4_kint4", 64)])
+def test_step_two_absorb_batch_tiles(fmt, heads):
+    # more than 64 sequences: the step's absorption runs in two batch tiles of
+    # 64 rows (the second one partial), and 100 store blocks follow them
+    rng = np.random.default_rng(heads)
+    lens = rng.integers(0, 90, size=100).tolist()
+    lens[0], lens[-1] = 0, 96  # an empty and a full sequence
+    cap = 96
+    B = len(lens)
+    cache, rows, _, _, wuk, wuv = random_problem(fmt, B, heads, lens, seed=201 + heads, cap=cap)
+    ckv_new, kpe_new, qn, qp = new_tokens(B, heads, 202 + heads, fmt)
+    cos, sin, rope = tables(cap + 1)
+    before = oracle_rows(rows, fmt)
+    out = cache.decode_step(0, ckv_new, kpe_new, qn, qp, wuk, wuv, TAU, rope=rope)
+    torch.cuda.synchronize()
+    assert cache.seq_lens[0].tolist() == [min(n + 1, cap) for n in lens]
+    out_h, qn_h, qp_h, wk, wv = f32(out), f32(qn), f32(qp), f32(wuk), f32(wuv)
+    cn, kn = f32(ckv_new), f32(kpe_new)
+    for b in range(B):
+        planes, n, ref = R.decode_step(before[b][0], before[b][1], lens[b], cap, cn[b], kn[b], qn_h[b], qp_h[b],
+                                       wk, wv, TAU, fmt, cos, sin)
+        assert_close(out_h[b], ref, f"{fmt} H{heads} B{B} seq {b} (len {lens[b]})")
+        if planes is not None:
+            got = {k: v[-1:] for k, v in cache.planes(0, b).items()}
+            assert_planes_equal(got, {k: v[None] for k, v in planes.items()}, fmt, f"{fmt} seq {b} stored row")
+
+
+def test_library_rope_tables_match_the_oracle_tables():
+    # mla_rope_tables (the tables the benchmark's decode step uses) against the
+    # oracle's, for positions up to the longest workload (131072 tokens and a
+    # few steps). Both evaluate cos and sin in fp64 and round to fp32, but
+    # theta_i = 10000^(-2i/64) comes from two fp64 pow routines (numpy's and
+    # the C library's) that can differ in the last bit; times a position near
+    # 131072 that moves an angle by ~1e-11, so entries agree to within one
+    # fp32 rounding of the value (2^-24) plus that, not bit for bit.
+    from mla_latent_kv_cache_amd import rope_tables
+    rows = 131072 + 64
+    cos, sin = rope_tables(rows)
+    torch.cuda.synchronize()
+    rc, rs = R.rope_tables(rows)
+    for got, ref, name in ((f32(cos), rc, "cos"), (f32(sin), rs, "sin")):
+        assert got.shape == ref.shape
+        err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
+        assert err.max() <= 2.0 ** -24 + 1e-9, f"{name}: max abs difference {err.max():.3g}"
+        frac = float((err != 0).mean())
+        print(f"  rope {name}: {frac:.2e} of entries differ, max {err.max():.2e}", flush=True)
+        assert frac < 1e-3
