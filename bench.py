@@ -70,22 +70,29 @@ def pct(xs):
 # ----------------------------------------------------------------- GPU side
 
 class Flusher:
-    """A 1 GiB device buffer written with a fill kernel on the stream, so that
-    the next launch finds none of its inputs in the last-level cache."""
+    """Reads a 1 GiB device buffer (mla_stream_read) on the stream, so that the
+    next launch finds none of its inputs in the last-level cache. A read, not a
+    write: written lines would be dirty in the cache and their write-back would
+    land inside the next timed launch."""
 
     def __init__(self, torch):
-        self.buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
-        self.k = 0
+        from mla_latent_kv_cache_amd import _lib
+        self.buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+        self.sink = torch.empty(4096, dtype=torch.int32, device="cuda")
+        self.lib = _lib
+        self.torch = torch
 
     def __call__(self):
-        self.k += 1
-        self.buf.fill_(self.k)
+        st = self.torch.cuda.current_stream()
+        self.lib.check(self.lib.lib().mla_stream_read(ctypes.c_void_p(self.buf.data_ptr()), FLUSH_BYTES,
+                                                      ctypes.c_void_p(self.sink.data_ptr()), 4096,
+                                                      ctypes.c_void_p(st.cuda_stream)), "flush")
 
 
 class Runner:
     """One workload's cache, weights, queries and the ctypes calls of a step."""
 
-    def __init__(self, wid, extra_steps, fmt=None, layers=None, page_size=0):
+    def __init__(self, wid, extra_steps, fmt=None, layers=None, page_size=0, splits=None):
         import dataclasses
         import torch
         from mla_latent_kv_cache_amd import LatentCache, _lib, rope_tables
@@ -144,7 +151,7 @@ class Runner:
         log(f"{w.name}: prefilled {int(self.lens0.sum()) * w.layers} tokens "
             f"({cache.bytes() / 1e9:.2f} GB of cache planes) in {time.time() - t0:.1f}s")
         self.H = w.heads
-        self.splits = w.num_splits
+        self.splits = w.num_splits if splits is None else splits
         L = w.layers
         q = [W.queries(wid, layer, dev) for layer in range(L)]
         wts = [W.weights(wid, layer, dev) for layer in range(L)]
@@ -259,13 +266,13 @@ def append_result(what, tokens, ms, fmt):
             "gb_per_s": tokens * per_token / (ms / 1e3) / 1e9, "bytes_per_token": per_token, "ms": ms}
 
 
-def measure_stack(wid, steps, warmup):
+def measure_stack(wid, steps, warmup, per_layer=True, splits=None):
     """The multi-layer workload: W untimed steps; K timed steps (one event
     between consecutive steps: value, ms_per_step and its spread); K steps
     with events around each partial-attention launch (its average duration,
     for the roofline); K steps as one-layer calls (81 launches each)."""
     import torch
-    r = Runner(wid, 3 * steps + warmup + 1, layers=None)
+    r = Runner(wid, 3 * steps + warmup + 1, layers=None, splits=splits)
     for _ in range(warmup):
         r.step()
     torch.cuda.synchronize()
@@ -290,16 +297,18 @@ def measure_stack(wid, steps, warmup):
     part_ms = [e0.elapsed_time(e1) for e0, e1 in events]
     part_bytes = [r.kv_tokens(first_ev + i) * row_bytes(r.w.fmt) for i in range(steps)]
     # the same steps as one-layer calls
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    first_pl = r.steps_done + 1
-    t0.record(r.stream)
-    for _ in range(steps):
-        r.step_per_layer()
-    t1.record(r.stream)
-    torch.cuda.synchronize()
-    ms_pl = t0.elapsed_time(t1)
-    kv_pl = sum(r.kv_tokens(first_pl + i) for i in range(steps))
+    ms_pl, kv_pl = float("nan"), 0
+    if per_layer:
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        first_pl = r.steps_done + 1
+        t0.record(r.stream)
+        for _ in range(steps):
+            r.step_per_layer()
+        t1.record(r.stream)
+        torch.cuda.synchronize()
+        ms_pl = t0.elapsed_time(t1)
+        kv_pl = sum(r.kv_tokens(first_pl + i) for i in range(steps))
     avg_ms = float(np.mean(part_ms))
     avg_bytes = float(np.mean(part_bytes))
     res = {
@@ -708,7 +717,8 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the GPU's clocks take some ten 2 ms steps to settle after the prefill
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--iters", type=int, default=100, help="timed iterations of each one-layer run")
     ap.add_argument("--workload", type=int, default=3, help="index into workloads.WORKLOADS")
     ap.add_argument("--int4-workload", type=int, default=2, help="-1 to skip")
@@ -717,6 +727,8 @@ def main():
                     help="skip the one-layer runs of the other formats, the paged layout and the 128-head workload")
     ap.add_argument("--no-latency", action="store_true", help="skip the small workloads' per-call latency")
     ap.add_argument("--only", choices=["stack", "layer"], help="profiling runs: only the stack or one layer")
+    ap.add_argument("--no-per-layer", action="store_true", help="(with --only stack) skip the one-layer calls")
+    ap.add_argument("--splits", type=int, help="(with --only stack) the split count instead of the workload's")
     ap.add_argument("--fmt", help="(with --only layer / --pmc-run) another cache format for the workload")
     ap.add_argument("--layers", type=int, help="(with --pmc-run) layers of the workload to use")
     ap.add_argument("--page-size", type=int, default=0, help="(with --only layer / --pmc-run) paged layout")
@@ -751,7 +763,7 @@ def main():
         pmc_run(args.workload, args.fmt, args.layers, args.page_size)
         return
     if args.only == "stack":
-        measure_stack(args.workload, args.steps, args.warmup)
+        measure_stack(args.workload, args.steps, args.warmup, per_layer=not args.no_per_layer, splits=args.splits)
         return
     if args.only == "layer":
         measure_layer(args.workload, args.iters, args.warmup, Flusher(torch), fmt=args.fmt,

@@ -76,6 +76,10 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kMaxSplits = 4096;
 constexpr int kAutoMinTiles = 4;           // fewest 32-token tiles per range of the automatic plan (full sequences)
 constexpr int kWgPerCu = 3;                // resident partial workgroups per CU
+#ifndef MLA_COMBINE_MFMA
+#define MLA_COMBINE_MFMA 1
+#endif
+constexpr bool kCombineMfma = MLA_COMBINE_MFMA;  // merge + W_UV projection on MFMA (combine_kernel)
 constexpr float kLazy = 8.0f;              // log2 of the largest softmax weight before a rescale
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -412,7 +416,7 @@ __global__ __launch_bounds__(128) void append_step_kernel(AppendArgs a) {
 // ------------------------------------------------------------------ absorb
 
 constexpr int kAbsorbBT = 64;              // batch rows per absorb block (four MFMA column blocks)
-constexpr int kAbsorbCB = 64;              // latent channels per absorb block, 16 per wave
+constexpr int kAbsorbCB = 128;             // latent channels per absorb block, 32 per wave
 constexpr int kAbsorbWRow = kAbsorbCB + 16;  // bf16 per LDS row of the staged W_UK tile (see below)
 
 // Per (sequence, head) record of absorbed queries, in fp16, each value v kept
@@ -440,16 +444,17 @@ __device__ __forceinline__ void split_store(_Float16 *hi, _Float16 *lo, float v)
 // q_abs[b,h,c] = qs * sum_d q_nope[b,h,d] W_UK[h,d,c] for c < 512, and
 // qs * q_pe[b,h,d] for the 64 RoPE channels; qs = softmax_scale * log2(e),
 // so the attention kernels work in base 2.
-// Grid (H, 512/64 channel blocks, ceil(B/64)), 256 threads. The block stages
-// its W_UK tile (128 d x 64 c, rows padded to 80 bf16 = 40 dwords so the four
-// rows of a transposed read start 8 banks apart) in LDS once. Wave w owns
-// channels 16w..16w+15 of the block and computes them for the block's batch
-// rows as [16 c x 32 d] x [32 d x 16 b] bf16 MFMAs with fp32 accumulation
-// (bf16 products are exact in fp32). The W_UK operand comes from LDS through
-// transposed reads, 8 consecutive d per lane; the query operand is those same
-// 8 d of one batch row, one 16-byte load.
-// One block of the absorption: head h, channel block cb, batch block bz. With
-// with_pe, the blocks of channel block 0 also write the scaled RoPE part.
+// One block of the absorption: head h, channel block cb (128 channels), batch
+// block bz (64 rows); 256 threads. The block stages its W_UK tile (128 d x
+// 128 c, rows padded to 144 bf16 = 72 dwords, so the four rows of a
+// transposed read start 8 banks apart) in LDS once. Wave w owns channels
+// 32w .. 32w+31 of the block as two 16-channel column blocks (each one latent
+// group) and computes them for the block's batch rows as [16 c x 32 d] x
+// [32 d x 16 b] bf16 MFMAs with fp32 accumulation (bf16 products are exact in
+// fp32). The W_UK operand comes from LDS through transposed reads, 8
+// consecutive d per lane; the query operand is those same 8 d of one batch
+// row, one 16-byte load. With with_pe, the blocks of channel block 0 also
+// write the scaled RoPE part.
 __device__ __forceinline__ void absorb_block(const uint16_t *q_nope, const uint16_t *q_pe,
                                              const uint16_t *w_uk, int B, int H, float qs, _Float16 *qa,
                                              int h, int cb, int bz, bool with_pe) {
@@ -457,14 +462,15 @@ __device__ __forceinline__ void absorb_block(const uint16_t *q_nope, const uint1
   const int b0 = bz * kAbsorbBT;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, g = lane >> 4, i = lane & 15;
+  constexpr int kCPR = kAbsorbCB / 8;  // 16-byte chunks per W_UK tile row
 
-  // W_UK[h][:, 64cb .. 64cb+63]: 128 rows of 128 bytes, 16 bytes per lane
+  // W_UK[h][:, 128cb .. 128cb+127]: 128 rows of 256 bytes, 16 bytes per lane
   const uint16_t *wsrc = w_uk + (int64_t)h * kNope * kLatent + cb * kAbsorbCB;
   constexpr int kWLoads = kNope * kAbsorbCB / 8 / 256;
   u32x4 wl[kWLoads];
 #pragma unroll
   for (int j = 0; j < kWLoads; ++j) {
-    const int k = tid + 256 * j, row = k >> 3, c8 = k & 7;
+    const int k = tid + 256 * j, row = k / kCPR, c8 = k % kCPR;
     wl[j] = *(const u32x4 *)(wsrc + (int64_t)row * kLatent + 8 * c8);
   }
   // every query operand of the block, in flight together with the tile
@@ -492,47 +498,49 @@ __device__ __forceinline__ void absorb_block(const uint16_t *q_nope, const uint1
   }
 #pragma unroll
   for (int j = 0; j < kWLoads; ++j) {
-    const int k = tid + 256 * j, row = k >> 3, c8 = k & 7;
+    const int k = tid + 256 * j, row = k / kCPR, c8 = k % kCPR;
     *(u32x4 *)(wt + row * kAbsorbWRow + 8 * c8) = wl[j];
   }
   __syncthreads();
-  // lane (i, g) of k-step kk: column 16w + i, rows 32kk + 8g .. +7 (two
-  // transposed reads of four rows each)
-  bf16x8 wa[kNope / 32];
 #pragma unroll
-  for (int kk = 0; kk < kNope / 32; ++kk) {
-    const uint16_t *p = wt + (32 * kk + 8 * g + (i >> 2)) * kAbsorbWRow + 16 * w + 4 * (i & 3);
-    const i16x4 r0 = lds_read_tr16_i16(p), r1 = lds_read_tr16_i16(p + 4 * kAbsorbWRow);
-    wa[kk] = bitcast<bf16x8>(i16x8{r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w});
-  }
-
-  const int c = cb * kAbsorbCB + 16 * w + 4 * g;  // this lane's 4 output channels
+  for (int cblk = 0; cblk < 2; ++cblk) {
+    // lane (i, g) of k-step kk: column 32w + 16cblk + i, rows 32kk + 8g .. +7
+    // (two transposed reads of four rows each)
+    bf16x8 wa[kNope / 32];
 #pragma unroll
-  for (int bb = 0; bb < kBB; ++bb) {
-    if (b0 + 16 * bb >= B) break;  // uniform
-    const int b = b0 + 16 * bb + i;
-    f32x4 d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < kNope / 32; ++kk)
-      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[kk], bitcast<bf16x8>(qv[bb][kk]), d, 0, 0, 0);
-    // lane (i, g) holds channels c .. c+3 of batch row b
-    f16x4 vh, vl;
-    float gsum = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float v = d[r] * qs;
-      vh[r] = (_Float16)v;
-      vl[r] = (_Float16)(v - (float)vh[r]);
-      gsum += v;
+    for (int kk = 0; kk < kNope / 32; ++kk) {
+      const uint16_t *p = wt + (32 * kk + 8 * g + (i >> 2)) * kAbsorbWRow + 32 * w + 16 * cblk + 4 * (i & 3);
+      const i16x4 r0 = lds_read_tr16_i16(p), r1 = lds_read_tr16_i16(p + 4 * kAbsorbWRow);
+      wa[kk] = bitcast<bf16x8>(i16x8{r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w});
     }
-    // the wave's 16 channels are one latent group: add the four lane groups
-    gsum += __shfl_xor(gsum, 16);
-    gsum += __shfl_xor(gsum, 32);
-    if (b < B) {
-      _Float16 *rec = qa + ((int64_t)b * H + h) * kQRec;
-      *(f16x4 *)(rec + kQHi + c) = vh;
-      *(f16x4 *)(rec + kQLo + c) = vl;
-      if (g == 0) split_store(rec + kQSumHi + c / 16, rec + kQSumLo + c / 16, gsum);
+    const int c = cb * kAbsorbCB + 32 * w + 16 * cblk + 4 * g;  // this lane's 4 output channels
+#pragma unroll
+    for (int bb = 0; bb < kBB; ++bb) {
+      if (b0 + 16 * bb >= B) break;  // uniform
+      const int b = b0 + 16 * bb + i;
+      f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < kNope / 32; ++kk)
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[kk], bitcast<bf16x8>(qv[bb][kk]), d, 0, 0, 0);
+      // lane (i, g) holds channels c .. c+3 of batch row b
+      f16x4 vh, vl;
+      float gsum = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = d[r] * qs;
+        vh[r] = (_Float16)v;
+        vl[r] = (_Float16)(v - (float)vh[r]);
+        gsum += v;
+      }
+      // the column block's 16 channels are one latent group: add the four lane groups
+      gsum += __shfl_xor(gsum, 16);
+      gsum += __shfl_xor(gsum, 32);
+      if (b < B) {
+        _Float16 *rec = qa + ((int64_t)b * H + h) * kQRec;
+        *(f16x4 *)(rec + kQHi + c) = vh;
+        *(f16x4 *)(rec + kQLo + c) = vl;
+        if (g == 0) split_store(rec + kQSumHi + c / 16, rec + kQSumLo + c / 16, gsum);
+      }
     }
   }
   if (pe) {
@@ -556,7 +564,7 @@ __device__ __forceinline__ void absorb_block(const uint16_t *q_nope, const uint1
   }
 }
 
-// Grid (H, 512/64, layers x nbz): blockIdx.z = l * nbz + bz. Every argument is
+// Grid (H, 512/128, layers x nbz): blockIdx.z = l * nbz + bz. Every argument is
 // layer-stacked: layer l's queries, weights and records follow layer l-1's.
 __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t *q_nope, const uint16_t *q_pe,
                                                      const uint16_t *w_uk, int B, int H, float qs,
@@ -767,10 +775,7 @@ __device__ __forceinline__ f16x4 lds_read_tr16(const _Float16 *p) {
 // channels 32g..32g+31 of the wave's block (two quantization groups); in the
 // accumulators, head i.
 constexpr int kT16 = 32;             // tokens per tile
-#ifndef MLA_NPF16
-#define MLA_NPF16 1
-#endif
-constexpr int kNpf16 = MLA_NPF16;    // tiles of loads in flight per wave
+constexpr int kNpf16 = 1;            // tiles of loads in flight per wave
 // A wave's value block: 32 rows (tokens) of 128 channels, then (INT4) the 8
 // zero-points of the wave's groups in one 16-byte chunk and the wave's group
 // scales, transposed, in the other; rows of 144 fp16 (72 dwords, 8 banks
@@ -1022,8 +1027,8 @@ __device__ __forceinline__ f16x8 cat8(f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
 }
 
 // Dequantize one half-tile row of this lane: hi/lo operands of the 4 latent
-// k-steps (8 channels each) and of the k_pe k-step (4 channels), and the hi
-// values in channel order, stored to the value block row `vrow`.
+// k-steps (8 channels each) and of the k_pe k-step (4 channels), and in vdat
+// the row's value-block data of the 4 k-steps (vstore16 stores it).
 //
 // INT4 operands keep the channel order in which the nibbles come out of a
 // dword, (0,4,1,5,2,6,3,7) within each 8 channels, and the queries are
@@ -1034,8 +1039,8 @@ __device__ __forceinline__ f16x8 cat8(f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
 // as in the other formats.
 template <int FMT>
 __device__ __forceinline__ void dequant16(const Raw16<FMT> &r, const Meta16 &m, int rb, f16x8 (&hi)[4],
-                                          f16x8 (&lo)[4], _Float16 *vrow, int swz, uint32_t magic,
-                                          f16x4 &khi, f16x4 &klo) {
+                                          f16x8 (&lo)[4], f16x8 (&vdat)[4], uint32_t magic, f16x4 &khi,
+                                          f16x4 &klo) {
   if (lat_fmt(FMT) == MLA_FMT_INT8) {
     const f16x2 s0 = splat_f16_bits(m.sc[rb] & 0xFFFFu), s1 = splat_f16_bits(m.sc[rb] >> 16);
 #pragma unroll
@@ -1051,8 +1056,7 @@ __device__ __forceinline__ void dequant16(const Raw16<FMT> &r, const Meta16 &m, 
       scale_split(q3, s2, h3, l3);
       hi[kk] = cat8(h0, h1, h2, h3);
       lo[kk] = cat8(l0, l1, l2, l3);
-      // columns lane_chan - 128 w = 16 g + 64 j + 8 h: vrow is at 16 g
-      *(f16x8 *)(vrow + 64 * (kk >> 1) + 8 * ((kk & 1) ^ swz)) = hi[kk];
+      vdat[kk] = hi[kk];
     }
   } else if (lat_fmt(FMT) == MLA_FMT_INT4) {
     const f16x2 s0 = splat_f16_bits(m.sc[rb] & 0xFFFFu), s1 = splat_f16_bits(m.sc[rb] >> 16);
@@ -1077,10 +1081,8 @@ __device__ __forceinline__ void dequant16(const Raw16<FMT> &r, const Meta16 &m, 
       hi[kk] = cat8(h04, h15, h26, h37);  // channels 0,4,1,5,2,6,3,7
       lo[kk] = cat8(l04, l15, l26, l37);
       // the codes themselves (exact in fp16) go to the value block: the
-      // values take the scale on the softmax side, as an exact hi/lo pair.
-      // Columns 32 g + 8 kk (vrow is at 32 g), same order; re-paired at the
-      // final store.
-      *(f16x8 *)(vrow + 8 * (kk ^ swz)) = cat8(q04, q15, q26, q37);
+      // values take the scale on the softmax side, as an exact hi/lo pair
+      vdat[kk] = cat8(q04, q15, q26, q37);
     }
   } else {
 #pragma unroll
@@ -1089,8 +1091,7 @@ __device__ __forceinline__ void dequant16(const Raw16<FMT> &r, const Meta16 &m, 
       hi[kk] = cat8(bf16x2_to_f16x2(v[0]), bf16x2_to_f16x2(v[1]), bf16x2_to_f16x2(v[2]),
                     bf16x2_to_f16x2(v[3]));
       lo[kk] = f16x8{};
-      // columns 32 kk + 8 g (vrow is at 8 (g ^ swz): the swap of chunk pairs)
-      *(f16x8 *)(vrow + 32 * kk) = hi[kk];
+      vdat[kk] = hi[kk];
     }
   }
   if (kpe_fmt(FMT) != kKpeBf16) {
@@ -1112,6 +1113,38 @@ __device__ __forceinline__ void dequant16(const Raw16<FMT> &r, const Meta16 &m, 
     const f16x2 a = bf16x2_to_f16x2(m.kq[rb].x), b = bf16x2_to_f16x2(m.kq[rb].y);
     khi = f16x4{a.x, a.y, b.x, b.y};
     klo = f16x4{};
+  }
+}
+
+// Store one half-tile row's value-block data (from dequant16) to this wave's
+// value block `vblk`, row 16 rb + i:
+//   INT8: columns lane_chan - 128 w = 16 g + 64 j + 8 h (k-step kk = 2 j + h);
+//   INT4: columns 32 g + 8 kk, the codes in the nibble order; and the
+//         zero-points of the wave's 8 groups in columns 128..135 (chunk 16),
+//         the scales of groups 2g, 2g+1 of token 16 rb + i transposed into the
+//         other chunk of columns 128..143: group n's 32 scales take rows
+//         4n..4n+3, in the token order the value product's B operand holds
+//         (lane group g': tokens 4g'..4g'+3, then 16+4g'..16+4g'+3);
+//   BF16: columns 32 kk + 8 g.
+// Chunk pairs of rows with vswz(row) set are swapped (see kVRow).
+template <int FMT>
+__device__ __forceinline__ void vstore16(_Float16 *vblk, int rb, int g, int i, const f16x8 (&vdat)[4],
+                                         const Meta16 &m) {
+  const int row = 16 * rb + i, swz = vswz(i);
+  _Float16 *vrow = vblk + row * kVRow;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    if (lat_fmt(FMT) == MLA_FMT_INT8) *(f16x8 *)(vrow + 16 * g + 64 * (kk >> 1) + 8 * ((kk & 1) ^ swz)) = vdat[kk];
+    else if (lat_fmt(FMT) == MLA_FMT_INT4) *(f16x8 *)(vrow + 32 * g + 8 * (kk ^ swz)) = vdat[kk];
+    else *(f16x8 *)(vrow + 8 * (g ^ swz) + 32 * kk) = vdat[kk];
+  }
+  if (has_zero(FMT)) {
+    *(uint32_t *)(vrow + 128 + 8 * swz + 2 * g) = m.zp[rb];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int trow = 4 * (2 * g + h2) + (i >> 2);
+      *(uint16_t *)(vblk + trow * kVRow + 136 - 8 * vswz(trow) + 4 * rb + (i & 3)) = (uint16_t)(m.sc[rb] >> (16 * h2));
+    }
   }
 }
 
@@ -1387,28 +1420,9 @@ void split16_kernel(SplitArgs a) {
     for (int rb = 0; rb < 2; ++rb) {
       f16x8 hi[4], lo[4];
       f16x4 khi, klo;
-      // this lane's first value-block column (the stores add per-k-step offsets)
-      const int vcol = lat_fmt(FMT) == MLA_FMT_INT8   ? 16 * g
-                       : lat_fmt(FMT) == MLA_FMT_INT4 ? 32 * g
-                                                      : 8 * (g ^ vswz(i));
-      dequant16<FMT>(raw[p], mt, rb, hi, lo, vblk + (16 * rb + i) * kVRow + vcol, vswz(i), magic, khi, klo);
-      // INT4: the zero-points of the wave's 8 groups go to columns 128..135 of
-      // its value block (chunk 16, swapped with 17 like the others), for the
-      // value-side zero-point product
-      if (kZp) {
-        *(uint32_t *)(vblk + (16 * rb + i) * kVRow + 128 + 8 * vswz(i) + 2 * g) = mt.zp[rb];
-        // The scales of the wave's groups 2g and 2g+1 for token 16 rb + i,
-        // transposed into the other 16-byte chunk of columns 128..143 (which
-        // the zero-points leave free on every row): group n's 32 scales take
-        // rows 4n..4n+3, token order as the value product's B operand holds
-        // them (lane group g': tokens 4g'..4g'+3, then 16+4g'..16+4g'+3).
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int trow = 4 * (2 * g + h2) + (i >> 2);
-          *(uint16_t *)(vblk + trow * kVRow + 136 - 8 * vswz(trow) + 4 * rb + (i & 3)) =
-              (uint16_t)(mt.sc[rb] >> (16 * h2));
-        }
-      }
+      f16x8 vdat[4];
+      dequant16<FMT>(raw[p], mt, rb, hi, lo, vdat, magic, khi, klo);
+      vstore16<FMT>(vblk, rb, g, i, vdat, mt);
       // Every score product is a 16x16x32 MFMA, so each accumulator is fed
       // by one MFMA shape only: on this GPU a 16x16x16 MFMA that takes as its
       // accumulator the result of a 16x16x32 MFMA issued just before it reads
@@ -1734,20 +1748,189 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const float *ws_
   if (bo < B) out[((int64_t)bo * H + h) * kVDim + e] = v;
 }
 
+// ------------------------------------------------------------------ combine
+
+// Merge of the partial records and projection through W_UV. Grid
+// (H, ceil(B / R), layers), 256 threads: the block serves head h and R
+// sequences of one layer (layer l's sequences are l * B .. l * B + B - 1 of
+// the record table and of out, and its W_UV follows layer l-1's). R = 16
+// where the grid is large (few blocks share each W_UV[h], so it is read from
+// the caches fewer times), R = 4 otherwise (more blocks for the record loads).
+//   1. Merge. TPR = 256 / R threads per sequence, each with CPT = 512 / TPR
+//      of the latent channels. The row's records (first record and count from
+//      the partial kernel's table) are weighted by
+//      2^(m_s - M) / sum_s 2^(m_s - M) l_s with M the largest m_s of a record
+//      holding tokens (l_s > 0); records with no tokens get weight zero and
+//      their sums are not read. One pass, NB records at a time with all their
+//      loads issued together, and a running maximum. o_lat goes to LDS as a
+//      bf16 hi/lo pair (hi = bf16(o),
+//      lo = bf16(o - hi)): the pair carries ~16 bits, and W_UV is bf16, so
+//      the products are exact in fp32. An empty sequence gives o_lat = 0.
+//   2. Projection on 16x16x32 bf16 MFMA (rows past R are zero), 128 latent
+//      channels of W_UV[h] at a time staged in LDS and read transposed
+//      (ds_read_b64_tr_b16): wave w computes output columns 32w .. 32w + 31 as
+//      o_hi W + o_lo W.
+constexpr int kCombChunk = 128;           // latent channels of W_UV staged at a time
+constexpr int kCombARow = kLatent + 8;    // bf16 per LDS row of o_lat (hi or lo): 16 B of padding
+constexpr int kCombWRow = kVDim + 16;     // bf16 per LDS row of the staged W_UV chunk (see absorb_block)
+constexpr int kCombBigGrid = 1024;        // blocks of 16 rows from which the 16-row form is used
+template <int R>
+__global__ __launch_bounds__(256) void combine_kernel(const float *ws_m, const float *ws_l, const float *ws_acc,
+                                                      const int32_t *rec_tab, const uint16_t *w_uv, int B, int H,
+                                                      float *out) {
+  constexpr int TPR = 256 / R;           // merge threads per sequence
+  constexpr int CPT = kLatent / TPR;     // channels per merge thread
+  constexpr int NV = CPT / 4;            // 16-byte loads per record and thread
+  constexpr int NB = NV < 8 ? 8 / NV : 1;  // records whose loads are in flight together
+  __shared__ __attribute__((aligned(16))) uint16_t ahi[R * kCombARow];
+  __shared__ __attribute__((aligned(16))) uint16_t alo[R * kCombARow];
+  __shared__ __attribute__((aligned(16))) uint16_t wt[kCombChunk * kCombWRow];
+  const int h = blockIdx.x;
+  const int b0 = blockIdx.y * R;
+  const int64_t layer_seq = (int64_t)blockIdx.z * B;  // the layer's first sequence
+  rec_tab += 2 * layer_seq;
+  out += layer_seq * H * kVDim;
+  w_uv += ((int64_t)blockIdx.z * H + h) * kLatent * kVDim;
+  const int tid = threadIdx.x;
+  const int wv = tid >> 6, lane = tid & 63, g = lane >> 4, i = lane & 15;
+  // W_UV rows ch0 .. ch0 + 127 (256 bytes each): 8 x 16 bytes per thread;
+  // the first chunk is in flight during the merge, each next one during the
+  // previous chunk's products
+  constexpr int kWL = kCombChunk * kVDim / 8 / 256;
+  u32x4 wl[kWL];
+  auto load_w = [&](int ch0) {
+#pragma unroll
+    for (int jj = 0; jj < kWL; ++jj) {
+      const int k = tid + 256 * jj, row = k >> 4, c8 = k & 15;
+      wl[jj] = *(const u32x4 *)(w_uv + (int64_t)(ch0 + row) * kVDim + 8 * c8);
+    }
+  };
+  load_w(0);
+
+  // ---- 1. merge
+  {
+    const int r = tid / TPR, c = tid % TPR;
+    const int b = b0 + r;
+    f32x4 o[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int first = b < B ? rec_tab[2 * b] : 0, count = b < B ? rec_tab[2 * b + 1] : 0;
+    // one pass over the records, NB at a time: their m, l and sums are loaded
+    // together; the running maximum M moves with each batch's maximum and what
+    // was merged before is rescaled by 2^(M_old - M_new)
+    float M = -INFINITY, Ls = 0.0f;
+    for (int s0 = 0; s0 < count; s0 += NB) {
+      f32x4 v[NB][NV];
+      float ms[NB], ls[NB];
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const int s = s0 + k;
+        const int64_t rec = (int64_t)(first + min(s, count - 1)) * H + h;
+        ls[k] = s < count ? ws_l[rec] : 0.0f;
+        ms[k] = ws_m[rec];
+        if (ls[k] > 0.0f) {
+          const f32x4 *src = (const f32x4 *)(ws_acc + rec * kLatent + CPT * c);
+#pragma unroll
+          for (int q = 0; q < NV; ++q) v[k][q] = src[q];
+        }
+      }
+      float mb = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < NB; ++k)
+        if (ls[k] > 0.0f) mb = fmaxf(mb, ms[k]);
+      if (mb == -INFINITY) continue;  // no record of the batch holds tokens (uniform per row)
+      const float mn = fmaxf(M, mb);
+      const float alpha = __builtin_amdgcn_exp2f(M - mn);  // 0 while nothing is merged
+      Ls *= alpha;
+#pragma unroll
+      for (int q = 0; q < NV; ++q) o[q] *= alpha;
+      M = mn;
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        if (ls[k] > 0.0f) {
+          const float wgt = __builtin_amdgcn_exp2f(ms[k] - M);
+          Ls += wgt * ls[k];
+#pragma unroll
+          for (int q = 0; q < NV; ++q) o[q] += wgt * v[k][q];
+        }
+      }
+    }
+    const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+#pragma unroll
+    for (int q = 0; q < NV; ++q) o[q] *= inv;
+    // bf16 hi / lo of the thread's channels, 8 at a time
+#pragma unroll
+    for (int k2 = 0; k2 < NV / 2; ++k2) {
+      u32x4 hv, lv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = o[2 * k2 + e / 2][2 * (e & 1)], x1 = o[2 * k2 + e / 2][2 * (e & 1) + 1];
+        const uint32_t h0 = f32_to_bf16_rne(x0), h1 = f32_to_bf16_rne(x1);
+        const uint32_t l0 = f32_to_bf16_rne(x0 - bf16_bits_to_f32(h0)), l1 = f32_to_bf16_rne(x1 - bf16_bits_to_f32(h1));
+        hv[e] = h0 | (h1 << 16);
+        lv[e] = l0 | (l1 << 16);
+      }
+      *(u32x4 *)(ahi + r * kCombARow + CPT * c + 8 * k2) = hv;
+      *(u32x4 *)(alo + r * kCombARow + CPT * c + 8 * k2) = lv;
+    }
+  }
+
+  // ---- 2. projection
+  f32x4 d[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  for (int ch0 = 0; ch0 < kLatent; ch0 += kCombChunk) {
+    __syncthreads();  // the previous chunk's reads of wt (and, the first time, the merge's stores) are done
+#pragma unroll
+    for (int jj = 0; jj < kWL; ++jj) {
+      const int k = tid + 256 * jj, row = k >> 4, c8 = k & 15;
+      *(u32x4 *)(wt + row * kCombWRow + 8 * c8) = wl[jj];
+    }
+    lds_stores_done();  // the registers of wl are reloaded next
+    if (ch0 + kCombChunk < kLatent) load_w(ch0 + kCombChunk);
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kCombChunk / 32; ++kk) {
+      // A: row i, channels ch0 + 32 kk + 8 g .. +7 (zero past the block's R rows)
+      bf16x8 a_hi = {}, a_lo = {};
+      if (i < R) {
+        a_hi = *(const bf16x8 *)(ahi + i * kCombARow + ch0 + 32 * kk + 8 * g);
+        a_lo = *(const bf16x8 *)(alo + i * kCombARow + ch0 + 32 * kk + 8 * g);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        // B: output column 32 wv + 16 nt + i, channels 32 kk + 8 g .. +7 of the chunk
+        const uint16_t *p = wt + (32 * kk + 8 * g + (i >> 2)) * kCombWRow + 32 * wv + 16 * nt + 4 * (i & 3);
+        const i16x4 r0 = lds_read_tr16_i16(p), r1 = lds_read_tr16_i16(p + 4 * kCombWRow);
+        const bf16x8 bw = bitcast<bf16x8>(i16x8{r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w});
+        d[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi, bw, d[nt], 0, 0, 0);
+        d[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo, bw, d[nt], 0, 0, 0);
+      }
+    }
+  }
+  // lane (g, i) holds rows 4g .. 4g + 3 of column 32 wv + 16 nt + i
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int b = b0 + 4 * g + r;
+      if (4 * g + r < R && b < B) out[((int64_t)b * H + h) * kVDim + 32 * wv + 16 * nt + i] = d[nt][r];
+    }
+}
+
 // -------------------------------------------------------- stream-read probe
 
 // Reads n16 16-byte words with the access pattern of a plain streaming read
 // (grid-stride, consecutive lanes on consecutive words, four loads in flight
-// per thread) and folds them into one word per workgroup, so that no load is
-// dead. A measurement aid for the achievable HBM read rate.
+// per thread, the default cache policy, so the lines are allocated in the
+// caches like any read's) and folds them into one word per workgroup, so
+// that no load is dead. A measurement aid for the achievable HBM read rate.
 __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4 *buf, int64_t n16, uint32_t *sink) {
   const int64_t stride = (int64_t)gridDim.x * 256;
   int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   uint32_t x = 0;
   for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 a = __builtin_nontemporal_load(buf + i), b = __builtin_nontemporal_load(buf + i + stride);
-    const u32x4 c = __builtin_nontemporal_load(buf + i + 2 * stride);
-    const u32x4 d = __builtin_nontemporal_load(buf + i + 3 * stride);
+    const u32x4 a = buf[i], b = buf[i + stride];
+    const u32x4 c = buf[i + 2 * stride];
+    const u32x4 d = buf[i + 3 * stride];
     x ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
   }
   for (; i < n16; i += stride) {
@@ -1955,7 +2138,7 @@ int auto_splits(const mla_cache *c, int heads, int layers, int *out) {
     return MLA_ERR_HIP;
   if (cus < 1) cus = 1;
   // Balanced plan: nsplit * batch ranges of equal work, times heads / 16 head
-  // slices, as many workgroups as are resident at once (three per CU), and at
+  // slices, as many workgroups as are resident at once (kWgPerCu per CU), and at
   // least kAutoMinTiles tiles per range when every sequence is full.
   int64_t ns = (int64_t)kWgPerCu * cus / ((int64_t)c->batch * (heads / 16));
   const int64_t by_len = ((int64_t)c->capacity * layers + kT16 * kAutoMinTiles - 1) / (kT16 * kAutoMinTiles);
@@ -2072,10 +2255,20 @@ int run_combine(const mla_cache *cache, const DecodePlan &pl, const void *w_uv, 
                 void *workspace, float *out, hipStream_t s) {
   const int B = cache->batch;
   uint8_t *ws = (uint8_t *)workspace;
-  hipLaunchKernelGGL(reduce_kernel, dim3(heads, (B + kReduceBT - 1) / kReduceBT, pl.layers), dim3(kReduceThreads),
-                     0, s, (const float *)(ws + pl.wl.m), (const float *)(ws + pl.wl.l),
-                     (const float *)(ws + pl.wl.acc), (const int32_t *)(ws + pl.wl.tab),
-                     (const uint16_t *)w_uv, B, heads, out);
+  const int64_t big = (int64_t)heads * ((B + 15) / 16) * pl.layers;
+  if (kCombineMfma && big >= kCombBigGrid)
+    hipLaunchKernelGGL(combine_kernel<16>, dim3(heads, (B + 15) / 16, pl.layers), dim3(256), 0, s,
+                       (const float *)(ws + pl.wl.m), (const float *)(ws + pl.wl.l), (const float *)(ws + pl.wl.acc),
+                       (const int32_t *)(ws + pl.wl.tab), (const uint16_t *)w_uv, B, heads, out);
+  else if (kCombineMfma)
+    hipLaunchKernelGGL(combine_kernel<4>, dim3(heads, (B + 3) / 4, pl.layers), dim3(256), 0, s,
+                       (const float *)(ws + pl.wl.m), (const float *)(ws + pl.wl.l), (const float *)(ws + pl.wl.acc),
+                       (const int32_t *)(ws + pl.wl.tab), (const uint16_t *)w_uv, B, heads, out);
+  else
+    hipLaunchKernelGGL(reduce_kernel, dim3(heads, (B + kReduceBT - 1) / kReduceBT, pl.layers),
+                       dim3(kReduceThreads), 0, s, (const float *)(ws + pl.wl.m), (const float *)(ws + pl.wl.l),
+                       (const float *)(ws + pl.wl.acc), (const int32_t *)(ws + pl.wl.tab),
+                       (const uint16_t *)w_uv, B, heads, out);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
