@@ -353,6 +353,27 @@ int mla_cache_get(const mla_cache *cache, int32_t layer, float *ckv_out, float *
 int mla_rope_tables(float *cos_out, float *sin_out, int32_t rows, double base, void *hip_stream);
 
 /*
+ * mla_decode_attn without a workspace argument, for callers that cannot
+ * allocate device memory at the call (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation). It allocates nothing:
+ * its workspace is a library-owned device array of MLA_STATIC_SCRATCH_BYTES,
+ * one per GPU, held until the process ends and shared by every call on that
+ * GPU. Calls that overlap on one GPU (on different streams, or from several
+ * threads) race on it and give undefined results; calls in stream order are
+ * fine. Its contents on entry do not matter.
+ *
+ * Arguments, results and errors as mla_decode_attn. MLA_ERR_WORKSPACE when
+ * the workspace this cache, head count and split count need (what
+ * mla_decode_workspace_bytes reports) exceeds MLA_STATIC_SCRATCH_BYTES;
+ * nothing is launched then. num_splits = 0 picks the split count as
+ * mla_decode_attn does.
+ */
+#define MLA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int mla_decode_attn_static(const mla_cache *cache, int32_t layer, const void *q_nope, const void *q_pe,
+                           const void *w_uk, const void *w_uv, int32_t heads, float softmax_scale,
+                           int32_t num_splits, float *out, void *hip_stream);
+
+/*
  * A measurement aid, not part of the decode path: reads `bytes` (a multiple of
  * 16) of device memory at `buf` (16-byte aligned) with a plain streaming
  * access pattern, as one launch of sink_words workgroups of 256 threads, and

@@ -17,6 +17,7 @@ MLA_ERR_UNSUPPORTED = -2
 MLA_ERR_WORKSPACE = -3
 MLA_ERR_CAPACITY = -4
 MLA_ERR_HIP = -5
+STATIC_SCRATCH_BYTES = 64 << 20  # MLA_STATIC_SCRATCH_BYTES of include/mla_kv.h
 
 FORMATS = {"bf16": 0, "int8": 1, "int4": 2, "int8_kbf16": 3, "int4_kint4": 4}
 
@@ -36,6 +37,7 @@ SYMBOLS = (
     "mla_decode_partial_layers",
     "mla_decode_combine_layers",
     "mla_stream_read",
+    "mla_decode_attn_static",
     "mla_decode_step_begin",
     "mla_decode_absorb",
     "mla_decode_partial",
@@ -117,6 +119,8 @@ def lib():
         L.mla_decode_partial_layers.restype = ctypes.c_int
         L.mla_decode_combine_layers.argtypes = [P, i32, vp, i32, i32, vp, sz, vp, vp]
         L.mla_decode_combine_layers.restype = ctypes.c_int
+        L.mla_decode_attn_static.argtypes = [P, i32, vp, vp, vp, vp, i32, ctypes.c_float, i32, vp, vp]
+        L.mla_decode_attn_static.restype = ctypes.c_int
         L.mla_stream_read.argtypes = [vp, sz, vp, i32, vp]
         L.mla_stream_read.restype = ctypes.c_int
         L.mla_decode_step_begin.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, i32, vp, i32, ctypes.c_float, i32,

@@ -33,6 +33,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "mla_kv.h"
@@ -2354,9 +2355,57 @@ int step_layers(const mla_cache *cache, int32_t layer0, int32_t layers, const vo
   return run_combine(cache, pl, w_uv, heads, workspace, out, s);
 }
 
+// ------------------------------------------------ the no-allocation variant
+
+// The workspace of mla_decode_attn_static: a file-scope device array, one
+// copy per GPU the library runs on, kept until the process ends. Host code
+// never passes the array's name to a kernel (in host code it is a stand-in,
+// not a device address): it passes the address hipGetSymbolAddress returns
+// for the current device, looked up once per device.
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+static_assert(kStaticScratchBytes == (size_t)MLA_STATIC_SCRATCH_BYTES, "header and library agree");
+__device__ __attribute__((aligned(256))) uint8_t scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (null on a HIP error).
+void *static_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 // ================================================================== C ABI
+
+extern "C" int mla_decode_attn_static(const mla_cache *cache, int32_t layer, const void *q_nope, const void *q_pe,
+                                      const void *w_uk, const void *w_uv, int32_t heads, float softmax_scale,
+                                      int32_t num_splits, float *out, void *hip_stream) {
+  // every argument first, the size limit before any HIP call
+  int st = check_cache(cache);
+  if (st != MLA_OK) return st;
+  if (layer < 0 || layer >= cache->num_layers) return MLA_ERR_INVALID_ARG;
+  if (!heads_ok(heads)) return MLA_ERR_UNSUPPORTED;
+  if ((st = check_absorb_args(q_nope, q_pe, w_uk, softmax_scale)) != MLA_OK) return st;
+  if ((st = check_combine_args(w_uv, out)) != MLA_OK) return st;
+  if (num_splits < 0 || num_splits > kMaxSplits) return MLA_ERR_INVALID_ARG;
+  int ns = num_splits;
+  if (ns == 0 && (st = auto_splits(cache, heads, 1, &ns)) != MLA_OK) return st;
+  if (ws_layout(cache->batch, 1, heads, ns).total > kStaticScratchBytes) return MLA_ERR_WORKSPACE;
+  void *ws = static_scratch();
+  if (!ws) return MLA_ERR_HIP;
+  return decode_layers(cache, layer, 1, q_nope, q_pe, w_uk, w_uv, heads, softmax_scale, ns, ws,
+                       kStaticScratchBytes, out, (hipStream_t)hip_stream);
+}
 
 extern "C" const char *mla_status_str(int status) {
   switch (status) {

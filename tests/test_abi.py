@@ -232,6 +232,23 @@ def test_size_limits_before_launch():
     assert _decode(wide, heads=128, splits=4096, ws_bytes=ws) == _lib.MLA_ERR_UNSUPPORTED
 
 
+def test_static_decode_validation_and_size_limit_before_any_device_call():
+    # mla_decode_attn_static checks its arguments and the size of the
+    # workspace it would need against its fixed array before it touches a
+    # device (here there is none)
+    L = _lib.lib()
+    s = cache_struct("int8", B=4, cap=4096)
+    big = _ws(s, 128, 2048)[1]
+    assert big > _lib.STATIC_SCRATCH_BYTES
+    call = lambda st, layer=0, heads=128, splits=2048, out=FAKE: L.mla_decode_attn_static(
+        ctypes.byref(st), layer, FAKE, FAKE, FAKE, FAKE, heads, 0.07, splits, out, None)
+    assert call(s) == _lib.MLA_ERR_WORKSPACE
+    assert call(s, layer=2) == _lib.MLA_ERR_INVALID_ARG
+    assert call(s, heads=24) == _lib.MLA_ERR_UNSUPPORTED
+    assert call(s, splits=-1) == _lib.MLA_ERR_INVALID_ARG
+    assert call(s, out=0) == _lib.MLA_ERR_INVALID_ARG
+
+
 def test_rope_tables_argument_validation_before_launch():
     L = _lib.lib()
     assert L.mla_rope_tables(0, FAKE, 10, 10000.0, None) == _lib.MLA_ERR_INVALID_ARG
