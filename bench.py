@@ -85,7 +85,7 @@ class Flusher:
     def __call__(self):
         st = self.torch.cuda.current_stream()
         self.lib.check(self.lib.lib().mla_stream_read(ctypes.c_void_p(self.buf.data_ptr()), FLUSH_BYTES,
-                                                      ctypes.c_void_p(self.sink.data_ptr()), 4096,
+                                                      ctypes.c_void_p(self.sink.data_ptr()), 4096, 0,
                                                       ctypes.c_void_p(st.cuda_stream)), "flush")
 
 
@@ -457,8 +457,9 @@ def measure_latency(wid, iters, flusher):
 
 
 def measure_stream_read(nbytes=4 << 30, iters=20):
-    """Achievable HBM read rate: mla_stream_read over a 4 GiB buffer, for a
-    few grid sizes; the best median."""
+    """Achievable HBM read rate: mla_stream_read (non-temporal loads, as the
+    partial kernel's latent loads) over a 4 GiB buffer, for a few grid sizes;
+    the best median."""
     import torch
     from mla_latent_kv_cache_amd import _lib
     L = _lib.lib()
@@ -475,7 +476,7 @@ def measure_stream_read(nbytes=4 << 30, iters=20):
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             _lib.check(L.mla_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()),
-                                         grid, ctypes.c_void_p(stream.cuda_stream)), "stream_read")
+                                         grid, 1, ctypes.c_void_p(stream.cuda_stream)), "stream_read")
             e1.record(stream)
             if k >= 3:
                 ms.append((e0, e1))
@@ -511,7 +512,9 @@ def roofline(res):
         "bound": "hbm", "achieved": round(res["partial_gb_per_s"], 1), "peak": HBM_PEAK_GBS,
         "unit": "GB/s", "frac": round(res["partial_gb_per_s"] / HBM_PEAK_GBS, 4),
         "traffic": stored_traffic(res["workload"]),
-        "kernel": "split16_kernel (mla_decode_partial%s)" % ("_layers" if res["layers"] > 1 else ""),
+        "kernel": "%s (mla_decode_partial%s)" % (
+            "wide_kernel" if res["heads"] > 16 and not res["fmt"].startswith("int4") else "split16_kernel",
+            "_layers" if res["layers"] > 1 else ""),
         "per_launch_bytes": res["partial_bytes_per_launch"],
         "avg_launch_us": round(res["partial_avg_us"], 2),
         "launches_timed": res["partial_launches"],
@@ -641,7 +644,7 @@ def summarize_stats(name, stats_csv, out_path, cmd):
             kname = r["Name"]
             if "at::" in kname or "rocclr" in kname:
                 continue  # torch kernels building the synthetic inputs, runtime copies
-            m = re.search(r"(\w+_kernel)(?:<(\d)((?:, ?(?:true|false))*)>|I?L?i?(\d)E)?", kname)
+            m = re.search(r"(\w+_kernel)(?:<(\d+)((?:, ?(?:true|false))*)>|I?L?i?(\d+)E)?", kname)
             flags = re.findall(r"true|false", m.group(3) or "") if m else []
             short = (m.group(1) + (f"<{m.group(2) or m.group(4)}>" if (m.group(2) or m.group(4)) else "")
                      + "".join(f" {tag}" for tag, f in zip(("paged", "sliced"), flags) if f == "true")) \
@@ -655,10 +658,13 @@ def summarize_stats(name, stats_csv, out_path, cmd):
         f"#   rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- python3 bench.py {cmd}",
         f"#   python3 bench.py --summarize-stats <dir>/run_kernel_stats.csv --stats-name {name} "
         f"--stats-cmd '{cmd}'",
-        "# Rows: this library's kernels (the torch kernels that build the synthetic inputs and flush the",
-        "# last-level cache are omitted). step_kernel<f>: mla_decode_step_begin[_layers] (store the new",
-        "# tokens with k_pe turned, absorb the turned queries); split16_kernel<f>: the partial attention;",
-        "# reduce_kernel: the merge and W_UV projection; append_kernel<f>: the prefill.",
+        "# Rows: this library's kernels (the torch kernels that build the synthetic inputs are omitted).",
+        "# step_kernel<f>: mla_decode_step_begin[_layers] (store the new tokens with k_pe turned, absorb",
+        "# the turned queries); split16_kernel<f>: the partial attention, 16 heads per workgroup (sliced:",
+        "# one workgroup per 16-head slice); wide_kernel<f>: the partial attention, 32 heads per workgroup;",
+        "# combine_kernel<R>: the merge of the partial records and the W_UV projection, R sequences per",
+        "# workgroup; append_kernel<f>: the prefill; stream_read_kernel: the read of a 1 GiB buffer that",
+        "# evicts the last-level cache between one-layer runs (not part of the decode).",
         "# <f>: 0 bf16, 1 INT8, 2 INT4, 3 INT8 latent + bf16 k_pe, 4 INT4 latent + INT4 k_pe.",
         f"{'kernel':32s}{'calls':>7s}{'avg_us':>11s}{'min_us':>11s}{'max_us':>11s}{'total_ms':>11s}",
     ]
@@ -797,17 +803,24 @@ def main():
             formats[key]["roofline"] = roofline(rf)
         # The wide-head workload (128 heads, INT4, 131072 tokens per sequence, 64 splits): bound by the
         # matrix units, not HBM, so its partial kernel is reported against the fp16 MFMA peak as well.
-        rw = measure_layer(4, max(20, args.iters // 4), args.warmup, flusher)
-        tokens = rw["partial_bytes_per_launch"] / row_bytes(rw["fmt"])
-        flops = tokens * rw["heads"] * 2 * (576 + 512)  # algorithmic score and value work per launch
-        tflops = flops / (rw["partial_avg_us"] / 1e6) / 1e12
-        wide = {k: rw[k] for k in keys if k in rw}
-        wide["unit"] = "KV-tokens/s"
-        wide["roofline"] = {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS,
-                            "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
-                            "flop_per_launch": flops, "avg_launch_us": round(rw["partial_avg_us"], 2),
-                            "kernel": "split16_kernel (mla_decode_partial), 8 head slices"}
-        wide["hbm_roofline"] = roofline(rw)
+        # The same inputs in the INT8 format run the 32-head kernel (wide_int8).
+        for key, fmt, kern in (("wide", None, "split16_kernel (mla_decode_partial), 8 head slices"),
+                               ("wide_int8", "int8", "wide_kernel (mla_decode_partial), 4 slices of 32 heads")):
+            rw = measure_layer(4, max(20, args.iters // 4), args.warmup, flusher, fmt=fmt)
+            tokens = rw["partial_bytes_per_launch"] / row_bytes(rw["fmt"])
+            flops = tokens * rw["heads"] * 2 * (576 + 512)  # algorithmic score and value work per launch
+            tflops = flops / (rw["partial_avg_us"] / 1e6) / 1e12
+            rec = {k: rw[k] for k in keys if k in rw}
+            rec["unit"] = "KV-tokens/s"
+            rec["roofline"] = {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS,
+                               "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                               "flop_per_launch": flops, "avg_launch_us": round(rw["partial_avg_us"], 2),
+                               "kernel": kern}
+            rec["hbm_roofline"] = roofline(rw)
+            if key == "wide":
+                wide = rec
+            else:
+                wide["int8"] = rec
     latency = None
     if not args.no_latency:
         latency = {}

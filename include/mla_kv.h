@@ -378,10 +378,13 @@ int mla_decode_attn_static(const mla_cache *cache, int32_t layer, const void *q_
  * 16) of device memory at `buf` (16-byte aligned) with a plain streaming
  * access pattern, as one launch of sink_words workgroups of 256 threads, and
  * writes one word per workgroup to sink (device uint32 [sink_words]), the XOR
- * of the words it read. Timing it gives the achievable HBM read rate beside
- * the published peak.
+ * of the words it read. nontemporal != 0: the loads carry the non-temporal
+ * hint (the lines are not kept in the caches); 0: the default policy (the
+ * lines are allocated in the caches, which evicts what they held). Timing it
+ * gives the achievable HBM read rate beside the published peak.
  */
-int mla_stream_read(const void *buf, size_t bytes, uint32_t *sink, int32_t sink_words, void *hip_stream);
+int mla_stream_read(const void *buf, size_t bytes, uint32_t *sink, int32_t sink_words, int32_t nontemporal,
+                    void *hip_stream);
 
 /* Static description of a status code. */
 const char *mla_status_str(int status);

@@ -121,7 +121,7 @@ def lib():
         L.mla_decode_combine_layers.restype = ctypes.c_int
         L.mla_decode_attn_static.argtypes = [P, i32, vp, vp, vp, vp, i32, ctypes.c_float, i32, vp, vp]
         L.mla_decode_attn_static.restype = ctypes.c_int
-        L.mla_stream_read.argtypes = [vp, sz, vp, i32, vp]
+        L.mla_stream_read.argtypes = [vp, sz, vp, i32, i32, vp]
         L.mla_stream_read.restype = ctypes.c_int
         L.mla_decode_step_begin.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, i32, vp, i32, ctypes.c_float, i32,
                                             vp, sz, vp]

@@ -1608,6 +1608,284 @@ void split16_kernel(SplitArgs a) {
   }
 }
 
+// ---- 32 heads per workgroup (32, 64 and 128 heads; BF16 and INT8 latents)
+//
+// The 16-head kernel run once per 16-head slice dequantizes every tile once
+// per slice; with many heads its vector work (the dequantization, the score
+// sums and the softmax that each of the four waves repeats) bounds it. This
+// kernel serves a slice of 32 heads per workgroup as two head groups of 16
+// (hg), so each tile is dequantized once for 32 heads and each dequantized
+// operand feeds the score products of both groups; and the softmax of the
+// tile is computed once, not in every wave: wave w takes heads 8w .. 8w+7 of
+// the slice (lane l: head 8w + l/8, tokens l%8 + 8k, k = 0..3), adds the four
+// waves' partial scores, moves each head's lazy reference, and writes the
+// weights (fp16, in the value product's operand order) and each head's
+// rescale factor to LDS, from where every wave takes all 32 heads' weights
+// for its value products. Per tile: dequantize and score (both groups),
+// partial scores to LDS, barrier, softmax of its 8 heads, stage the next
+// tile's small planes, barrier, values (both groups). Two workgroups per CU
+// (the queries and sums of 32 heads take 256 registers per lane). INT4
+// latents are not served here: their exact value product (codes times p s as
+// an fp16 hi/lo pair, per head group) needs more registers than two waves per
+// SIMD allow, and at one wave per SIMD the kernel was slower than the 16-head
+// kernel per slice.
+__device__ __forceinline__ float dpp_xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+}
+__device__ __forceinline__ float dpp_xor2(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+}
+__device__ __forceinline__ float dpp_mirror8(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));  // row_half_mirror
+}
+// max and sum over each group of 8 lanes (8k .. 8k+7)
+__device__ __forceinline__ float max8(float x) {
+  x = fmaxf(x, dpp_xor1(x));
+  x = fmaxf(x, dpp_xor2(x));
+  return fmaxf(x, dpp_mirror8(x));
+}
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp_xor1(x);
+  x += dpp_xor2(x);
+  return x + dpp_mirror8(x);
+}
+
+constexpr int kWideHeads = 32;
+constexpr int kWideWgPerCu = 2;
+constexpr int kPartWide = kWaves * 2 * 2 * 64 * 4;  // floats: [wave][hg][half][lane][4]
+
+// (one workgroup of four waves per SIMD slot: kWideWgPerCu waves per SIMD)
+template <int FMT, bool PAGED>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                          amdgpu_waves_per_eu(kWideWgPerCu, kWideWgPerCu)))
+void wide_kernel(SplitArgs a) {
+  static_assert(!has_zero(FMT), "INT4 latents take the 16-head kernel per slice");
+  constexpr bool kLo = FMT != MLA_FMT_BF16;
+  constexpr int kPol = kSliceLoadPolicy;  // slices of a range read its latent from the caches
+  __shared__ __attribute__((aligned(16))) _Float16 wblk[kWaves * kWBlk];
+  __shared__ __attribute__((aligned(16))) float part[kPartWide];
+  __shared__ __attribute__((aligned(16))) uint8_t aux[Aux16<FMT>::kBytes];
+  __shared__ __attribute__((aligned(16))) _Float16 pw[kWideHeads * kT16];
+  __shared__ float alpha_s[kWideHeads];
+  __shared__ int resc_s[kWaves];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int g = lane >> 4, i = lane & 15;
+  // slices of 32 heads, the slices of a range 8 workgroup indices apart (one XCD)
+  const int nslice = a.H / kWideHeads;
+  const int win = blockIdx.x / (8 * nslice), in_win = blockIdx.x % (8 * nslice);
+  const int hs = in_win / 8, rng = 8 * win + in_win % 8;
+  const PlanStart plan = plan_start(a, a.W, rng, (int *)part);
+  int b = plan.b, S = plan.S, L = plan.L;
+  // the softmax lanes: head hh of the slice, tokens j + 8k
+  const int hh = 8 * w + (lane >> 3), j = lane & 7;
+  _Float16 *vblk = wblk + w * kWBlk;
+  const Off16<FMT> off = offsets16<FMT>(w, lane);
+  const bool zero_b = off.b_zero;
+
+  while (b < a.B) {
+  b = __builtin_amdgcn_readfirstlane(b);
+  S = __builtin_amdgcn_readfirstlane(S);
+  L = __builtin_amdgcn_readfirstlane(L);
+  const int n = tiles_of(L);
+  const int t_begin = __builtin_amdgcn_readfirstlane((max(plan.g0, S) - S) * kT16);
+  const int t_end = __builtin_amdgcn_readfirstlane(min(L, (min(plan.g1, S + n) - S) * kT16));
+  const int64_t ws_row = ((int64_t)rng + b) * a.H + kWideHeads * hs;
+  const int ntiles = (t_end - t_begin + kT16 - 1) / kT16;
+
+  // queries of head 16 hg + i of the slice for this wave's channels
+  f16x8 qh[2][4], ql[2][4], kzh[2], kzl[2];
+#pragma unroll
+  for (int hg = 0; hg < 2; ++hg) {
+    const _Float16 *q = a.qa + ((int64_t)b * a.H + kWideHeads * hs + 16 * hg + i) * kQRec;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      qh[hg][kk] = *(const f16x8 *)(q + kQHi + lane_chan<FMT>(w, g, kk));
+      ql[hg][kk] = *(const f16x8 *)(q + kQLo + lane_chan<FMT>(w, g, kk));
+    }
+    const f16x4 kh = *(const f16x4 *)(q + kQHi + kLatent + 16 * w + 4 * g);
+    const f16x4 kl = *(const f16x4 *)(q + kQLo + kLatent + 16 * w + 4 * g);
+    const _Float16 z0 = (_Float16)0.0f;
+    kzh[hg] = f16x8{kh.x, kh.y, kh.z, kh.w, z0, z0, z0, z0};
+    kzl[hg] = f16x8{kl.x, kl.y, kl.z, kl.w, z0, z0, z0, z0};
+  }
+
+  f32x4 acc[2][8];
+#pragma unroll
+  for (int hg = 0; hg < 2; ++hg)
+#pragma unroll
+    for (int nn = 0; nn < 8; ++nn) acc[hg][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_part = 0.0f;  // head hh (same in its 8 lanes); this lane's share of l
+
+  Raw16<FMT> raw;
+  constexpr bool paged = PAGED;
+  const int pb_row = paged ? b % a.pg.batch : 0;
+  const int64_t pool = paged ? (int64_t)(b / a.pg.batch) * a.pg.layer_rows : 0;
+  const __amdgpu_buffer_rsrc_t trow =
+      make_rsrc(paged ? (const void *)(a.pg.table + (int64_t)pb_row * a.pg.max_pages) : a.kpe,
+                paged ? a.pg.max_pages * 4 : 0);
+  auto page_entry = [&](int r) { return __builtin_amdgcn_raw_buffer_load_b32(trow, (r >> a.pg.shift) * 4, 0, 0); };
+  auto checked = [&](uint32_t entry, int r) {
+    const int pg = (int)__builtin_amdgcn_readfirstlane(entry);
+    return (r < t_end && pg >= 0 && pg < a.pg.num_pages) ? pg : -1;
+  };
+  auto rsrc_of = [&](int r0, int page) {
+    if constexpr (PAGED) return page_rsrc<FMT>(a, pool, page, r0, t_end);
+    else return tile_rsrc<FMT>(a, b, r0, t_end);
+  };
+  {
+    const SplitRsrc rs0 = rsrc_of(t_begin, paged ? checked(page_entry(t_begin), t_begin) : 0);
+    load16_small<FMT>(raw, rs0, off, zero_b);
+    load16_lat<FMT, kPol>(raw, rs0, off, t_end - t_begin, i);
+  }
+  uint32_t next_entry = paged ? page_entry(t_begin + kT16) : 0u;
+  stage16<FMT>(raw, off, aux);
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    // ---- dequantize once, scores of both head groups
+    const Meta16 mt = meta16<FMT>(aux, w, g, i);
+    const int r_next = t_begin + (it + 1) * kT16;
+    const SplitRsrc rs_next = rsrc_of(r_next, paged ? checked(next_entry, r_next) : 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load16_small<FMT>(raw, rs_next, off, zero_b);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 sc[2][2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      f16x8 hi[4], lo[4], vdat[4];
+      f16x4 khi, klo;
+      dequant16<FMT>(raw, mt, rb, hi, lo, vdat, 0u, khi, klo);
+      vstore16<FMT>(vblk, rb, g, i, vdat, mt);
+      const _Float16 z0 = (_Float16)0.0f;
+      const f16x8 akh = {khi.x, khi.y, khi.z, khi.w, z0, z0, z0, z0};
+      const f16x8 akl = {klo.x, klo.y, klo.z, klo.w, z0, z0, z0, z0};
+#pragma unroll
+      for (int hg = 0; hg < 2; ++hg) {
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          s = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi[kk], qh[hg][kk], s, 0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi[kk], ql[hg][kk], s, 0, 0, 0);
+          if (kLo) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo[kk], qh[hg][kk], s, 0, 0, 0);
+        }
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(akh, kzh[hg], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(akh, kzl[hg], s, 0, 0, 0);
+        if (kLo) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(akl, kzh[hg], s, 0, 0, 0);
+        sc[hg][rb] = s;
+      }
+    }
+    // partial scores [wave][hg][half][lane][4]; then the next tile's latent
+    // loads (after the score results were read back: see split16_kernel)
+#pragma unroll
+    for (int hg = 0; hg < 2; ++hg)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) *(f32x4 *)(part + (((w * 2 + hg) * 2 + rb) * 64 + lane) * 4) = sc[hg][rb];
+    __builtin_amdgcn_sched_barrier(0);
+    load16_lat<FMT, kPol>(raw, rs_next, off, t_end - r_next, i);
+    if (paged) next_entry = page_entry(r_next + kT16);
+    __syncthreads();
+
+    // ---- softmax (base 2) of head hh: tokens j + 8k. The partial score of
+    // (token 16 h + 4 g' + r, head 16 hg + c) sits at lane 16 g' + c, slot r
+    // of block (hg, h) of each wave.
+    {
+      const int hg = hh >> 4, c = hh & 15;
+      const int left = t_end - (t_begin + it * kT16);  // uniform
+      float sv[4];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int t = j + 8 * k, h = t >> 4, tt = t & 15;
+        const float *pp = part + ((hg * 2 + h) * 64 + 16 * (tt >> 2) + c) * 4 + (tt & 3);
+        float x = pp[0];
+#pragma unroll
+        for (int v = 1; v < kWaves; ++v) x += pp[v * 2 * 2 * 64 * 4];
+        sv[k] = t < left ? x : -INFINITY;
+        tmax = fmaxf(tmax, sv[k]);
+      }
+      tmax = max8(tmax);
+      float alpha = 1.0f;
+      const bool mv = tmax > m_run + kLazy;  // the lazy reference of split16_kernel
+      if (mv) {
+        const float m_new = fmaxf(m_run, tmax);
+        alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+      }
+      float ps = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int t = j + 8 * k;
+        const float p = __builtin_amdgcn_exp2f(sv[k] - m_run);
+        ps += p;
+        // the value product's B order: head c, lane group g' holds tokens
+        // 4g'..4g'+3 then 16+4g'..16+4g'+3
+        pw[hh * kT16 + 8 * ((t & 15) >> 2) + 4 * (t >> 4) + (t & 3)] = (_Float16)p;
+      }
+      l_part = l_part * alpha + ps;
+      if (j == 0) alpha_s[hh] = alpha;
+      const bool any = __builtin_amdgcn_ballot_w64(mv) != 0;
+      if (lane == 0) resc_s[w] = any;
+    }
+    stage16<FMT>(raw, off, aux);  // the next tile's small planes
+    __syncthreads();
+
+    // ---- values of this wave's 128 channels, both head groups
+    if (resc_s[0] | resc_s[1] | resc_s[2] | resc_s[3]) {  // uniform
+#pragma unroll
+      for (int hg = 0; hg < 2; ++hg) {
+        const float al = alpha_s[16 * hg + i];
+#pragma unroll
+        for (int nn = 0; nn < 8; ++nn) acc[hg][nn] *= al;
+      }
+    }
+    f16x8 pb[2];
+#pragma unroll
+    for (int hg = 0; hg < 2; ++hg) pb[hg] = *(const f16x8 *)(pw + (16 * hg + i) * kT16 + 8 * g);
+    const int sg = vswz(4 * g);
+    const int col = 8 * (((i >> 1) & 1) ^ sg) + 4 * (i & 1);
+    const _Float16 *v0 = vblk + (4 * g + (i >> 2)) * kVRow + col;
+    const _Float16 *v1 = v0 + 16 * kVRow;
+#pragma unroll
+    for (int nn = 0; nn < 8; ++nn) {
+      const f16x4 a0 = lds_read_tr16(v0 + 16 * nn);
+      const f16x4 a1 = lds_read_tr16(v1 + 16 * nn);
+      const f16x8 av = f16x8{a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+      for (int hg = 0; hg < 2; ++hg)
+        acc[hg][nn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb[hg], acc[hg][nn], 0, 0, 0);
+    }
+    // the value block is rewritten by the next tile's dequantization: its
+    // transposed reads above come first (in-order LDS queue; the fence keeps
+    // the compiler from moving the stores above them)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // ---- this unit's partial record
+  const float l_run = sum8(l_part);
+#pragma unroll
+  for (int hg = 0; hg < 2; ++hg) {
+    float *dst = a.ws_acc + (ws_row + 16 * hg + i) * kLatent + 128 * w + 4 * g;
+#pragma unroll
+    for (int nn = 0; nn < 8; ++nn) *(f32x4 *)(dst + 16 * nn) = acc[hg][nn];
+  }
+  if (j == 0) {
+    a.ws_m[ws_row + hh] = m_run;
+    a.ws_l[ws_row + hh] = l_run;
+  }
+  S += n;
+  if (S >= plan.g1) break;
+  do {
+    ++b;
+    L = b < a.B ? clamp_len(a.seq_lens[b], a.cap) : 0;
+  } while (b < a.B && L == 0);
+  __syncthreads();  // the staging area and the softmax state in LDS are reused by the next pass
+  }
+}
+
 // ------------------------------------------------------------------ reduce
 
 constexpr int kReduceBT = 4;  // batch rows per combine block
@@ -1782,7 +2060,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *ws_m, const f
   constexpr int TPR = 256 / R;           // merge threads per sequence
   constexpr int CPT = kLatent / TPR;     // channels per merge thread
   constexpr int NV = CPT / 4;            // 16-byte loads per record and thread
-  constexpr int NB = NV < 8 ? 8 / NV : 1;  // records whose loads are in flight together
+  constexpr int NB = NV < 8 ? 16 / NV : 1;  // records whose loads are in flight together
   __shared__ __attribute__((aligned(16))) uint16_t ahi[R * kCombARow];
   __shared__ __attribute__((aligned(16))) uint16_t alo[R * kCombARow];
   __shared__ __attribute__((aligned(16))) uint16_t wt[kCombChunk * kCombWRow];
@@ -1921,17 +2199,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *ws_m, const f
 
 // Reads n16 16-byte words with the access pattern of a plain streaming read
 // (grid-stride, consecutive lanes on consecutive words, four loads in flight
-// per thread, the default cache policy, so the lines are allocated in the
-// caches like any read's) and folds them into one word per workgroup, so
-// that no load is dead. A measurement aid for the achievable HBM read rate.
+// per thread) and folds them into one word per workgroup, so that no load is
+// dead. NT: non-temporal loads (the lines are not kept in the caches);
+// otherwise the default policy, so the lines are allocated in the caches
+// like any read's. A measurement aid for the achievable HBM read rate.
+template <bool NT>
+__device__ __forceinline__ u32x4 stream_ld(const u32x4 *p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <bool NT>
 __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4 *buf, int64_t n16, uint32_t *sink) {
   const int64_t stride = (int64_t)gridDim.x * 256;
   int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   uint32_t x = 0;
   for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 a = buf[i], b = buf[i + stride];
-    const u32x4 c = buf[i + 2 * stride];
-    const u32x4 d = buf[i + 3 * stride];
+    const u32x4 a = stream_ld<NT>(buf + i), b = stream_ld<NT>(buf + i + stride);
+    const u32x4 c = stream_ld<NT>(buf + i + 2 * stride);
+    const u32x4 d = stream_ld<NT>(buf + i + 3 * stride);
     x ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
   }
   for (; i < n16; i += stride) {
@@ -2132,16 +2417,23 @@ WsLayout ws_layout(int batch, int layers, int H, int nsplit) {
   return w;
 }
 
+// More than 16 heads: the 32-head kernel for the formats without zero-points;
+// INT4 latents run the 16-head kernel per slice (the 32-head kernel's INT4
+// value product needs registers for only one wave per SIMD, and was slower).
+bool use_wide(int fmt, int heads) { return heads > 16 && !has_zero(fmt); }
+
 int auto_splits(const mla_cache *c, int heads, int layers, int *out) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return MLA_ERR_HIP;
   if (cus < 1) cus = 1;
-  // Balanced plan: nsplit * batch ranges of equal work, times heads / 16 head
-  // slices, as many workgroups as are resident at once (kWgPerCu per CU), and at
+  // Balanced plan: nsplit * batch ranges of equal work (times heads / 32 head
+  // slices for more than 16 heads), as many workgroups as are resident at
+  // once (three per CU for 16 heads, two for the 32-head workgroups), and at
   // least kAutoMinTiles tiles per range when every sequence is full.
-  int64_t ns = (int64_t)kWgPerCu * cus / ((int64_t)c->batch * (heads / 16));
+  int64_t ns = use_wide(c->format, heads) ? (int64_t)kWideWgPerCu * cus / ((int64_t)c->batch * (heads / kWideHeads))
+                               : (int64_t)kWgPerCu * cus / ((int64_t)c->batch * (heads / 16));
   const int64_t by_len = ((int64_t)c->capacity * layers + kT16 * kAutoMinTiles - 1) / (kT16 * kAutoMinTiles);
   if (ns > by_len) ns = by_len;
   if (ns < 1) ns = 1;
@@ -2151,14 +2443,25 @@ int auto_splits(const mla_cache *c, int heads, int layers, int *out) {
 }
 
 
+// Head slices of the partial kernel: 16 heads per workgroup (split16_kernel),
+// or 32 for more than 16 heads when the 32-head kernel is built in.
+int head_slices(int fmt, int heads) { return use_wide(fmt, heads) ? heads / kWideHeads : heads / 16; }
+
 template <int FMT>
 hipError_t launch_split_fmt(const SplitArgs &a, dim3 grid, hipStream_t st) {
-  const bool sliced = a.H > 16;
-  if (a.pg.size != 0) {
-    if (sliced) hipLaunchKernelGGL((split16_kernel<FMT, true, true>), grid, dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL((split16_kernel<FMT, true, false>), grid, dim3(kThreads), 0, st, a);
+  const bool paged = a.pg.size != 0;
+  if constexpr (!has_zero(FMT)) {
+    if (use_wide(FMT, a.H)) {
+      if (paged) hipLaunchKernelGGL((wide_kernel<FMT, true>), grid, dim3(kThreads), 0, st, a);
+      else hipLaunchKernelGGL((wide_kernel<FMT, false>), grid, dim3(kThreads), 0, st, a);
+      return hipGetLastError();
+    }
+  }
+  if (a.H > 16) {
+    if (paged) hipLaunchKernelGGL((split16_kernel<FMT, true, true>), grid, dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((split16_kernel<FMT, false, true>), grid, dim3(kThreads), 0, st, a);
   } else {
-    if (sliced) hipLaunchKernelGGL((split16_kernel<FMT, false, true>), grid, dim3(kThreads), 0, st, a);
+    if (paged) hipLaunchKernelGGL((split16_kernel<FMT, true, false>), grid, dim3(kThreads), 0, st, a);
     else hipLaunchKernelGGL((split16_kernel<FMT, false, false>), grid, dim3(kThreads), 0, st, a);
   }
   return hipGetLastError();
@@ -2191,7 +2494,8 @@ int plan_decode(const mla_cache *cache, int layers, int heads, int num_splits, c
   // ranges x head slices, rounded up to whole windows of 8 ranges; the plan
   // counts the tiles of all the call's sequences in 32-bit integers
   const int64_t seqs = (int64_t)cache->batch * layers;
-  if (((int64_t)ns * cache->batch + 7) / 8 * 8 * (heads / 16) > kMaxGrid) return MLA_ERR_UNSUPPORTED;
+  if (((int64_t)ns * cache->batch + 7) / 8 * 8 * head_slices(cache->format, heads) > kMaxGrid)
+    return MLA_ERR_UNSUPPORTED;
   if (seqs * ((cache->capacity + kT16 - 1) / kT16) > kMaxGrid) return MLA_ERR_UNSUPPORTED;
   plan->ns = ns;
   plan->layers = layers;
@@ -2243,10 +2547,10 @@ int run_partial(const mla_cache *cache, const DecodePlan &pl, int layer0, int he
   a.cap = cache->capacity;
   a.pg = paging_of(cache);
   a.rec_tab = (int32_t *)(ws + pl.wl.tab);
-  // the balanced plan's nsplit * batch ranges, each as heads / 16 head slices,
+  // the balanced plan's nsplit * batch ranges, each as head_slices workgroups,
   // rounded up to whole windows of 8 ranges (see split16_kernel)
   a.W = pl.ns * cache->batch;
-  const dim3 grid((unsigned)(((int64_t)a.W + 7) / 8 * 8 * (heads / 16)));
+  const dim3 grid((unsigned)(((int64_t)a.W + 7) / 8 * 8 * head_slices(cache->format, heads)));
   hipError_t e = hipSuccess;
   with_format(cache->format, [&](auto f) { e = launch_split_fmt<decltype(f)::value>(a, grid, s); });
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
@@ -2633,12 +2937,16 @@ extern "C" int mla_decode_combine(const mla_cache *cache, const void *w_uv, int3
 }
 
 extern "C" int mla_stream_read(const void *buf, size_t bytes, uint32_t *sink, int32_t sink_words,
-                               void *hip_stream) {
+                               int32_t nontemporal, void *hip_stream) {
   if (!buf || !sink || !aligned16(buf) || (bytes & 15u) || ((uintptr_t)sink & 3u) || sink_words < 1)
     return MLA_ERR_INVALID_ARG;
   if (bytes == 0) return MLA_OK;
-  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)sink_words), dim3(256), 0, (hipStream_t)hip_stream,
-                     (const u32x4 *)buf, (int64_t)(bytes / 16), sink);
+  if (nontemporal)
+    hipLaunchKernelGGL(stream_read_kernel<true>, dim3((unsigned)sink_words), dim3(256), 0, (hipStream_t)hip_stream,
+                       (const u32x4 *)buf, (int64_t)(bytes / 16), sink);
+  else
+    hipLaunchKernelGGL(stream_read_kernel<false>, dim3((unsigned)sink_words), dim3(256), 0, (hipStream_t)hip_stream,
+                       (const u32x4 *)buf, (int64_t)(bytes / 16), sink);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
