@@ -607,7 +607,7 @@ def _pmc_means(csv_path, counter):
             if row["Counter_Name"] != counter:
                 continue
             name = row["Kernel_Name"]
-            kind = "partial" if "split16_kernel" in name else \
+            kind = "partial" if "split16_kernel" in name or "wide_kernel" in name else \
                 "copy" if "copyBuffer" in name or "copy" in name.lower() else None
             if kind is None:
                 continue

@@ -2032,9 +2032,13 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const float *ws_
 // Merge of the partial records and projection through W_UV. Grid
 // (H, ceil(B / R), layers), 256 threads: the block serves head h and R
 // sequences of one layer (layer l's sequences are l * B .. l * B + B - 1 of
-// the record table and of out, and its W_UV follows layer l-1's). R = 16
-// where the grid is large (few blocks share each W_UV[h], so it is read from
-// the caches fewer times), R = 4 otherwise (more blocks for the record loads).
+// the record table and of out, and its W_UV follows layer l-1's). Launched
+// with R = 16 where the grid is large (a layer-range call: few blocks share
+// each W_UV[h], so it is read from the caches fewer times); smaller grids take
+// reduce_kernel, whose two waves per sequence keep more record loads in
+// flight (measured: 5-9 µs against 6-13 µs for one layer of 1 to 64
+// sequences, 49 against 62 µs at 128 heads; 36 µs for both forms over 27
+// layers of 64 sequences, where reduce_kernel alone took 89 µs).
 //   1. Merge. TPR = 256 / R threads per sequence, each with CPT = 512 / TPR
 //      of the latent channels. The row's records (first record and count from
 //      the partial kernel's table) are weighted by
@@ -2563,10 +2567,6 @@ int run_combine(const mla_cache *cache, const DecodePlan &pl, const void *w_uv, 
   const int64_t big = (int64_t)heads * ((B + 15) / 16) * pl.layers;
   if (kCombineMfma && big >= kCombBigGrid)
     hipLaunchKernelGGL(combine_kernel<16>, dim3(heads, (B + 15) / 16, pl.layers), dim3(256), 0, s,
-                       (const float *)(ws + pl.wl.m), (const float *)(ws + pl.wl.l), (const float *)(ws + pl.wl.acc),
-                       (const int32_t *)(ws + pl.wl.tab), (const uint16_t *)w_uv, B, heads, out);
-  else if (kCombineMfma)
-    hipLaunchKernelGGL(combine_kernel<4>, dim3(heads, (B + 3) / 4, pl.layers), dim3(256), 0, s,
                        (const float *)(ws + pl.wl.m), (const float *)(ws + pl.wl.l), (const float *)(ws + pl.wl.acc),
                        (const int32_t *)(ws + pl.wl.tab), (const uint16_t *)w_uv, B, heads, out);
   else
