@@ -109,11 +109,12 @@ def random_problem(fmt, B, H, lens, seed, cap=None, device="cuda"):
     return cache, rows, q_nope, q_pe, w_uk, w_uv
 
 
-def build_workload(wid, device="cuda"):
-    """Prefill the cache of a named workload through mla_cache_append."""
+def build_workload(wid, device="cuda", fmt=None):
+    """Prefill the cache of a named workload through mla_cache_append (fmt:
+    the same inputs stored in another cache format)."""
     w = W.WORKLOADS[wid]
     lens = W.lengths(wid)
-    cache = LatentCache(w.fmt, w.layers, w.batch, W.capacity(wid), device=device)
+    cache = LatentCache(fmt or w.fmt, w.layers, w.batch, W.capacity(wid), device=device)
     ragged = isinstance(w.seq, tuple)
     for layer in range(w.layers):
         ckv, kpe = W.latent_batch(wid, layer, int(lens.max()), device=device,

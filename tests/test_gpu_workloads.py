@@ -20,10 +20,11 @@ def rows_of(wid, layer, b, n):
     return W.latent_rows(wid, layer, b, n, device="cuda")
 
 
-def check_sequences(wid, cache, layer, samples, out, q_nope, q_pe, w_uk, w_uv, extra=None):
+def check_sequences(wid, cache, layer, samples, out, q_nope, q_pe, w_uk, w_uv, extra=None, fmt=None):
     """Every sampled sequence's output against the fp64 oracle, one by one
     (the oracle work runs on a host thread pool)."""
     w = W.WORKLOADS[wid]
+    fmt = fmt or w.fmt
     lens = cache.lengths(layer)
     qn, qp, wk, wv = f32(q_nope), f32(q_pe), f32(w_uk), f32(w_uv)
     out_h = f32(out)
@@ -35,7 +36,7 @@ def check_sequences(wid, cache, layer, samples, out, q_nope, q_pe, w_uk, w_uv, e
                 c = torch.cat([c, extra[0][b]])
                 k = torch.cat([k, extra[1][b]])
             assert c.shape[0] == lens[b]
-            yield b, oracle_decode_np, (f32(c), f32(k), w.fmt, qn[b], qp[b], wk, wv)
+            yield b, oracle_decode_np, (f32(c), f32(k), fmt, qn[b], qp[b], wk, wv)
 
     worst = 0.0
     for b, ref in run_oracle_jobs(jobs()):
@@ -138,6 +139,20 @@ def test_workload4_int4_wide_heads_64_splits_full():
     torch.cuda.synchronize()
     assert torch.isfinite(out).all()
     check_sequences(wid, cache, 0, range(w.batch), out, qn, qp, wuk, wuv)
+
+
+def test_workload4_inputs_int8_32_head_kernel_full():
+    """The 128-head inputs stored as INT8 (the layer the benchmark times on the
+    32-head kernel), 64 splits: every sequence against the oracle."""
+    wid = 4
+    w = W.WORKLOADS[wid]
+    cache, lens = build_workload(wid, fmt="int8")
+    qn, qp = W.queries(wid, 0, "cuda")
+    wuk, wuv = W.weights(wid, 0, "cuda")
+    out = cache.decode(0, qn, qp, wuk, wuv, W.SOFTMAX_SCALE, num_splits=w.num_splits)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    check_sequences(wid, cache, 0, range(w.batch), out, qn, qp, wuk, wuv, fmt="int8")
 
 
 def test_workload3_int8_one_layer_paged64():
