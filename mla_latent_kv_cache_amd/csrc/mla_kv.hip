@@ -1752,6 +1752,7 @@ void wide_kernel(SplitArgs a) {
     load16_small<FMT>(raw, rs_next, off, zero_b);
     __builtin_amdgcn_sched_barrier(0);
     f32x4 sc[2][2];
+    __builtin_amdgcn_s_setprio(2);  // as in split16_kernel
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       f16x8 hi[4], lo[4], vdat[4];
@@ -1776,6 +1777,7 @@ void wide_kernel(SplitArgs a) {
         sc[hg][rb] = s;
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     // partial scores [wave][hg][half][lane][4]; then the next tile's latent
     // loads (after the score results were read back: see split16_kernel)
 #pragma unroll
@@ -1840,6 +1842,7 @@ void wide_kernel(SplitArgs a) {
         for (int nn = 0; nn < 8; ++nn) acc[hg][nn] *= al;
       }
     }
+    __builtin_amdgcn_s_setprio(2);
     f16x8 pb[2];
 #pragma unroll
     for (int hg = 0; hg < 2; ++hg) pb[hg] = *(const f16x8 *)(pw + (16 * hg + i) * kT16 + 8 * g);
@@ -1856,6 +1859,7 @@ void wide_kernel(SplitArgs a) {
       for (int hg = 0; hg < 2; ++hg)
         acc[hg][nn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb[hg], acc[hg][nn], 0, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
     // the value block is rewritten by the next tile's dequantization: its
     // transposed reads above come first (in-order LDS queue; the fence keeps
     // the compiler from moving the stores above them)
