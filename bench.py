@@ -493,6 +493,34 @@ def measure_stream_read(nbytes=4 << 30, iters=20):
             "workgroups": best[1], "by_workgroups": rows, "kernel": "stream_read_kernel (mla_stream_read)"}
 
 
+def measure_mfma_rate(iters=4000, reps=5):
+    """Achievable fp16 matrix-unit rate: mla_mfma_rate with four waves per
+    SIMD (4 workgroups of 256 threads per CU); the best of a few launches."""
+    import torch
+    from mla_latent_kv_cache_amd import _lib
+    L = _lib.lib()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wgs = 4 * cus
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    best = 0.0
+    for k in range(reps + 2):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        _lib.check(L.mla_mfma_rate(ctypes.c_void_p(sink.data_ptr()), wgs, iters, ctypes.c_void_p(stream.cuda_stream)),
+                   "mfma_rate")
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if k >= 2:
+            flops = wgs * 4 * iters * 8 * 16 * 16 * 32 * 2
+            best = max(best, flops / (e0.elapsed_time(e1) / 1e3) / 1e12)
+    log(f"matrix units: {best:.0f} TFLOP/s of 16x16x32 fp16 products ({best / MFMA_F16_PEAK_TFLOPS:.3f} of the "
+        f"{MFMA_F16_PEAK_TFLOPS:.0f} TFLOP/s peak)")
+    return {"tflop_per_s": round(best, 1), "frac_of_peak": round(best / MFMA_F16_PEAK_TFLOPS, 4),
+            "workgroups": wgs, "kernel": "mfma_rate_kernel (mla_mfma_rate), 8 independent chains per wave"}
+
+
 def stored_traffic(name):
     """Counter-measured HBM bytes per partial launch, from profiles/, if the
     kernel source is unchanged since the counters were taken."""
@@ -777,6 +805,7 @@ def main():
         return
 
     ceiling = measure_stream_read()
+    mfma_ceiling = measure_mfma_rate()
     main_res = measure_stack(args.workload, args.steps, args.warmup)
     flusher = Flusher(torch)
     keys = ("workload", "value", "ms_per_step", "ms_per_step_spread", "gb_per_s", "hbm_frac", "kv_tokens_per_step",
@@ -814,6 +843,7 @@ def main():
             rec["unit"] = "KV-tokens/s"
             rec["roofline"] = {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS,
                                "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                               "frac_of_measured_mfma_rate": round(tflops / mfma_ceiling["tflop_per_s"], 4),
                                "flop_per_launch": flops, "avg_launch_us": round(rw["partial_avg_us"], 2),
                                "kernel": kern}
             rec["hbm_roofline"] = roofline(rw)
@@ -860,6 +890,7 @@ def main():
         "per_layer_calls": main_res["per_layer_calls"],
         "roofline": roofline(main_res),
         "hbm_ceiling": ceiling,
+        "mfma_ceiling": mfma_ceiling,
         "cpu_baseline": cpu,
         "int4": int4,
         "formats": formats,

@@ -386,6 +386,17 @@ int mla_decode_attn_static(const mla_cache *cache, int32_t layer, const void *q_
 int mla_stream_read(const void *buf, size_t bytes, uint32_t *sink, int32_t sink_words, int32_t nontemporal,
                     void *hip_stream);
 
+/*
+ * A measurement aid, not part of the decode path: one launch of `workgroups`
+ * workgroups of 256 threads, each wave issuing iters x 8 independent 16x16x32
+ * fp16 matrix products (16384 flop each) in 8 accumulator chains; sink
+ * (device float [workgroups * 256]) receives each lane's sum of its
+ * accumulators. Timing it gives the achievable matrix-unit rate beside the
+ * published dense fp16 peak. MLA_ERR_INVALID_ARG for a null or misaligned sink,
+ * workgroups < 1 or iters < 0.
+ */
+int mla_mfma_rate(float *sink, int32_t workgroups, int32_t iters, void *hip_stream);
+
 /* Static description of a status code. */
 const char *mla_status_str(int status);
 

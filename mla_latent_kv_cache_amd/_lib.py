@@ -37,6 +37,7 @@ SYMBOLS = (
     "mla_decode_partial_layers",
     "mla_decode_combine_layers",
     "mla_stream_read",
+    "mla_mfma_rate",
     "mla_decode_attn_static",
     "mla_decode_step_begin",
     "mla_decode_absorb",
@@ -123,6 +124,8 @@ def lib():
         L.mla_decode_attn_static.restype = ctypes.c_int
         L.mla_stream_read.argtypes = [vp, sz, vp, i32, i32, vp]
         L.mla_stream_read.restype = ctypes.c_int
+        L.mla_mfma_rate.argtypes = [vp, i32, i32, vp]
+        L.mla_mfma_rate.restype = ctypes.c_int
         L.mla_decode_step_begin.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, i32, vp, i32, ctypes.c_float, i32,
                                             vp, sz, vp]
         L.mla_decode_step_begin.restype = ctypes.c_int

@@ -259,6 +259,18 @@ def test_rope_tables_argument_validation_before_launch():
     assert L.mla_rope_tables(FAKE, FAKE, 0, 10000.0, None) == _lib.MLA_OK  # nothing to launch
 
 
+def test_measurement_aids_validate_before_launch():
+    L = _lib.lib()
+    assert L.mla_stream_read(0, 1 << 20, FAKE, 16, 1, None) == _lib.MLA_ERR_INVALID_ARG
+    assert L.mla_stream_read(FAKE, 1000, FAKE, 16, 1, None) == _lib.MLA_ERR_INVALID_ARG  # not a multiple of 16
+    assert L.mla_stream_read(FAKE, 1 << 20, FAKE, 0, 0, None) == _lib.MLA_ERR_INVALID_ARG
+    assert L.mla_stream_read(FAKE, 0, FAKE, 16, 0, None) == _lib.MLA_OK  # nothing to read
+    assert L.mla_mfma_rate(0, 16, 10, None) == _lib.MLA_ERR_INVALID_ARG
+    assert L.mla_mfma_rate(FAKE + 2, 16, 10, None) == _lib.MLA_ERR_INVALID_ARG
+    assert L.mla_mfma_rate(FAKE, 0, 10, None) == _lib.MLA_ERR_INVALID_ARG
+    assert L.mla_mfma_rate(FAKE, 16, -1, None) == _lib.MLA_ERR_INVALID_ARG
+
+
 def test_python_binding_has_no_fallback(monkeypatch, tmp_path):
     # With the library missing the binding raises instead of computing anything.
     monkeypatch.setattr(_lib, "_lib", None)
