@@ -20,8 +20,10 @@ pytestmark = pytest.mark.gpu
 TAU = 1.0 / np.sqrt(192.0)
 
 
-def stacked_problem(fmt, L, B, H, lens, seed, cap, page_size=0, table=None):
-    """lens [L][B]; returns (cache, rows[l][b], q_nope [L,B,H,128], q_pe, w_uk [L,...], w_uv)."""
+def stacked_problem(fmt, L, B, H, lens, seed, cap, page_size=0, table=None, dist=None):
+    """lens [L][B]; returns (cache, rows[l][b], q_nope [L,B,H,128], q_pe, w_uk [L,...], w_uv).
+    dist: the latent distribution (default: skewed for INT4 latents, outlier
+    channels otherwise)."""
     kw = {}
     if page_size:
         kw = dict(page_size=page_size, num_pages=table.numel() + 3, block_table=table)
@@ -33,7 +35,7 @@ def stacked_problem(fmt, L, B, H, lens, seed, cap, page_size=0, table=None):
         kpe = torch.zeros((B, n, 64), dtype=torch.bfloat16, device="cuda")
         rl = []
         for b in range(B):
-            c, k = random_rows(n, seed * 1009 + l * 101 + b, "skew" if fmt.startswith("int4") else "outlier")
+            c, k = random_rows(n, seed * 1009 + l * 101 + b, dist or ("skew" if fmt.startswith("int4") else "outlier"))
             ckv[b], kpe[b] = c, k
             rl.append((c[:lens[l][b]], k[:lens[l][b]]))
         cache.append(l, ckv, kpe, n_new=lens[l])
@@ -78,6 +80,39 @@ def test_decode_layers_against_oracle(fmt, heads):
                                    num_splits=3)
         torch.cuda.synchronize()
         assert torch.equal(one, many[0])
+
+
+@pytest.mark.parametrize("fmt,heads,L,B", [("int8", 128, 4, 20), ("int4", 16, 22, 36), ("bf16", 64, 8, 17)])
+def test_sixteen_sequence_combine_against_oracle(fmt, heads, L, B):
+    """Layer ranges large enough for the merge that serves 16 sequences per
+    block (heads x ceil(B / 16) x layers >= 1024 blocks), with B not a multiple
+    of 16 (rows past the batch in the last block) and empty sequences. The
+    latents carry no outlier channels: with them, short INT8 sequences reach
+    the limit of the fp16 value operand (one element of 1.3 M at 1.15x the
+    tolerance here, from the partial kernel, the same through either merge),
+    which test_gpu_decode's short-sequence test covers at its own sizes."""
+    assert heads * ((B + 15) // 16) * L >= 1024
+    cap = 64
+    rng = np.random.default_rng(B + L)
+    lens = rng.integers(0, cap + 1, size=(L, B)).tolist()
+    lens[0][B - 1] = 0
+    lens[L - 1] = [0] * (B // 2) + lens[L - 1][B // 2:]
+    cache, rows, qn, qp, wuk, wuv = stacked_problem(fmt, L, B, heads, lens, seed=31 + heads, cap=cap, dist="normal")
+    out = cache.decode_layers(0, qn, qp, wuk, wuv, TAU, num_splits=2)
+    torch.cuda.synchronize()
+    qn_h, qp_h, wk_h, wv_h = f32(qn), f32(qp), f32(wuk), f32(wuv)
+    out_h = f32(out)
+
+    def jobs():
+        for l in range(L):
+            for b in range(B):
+                c, k = rows[l][b]
+                yield (l, b), oracle_decode_np, (f32(c), f32(k), fmt, qn_h[l, b], qp_h[l, b], wk_h[l], wv_h[l], TAU)
+
+    for (l, b), ref in run_oracle_jobs(jobs()):
+        assert_close(out_h[l, b], ref, f"{fmt} H{heads} layer {l} seq {b} (len {lens[l][b]})")
+        if lens[l][b] == 0:
+            assert not out_h[l, b].any()
 
 
 @pytest.mark.parametrize("fmt,heads", [("int8", 16), ("int4", 32), ("int4_kint4", 128)])
