@@ -785,8 +785,8 @@ def main():
                       args.summarize_pmc[1], os.path.join(ROOT, "profiles", f"pmc_partial_{name}.txt"))
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: the decode path here is single-GPU "
-              "(see DESIGN.md for how it would shard). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the decode path here runs on a single GPU. "
+              "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():

@@ -45,7 +45,7 @@ extern "C" {
 typedef enum {
   MLA_OK = 0,
   MLA_ERR_INVALID_ARG = -1, /* null pointer, bad size, layer out of range, misalignment */
-  MLA_ERR_UNSUPPORTED = -2, /* a dimension or head count this build does not handle */
+  MLA_ERR_UNSUPPORTED = -2, /* a dimension, head count or size the library does not handle */
   MLA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
   MLA_ERR_CAPACITY = -4,    /* (Python binding) an append would exceed capacity */
   MLA_ERR_HIP = -5          /* a HIP launch or runtime call failed */
