@@ -23,7 +23,9 @@
  * Conventions for every call:
  *   - Every pointer argument except `cache` and the status string is a DEVICE
  *     pointer, allocated and owned by the caller. The library allocates no
- *     memory and keeps no state between calls; calls are reentrant.
+ *     memory and keeps no state between calls; calls are reentrant. The one
+ *     exception is mla_decode_attn_static (below), whose workspace is a
+ *     device array of the library's own, one per GPU, shared by its calls.
  *   - `hip_stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Work is enqueued asynchronously on it; no call synchronizes the host.
  *   - Arguments are checked on the host before anything is enqueued; a
