@@ -127,7 +127,9 @@ typedef struct mla_cache {
    * block_table[b][p / page_size] in every layer.
    * page_size: a power of two >= 32 dividing capacity; num_pages >= 1;
    * block_table: device int32 [batch][capacity / page_size]. A page index
-   * outside [0, num_pages) reads as an empty page and is never written.
+   * outside [0, num_pages) is never written, and the decode reads its tokens
+   * as all-zero rows (they still count as tokens: score 0, value 0), so every
+   * entry below a sequence's length should name a page of the pool.
    * page_size = 0 (and block_table = NULL): the contiguous planes above. */
   int32_t page_size;
   int32_t num_pages;

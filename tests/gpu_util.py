@@ -153,3 +153,32 @@ def oracle_decode_np(ckv, kpe, fmt, q_nope, q_pe, w_uk, w_uv, scale=W.SOFTMAX_SC
     """oracle_decode on host float32 arrays (thread-pool friendly: no torch)."""
     ch, kh = Q.dequantize_rows(Q.quantize_rows(ckv, kpe, fmt), fmt)
     return A.decode_absorbed(q_nope, q_pe, w_uk, w_uv, ch, kh, scale)
+
+
+def stacked_problem(fmt, L, B, H, lens, seed, cap, page_size=0, table=None, dist=None):
+    """lens [L][B]; returns (cache, rows[l][b], q_nope [L,B,H,128], q_pe, w_uk [L,...], w_uv).
+    dist: the latent distribution (default: skewed for INT4 latents, outlier
+    channels otherwise)."""
+    kw = {}
+    if page_size:
+        kw = dict(page_size=page_size, num_pages=table.numel() + 3, block_table=table)
+    cache = LatentCache(fmt, L, B, cap, device="cuda", **kw)
+    rows = []
+    n = max(1, max(max(r) for r in lens))
+    for l in range(L):
+        ckv = torch.zeros((B, n, 512), dtype=torch.bfloat16, device="cuda")
+        kpe = torch.zeros((B, n, 64), dtype=torch.bfloat16, device="cuda")
+        rl = []
+        for b in range(B):
+            c, k = random_rows(n, seed * 1009 + l * 101 + b, dist or ("skew" if fmt.startswith("int4") else "outlier"))
+            ckv[b], kpe[b] = c, k
+            rl.append((c[:lens[l][b]], k[:lens[l][b]]))
+        cache.append(l, ckv, kpe, n_new=lens[l])
+        rows.append(rl)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    qn = torch.randn((L, B, H, 128), generator=g, device="cuda").to(torch.bfloat16)
+    qp = torch.randn((L, B, H, 64), generator=g, device="cuda").to(torch.bfloat16)
+    wuk = (torch.randn((L, H, 128, 512), generator=g, device="cuda") / 512 ** 0.5).to(torch.bfloat16)
+    wuv = (torch.randn((L, H, 512, 128), generator=g, device="cuda") / 512 ** 0.5).to(torch.bfloat16)
+    return cache, rows, qn, qp, wuk, wuv

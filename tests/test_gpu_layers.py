@@ -14,39 +14,10 @@ from oracle import quant as Q
 from oracle import rope as R
 
 from gpu_util import (assert_close, assert_planes_equal, f32, oracle_decode, oracle_decode_np, oracle_planes,
-                      random_rows, run_oracle_jobs)
+                      random_rows, run_oracle_jobs, stacked_problem)
 
 pytestmark = pytest.mark.gpu
 TAU = 1.0 / np.sqrt(192.0)
-
-
-def stacked_problem(fmt, L, B, H, lens, seed, cap, page_size=0, table=None, dist=None):
-    """lens [L][B]; returns (cache, rows[l][b], q_nope [L,B,H,128], q_pe, w_uk [L,...], w_uv).
-    dist: the latent distribution (default: skewed for INT4 latents, outlier
-    channels otherwise)."""
-    kw = {}
-    if page_size:
-        kw = dict(page_size=page_size, num_pages=table.numel() + 3, block_table=table)
-    cache = LatentCache(fmt, L, B, cap, device="cuda", **kw)
-    rows = []
-    n = max(1, max(max(r) for r in lens))
-    for l in range(L):
-        ckv = torch.zeros((B, n, 512), dtype=torch.bfloat16, device="cuda")
-        kpe = torch.zeros((B, n, 64), dtype=torch.bfloat16, device="cuda")
-        rl = []
-        for b in range(B):
-            c, k = random_rows(n, seed * 1009 + l * 101 + b, dist or ("skew" if fmt.startswith("int4") else "outlier"))
-            ckv[b], kpe[b] = c, k
-            rl.append((c[:lens[l][b]], k[:lens[l][b]]))
-        cache.append(l, ckv, kpe, n_new=lens[l])
-        rows.append(rl)
-    g = torch.Generator(device="cuda")
-    g.manual_seed(seed)
-    qn = torch.randn((L, B, H, 128), generator=g, device="cuda").to(torch.bfloat16)
-    qp = torch.randn((L, B, H, 64), generator=g, device="cuda").to(torch.bfloat16)
-    wuk = (torch.randn((L, H, 128, 512), generator=g, device="cuda") / 512 ** 0.5).to(torch.bfloat16)
-    wuv = (torch.randn((L, H, 512, 128), generator=g, device="cuda") / 512 ** 0.5).to(torch.bfloat16)
-    return cache, rows, qn, qp, wuk, wuv
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "int8", "int4", "int8_kbf16", "int4_kint4"])

@@ -152,3 +152,26 @@ def test_table_entries_past_the_length_are_never_used():
     o2 = odd.decode(0, qn, qp, wuk, wuv, TAU, num_splits=2)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("fmt", ["int8", "int4", "bf16"])
+def test_out_of_pool_page_reads_as_zero_rows(fmt):
+    """A page index outside the pool below a sequence's length: its rows are
+    never written, and the decode reads them as all-zero rows (score 0, value
+    0): the output equals the oracle's over the sequence with those rows zero."""
+    lens, cap, ps, H = [150, 200], 256, 64, 16
+    B = 2
+    table = torch.tensor([[3, 7, 0, 4], [5, 8, 6, 2]], dtype=torch.int32)  # page 8 is outside a pool of 8
+    cache = LatentCache(fmt, 1, B, cap, page_size=ps, num_pages=8, block_table=table)
+    rows = fill(cache, lens, 41, fmt)
+    qn, qp, wuk, wuv = queries(B, H, 42)
+    out = cache.decode(0, qn, qp, wuk, wuv, TAU, num_splits=3)
+    torch.cuda.synchronize()
+    for b in range(B):
+        c, k = rows[b]
+        if b == 1:  # tokens 64..127 sit on the out-of-pool page
+            c, k = c.clone(), k.clone()
+            c[64:128] = 0
+            k[64:128] = 0
+        ref = oracle_decode(c, k, fmt, qn[b], qp[b], wuk, wuv, TAU)
+        assert_close(f32(out[b]), ref, f"{fmt} seq {b}")
