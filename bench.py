@@ -18,10 +18,14 @@ the paged layout and the 128-head workload under "formats" and "wide_heads";
 the two small workloads (bf16 B1 S256, INT8 B8 S4096 with its 64-token
 append) as microseconds per decode call under "latency".
 
-One-layer runs: each timed iteration writes a 1 GiB scratch buffer (outside
-the timed events) so that the 256 MB last-level cache holds none of the
-layer, and resets the sequence lengths, so every iteration attends exactly the
-named length plus the step's own token.
+One-layer runs: before each timed iteration (outside the timed events) a
+1 GiB buffer is read through the library's stream-read aid, so that the
+256 MB last-level cache holds none of the layer (a read, so no dirty lines
+are written back inside the timed launch), and the sequence lengths are
+reset, so every iteration attends exactly the named length plus the step's
+own token. The same run measures the achievable HBM read rate
+("hbm_ceiling") and matrix-unit rate ("mfma_ceiling") with the library's
+measurement aids, and times the oracle on the host cores ("cpu_baseline").
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
