@@ -1046,7 +1046,7 @@ __device__ __forceinline__ f16x8 cat8(f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
 // as in the other formats.
 template <int FMT>
 __device__ __forceinline__ void dequant16(const Raw16<FMT> &r, const Meta16 &m, int rb, f16x8 (&hi)[4],
-                                          f16x8 (&lo)[4], f16x8 (&vdat)[4], uint32_t magic, f16x4 &khi,
+                                          f16x8 (&lo)[4], f16x8 (&vdat)[4], uint2 magic, f16x4 &khi,
                                           f16x4 &klo) {
   if (lat_fmt(FMT) == MLA_FMT_INT8) {
     const f16x2 s0 = splat_f16_bits(m.sc[rb] & 0xFFFFu), s1 = splat_f16_bits(m.sc[rb] >> 16);
@@ -1067,19 +1067,25 @@ __device__ __forceinline__ void dequant16(const Raw16<FMT> &r, const Meta16 &m, 
     }
   } else if (lat_fmt(FMT) == MLA_FMT_INT4) {
     const f16x2 s0 = splat_f16_bits(m.sc[rb] & 0xFFFFu), s1 = splat_f16_bits(m.sc[rb] >> 16);
-    const f16x2 bias = {(_Float16)1024.0f, (_Float16)1024.0f};
-    // (x & 0x000F000F) | magic as one bit-field insert: magic (the fp16
-    // exponent bits of 1024 in both halves) sits in a register the compiler
-    // cannot see through, so the pattern stays a v_bfi_b32
-    const auto nib = [magic](uint32_t x) { return (x & 0x000F000Fu) | (magic & ~0x000F000Fu); };
+    const f16x2 bias0 = {(_Float16)1024.0f, (_Float16)1024.0f};
+    const f16x2 bias1 = {(_Float16)64.0f, (_Float16)64.0f};
+    // A nibble q in bits 0..3 of a half-word under the exponent bits of 1024
+    // reads as the fp16 1024 + q; in bits 4..7 under those of 64, as 64 + q
+    // (the mantissa's unit there is 1/16). So both lower nibbles of each
+    // half-word come out without a shift, and the upper two after one shift
+    // by 8. (x & mask) | magic is one bit-field insert: the magics sit in
+    // registers the compiler cannot see through, so the pattern stays one
+    // instruction.
+    const auto nib0 = [magic](uint32_t x) { return (x & 0x000F000Fu) | (magic.x & ~0x000F000Fu); };
+    const auto nib1 = [magic](uint32_t x) { return (x & 0x00F000F0u) | (magic.y & ~0x00F000F0u); };
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const uint32_t w = r.lat[rb][0][kk];
+      const uint32_t w = r.lat[rb][0][kk], w8 = w >> 8;
       const f16x2 s2 = kk < 2 ? s0 : s1;
-      const f16x2 q04 = bitcast<f16x2>(nib(w)) - bias;
-      const f16x2 q15 = bitcast<f16x2>(nib(w >> 4)) - bias;
-      const f16x2 q26 = bitcast<f16x2>(nib(w >> 8)) - bias;
-      const f16x2 q37 = bitcast<f16x2>(nib(w >> 12)) - bias;
+      const f16x2 q04 = bitcast<f16x2>(nib0(w)) - bias0;
+      const f16x2 q15 = bitcast<f16x2>(nib1(w)) - bias1;
+      const f16x2 q26 = bitcast<f16x2>(nib0(w8)) - bias0;
+      const f16x2 q37 = bitcast<f16x2>(nib1(w8)) - bias1;
       f16x2 h04, l04, h15, l15, h26, l26, h37, l37;
       scale_split(q04, s2, h04, l04);
       scale_split(q15, s2, h15, l15);
@@ -1355,8 +1361,13 @@ void split16_kernel(SplitArgs a) {
   }
 
   _Float16 *vblk = wblk + w * kWBlk;  // [32][kVRow] C_hi of this wave's channels
-  uint32_t magic = 0;  // INT4: 0x64006400 in a VGPR, opaque to the optimizer
-  if constexpr (kZp) asm("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+  // INT4: the fp16 exponent bits of 1024 and of 64 in both halves, in VGPRs
+  // opaque to the optimizer (see dequant16)
+  uint2 magic = {0u, 0u};
+  if constexpr (kZp) {
+    asm("v_mov_b32 %0, 0x64006400" : "=v"(magic.x));
+    asm("v_mov_b32 %0, 0x54005400" : "=v"(magic.y));
+  }
 
   f32x4 acc[8];
 #pragma unroll
@@ -1763,7 +1774,7 @@ void wide_kernel(SplitArgs a) {
     for (int rb = 0; rb < 2; ++rb) {
       f16x8 hi[4], lo[4], vdat[4];
       f16x4 khi, klo;
-      dequant16<FMT>(raw, mt, rb, hi, lo, vdat, 0u, khi, klo);
+      dequant16<FMT>(raw, mt, rb, hi, lo, vdat, uint2{0u, 0u}, khi, klo);
       vstore16<FMT>(vblk, rb, g, i, vdat, mt);
       const _Float16 z0 = (_Float16)0.0f;
       const f16x8 akh = {khi.x, khi.y, khi.z, khi.w, z0, z0, z0, z0};
