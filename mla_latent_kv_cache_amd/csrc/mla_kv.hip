@@ -419,6 +419,12 @@ __global__ __launch_bounds__(128) void append_step_kernel(AppendArgs a) {
 constexpr int kAbsorbBT = 64;              // batch rows per absorb block (four MFMA column blocks)
 constexpr int kAbsorbCB = 128;             // latent channels per absorb block, 32 per wave
 constexpr int kAbsorbWRow = kAbsorbCB + 16;  // bf16 per LDS row of the staged W_UK tile (see below)
+// fp16 per LDS row of the staged records: 128 hi, 128 lo, 8 + 8 group sums, and
+// 8 of padding (rows 35 x 16 bytes apart, so the 16 rows of one store fall on
+// different banks)
+constexpr int kAbsorbORow = 2 * kAbsorbCB + 16 + 8;
+static_assert(kAbsorbBT * kAbsorbORow <= kNope * kAbsorbWRow, "the record stage fits in the W_UK tile's LDS");
+static_assert(kAbsorbCB == 128, "34 record pieces of 16 bytes per row (16 + 16 + 1 + 1), as the copy-out assumes");
 
 // Per (sequence, head) record of absorbed queries, in fp16, each value v kept
 // as hi = fp16(v) and lo = fp16(v - hi), so that hi + lo carries ~22 bits:
@@ -503,27 +509,34 @@ __device__ __forceinline__ void absorb_block(const uint16_t *q_nope, const uint1
     *(u32x4 *)(wt + row * kAbsorbWRow + 8 * c8) = wl[j];
   }
   __syncthreads();
+  // lane (i, g) of k-step kk of column block cblk: column 32w + 16cblk + i,
+  // rows 32kk + 8g .. +7 (two transposed reads of four rows each)
+  bf16x8 wa[2][kNope / 32];
 #pragma unroll
-  for (int cblk = 0; cblk < 2; ++cblk) {
-    // lane (i, g) of k-step kk: column 32w + 16cblk + i, rows 32kk + 8g .. +7
-    // (two transposed reads of four rows each)
-    bf16x8 wa[kNope / 32];
+  for (int cblk = 0; cblk < 2; ++cblk)
 #pragma unroll
     for (int kk = 0; kk < kNope / 32; ++kk) {
       const uint16_t *p = wt + (32 * kk + 8 * g + (i >> 2)) * kAbsorbWRow + 32 * w + 16 * cblk + 4 * (i & 3);
       const i16x4 r0 = lds_read_tr16_i16(p), r1 = lds_read_tr16_i16(p + 4 * kAbsorbWRow);
-      wa[kk] = bitcast<bf16x8>(i16x8{r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w});
+      wa[cblk][kk] = bitcast<bf16x8>(i16x8{r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w});
     }
-    const int c = cb * kAbsorbCB + 32 * w + 16 * cblk + 4 * g;  // this lane's 4 output channels
+  // Every wave holds its W_UK operands: the tile's LDS now stages the block's
+  // records (row r: the 128 hi, the 128 lo, the 8 group-sum hi, the 8 lo), so
+  // that they leave in whole 16-byte pieces of contiguous record bytes instead
+  // of 8-byte pieces of 16 different records per store.
+  __syncthreads();
+  _Float16 *srec = (_Float16 *)wt;
+#pragma unroll
+  for (int cblk = 0; cblk < 2; ++cblk) {
+    const int cl = 32 * w + 16 * cblk + 4 * g;  // this lane's 4 output channels in the block
 #pragma unroll
     for (int bb = 0; bb < kBB; ++bb) {
       if (b0 + 16 * bb >= B) break;  // uniform
-      const int b = b0 + 16 * bb + i;
       f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < kNope / 32; ++kk)
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[kk], bitcast<bf16x8>(qv[bb][kk]), d, 0, 0, 0);
-      // lane (i, g) holds channels c .. c+3 of batch row b
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[cblk][kk], bitcast<bf16x8>(qv[bb][kk]), d, 0, 0, 0);
+      // lane (i, g) holds channels cl .. cl+3 of batch row b0 + 16bb + i
       f16x4 vh, vl;
       float gsum = 0.0f;
 #pragma unroll
@@ -536,13 +549,24 @@ __device__ __forceinline__ void absorb_block(const uint16_t *q_nope, const uint1
       // the column block's 16 channels are one latent group: add the four lane groups
       gsum += __shfl_xor(gsum, 16);
       gsum += __shfl_xor(gsum, 32);
-      if (b < B) {
-        _Float16 *rec = qa + ((int64_t)b * H + h) * kQRec;
-        *(f16x4 *)(rec + kQHi + c) = vh;
-        *(f16x4 *)(rec + kQLo + c) = vl;
-        if (g == 0) split_store(rec + kQSumHi + c / 16, rec + kQSumLo + c / 16, gsum);
-      }
+      _Float16 *srow = srec + (16 * bb + i) * kAbsorbORow;
+      *(f16x4 *)(srow + cl) = vh;
+      *(f16x4 *)(srow + kAbsorbCB + cl) = vl;
+      if (g == 0) split_store(srow + 2 * kAbsorbCB + 2 * w + cblk, srow + 2 * kAbsorbCB + 8 + 2 * w + cblk, gsum);
     }
+  }
+  __syncthreads();
+  // 34 pieces of 16 bytes per row: 16 of hi, 16 of lo, the sums' hi and lo
+  const int nrows = min(kAbsorbBT, B - b0);
+  for (int k = tid; k < nrows * 34; k += 256) {
+    const int row = k / 34, part = k - 34 * row;
+    const u32x4 v = *(const u32x4 *)(srec + row * kAbsorbORow + 8 * part);
+    _Float16 *rec = qa + ((int64_t)(b0 + row) * H + h) * kQRec;
+    const int off = part < 16   ? kQHi + cb * kAbsorbCB + 8 * part
+                    : part < 32 ? kQLo + cb * kAbsorbCB + 8 * (part - 16)
+                    : part == 32 ? kQSumHi + cb * (kAbsorbCB / 16)
+                                 : kQSumLo + cb * (kAbsorbCB / 16);
+    *(u32x4 *)(rec + off) = v;
   }
   if (pe) {
 #pragma unroll
@@ -1519,16 +1543,19 @@ void split16_kernel(SplitArgs a) {
       for (int n = 0; n < 8; ++n) acc[n] *= alpha;
       if (kZp) accz *= alpha;
     }
-    float psum = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      p8[r] = __builtin_amdgcn_exp2f(p8[r] - m_run);
-      psum += p8[r];
-    }
-    l_run += psum;
+    for (int r = 0; r < 8; ++r) p8[r] = __builtin_amdgcn_exp2f(p8[r] - m_run);
     f16x8 pb;
 #pragma unroll
     for (int r = 0; r < 8; ++r) pb[r] = (_Float16)p8[r];
+    // The normalizer sums the same fp16 weights the value products take (two
+    // per dot instruction, fp32 accumulation), so the output is a weighted
+    // mean of the value rows with exactly those weights.
+    {
+      const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) l_run = __builtin_amdgcn_fdot2(f16x2{pb[2 * r], pb[2 * r + 1]}, one2, l_run, false);
+    }
 
     __builtin_amdgcn_s_setprio(2);
     // values of this wave's 128 channels (its own block, no barrier needed)
