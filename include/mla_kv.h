@@ -189,7 +189,8 @@ int mla_decode_auto_splits(const mla_cache *cache, int32_t heads, int32_t *num_s
  *                   lengths; the partial phase runs each run once per slice
  *                   of 16 heads (W * heads / 16 workgroups). Auto: about
  *                   three workgroups per CU, at least 4 tiles per run for
- *                   full sequences.
+ *                   full sequences (up to 8 runs per sequence of 1 tile or
+ *                   more where the capacity holds fewer than 32 tiles).
  *   workspace       device scratch of at least mla_decode_workspace_bytes;
  *                   its contents on entry do not matter
  *   out      fp32 [batch][heads][128]

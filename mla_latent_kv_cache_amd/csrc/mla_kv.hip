@@ -76,6 +76,7 @@ constexpr int kWaves = 4;                  // waves per split workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kMaxSplits = 4096;
 constexpr int kAutoMinTiles = 4;           // fewest 32-token tiles per range of the automatic plan (full sequences)
+constexpr int kAutoShortRuns = 8;          // ranges per sequence the automatic plan allows a short cache
 constexpr int kWgPerCu = 3;                // resident partial workgroups per CU
 #ifndef MLA_COMBINE_MFMA
 #define MLA_COMBINE_MFMA 1
@@ -2486,7 +2487,12 @@ int auto_splits(const mla_cache *c, int heads, int layers, int *out) {
   // least kAutoMinTiles tiles per range when every sequence is full.
   int64_t ns = use_wide(c->format, heads) ? (int64_t)kWideWgPerCu * cus / ((int64_t)c->batch * (heads / kWideHeads))
                                : (int64_t)kWgPerCu * cus / ((int64_t)c->batch * (heads / 16));
-  const int64_t by_len = ((int64_t)c->capacity * layers + kT16 * kAutoMinTiles - 1) / (kT16 * kAutoMinTiles);
+  // Short caches (under kAutoShortRuns * kAutoMinTiles tiles) may still take
+  // kAutoShortRuns runs of a tile or more: there the launch is latency-bound
+  // and the few records merge at once.
+  const int64_t cap_tiles = ((int64_t)c->capacity * layers + kT16 - 1) / kT16;
+  int64_t by_len = (cap_tiles + kAutoMinTiles - 1) / kAutoMinTiles;
+  if (by_len < kAutoShortRuns) by_len = cap_tiles < kAutoShortRuns ? cap_tiles : kAutoShortRuns;
   if (ns > by_len) ns = by_len;
   if (ns < 1) ns = 1;
   if (ns > kMaxSplits) ns = kMaxSplits;

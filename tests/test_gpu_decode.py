@@ -147,11 +147,17 @@ def test_balanced_plan_runs(fmt):
 def test_auto_split_rule_16_heads():
     # 16 heads, num_splits = 0: floor(3 * CUs / batch) workgroups per sequence
     # on average (three resident per CU), at most ceil(capacity / 128) (4 tiles
-    # each for full sequences), at least 1
+    # each for full sequences) or, for a capacity under 32 tiles, at most
+    # min(8, its tiles), at least 1
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    for B, cap in ((1, 256), (8, 4160), (32, 2048), (64, 4096), (300, 64), (1000, 64)):
+    for B, cap in ((1, 256), (1, 320), (1, 31), (1, 1000), (1, 1100), (8, 4160), (32, 2048), (64, 4096),
+                   (300, 64), (1000, 64)):
         cache = LatentCache("int8", 1, B, cap, device=torch.device("cuda"))
-        want = max(1, min(3 * cus // B, -(-cap // 128)))
+        tiles = -(-cap // 32)
+        by_len = -(-tiles // 4)
+        if by_len < 8:
+            by_len = min(tiles, 8)
+        want = max(1, min(3 * cus // B, by_len))
         assert cache.auto_splits(16) == want, (B, cap)
 
 
