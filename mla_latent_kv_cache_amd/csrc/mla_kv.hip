@@ -2076,6 +2076,132 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const float *ws_
   if (bo < B) out[((int64_t)bo * H + h) * kVDim + e] = v;
 }
 
+// The same merge and projection for small grids, one sequence per block
+// (grid (H, B, layers), 512 threads): every one of the eight waves takes
+// records w, w + 8, ... (kReduce1Recs of them per round of loads, so a
+// sequence of up to 48 records is read in one round), all 512 channels of
+// each (8 per lane), and merges them with its own running maximum; the waves'
+// merges then meet in LDS under the block's maximum. The block's W_UV rows
+// are requested first, so they arrive during the merge. Used where the grid
+// has at most one block per CU: there the latency of the rounds of loads is
+// the launch's time, and one sequence per block spreads the records over
+// more CUs (each block reads its head's W_UV, from L2 after the first).
+constexpr int kReduce1Recs = 6;
+constexpr int kReduce1MaxBlocks = 256;
+
+__global__ __launch_bounds__(kReduceThreads) void reduce1_kernel(const float *ws_m, const float *ws_l,
+                                                                 const float *ws_acc, const int32_t *rec_tab,
+                                                                 const uint16_t *w_uv, int B, int H, float *out) {
+  __shared__ __attribute__((aligned(16))) float olat[kReduceThreads / 64][kLatent];
+  __shared__ float orow[kLatent];
+  __shared__ float red[kReduceCS][kVDim];
+  __shared__ float wm[kReduceThreads / 64], wls[kReduceThreads / 64];
+  constexpr int NW = kReduceThreads / 64;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int64_t layer_seq = (int64_t)blockIdx.z * B;
+  rec_tab += 2 * layer_seq;
+  out += layer_seq * H * kVDim;
+  w_uv += ((int64_t)blockIdx.z * H + h) * kLatent * kVDim;
+  const int tid = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  // this thread's W_UV rows (8 output columns of 16 latent rows)
+  const int eg = tid & 15, cs = tid >> 4;
+  const uint16_t *w = w_uv + ((int64_t)cs * 16) * kVDim + 8 * eg;
+  u32x4 wr[16];
+#pragma unroll
+  for (int cc = 0; cc < 16; ++cc) wr[cc] = *(const u32x4 *)(w + cc * kVDim);
+
+  const int first = __builtin_amdgcn_readfirstlane(rec_tab[2 * b]);
+  const int count = __builtin_amdgcn_readfirstlane(rec_tab[2 * b + 1]);
+  const int64_t base = (int64_t)first * H + h;
+  float M = -INFINITY, Ls = 0.0f;
+  f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+  for (int r0 = 0; r0 < count; r0 += NW * kReduce1Recs) {
+    f32x4 a[kReduce1Recs][2];
+    float ms[kReduce1Recs], ls[kReduce1Recs];
+#pragma unroll
+    for (int k = 0; k < kReduce1Recs; ++k) {
+      const int sidx = r0 + wv + NW * k;  // uniform across the wave
+      const int64_t rec = base + (int64_t)min(sidx, count - 1) * H;
+      ls[k] = sidx < count ? ws_l[rec] : 0.0f;
+      ms[k] = ws_m[rec];
+      if (ls[k] > 0.0f) {
+        const f32x4 *src = (const f32x4 *)(ws_acc + rec * kLatent + 8 * lane);
+        a[k][0] = src[0];
+        a[k][1] = src[1];
+      }
+    }
+    float mb = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kReduce1Recs; ++k)
+      if (ls[k] > 0.0f) mb = fmaxf(mb, ms[k]);
+    if (mb == -INFINITY) continue;  // no record of the round holds tokens (uniform)
+    const float mn = fmaxf(M, mb);
+    const float alpha = __builtin_amdgcn_exp2f(M - mn);  // 0 while nothing is merged
+    Ls *= alpha;
+    o0 *= alpha;
+    o1 *= alpha;
+    M = mn;
+#pragma unroll
+    for (int k = 0; k < kReduce1Recs; ++k) {
+      if (ls[k] > 0.0f) {
+        const float wgt = __builtin_amdgcn_exp2f(ms[k] - M);
+        Ls += wgt * ls[k];
+        o0 += wgt * a[k][0];
+        o1 += wgt * a[k][1];
+      }
+    }
+  }
+  if (lane == 0) {
+    wm[wv] = M;
+    wls[wv] = Ls;
+  }
+  __syncthreads();
+  float Mall = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) Mall = fmaxf(Mall, wm[v]);
+  const float sc = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - Mall);
+  *(f32x4 *)&olat[wv][8 * lane] = o0 * sc;
+  *(f32x4 *)&olat[wv][8 * lane + 4] = o1 * sc;
+  __syncthreads();
+  float Lall = 0.0f;
+#pragma unroll
+  for (int v = 0; v < NW; ++v)
+    if (wm[v] != -INFINITY) Lall += wls[v] * __builtin_amdgcn_exp2f(wm[v] - Mall);
+  const float inv = Lall > 0.0f ? 1.0f / Lall : 0.0f;
+  {
+    float x = 0.0f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) x += olat[v][tid];
+    orow[tid] = x * inv;
+  }
+  __syncthreads();
+  float acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
+#pragma unroll
+  for (int cc = 0; cc < 16; ++cc) {
+    const float ov = orow[cs * 16 + cc];
+    const u32x4 wq = wr[cc];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc[2 * k] += ov * bf16_bits_to_f32(wq[k] & 0xFFFFu);
+      acc[2 * k + 1] += ov * bf16_bits_to_f32(wq[k] >> 16);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) red[cs][8 * eg + k] = acc[k];
+  __syncthreads();
+  if (tid < kVDim) {
+    float v = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kReduceCS; ++q) v += red[q][tid];
+    out[((int64_t)b * H + h) * kVDim + tid] = v;
+  }
+}
+static_assert(kReduceThreads == kLatent && 64 * 8 == kLatent,
+              "one latent channel per thread in the sum over the waves, 8 per lane in the merge");
+
 // ------------------------------------------------------------------ combine
 
 // Merge of the partial records and projection through W_UV. Grid
@@ -2125,19 +2251,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *ws_m, const f
   w_uv += ((int64_t)blockIdx.z * H + h) * kLatent * kVDim;
   const int tid = threadIdx.x;
   const int wv = tid >> 6, lane = tid & 63, g = lane >> 4, i = lane & 15;
-  // W_UV rows ch0 .. ch0 + 127 (256 bytes each): 8 x 16 bytes per thread;
-  // the first chunk is in flight during the merge, each next one during the
-  // previous chunk's products
+  // W_UV rows ch0 .. ch0 + 127 of each chunk (256 bytes each): 8 x 16 bytes
+  // per thread and chunk; all four chunks are requested here, so the head's
+  // W_UV arrives during the merge in one round of loads
   constexpr int kWL = kCombChunk * kVDim / 8 / 256;
-  u32x4 wl[kWL];
-  auto load_w = [&](int ch0) {
+  constexpr int kNChunk = kLatent / kCombChunk;
+  u32x4 wl[kNChunk][kWL];
+#pragma unroll
+  for (int ck = 0; ck < kNChunk; ++ck)
 #pragma unroll
     for (int jj = 0; jj < kWL; ++jj) {
       const int k = tid + 256 * jj, row = k >> 4, c8 = k & 15;
-      wl[jj] = *(const u32x4 *)(w_uv + (int64_t)(ch0 + row) * kVDim + 8 * c8);
+      wl[ck][jj] = *(const u32x4 *)(w_uv + (int64_t)(kCombChunk * ck + row) * kVDim + 8 * c8);
     }
-  };
-  load_w(0);
 
   // ---- 1. merge
   {
@@ -2209,15 +2335,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *ws_m, const f
 
   // ---- 2. projection
   f32x4 d[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-  for (int ch0 = 0; ch0 < kLatent; ch0 += kCombChunk) {
+#pragma unroll
+  for (int ck = 0; ck < kNChunk; ++ck) {
+    const int ch0 = kCombChunk * ck;
     __syncthreads();  // the previous chunk's reads of wt (and, the first time, the merge's stores) are done
 #pragma unroll
     for (int jj = 0; jj < kWL; ++jj) {
       const int k = tid + 256 * jj, row = k >> 4, c8 = k & 15;
-      *(u32x4 *)(wt + row * kCombWRow + 8 * c8) = wl[jj];
+      *(u32x4 *)(wt + row * kCombWRow + 8 * c8) = wl[ck][jj];
     }
-    lds_stores_done();  // the registers of wl are reloaded next
-    if (ch0 + kCombChunk < kLatent) load_w(ch0 + kCombChunk);
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < kCombChunk / 32; ++kk) {
@@ -2621,6 +2747,10 @@ int run_combine(const mla_cache *cache, const DecodePlan &pl, const void *w_uv, 
   const int64_t big = (int64_t)heads * ((B + 15) / 16) * pl.layers;
   if (kCombineMfma && big >= kCombBigGrid)
     hipLaunchKernelGGL(combine_kernel<16>, dim3(heads, (B + 15) / 16, pl.layers), dim3(256), 0, s,
+                       (const float *)(ws + pl.wl.m), (const float *)(ws + pl.wl.l), (const float *)(ws + pl.wl.acc),
+                       (const int32_t *)(ws + pl.wl.tab), (const uint16_t *)w_uv, B, heads, out);
+  else if ((int64_t)heads * B * pl.layers <= kReduce1MaxBlocks)
+    hipLaunchKernelGGL(reduce1_kernel, dim3(heads, B, pl.layers), dim3(kReduceThreads), 0, s,
                        (const float *)(ws + pl.wl.m), (const float *)(ws + pl.wl.l), (const float *)(ws + pl.wl.acc),
                        (const int32_t *)(ws + pl.wl.tab), (const uint16_t *)w_uv, B, heads, out);
   else
