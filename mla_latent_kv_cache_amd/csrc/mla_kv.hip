@@ -2213,7 +2213,8 @@ static_assert(kReduceThreads == kLatent && 64 * 8 == kLatent,
 // reduce_kernel, whose two waves per sequence keep more record loads in
 // flight (measured: 5-9 µs against 6-13 µs for one layer of 1 to 64
 // sequences, 49 against 62 µs at 128 heads; 36 µs for both forms over 27
-// layers of 64 sequences, where reduce_kernel alone took 89 µs).
+// layers of 64 sequences, where reduce_kernel alone took 89 µs), and grids of
+// at most 256 (head, sequence) pairs reduce1_kernel.
 //   1. Merge. TPR = 256 / R threads per sequence, each with CPT = 512 / TPR
 //      of the latent channels. The row's records (first record and count from
 //      the partial kernel's table) are weighted by
@@ -2227,7 +2228,8 @@ static_assert(kReduceThreads == kLatent && 64 * 8 == kLatent,
 //   2. Projection on 16x16x32 bf16 MFMA (rows past R are zero), 128 latent
 //      channels of W_UV[h] at a time staged in LDS and read transposed
 //      (ds_read_b64_tr_b16): wave w computes output columns 32w .. 32w + 31 as
-//      o_hi W + o_lo W.
+//      o_hi W + o_lo W. The whole of W_UV[h] is requested into registers at
+//      the start, so it arrives during the merge.
 constexpr int kCombChunk = 128;           // latent channels of W_UV staged at a time
 constexpr int kCombARow = kLatent + 8;    // bf16 per LDS row of o_lat (hi or lo): 16 B of padding
 constexpr int kCombWRow = kVDim + 16;     // bf16 per LDS row of the staged W_UV chunk (see absorb_block)
