@@ -221,3 +221,19 @@ def test_groups_at_the_edge_of_the_fp16_domain(fmt):
         out = cache.decode(0, qn, qp, wuk, wuv, TAU, num_splits=splits)
         torch.cuda.synchronize()
         check_all(cache, rows, qn, qp, wuk, wuv, out, fmt, f"{fmt} edge groups splits {splits}")
+
+
+@pytest.mark.parametrize("fmt", ["int8", "int4"])
+def test_small_grid_merge_across_rounds_of_records(fmt):
+    # 16 heads x 3 sequences: at most 256 (head, sequence) pairs, so the merge
+    # runs one sequence per block, eight waves taking six records each per
+    # round of loads (48 a round). Split counts on both sides of 48 records per
+    # sequence, several rounds, and an empty sequence among full ones.
+    lens = [4000, 0, 2900]
+    cache, rows, qn, qp, wuk, wuv = random_problem(fmt, len(lens), 16, lens, seed=77, cap=4096)
+    ws = cache.workspace(16, 120)
+    for splits in (40, 47, 48, 49, 60, 97, 120):
+        out = cache.decode(0, qn, qp, wuk, wuv, TAU, num_splits=splits, workspace=ws)
+        torch.cuda.synchronize()
+        check_all(cache, rows, qn, qp, wuk, wuv, out, fmt, f"{fmt} splits {splits}")
+        assert not out[1].any()  # empty sequence -> zeros
