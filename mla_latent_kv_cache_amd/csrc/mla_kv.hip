@@ -2225,19 +2225,22 @@ static_assert(kReduceThreads == kLatent && 64 * 8 == kLatent,
 //      bf16 hi/lo pair (hi = bf16(o),
 //      lo = bf16(o - hi)): the pair carries ~16 bits, and W_UV is bf16, so
 //      the products are exact in fp32. An empty sequence gives o_lat = 0.
-//   2. Projection on 16x16x32 bf16 MFMA (rows past R are zero), 128 latent
+//   2. Projection on 16x16x32 bf16 MFMA (rows past R are zero), 64 latent
 //      channels of W_UV[h] at a time staged in LDS and read transposed
 //      (ds_read_b64_tr_b16): wave w computes output columns 32w .. 32w + 31 as
-//      o_hi W + o_lo W. The whole of W_UV[h] is requested into registers at
-//      the start, so it arrives during the merge.
-constexpr int kCombChunk = 128;           // latent channels of W_UV staged at a time
+//      o_hi W + o_lo W. The first two chunks are requested before the merge,
+//      each later one two chunks ahead. With 64-row chunks the block takes
+//      52 KB of LDS and 128 VGPRs, so three blocks share a CU (47.5 -> 40.3 us
+//      for 27 layers of 64 sequences with cold caches, against 128-row chunks
+//      at two blocks per CU).
+constexpr int kCombChunk = 64;            // latent channels of W_UV staged at a time
 constexpr int kCombARow = kLatent + 8;    // bf16 per LDS row of o_lat (hi or lo): 16 B of padding
 constexpr int kCombWRow = kVDim + 16;     // bf16 per LDS row of the staged W_UV chunk (see absorb_block)
 constexpr int kCombBigGrid = 1024;        // blocks of 16 rows from which the 16-row form is used
 template <int R>
-__global__ __launch_bounds__(256) void combine_kernel(const float *ws_m, const float *ws_l, const float *ws_acc,
-                                                      const int32_t *rec_tab, const uint16_t *w_uv, int B, int H,
-                                                      float *out) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void combine_kernel(const float *ws_m, const float *ws_l, const float *ws_acc, const int32_t *rec_tab,
+                    const uint16_t *w_uv, int B, int H, float *out) {
   constexpr int TPR = 256 / R;           // merge threads per sequence
   constexpr int CPT = kLatent / TPR;     // channels per merge thread
   constexpr int NV = CPT / 4;            // 16-byte loads per record and thread
@@ -2253,19 +2256,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *ws_m, const f
   w_uv += ((int64_t)blockIdx.z * H + h) * kLatent * kVDim;
   const int tid = threadIdx.x;
   const int wv = tid >> 6, lane = tid & 63, g = lane >> 4, i = lane & 15;
-  // W_UV rows ch0 .. ch0 + 127 of each chunk (256 bytes each): 8 x 16 bytes
-  // per thread and chunk; all four chunks are requested here, so the head's
-  // W_UV arrives during the merge in one round of loads
+  // W_UV rows ch0 .. ch0 + 63 of a chunk (256 bytes each): 4 x 16 bytes per
+  // thread and chunk, two chunks in flight
   constexpr int kWL = kCombChunk * kVDim / 8 / 256;
   constexpr int kNChunk = kLatent / kCombChunk;
-  u32x4 wl[kNChunk][kWL];
-#pragma unroll
-  for (int ck = 0; ck < kNChunk; ++ck)
+  constexpr int kAhead = 2;
+  u32x4 wl[kAhead][kWL];
+  auto load_chunk = [&](int ck, int slot) {
 #pragma unroll
     for (int jj = 0; jj < kWL; ++jj) {
       const int k = tid + 256 * jj, row = k >> 4, c8 = k & 15;
-      wl[ck][jj] = *(const u32x4 *)(w_uv + (int64_t)(kCombChunk * ck + row) * kVDim + 8 * c8);
+      wl[slot][jj] = *(const u32x4 *)(w_uv + (int64_t)(kCombChunk * ck + row) * kVDim + 8 * c8);
     }
+  };
+#pragma unroll
+  for (int ck = 0; ck < kAhead; ++ck) load_chunk(ck, ck);
 
   // ---- 1. merge
   {
@@ -2344,8 +2349,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *ws_m, const f
 #pragma unroll
     for (int jj = 0; jj < kWL; ++jj) {
       const int k = tid + 256 * jj, row = k >> 4, c8 = k & 15;
-      *(u32x4 *)(wt + row * kCombWRow + 8 * c8) = wl[ck][jj];
+      *(u32x4 *)(wt + row * kCombWRow + 8 * c8) = wl[ck % kAhead][jj];
     }
+    lds_stores_done();
+    if (ck + kAhead < kNChunk) load_chunk(ck + kAhead, ck % kAhead);
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < kCombChunk / 32; ++kk) {
