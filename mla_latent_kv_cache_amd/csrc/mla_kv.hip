@@ -903,7 +903,6 @@ template <int FMT> struct Off16 {
 template <int FMT>
 __device__ __forceinline__ Off16<FMT> offsets16(int w, int lane) {
   using AX = Aux16<FMT>;
-  const int g = lane >> 4, i = lane & 15;
   Off16<FMT> o;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
