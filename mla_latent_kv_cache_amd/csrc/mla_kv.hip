@@ -481,16 +481,26 @@ __device__ __forceinline__ void absorb_block(const uint16_t *q_nope, const uint1
     const int k = tid + 256 * j, row = k / kCPR, c8 = k % kCPR;
     wl[j] = *(const u32x4 *)(wsrc + (int64_t)row * kLatent + 8 * c8);
   }
-  // every query operand of the block, in flight together with the tile
-  // (rows past the batch repeat its last row and are not stored)
-  constexpr int kBB = kAbsorbBT / 16;
-  u32x4 qv[kBB][kNope / 32];
-#pragma unroll
-  for (int bb = 0; bb < kBB; ++bb) {
-    const int b = min(b0 + 16 * bb + i, B - 1);
+  // Work split: the block's rows form nbb groups of 16; each group is served by
+  // wpb waves (4 / nbb rounded up to a power of two), each of which takes
+  // kCBk / wpb of the 16-channel column blocks. A full block (64 rows) gives
+  // each wave one row group and all 128 channels, so every query row is loaded
+  // once; a small batch keeps all four waves busy on its rows.
+  constexpr int kCBk = kAbsorbCB / 16;
+  const int nbb = (min(kAbsorbBT, B - b0) + 15) >> 4;  // 1 .. 4
+  const int wpb = nbb == 1 ? 4 : nbb == 2 ? 2 : 1;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int bbw = wu / wpb;                           // this wave's row group
+  const int c0 = (wu % wpb) * (kCBk / wpb), c1 = c0 + kCBk / wpb;  // its column blocks
+  const bool rows_live = bbw < nbb;                   // uniform
+  // the query operands of this wave's 16 batch rows (rows past the batch
+  // repeat its last row and are not stored), in flight together with the tile
+  u32x4 qv[kNope / 32];
+  {
+    const int b = min(b0 + 16 * bbw + i, B - 1);
     const uint16_t *qrow = q_nope + ((int64_t)b * H + h) * kNope + 8 * g;
 #pragma unroll
-    for (int kk = 0; kk < kNope / 32; ++kk) qv[bb][kk] = *(const u32x4 *)(qrow + 32 * kk);
+    for (int kk = 0; kk < kNope / 32; ++kk) qv[kk] = *(const u32x4 *)(qrow + 32 * kk);
   }
   // blocks of channel block 0 also scale the RoPE part: 8 values per 16-byte
   // chunk, 64 rows of 8 chunks
@@ -510,50 +520,52 @@ __device__ __forceinline__ void absorb_block(const uint16_t *q_nope, const uint1
     *(u32x4 *)(wt + row * kAbsorbWRow + 8 * c8) = wl[j];
   }
   __syncthreads();
-  // lane (i, g) of k-step kk of column block cblk: column 32w + 16cblk + i,
-  // rows 32kk + 8g .. +7 (two transposed reads of four rows each)
-  bf16x8 wa[2][kNope / 32];
+  // The wave's column blocks, one 16-channel block (one latent group) at a
+  // time: lane (i, g) of k-step kk takes column 16 cbk + i, rows 32kk + 8g ..
+  // +7 of the tile (two transposed reads of four rows each), and ends with
+  // channels 16 cbk + 4g .. +3 of row 16 bbw + i. The results wait in
+  // registers until every wave has read the tile; its LDS then stages the
+  // block's records (row r: the 128 hi, the 128 lo, the 8 group-sum hi, the 8
+  // lo), so that they leave in whole 16-byte pieces of contiguous record bytes
+  // instead of 8-byte pieces of 16 different records per store.
+  f16x4 vh[kCBk], vl[kCBk];
+  float gs[kCBk];
+  if (rows_live) {
 #pragma unroll
-  for (int cblk = 0; cblk < 2; ++cblk)
-#pragma unroll
-    for (int kk = 0; kk < kNope / 32; ++kk) {
-      const uint16_t *p = wt + (32 * kk + 8 * g + (i >> 2)) * kAbsorbWRow + 32 * w + 16 * cblk + 4 * (i & 3);
-      const i16x4 r0 = lds_read_tr16_i16(p), r1 = lds_read_tr16_i16(p + 4 * kAbsorbWRow);
-      wa[cblk][kk] = bitcast<bf16x8>(i16x8{r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w});
-    }
-  // Every wave holds its W_UK operands: the tile's LDS now stages the block's
-  // records (row r: the 128 hi, the 128 lo, the 8 group-sum hi, the 8 lo), so
-  // that they leave in whole 16-byte pieces of contiguous record bytes instead
-  // of 8-byte pieces of 16 different records per store.
-  __syncthreads();
-  _Float16 *srec = (_Float16 *)wt;
-#pragma unroll
-  for (int cblk = 0; cblk < 2; ++cblk) {
-    const int cl = 32 * w + 16 * cblk + 4 * g;  // this lane's 4 output channels in the block
-#pragma unroll
-    for (int bb = 0; bb < kBB; ++bb) {
-      if (b0 + 16 * bb >= B) break;  // uniform
+    for (int cbk = 0; cbk < kCBk; ++cbk) {
+      if (cbk < c0 || cbk >= c1) continue;  // uniform
       f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < kNope / 32; ++kk)
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[cblk][kk], bitcast<bf16x8>(qv[bb][kk]), d, 0, 0, 0);
-      // lane (i, g) holds channels cl .. cl+3 of batch row b0 + 16bb + i
-      f16x4 vh, vl;
+      for (int kk = 0; kk < kNope / 32; ++kk) {
+        const uint16_t *p = wt + (32 * kk + 8 * g + (i >> 2)) * kAbsorbWRow + 16 * cbk + 4 * (i & 3);
+        const i16x4 r0 = lds_read_tr16_i16(p), r1 = lds_read_tr16_i16(p + 4 * kAbsorbWRow);
+        const bf16x8 wa = bitcast<bf16x8>(i16x8{r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w});
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, bitcast<bf16x8>(qv[kk]), d, 0, 0, 0);
+      }
       float gsum = 0.0f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float v = d[r] * qs;
-        vh[r] = (_Float16)v;
-        vl[r] = (_Float16)(v - (float)vh[r]);
+        vh[cbk][r] = (_Float16)v;
+        vl[cbk][r] = (_Float16)(v - (float)vh[cbk][r]);
         gsum += v;
       }
       // the column block's 16 channels are one latent group: add the four lane groups
       gsum += __shfl_xor(gsum, 16);
       gsum += __shfl_xor(gsum, 32);
-      _Float16 *srow = srec + (16 * bb + i) * kAbsorbORow;
-      *(f16x4 *)(srow + cl) = vh;
-      *(f16x4 *)(srow + kAbsorbCB + cl) = vl;
-      if (g == 0) split_store(srow + 2 * kAbsorbCB + 2 * w + cblk, srow + 2 * kAbsorbCB + 8 + 2 * w + cblk, gsum);
+      gs[cbk] = gsum;
+    }
+  }
+  __syncthreads();  // every wave has read the W_UK tile
+  _Float16 *srec = (_Float16 *)wt;
+  if (rows_live) {
+    _Float16 *srow = srec + (16 * bbw + i) * kAbsorbORow;
+#pragma unroll
+    for (int cbk = 0; cbk < kCBk; ++cbk) {
+      if (cbk < c0 || cbk >= c1) continue;  // uniform
+      *(f16x4 *)(srow + 16 * cbk + 4 * g) = vh[cbk];
+      *(f16x4 *)(srow + kAbsorbCB + 16 * cbk + 4 * g) = vl[cbk];
+      if (g == 0) split_store(srow + 2 * kAbsorbCB + cbk, srow + 2 * kAbsorbCB + 8 + cbk, gs[cbk]);
     }
   }
   __syncthreads();
