@@ -443,10 +443,23 @@ __device__ __forceinline__ i16x4 lds_read_tr16_i16(const uint16_t *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(p));
 }
 
+// v as an fp16 pair: hi = fp16(v), lo = fp16(v - hi). v passes through an
+// empty asm first, so that both uses of hi round this very fp32 value: the
+// compiler may otherwise fold the product that made v into a mixed-precision
+// fma that rounds to fp16 once (v_fma_mixlo_f16) for one use and keep the fp32
+// product for the other, and in the rare cases where the two roundings differ
+// lo then carries the wrong sign and hi + lo is off by one fp16 ulp of hi.
+__device__ __forceinline__ void split_f16(float v, _Float16 &hi, _Float16 &lo) {
+  asm volatile("" : "+v"(v));
+  hi = (_Float16)v;
+  lo = (_Float16)(v - (float)hi);
+}
+
 __device__ __forceinline__ void split_store(_Float16 *hi, _Float16 *lo, float v) {
-  const _Float16 h = (_Float16)v;
+  _Float16 h, l;
+  split_f16(v, h, l);
   *hi = h;
-  *lo = (_Float16)(v - (float)h);
+  *lo = l;
 }
 
 // q_abs[b,h,c] = qs * sum_d q_nope[b,h,d] W_UK[h,d,c] for c < 512, and
@@ -546,8 +559,10 @@ __device__ __forceinline__ void absorb_block(const uint16_t *q_nope, const uint1
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float v = d[r] * qs;
-        vh[cbk][r] = (_Float16)v;
-        vl[cbk][r] = (_Float16)(v - (float)vh[cbk][r]);
+        _Float16 h16, l16;
+        split_f16(v, h16, l16);
+        vh[cbk][r] = h16;
+        vl[cbk][r] = l16;
         gsum += v;
       }
       // the column block's 16 channels are one latent group: add the four lane groups
@@ -590,9 +605,10 @@ __device__ __forceinline__ void absorb_block(const uint16_t *q_nope, const uint1
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint32_t bits = (qpv[j][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-          const float v = bf16_bits_to_f32(bits) * qs;
-          vh[e] = (_Float16)v;
-          vl[e] = (_Float16)(v - (float)vh[e]);
+          _Float16 h16, l16;
+          split_f16(bf16_bits_to_f32(bits) * qs, h16, l16);
+          vh[e] = h16;
+          vl[e] = l16;
         }
         _Float16 *rec = qa + ((int64_t)b * H + h) * kQRec + kLatent + 8 * (k & 7);
         *(f16x8 *)(rec + kQHi) = vh;
