@@ -700,8 +700,9 @@ def summarize_stats(name, stats_csv, out_path, cmd):
         "# the turned queries); split16_kernel<f>: the partial attention, 16 heads per workgroup (sliced:",
         "# one workgroup per 16-head slice); wide_kernel<f>: the partial attention, 32 heads per workgroup;",
         "# combine_kernel<R>: the merge of the partial records and the W_UV projection, R sequences per",
-        "# workgroup; append_kernel<f>: the prefill; stream_read_kernel: the read of a 1 GiB buffer that",
-        "# evicts the last-level cache between one-layer runs (not part of the decode).",
+        "# workgroup (reduce_kernel: 4, reduce1_kernel: one, for smaller grids); append_kernel<f>: the",
+        "# prefill; stream_read_kernel: the read of a 1 GiB buffer that evicts the last-level cache between",
+        "# one-layer runs (not part of the decode).",
         "# <f>: 0 bf16, 1 INT8, 2 INT4, 3 INT8 latent + bf16 k_pe, 4 INT4 latent + INT4 k_pe.",
         f"{'kernel':32s}{'calls':>7s}{'avg_us':>11s}{'min_us':>11s}{'max_us':>11s}{'total_ms':>11s}",
     ]
