@@ -16,7 +16,8 @@
 // Kernels, in launch order:
 //   append_kernel       quantize new bf16 rows into the cache planes
 //   seqlen_kernel       advance seq_lens after an append
-//   absorb_kernel       q_abs = scale*log2(e) * q_nope W_UK[h]  -> fp16 workspace
+//   absorb_kernel       q_abs = scale*log2(e) * q_nope W_UK[h]  -> fp16 hi/lo
+//                       records in the workspace
 //   append_step_kernel  one new token per sequence (the decode step's append)
 //   step_kernel         the fused step's first launch: absorb, turn and store
 //   split16_kernel      split-KV partial attention: each workgroup takes an
@@ -24,8 +25,16 @@
 //                       (a head slice of the query); 16-byte loads of codes,
 //                       in-register dequant to fp16, MFMA scores and value
 //                       sums, online softmax in base 2
-//   reduce_kernel       log-sum-exp merge of the splits, then o_lat W_UV[h]
+//   wide_kernel         the same for 32 heads per workgroup (BF16 and INT8
+//                       latents at 32-128 heads)
+//   combine_kernel      log-sum-exp merge of the splits for 16 sequences,
+//                       then o_lat W_UV[h] on MFMA (grids of 1024+ blocks)
+//   reduce_kernel       the same merge, W_UV on VALU, 4 sequences per block
+//   reduce1_kernel      the same, one sequence per block (small grids)
 //   get_kernel          dequantize a layer to fp32 (inspection aid)
+//   rope_table_kernel   the fused step's fp32 angle tables
+//   stream_read_kernel, mfma_rate_kernel   measurement aids (read ceiling,
+//                       matrix-unit rate)
 
 #include <hip/hip_runtime.h>
 
@@ -468,14 +477,14 @@ __device__ __forceinline__ void split_store(_Float16 *hi, _Float16 *lo, float v)
 // One block of the absorption: head h, channel block cb (128 channels), batch
 // block bz (64 rows); 256 threads. The block stages its W_UK tile (128 d x
 // 128 c, rows padded to 144 bf16 = 72 dwords, so the four rows of a
-// transposed read start 8 banks apart) in LDS once. Wave w owns channels
-// 32w .. 32w+31 of the block as two 16-channel column blocks (each one latent
-// group) and computes them for the block's batch rows as [16 c x 32 d] x
-// [32 d x 16 b] bf16 MFMAs with fp32 accumulation (bf16 products are exact in
-// fp32). The W_UK operand comes from LDS through transposed reads, 8
-// consecutive d per lane; the query operand is those same 8 d of one batch
-// row, one 16-byte load. With with_pe, the blocks of channel block 0 also
-// write the scaled RoPE part.
+// transposed read start 8 banks apart) in LDS once. The block's channels form
+// eight 16-channel column blocks (each one latent group) and its batch rows
+// groups of 16; each wave takes one row group and some of the column blocks
+// (the work split below), as [16 c x 32 d] x [32 d x 16 b] bf16 MFMAs with
+// fp32 accumulation (bf16 products are exact in fp32). The W_UK operand comes
+// from LDS through transposed reads, 8 consecutive d per lane; the query
+// operand is those same 8 d of one batch row, one 16-byte load. With with_pe,
+// the blocks of channel block 0 also write the scaled RoPE part.
 __device__ __forceinline__ void absorb_block(const uint16_t *q_nope, const uint16_t *q_pe,
                                              const uint16_t *w_uk, int B, int H, float qs, _Float16 *qa,
                                              int h, int cb, int bz, bool with_pe) {
@@ -832,8 +841,8 @@ __device__ __forceinline__ f16x4 lds_read_tr16(const _Float16 *p) {
 //           registers (INT4: P times each group's scales, as an exact fp16
 //           hi/lo pair).
 // Lane l = 16g + i: in the score, row i of each 16-token half of the tile and
-// channels 32g..32g+31 of the wave's block (two quantization groups); in the
-// accumulators, head i.
+// the 32 channels of the wave's block that lane_chan gives lane group g (two
+// quantization groups); in the accumulators, head i.
 constexpr int kT16 = 32;             // tokens per tile
 constexpr int kNpf16 = 1;            // tiles of loads in flight per wave
 // A wave's value block: 32 rows (tokens) of 128 channels, then (INT4) the 8
@@ -1215,15 +1224,17 @@ __device__ __forceinline__ void vstore16(_Float16 *vblk, int rb, int g, int i, c
 
 // Per tile, every wave:
 //   1. stages its chunks of the tile's small planes, barrier (the staging
-//      area and the partial-score slots of the previous tile are then free);
+//      area and the partial-score slots of the previous tile are then free),
+//      and issues the next tile's small-plane loads;
 //   2. reads its scales, k_pe codes and zero-points back, dequantizes its
-//      latent channels in registers, stores C_hi to its value block, and
-//      issues the MFMAs of its partial scores;
-//   3. issues all loads of the next tile (after the score sums are read back
-//      from the MFMA results);
+//      latent channels in registers, stores C_hi (INT4: the codes) to its
+//      value block, and issues the MFMAs of its partial scores;
+//   3. issues the next tile's latent loads (after the score sums are read
+//      back from the MFMA results);
 //   4. stores its partial scores, barrier, and adds the four waves' partials
 //      in a fixed order;
 //   5. online softmax and the value MFMAs of its channels.
+
 // ---- balanced plan of the 16-head partial kernel
 //
 // The batch's tiles (ceil(L_b / 32) per sequence, sequences in batch order)
