@@ -1017,6 +1017,20 @@ __device__ __forceinline__ void load16_lat(Raw16<FMT> &r, const SplitRsrc &rs, c
     }
 }
 
+// The latent loads of half-tile rb only (the 16-head kernel's early issue
+// for INT8 latents). Kept apart from load16_lat: written as a loop over
+// this function, load16_lat compiles to a schedule that spills in the
+// 32-head bf16 kernel.
+template <int FMT, int POL>
+__device__ __forceinline__ void load16_lat_half(Raw16<FMT> &r, const SplitRsrc &rs, const Off16<FMT> &o, int left,
+                                                int i, int rb) {
+#pragma unroll
+  for (int j = 0; j < Raw16<FMT>::kLat; ++j) {
+    const int off = lat_fmt(FMT) == MLA_FMT_BF16 && 16 * rb + i >= left ? kOffNone : o.lat[rb][j];
+    r.lat[rb][j] = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rs.ckv, off, 0, POL));
+  }
+}
+
 // The small planes' loads of a tile. They are issued a tile ahead of their
 // use and before the same tile's latent loads: loads return in order, so the
 // staging of the small planes never waits for latent bytes.
@@ -1229,8 +1243,8 @@ __device__ __forceinline__ void vstore16(_Float16 *vblk, int rb, int g, int i, c
 //   2. reads its scales, k_pe codes and zero-points back, dequantizes its
 //      latent channels in registers, stores C_hi (INT4: the codes) to its
 //      value block, and issues the MFMAs of its partial scores;
-//   3. issues the next tile's latent loads (after the score sums are read
-//      back from the MFMA results);
+//   3. issues the next tile's latent loads (INT8 latents: each half-tile's
+//      share in step 2, right after that half's dequantization);
 //   4. stores its partial scores, barrier, and adds the four waves' partials
 //      in a fixed order;
 //   5. online softmax and the value MFMAs of its channels.
@@ -1348,6 +1362,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgp
 void split16_kernel(SplitArgs a) {
   constexpr bool kLo = FMT != MLA_FMT_BF16;
   constexpr bool kZp = has_zero(FMT);  // INT4 latent: zero-points, and the nibble operand order
+  constexpr bool kEarly = lat_fmt(FMT) == MLA_FMT_INT8;  // the next tile's latent loads per half-tile (step 3)
   // The softmax weights are p = 2^(s - m_run) for a reference m_run that
   // moves lazily (below). kSlack: log2 of the largest weight allowed before
   // the reference moves; kHead: how far above the tile maximum it is placed.
@@ -1503,6 +1518,14 @@ void split16_kernel(SplitArgs a) {
       f16x4 khi, klo;
       f16x8 vdat[4];
       dequant16<FMT>(raw[p], mt, rb, hi, lo, vdat, magic, khi, klo);
+      if constexpr (kEarly) {
+        // this half-tile's codes are consumed: its share of the next tile's
+        // latent loads goes out now (the raw registers stay live, so the
+        // score products below read other registers)
+        __builtin_amdgcn_sched_barrier(0);
+        load16_lat_half<FMT, kPol>(raw[p], rs_next, off, t_end - r_next, i, rb);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       vstore16<FMT>(vblk, rb, g, i, vdat, mt);
       // Every score product is a 16x16x32 MFMA, so each accumulator is fed
       // by one MFMA shape only: on this GPU a 16x16x16 MFMA that takes as its
@@ -1531,15 +1554,17 @@ void split16_kernel(SplitArgs a) {
     }
 
     __builtin_amdgcn_s_setprio(0);
-    // ---- 3. the next tile's loads. They go out only after the score sums
-    // above have been read back from the MFMA results, so no matrix
-    // instruction is still pending when they are issued: a load that falls
-    // wholly past the split returns (zeros) within a few cycles, and must not
-    // land in a register that a queued MFMA of this tile has yet to read.
-    // Always issued, so the count of outstanding loads is the same on every
-    // path.
-    __builtin_amdgcn_sched_barrier(0);
-    load16_lat<FMT, kPol>(raw[p], rs_next, off, t_end - r_next, i);
+    // ---- 3. the next tile's latent loads (INT4 and BF16 latents), after
+    // this tile's score products have been issued. INT8 latents issue each
+    // half-tile's share earlier, right after that half's dequantization
+    // (above), so their loads are in flight during the score products too
+    // (1-4% on the INT8 launches); for the other formats the registers that
+    // keeps live spill in the tile loop. Always issued, so the count of
+    // outstanding loads is the same on every path.
+    if constexpr (!kEarly) {
+      __builtin_amdgcn_sched_barrier(0);
+      load16_lat<FMT, kPol>(raw[p], rs_next, off, t_end - r_next, i);
+    }
     if (paged) next_entry = page_entry(r_next + kT16);
 
     // ---- 4. partial scores of the four waves
